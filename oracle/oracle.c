@@ -1,0 +1,332 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU reference for block-sparse attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or constant with the HIP library; it is built with gcc.
+ *
+ * Sources (cited by page title and section; no listing is reproduced):
+ *  [G]  "Sparse Attention" glossary entry (Ultralytics; German, Turkish,
+ *       Vietnamese and Spanish editions carry the same content).
+ *       - section on common sparsity patterns: sliding window over previous
+ *         tokens, strided tokens, global tokens, random links (BigBird),
+ *         attention sinks; content-based DeepSeek Sparse Attention, whose
+ *         indexer scores every earlier token and keeps the 2,048 best.
+ *       - section on turning a pattern into savings: the local_plus_sinks
+ *         mask function (causal AND (q-kv <= window OR kv < sinks)), the
+ *         split of the mask into 128 x 128 blocks and the sparsity figure
+ *         defined as the share of blocks holding no allowed pair.
+ *  [B]  "Sparse transformers: how to cut the O(n^2) of attention" blog
+ *       (1gpt.online), section on how it looks in code: dense scores
+ *       q.k^T / sqrt(d), disallowed pairs set to -inf, softmax, times V;
+ *       section on the main sparsity templates (strided, fixed, sliding
+ *       window, global tokens) and on combining them.
+ *
+ * What is computed (the plain definitions; nothing is blocked or fused):
+ *  - orc_allowed: the per-pair predicate, a union of the pattern terms,
+ *    intersected with causality when requested ([G] patterns, [B] templates).
+ *  - orc_block_lists: for every (query block, key block) cell, the number of
+ *    allowed pairs inside the clipped tile; live = count > 0, full = count ==
+ *    tile size, partial otherwise; live key blocks listed in ascending order
+ *    ([G] block split and sparsity definition).
+ *  - orc_attn_rows: for each requested (batch*head, query) row, fp64 scores
+ *    over every allowed key, m = max, LSE = m + ln(sum exp(s - m)),
+ *    O = sum exp(s - LSE) v  ([B] masked attention: masking with -inf and a
+ *    softmax is the same as a softmax restricted to the allowed keys).
+ *    A row with no allowed key gives O = 0, LSE = -inf.
+ *  - orc_attn_gather_rows: the same softmax restricted to an explicit key
+ *    list (the per-query top-k set of [G] DeepSeek Sparse Attention).
+ *  - orc_indexer_scores: indexer score of query t and key s <= t as a
+ *    float32 sequential fused-multiply-add chain over the indexer dimension
+ *    (the pages give no formula; this fixed order is the reading adopted),
+ *    plus the fp64 value of the same dot product.
+ *  - orc_topk_rows: the k candidates that come first in the total order
+ *    (score descending, index ascending), emitted in ascending index order.
+ *
+ * Inputs are raw bfloat16 bit patterns (uint16); each is widened exactly.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+    int64_t causal;
+    int64_t q_offset;
+    int64_t window_left;   /* < 0: local term off */
+    int64_t window_right;
+    int64_t sinks;
+    int64_t stride;        /* <= 0: strided term off */
+    int64_t stride_phase;
+    int64_t global_tokens;
+    int64_t unit;          /* <= 0: unit-level terms off */
+    int64_t unit_window;   /* < 0: unit band off */
+    const int32_t *rand_units; /* host table [rand_rows, n_rand], -1 = empty */
+    int64_t n_rand;
+    int64_t rand_rows;
+} orc_pattern;
+
+static double bf16_to_f64(uint16_t b)
+{
+    uint32_t u = ((uint32_t)b) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static float bf16_to_f32(uint16_t b)
+{
+    uint32_t u = ((uint32_t)b) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Is the pair (query position q, key position kv) allowed?  q and kv are
+ * absolute positions (q already includes the pattern's offset). */
+int orc_allowed(const orc_pattern *p, int64_t q, int64_t kv)
+{
+    if (p->causal && kv > q)
+        return 0;
+    if (p->window_left >= 0 && q - kv <= p->window_left && kv - q <= p->window_right)
+        return 1;
+    if (kv < p->sinks)
+        return 1;
+    if (p->stride > 0 && q >= kv && (q - kv) % p->stride == p->stride_phase)
+        return 1;
+    if (q < p->global_tokens || kv < p->global_tokens)
+        return 1;
+    if (p->unit > 0) {
+        int64_t qu = q / p->unit, ku = kv / p->unit;
+        int64_t du = qu > ku ? qu - ku : ku - qu;
+        if (p->unit_window >= 0 && du <= p->unit_window)
+            return 1;
+        if (p->rand_units && p->n_rand > 0 && qu < p->rand_rows) {
+            for (int64_t r = 0; r < p->n_rand; ++r)
+                if (p->rand_units[qu * p->n_rand + r] == ku)
+                    return 1;
+        }
+    }
+    return 0;
+}
+
+/* Block lists by brute force over every pair of every cell.
+ * kv_count [nqb], kv_index [nqb, nkb] (ascending, -1 padded),
+ * kv_partial [nqb, nkb] aligned with kv_index (1 = partial, 0 = full or pad),
+ * live_pairs = total allowed pairs, cell_counts [nqb, nkb] optional. */
+void orc_block_lists(const orc_pattern *p, int64_t n_q, int64_t n_kv, int32_t bq, int32_t bk,
+                     int32_t *kv_count, int32_t *kv_index, uint8_t *kv_partial,
+                     int64_t *live_pairs, int64_t *cell_counts)
+{
+    int64_t nqb = (n_q + bq - 1) / bq, nkb = (n_kv + bk - 1) / bk;
+    int64_t total = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : total)
+    for (int64_t i = 0; i < nqb; ++i) {
+        int64_t q0 = i * bq, q1 = q0 + bq < n_q ? q0 + bq : n_q;
+        int32_t n_live = 0;
+        for (int64_t j = 0; j < nkb; ++j) {
+            int64_t k0 = j * bk, k1 = k0 + bk < n_kv ? k0 + bk : n_kv;
+            int64_t c = 0;
+            for (int64_t q = q0; q < q1; ++q)
+                for (int64_t kv = k0; kv < k1; ++kv)
+                    c += orc_allowed(p, q + p->q_offset, kv);
+            if (cell_counts)
+                cell_counts[i * nkb + j] = c;
+            total += c;
+            if (c > 0) {
+                kv_index[i * nkb + n_live] = (int32_t)j;
+                kv_partial[i * nkb + n_live] = (uint8_t)(c != (q1 - q0) * (k1 - k0));
+                ++n_live;
+            }
+        }
+        kv_count[i] = n_live;
+        for (int64_t e = n_live; e < nkb; ++e) {
+            kv_index[i * nkb + e] = -1;
+            kv_partial[i * nkb + e] = 0;
+        }
+    }
+    *live_pairs = total;
+}
+
+/* Softmax-weighted sum over an explicit key list, fp64 throughout. */
+static void attend_list(const uint16_t *qrow, const uint16_t *kbase, const uint16_t *vbase,
+                        int32_t d, double scale, const int64_t *keys, int64_t nk,
+                        double *s_buf, double *o, double *lse)
+{
+    for (int32_t c = 0; c < d; ++c)
+        o[c] = 0.0;
+    if (nk == 0) {
+        *lse = -INFINITY;
+        return;
+    }
+    double m = -INFINITY;
+    for (int64_t e = 0; e < nk; ++e) {
+        const uint16_t *krow = kbase + keys[e] * (int64_t)d;
+        double acc = 0.0;
+        for (int32_t c = 0; c < d; ++c)
+            acc += bf16_to_f64(qrow[c]) * bf16_to_f64(krow[c]);
+        s_buf[e] = acc * scale;
+        if (s_buf[e] > m)
+            m = s_buf[e];
+    }
+    double sum = 0.0;
+    for (int64_t e = 0; e < nk; ++e)
+        sum += exp(s_buf[e] - m);
+    double L = m + log(sum);
+    for (int64_t e = 0; e < nk; ++e) {
+        double w = exp(s_buf[e] - L);
+        const uint16_t *vrow = vbase + keys[e] * (int64_t)d;
+        for (int32_t c = 0; c < d; ++c)
+            o[c] += w * bf16_to_f64(vrow[c]);
+    }
+    *lse = L;
+}
+
+/* rows[r] = (b*H + h) * n_q + query_row; tensors contiguous [B, H, N, d]. */
+void orc_attn_rows(const orc_pattern *p, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                   int64_t n_q, int64_t n_kv, int32_t d, double scale, const int64_t *rows,
+                   int64_t n_rows, double *o, double *lse, int64_t *n_allowed)
+{
+#pragma omp parallel
+    {
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_kv > 0 ? n_kv : 1));
+        double *s_buf = (double *)malloc(sizeof(double) * (size_t)(n_kv > 0 ? n_kv : 1));
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < n_rows; ++r) {
+            int64_t bh = rows[r] / n_q, qi = rows[r] % n_q;
+            int64_t qpos = qi + p->q_offset;
+            int64_t nk = 0;
+            for (int64_t kv = 0; kv < n_kv; ++kv)
+                if (orc_allowed(p, qpos, kv))
+                    keys[nk++] = kv;
+            if (n_allowed)
+                n_allowed[r] = nk;
+            attend_list(q + (bh * n_q + qi) * (int64_t)d, k + bh * n_kv * (int64_t)d,
+                        v + bh * n_kv * (int64_t)d, d, scale, keys, nk, s_buf, o + r * (int64_t)d,
+                        lse + r);
+        }
+        free(keys);
+        free(s_buf);
+    }
+}
+
+/* Gather attention: idx [n_q, topk] (per query row; -1 entries are padding),
+ * shared by every (b, h) when idx_bh_stride == 0, else offset by bh * stride. */
+void orc_attn_gather_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t n_q,
+                          int64_t n_kv, int32_t d, double scale, const int32_t *idx, int32_t topk,
+                          int64_t idx_bh_stride, const int64_t *rows, int64_t n_rows, double *o,
+                          double *lse)
+{
+#pragma omp parallel
+    {
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)(topk > 0 ? topk : 1));
+        double *s_buf = (double *)malloc(sizeof(double) * (size_t)(topk > 0 ? topk : 1));
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < n_rows; ++r) {
+            int64_t bh = rows[r] / n_q, qi = rows[r] % n_q;
+            const int32_t *list = idx + bh * idx_bh_stride + qi * (int64_t)topk;
+            int64_t nk = 0;
+            for (int32_t e = 0; e < topk; ++e)
+                if (list[e] >= 0 && list[e] < n_kv)
+                    keys[nk++] = list[e];
+            attend_list(q + (bh * n_q + qi) * (int64_t)d, k + bh * n_kv * (int64_t)d,
+                        v + bh * n_kv * (int64_t)d, d, scale, keys, nk, s_buf, o + r * (int64_t)d,
+                        lse + r);
+        }
+        free(keys);
+        free(s_buf);
+    }
+}
+
+/* Indexer scores for query rows `rows` (row r has position q_offset + r) and
+ * every key s < n_kv: candidates s <= t get the fp32 FMA chain value, the
+ * others -inf.  exact (optional) gets the fp64 dot product. */
+void orc_indexer_scores(const uint16_t *qi, const uint16_t *ki, int64_t n_kv, int32_t d,
+                        int64_t q_offset, const int64_t *rows, int64_t n_rows, float *sigma,
+                        double *exact)
+{
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t t = rows[r] + q_offset;
+        const uint16_t *qr = qi + rows[r] * (int64_t)d;
+        for (int64_t s = 0; s < n_kv; ++s) {
+            float *out = sigma + r * n_kv + s;
+            if (s > t) {
+                *out = -INFINITY;
+                if (exact)
+                    exact[r * n_kv + s] = -INFINITY;
+                continue;
+            }
+            const uint16_t *kr = ki + s * (int64_t)d;
+            float acc = 0.0f;
+            double ex = 0.0;
+            for (int32_t c = 0; c < d; ++c) {
+                acc = fmaf(bf16_to_f32(qr[c]), bf16_to_f32(kr[c]), acc);
+                ex += bf16_to_f64(qr[c]) * bf16_to_f64(kr[c]);
+            }
+            *out = acc;
+            if (exact)
+                exact[r * n_kv + s] = ex;
+        }
+    }
+}
+
+typedef struct {
+    float key;
+    int32_t idx;
+} orc_scored;
+
+/* Total order: larger score first, then smaller index first. */
+static int cmp_scored(const void *a, const void *b)
+{
+    const orc_scored *x = (const orc_scored *)a, *y = (const orc_scored *)b;
+    if (x->key > y->key)
+        return -1;
+    if (x->key < y->key)
+        return 1;
+    return (x->idx > y->idx) - (x->idx < y->idx);
+}
+
+static int cmp_i32(const void *a, const void *b)
+{
+    int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+    return (x > y) - (x < y);
+}
+
+/* Top-k per row: candidates are the first n_cand[r] entries of sigma row r.
+ * Output idx [n_rows, k]: the selected indices ascending, -1 padded. */
+void orc_topk_rows(const float *sigma, const int64_t *n_cand, int64_t n_rows, int64_t n_kv,
+                   int32_t k, int32_t *idx)
+{
+#pragma omp parallel
+    {
+        orc_scored *buf = (orc_scored *)malloc(sizeof(orc_scored) * (size_t)(n_kv > 0 ? n_kv : 1));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < n_rows; ++r) {
+            int64_t nc = n_cand[r] < n_kv ? n_cand[r] : n_kv;
+            for (int64_t s = 0; s < nc; ++s) {
+                buf[s].key = sigma[r * n_kv + s];
+                buf[s].idx = (int32_t)s;
+            }
+            qsort(buf, (size_t)nc, sizeof(orc_scored), cmp_scored);
+            int64_t take = nc < k ? nc : k;
+            int32_t *out = idx + r * (int64_t)k;
+            for (int64_t e = 0; e < take; ++e)
+                out[e] = buf[e].idx;
+            qsort(out, (size_t)take, sizeof(int32_t), cmp_i32);
+            for (int64_t e = take; e < k; ++e)
+                out[e] = -1;
+        }
+        free(buf);
+    }
+}
+
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
