@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse attention forward on one MI355X.
+
+Workload (the glossary's worked pattern): B=1, H=32, N=8192, d=128, causal
+sliding window 1024 (inclusive) + 4 sink tokens, 128x128 blocks; Q, K, V
+bfloat16 ~ N(0, 1) from fixed seeds.  One step = one pass of the hot path:
+the block-list builder followed by the fused block-sparse attention (element
+masks on partial tiles only), inputs resident in HBM.
+
+Metric: effective TFLOP/s over live pairs = 4 * d * live_pairs / step time
+(2 products x 2 flop per multiply-add; the softmax is not counted).
+
+Also reported on the same JSON line:
+  roofline      the attention kernel's achieved TFLOP/s over live pairs per
+                launch (HIP events on the launch stream) against the bf16
+                dense MFMA peak, plus HBM traffic from committed rocprofv3
+                counters when they belong to the current kernel source;
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
+                workload on this machine's host cores;
+  dsa_prefill   the content-selected path on its own workload (1,024
+                queries at the end of a 65,536-token context, H=16, d=128,
+                indexer d_I=64, top-2048): indexer, top-k and gather times.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_block_window1024_sinks4_n8192_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_sa_amd", "csrc", "attn_block.hip")
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def src_hash(path=ATTN_SRC) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic():
+    """HBM bytes per attention launch from committed counters, if they match this source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != src_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--o-dtype", choices=["f32", "bf16"], default="f32")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dsa", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=2,
+                    help="heads of the workload the CPU oracle runs (all 8192 rows each)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_sa_amd as sa
+    from block_sparse_attention_sa_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+
+    def dev_bf16(u16):
+        return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    cfg = W.attn_config(2)
+    _log(f"bench: generating inputs for {cfg.name}")
+    inp = W.attn_inputs(cfg)
+    q, k, v = (dev_bf16(inp[t]) for t in ("q", "k", "v"))
+    o_dtype = torch.float32 if args.o_dtype == "f32" else torch.bfloat16
+    out = torch.empty((cfg.B, cfg.H, cfg.N, cfg.d), dtype=o_dtype, device=dev)
+    lse = torch.empty((cfg.B, cfg.H, cfg.N), dtype=torch.float32, device=dev)
+    bl = sa.build_block_mask(cfg.pattern, cfg.N, cfg.N, cfg.block, cfg.block, device=dev)
+    torch.cuda.synchronize()
+    live_pairs_per_head = int(bl.live_pairs.cpu()[0])
+    live_blocks = int(bl.kv_count.sum())
+    n_partial = int(sum(int(bl.kv_partial[i, : int(bl.kv_count[i])].sum()) for i in range(bl.kv_count.numel())))
+    assert live_blocks == 595 and live_pairs_per_head == 7900662, (live_blocks, live_pairs_per_head)
+    live_pairs = live_pairs_per_head * cfg.B * cfg.H
+    flops = 4.0 * cfg.d * live_pairs
+    tile_flops = 4.0 * cfg.d * cfg.block * cfg.block * live_blocks * cfg.B * cfg.H
+
+    def step():
+        sa.build_block_mask(cfg.pattern, cfg.N, cfg.N, cfg.block, cfg.block, device=dev, out=bl)
+        sa.attn_fwd(q, k, v, bl, out=out, lse=lse)
+
+    _log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    _log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        sa.build_block_mask(cfg.pattern, cfg.N, cfg.N, cfg.block, cfg.block, device=dev, out=bl)
+        ev[i][1].record(stream)
+        sa.attn_fwd(q, k, v, bl, out=out, lse=lse)
+        ev[i][2].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    builder_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    _log(f"bench: step {ms_per_step * 1e3:.1f} us (builder {builder_ms * 1e3:.1f} us, attention "
+         f"{attn_ms * 1e3:.1f} us) -> {value:.1f} TFLOP/s over live pairs")
+
+    traffic = _traffic()
+    result = {
+        "metric": "effective TFLOP/s over live pairs (and % bf16 MFMA peak), 1x MI355X",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "causal sliding window 1024 + 4 sinks, B=1 H=32 N=8192 d=128, 128x128 blocks "
+                        "(the glossary's worked pattern)",
+            "batch": cfg.B, "heads": cfg.H, "seq_len": cfg.N, "head_dim": cfg.d,
+            "block": cfg.block, "live_blocks_per_head": live_blocks, "partial_blocks_per_head": n_partial,
+            "live_pairs": live_pairs, "o_dtype": args.o_dtype,
+            "pct_bf16_peak_over_live_pairs": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+            "builder_us": round(builder_ms * 1e3, 2), "attention_us": round(attn_ms * 1e3, 2),
+            "attention_tflops_over_live_tiles": round(tile_flops / (attn_ms * 1e-3) / 1e12, 2),
+        },
+        "roofline": {
+            "kernel": "attn_block_kernel<128,128,128>",
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "algorithmic_flop_per_launch": flops,
+        },
+    }
+
+    if not args.no_dsa:
+        result["dsa_prefill"] = _bench_dsa(sa, W, np, torch, dev, dev_bf16)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = _cpu_baseline(cfg, inp, args.cpu_heads, np)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def _bench_dsa(sa, W, np, torch, dev, dev_bf16, reps=5):
+    tc = W.topk_config(5)
+    _log("bench: generating configuration-5 inputs (64K context)")
+    ti = W.topk_inputs(tc)
+    qi, ki = dev_bf16(ti["q_idx"]), dev_bf16(ti["k_idx"])
+    q, k, v = (dev_bf16(ti[t]) for t in ("q", "k", "v"))
+    scores = torch.empty((tc.n_q, tc.n_kv), dtype=torch.float32, device=dev)
+    idx = torch.empty((tc.n_q, tc.topk), dtype=torch.int32, device=dev)
+    o = torch.empty((1, tc.H, tc.n_q, tc.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((1, tc.H, tc.n_q), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run():
+        sa.indexer_scores(qi, ki, tc.q_offset, scores=scores)
+        sa.topk(scores, tc.q_offset, tc.topk, out=idx)
+        sa.attn_fwd(q, k, v, gather_idx=idx, out=o, lse=lse)
+
+    run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    for e in ev:
+        e[0].record(stream)
+        sa.indexer_scores(qi, ki, tc.q_offset, scores=scores)
+        e[1].record(stream)
+        sa.topk(scores, tc.q_offset, tc.topk, out=idx)
+        e[2].record(stream)
+        sa.attn_fwd(q, k, v, gather_idx=idx, out=o, lse=lse)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    t_idx = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+    t_topk = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    t_gat = float(np.mean([e[2].elapsed_time(e[3]) for e in ev])) * 1e-3
+    cand = sum(min(tc.q_offset + r + 1, tc.n_kv) for r in range(tc.n_q))
+    idx_bytes = 2 * (tc.n_q + tc.n_kv) * tc.d_idx + 4 * cand
+    topk_bytes = 4 * cand + 4 * tc.n_q * tc.topk
+    pairs = tc.H * tc.n_q * tc.topk
+    gather_bytes = pairs * tc.d * 2 * 2 + tc.H * tc.n_q * tc.d * (2 + 4)
+    return {
+        "workload": "1024 queries at the end of a 65536-token causal context, H=16 d=128, indexer d_I=64, top-2048",
+        "indexer_us": round(t_idx * 1e6, 1),
+        "indexer_gbs": round(idx_bytes / t_idx / 1e9, 1),
+        "indexer_tflops_fp32": round(2.0 * tc.d_idx * cand / t_idx / 1e12, 2),
+        "topk_us": round(t_topk * 1e6, 1),
+        "topk_gbs": round(topk_bytes / t_topk / 1e9, 1),
+        "gather_us": round(t_gat * 1e6, 1),
+        "gather_gbs": round(gather_bytes / t_gat / 1e9, 1),
+        "gather_tflops_over_pairs": round(4.0 * tc.d * pairs / t_gat / 1e12, 2),
+        "total_us": round((t_idx + t_topk + t_gat) * 1e6, 1),
+        "hbm_peak_gbs": PEAK_HBM_GBS,
+    }
+
+
+def _cpu_baseline(cfg, inp, heads, np):
+    import oracle  # the CPU oracle is the baseline leg here, nothing else
+    heads = max(1, min(heads, cfg.H))
+    rows = np.arange(heads * cfg.N, dtype=np.int64)
+    _log(f"bench: cpu oracle on {heads} head(s) x {cfg.N} rows")
+    t0 = time.perf_counter()
+    bl = oracle.block_lists(cfg.pattern, cfg.N, cfg.N, cfg.block, cfg.block)
+    t1 = time.perf_counter()
+    _, _, cnt = oracle.attn_rows(cfg.pattern, inp["q"], inp["k"], inp["v"], rows=rows, return_counts=True)
+    t2 = time.perf_counter()
+    pairs = int(cnt.sum())
+    value = 4.0 * cfg.d * pairs / (t2 - t1) / 1e12
+    return {
+        "value": round(value, 6),
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"fp64 oracle attention on {heads} of {cfg.H} heads (all {cfg.N} rows each, {pairs} live "
+                  f"pairs) in {t2 - t1:.2f} s; its block lists for the whole matrix took {t1 - t0:.2f} s",
+    }
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,1 +1,263 @@
-"""Block-sparse attention forward for MI355X (gfx950)."""
+"""Block-sparse attention forward for MI355X (gfx950).
+
+Python binding of libsa.so (C ABI in include/sa.h).  PyTorch supplies device
+memory and streams; every step of the computation runs in the HIP kernels of
+the library.  The functions mirror the library's entry points:
+
+* :func:`build_block_mask`  -> ``sa_build_block_mask``
+* :func:`attn_fwd`          -> ``sa_attn_fwd`` (block lists or gather lists)
+* :func:`indexer_scores`, :func:`topk`, :func:`indexer_topk`
+                            -> ``sa_indexer_scores``, ``sa_topk``, ``sa_indexer_topk``
+
+There is no CPU fallback: without the built library (or without a GPU) the
+calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+from . import _lib
+from ._lib import SaError  # noqa: F401
+
+__all__ = ["BlockLists", "build_block_mask", "attn_fwd", "indexer_scores", "topk", "indexer_topk",
+           "describe", "SaError"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _get(pattern, key, default):
+    if isinstance(pattern, dict):
+        return pattern.get(key, default)
+    return getattr(pattern, key, default)
+
+
+@dataclasses.dataclass
+class DevicePattern:
+    """A pattern with its random table resident on the device."""
+
+    struct: _lib.SaPattern
+    table: Optional[object]  # torch tensor kept alive
+
+
+def device_pattern(pattern, device) -> DevicePattern:
+    torch = _torch()
+    table = _get(pattern, "rand_table", None)
+    t = None
+    if table is not None:
+        arr = np.ascontiguousarray(table, dtype=np.int32)
+        t = torch.from_numpy(arr).to(device)
+    s = _lib.SaPattern(
+        causal=int(_get(pattern, "causal", 0)),
+        q_offset=int(_get(pattern, "q_offset", 0)),
+        window_left=int(_get(pattern, "window_left", -1)),
+        window_right=int(_get(pattern, "window_right", 0)),
+        sinks=int(_get(pattern, "sinks", 0)),
+        stride=int(_get(pattern, "stride", 0)),
+        stride_phase=int(_get(pattern, "stride_phase", 0)),
+        global_tokens=int(_get(pattern, "global_tokens", 0)),
+        unit=int(_get(pattern, "unit", 0)),
+        unit_window=int(_get(pattern, "unit_window", -1)),
+        rand_units=t.data_ptr() if t is not None else None,
+        n_rand=int(t.shape[1]) if t is not None else 0,
+        rand_rows=int(t.shape[0]) if t is not None else 0,
+    )
+    return DevicePattern(s, t)
+
+
+@dataclasses.dataclass
+class BlockLists:
+    """Output of :func:`build_block_mask` (device tensors)."""
+
+    kv_count: object    # int32 [nqb]
+    kv_index: object    # int32 [nqb, nkb]
+    kv_partial: object  # uint8 [nqb, nkb]
+    live_pairs: object  # int64 [1]
+    n_q: int
+    n_kv: int
+    block_q: int
+    block_kv: int
+    pattern: DevicePattern
+
+
+def build_block_mask(pattern, n_q: int, n_kv: int, block_q: int, block_kv: int,
+                     device="cuda", out: Optional[BlockLists] = None) -> BlockLists:
+    """Per-query-block live key-block lists of ``pattern`` (``sa_build_block_mask``)."""
+    torch = _torch()
+    device = torch.device(device)
+    nqb, nkb = -(-n_q // block_q), -(-n_kv // block_kv)
+    if out is None:
+        dp = device_pattern(pattern, device)
+        out = BlockLists(
+            kv_count=torch.empty(nqb, dtype=torch.int32, device=device),
+            kv_index=torch.empty((nqb, nkb), dtype=torch.int32, device=device),
+            kv_partial=torch.empty((nqb, nkb), dtype=torch.uint8, device=device),
+            live_pairs=torch.empty(1, dtype=torch.int64, device=device),
+            n_q=n_q, n_kv=n_kv, block_q=block_q, block_kv=block_kv, pattern=dp)
+    _lib.check(_lib.lib().sa_build_block_mask(
+        ctypes.byref(out.pattern.struct), n_q, n_kv, block_q, block_kv,
+        out.kv_count.data_ptr(), out.kv_index.data_ptr(), out.kv_partial.data_ptr(),
+        out.live_pairs.data_ptr(), _stream_ptr(device)))
+    return out
+
+
+def _strides3(t) -> list:
+    if t.numel() == 0:  # nothing is read or written: report the contiguous strides
+        d = int(t.shape[-1])
+        return [int(t.shape[1]) * int(t.shape[2]) * d, int(t.shape[2]) * d, d]
+    s = t.stride()
+    if s[-1] != 1:
+        raise ValueError("the last dimension must be contiguous")
+    return [int(s[0]), int(s[1]), int(s[2])]
+
+
+def attn_fwd(q, k, v, blocks: Optional[BlockLists] = None, gather_idx=None, *,
+             o_dtype=None, softmax_scale: Optional[float] = None, out=None, lse=None,
+             want_lse: bool = True):
+    """Block-sparse (``blocks``) or per-query gather (``gather_idx``) attention forward.
+
+    q [B, H, n_q, d], k/v [B, H, n_kv, d] bfloat16 on the GPU.  ``gather_idx``
+    is int32 [n_q, topk] shared by every (b, h), or [B, H, n_q, topk].
+    Returns (O [B, H, n_q, d] in ``o_dtype`` (default float32), LSE float32
+    [B, H, n_q] or None).
+    """
+    torch = _torch()
+    if (blocks is None) == (gather_idx is None):
+        raise ValueError("pass exactly one of blocks / gather_idx")
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 4:
+            raise ValueError("q, k, v must be 4-d bfloat16 CUDA tensors")
+    B, H, n_q, d = q.shape
+    n_kv = k.shape[2]
+    if k.shape != (B, H, n_kv, d) or v.shape != (B, H, n_kv, d):
+        raise ValueError("k/v shape mismatch")
+    o_dtype = torch.float32 if o_dtype is None else o_dtype
+    if out is None:
+        out = torch.empty((B, H, n_q, d), dtype=o_dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    a = _lib.SaAttnArgs()
+    a.q, a.k, a.v, a.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()
+    a.lse = lse.data_ptr() if lse is not None else None
+    a.batch, a.heads, a.n_q, a.n_kv, a.head_dim = B, H, n_q, n_kv, d
+    a.o_dtype = _lib.SA_DTYPE_F32 if out.dtype == torch.float32 else _lib.SA_DTYPE_BF16
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("o_dtype must be float32 or bfloat16")
+    a.q_strides[:] = _strides3(q)
+    a.k_strides[:] = _strides3(k)
+    a.v_strides[:] = _strides3(v)
+    a.o_strides[:] = _strides3(out)
+    a.softmax_scale = float(softmax_scale) if softmax_scale else 0.0
+    keep = []
+    if blocks is not None:
+        if blocks.n_q != n_q or blocks.n_kv != n_kv:
+            raise ValueError("block lists were built for another n_q / n_kv")
+        a.mode = _lib.SA_MODE_BLOCKS
+        a.block_q, a.block_kv = blocks.block_q, blocks.block_kv
+        a.kv_count = blocks.kv_count.data_ptr()
+        a.kv_index = blocks.kv_index.data_ptr()
+        a.kv_partial = blocks.kv_partial.data_ptr()
+        a.pattern = blocks.pattern.struct
+    else:
+        g = gather_idx
+        if g.dtype != torch.int32 or not g.is_cuda or not g.is_contiguous():
+            raise ValueError("gather_idx must be a contiguous int32 CUDA tensor")
+        a.mode = _lib.SA_MODE_GATHER
+        a.gather_idx = g.data_ptr()
+        a.topk = int(g.shape[-1])
+        if g.dim() == 2:
+            if g.shape[0] != n_q:
+                raise ValueError("gather_idx rows must equal n_q")
+            a.gather_bh_stride = 0
+        elif g.dim() == 4 and tuple(g.shape[:3]) == (B, H, n_q):
+            a.gather_bh_stride = n_q * a.topk
+        else:
+            raise ValueError("gather_idx must be [n_q, topk] or [B, H, n_q, topk]")
+        keep.append(g)
+    _lib.check(_lib.lib().sa_attn_fwd(ctypes.byref(a), _stream_ptr(q.device)))
+    return out, lse
+
+
+def indexer_scores(q_idx, k_idx, q_offset: int, scores=None):
+    """float32 [n_q, n_kv] indexer scores (entries s > q_offset + r untouched)."""
+    torch = _torch()
+    n_q, d = q_idx.shape
+    n_kv = k_idx.shape[0]
+    _check_idx(q_idx, k_idx)
+    if scores is None:
+        scores = torch.empty((n_q, n_kv), dtype=torch.float32, device=q_idx.device)
+    _lib.check(_lib.lib().sa_indexer_scores(q_idx.data_ptr(), k_idx.data_ptr(), n_q, n_kv, d,
+                                            int(q_offset), scores.data_ptr(),
+                                            _stream_ptr(q_idx.device)))
+    return scores
+
+
+def topk(scores, q_offset: int, k: int, out=None):
+    """int32 [n_q, k]: per row the k best candidates (score desc, index asc), ascending."""
+    torch = _torch()
+    if scores.dtype != torch.float32 or not scores.is_contiguous():
+        raise ValueError("scores must be contiguous float32")
+    n_q, n_kv = scores.shape
+    if out is None:
+        out = torch.empty((n_q, k), dtype=torch.int32, device=scores.device)
+    _lib.check(_lib.lib().sa_topk(scores.data_ptr(), n_q, n_kv, int(q_offset), int(k),
+                                  out.data_ptr(), _stream_ptr(scores.device)))
+    return out
+
+
+def indexer_topk(q_idx, k_idx, q_offset: int, k: int, scores=None, out=None):
+    """Indexer scores into ``scores`` (workspace) then the top-k; returns (idx, scores)."""
+    torch = _torch()
+    n_q, d = q_idx.shape
+    n_kv = k_idx.shape[0]
+    _check_idx(q_idx, k_idx)
+    if scores is None:
+        scores = torch.empty((n_q, n_kv), dtype=torch.float32, device=q_idx.device)
+    if out is None:
+        out = torch.empty((n_q, k), dtype=torch.int32, device=q_idx.device)
+    _lib.check(_lib.lib().sa_indexer_topk(q_idx.data_ptr(), k_idx.data_ptr(), n_q, n_kv, d,
+                                          int(q_offset), int(k), scores.data_ptr(),
+                                          out.data_ptr(), _stream_ptr(q_idx.device)))
+    return out, scores
+
+
+def _check_idx(q_idx, k_idx):
+    torch = _torch()
+    for t in (q_idx, k_idx):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 2 or not t.is_contiguous():
+            raise ValueError("indexer inputs must be contiguous 2-d bfloat16 CUDA tensors")
+    if q_idx.shape[1] != k_idx.shape[1]:
+        raise ValueError("indexer dims differ")
+
+
+def describe(blocks: BlockLists, max_rows: int = 16) -> str:
+    """Sparsity summary and an ASCII map of the live blocks ('#' full, '+' partial)."""
+    cnt = blocks.kv_count.cpu().numpy()
+    idx = blocks.kv_index.cpu().numpy()
+    par = blocks.kv_partial.cpu().numpy()
+    nqb, nkb = idx.shape
+    live = int(cnt.sum())
+    n_part = int(sum(par[i, : cnt[i]].sum() for i in range(nqb)))
+    lines = [f"blocks {nqb}x{nkb} of {blocks.block_q}x{blocks.block_kv}: live {live} "
+             f"(full {live - n_part}, partial {n_part}), sparsity "
+             f"{100.0 * (nqb * nkb - live) / max(1, nqb * nkb):.2f}%, "
+             f"live pairs {int(blocks.live_pairs.cpu()[0])}"]
+    step = max(1, nqb // max_rows)
+    for i in range(0, nqb, step):
+        row = ["."] * nkb
+        for e in range(cnt[i]):
+            row[idx[i, e]] = "+" if par[i, e] else "#"
+        lines.append("".join(row[:: max(1, nkb // 64)]))
+    return "\n".join(lines)

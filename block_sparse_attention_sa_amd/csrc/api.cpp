@@ -1,0 +1,297 @@
+// api.cpp -- the C ABI of libsa.so (declared in include/sa.h): argument
+// validation on the host, conversion to the kernels' parameter blocks, and
+// launches on the caller's stream.  No device memory is allocated here.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/sa.h"
+#include "sa_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+sa_status fail(sa_status st, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+sa_status ok()
+{
+    return SA_OK;
+}
+
+constexpr int64_t kI32Max = 2147483647LL;
+
+int32_t clamp32(int64_t v)
+{
+    if (v > kI32Max) return (int32_t)kI32Max;
+    if (v < -kI32Max) return (int32_t)-kI32Max;
+    return (int32_t)v;
+}
+
+bool aligned16(const void* p)
+{
+    return ((uintptr_t)p & 15u) == 0;
+}
+
+// Validates the pattern and fills the kernels' form of it.
+sa_status make_pattern(const sa_pattern* p, int64_t n_q, sa::DevPattern& d)
+{
+    if (!p) return fail(SA_ERR_INVALID_ARG, "pattern is NULL");
+    if (p->q_offset < 0) return fail(SA_ERR_INVALID_ARG, "pattern.q_offset must be >= 0");
+    if (p->q_offset + n_q > kI32Max)
+        return fail(SA_ERR_UNSUPPORTED, "query positions must stay below 2^31");
+    if (p->window_left >= 0 && p->window_right < 0)
+        return fail(SA_ERR_INVALID_ARG, "pattern.window_right must be >= 0 when the window is on");
+    if (p->sinks < 0 || p->global_tokens < 0)
+        return fail(SA_ERR_INVALID_ARG, "pattern.sinks and pattern.global_tokens must be >= 0");
+    if (p->stride > 0 && (p->stride_phase < 0 || p->stride_phase >= p->stride))
+        return fail(SA_ERR_INVALID_ARG, "pattern.stride_phase must be in [0, stride)");
+    if (p->stride > kI32Max || p->unit > kI32Max)
+        return fail(SA_ERR_UNSUPPORTED, "pattern.stride / pattern.unit must be below 2^31");
+    if (p->n_rand < 0 || p->n_rand > sa::kMaxRand)
+        return fail(SA_ERR_UNSUPPORTED, "pattern.n_rand must be in [0, %d]", sa::kMaxRand);
+    if ((p->n_rand > 0 || p->unit_window >= 0) && p->unit <= 0)
+        return fail(SA_ERR_INVALID_ARG, "pattern.unit must be > 0 for unit-level terms");
+    if (p->n_rand > 0 && (!p->rand_units || p->rand_rows < 0))
+        return fail(SA_ERR_INVALID_ARG, "pattern.rand_units is NULL or rand_rows < 0");
+    d = sa::DevPattern{};
+    d.causal = p->causal != 0;
+    d.q_offset = (int32_t)p->q_offset;
+    d.window_left = p->window_left < 0 ? -1 : clamp32(p->window_left);
+    d.window_right = clamp32(p->window_right < 0 ? 0 : p->window_right);
+    d.sinks = clamp32(p->sinks);
+    d.stride = p->stride > 0 ? (int32_t)p->stride : 0;
+    d.stride_phase = (int32_t)(p->stride > 0 ? p->stride_phase : 0);
+    d.global_tokens = clamp32(p->global_tokens);
+    d.unit = p->unit > 0 ? (int32_t)p->unit : 0;
+    d.unit_window = p->unit > 0 && p->unit_window >= 0 ? clamp32(p->unit_window) : -1;
+    d.n_rand = p->unit > 0 ? (int32_t)p->n_rand : 0;
+    d.rand_rows = d.n_rand > 0 ? clamp32(p->rand_rows) : 0;
+    d.rand_units = d.n_rand > 0 ? p->rand_units : nullptr;
+    d.stride_div = sa::make_fastdiv(d.stride > 0 ? d.stride : 1);
+    d.unit_div = sa::make_fastdiv(d.unit > 0 ? d.unit : 1);
+    return SA_OK;
+}
+
+sa_status launched(hipError_t e, const char* what)
+{
+    if (e != hipSuccess) return fail(SA_ERR_DEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sa_abi_version(void)
+{
+    return SA_ABI_VERSION;
+}
+
+const char* sa_last_error(void)
+{
+    return g_err.c_str();
+}
+
+sa_status sa_build_block_mask(const sa_pattern* pattern, int64_t n_q, int64_t n_kv, int32_t block_q,
+                              int32_t block_kv, int32_t* kv_count, int32_t* kv_index,
+                              uint8_t* kv_partial, int64_t* live_pairs, void* stream)
+{
+    try {
+        if (n_q < 0 || n_kv < 0) return fail(SA_ERR_INVALID_ARG, "n_q and n_kv must be >= 0");
+        if (n_kv > kI32Max) return fail(SA_ERR_UNSUPPORTED, "n_kv must be below 2^31");
+        if (block_q < 32 || block_q > 1024 || block_q % 32 || block_kv < 32 || block_kv > 1024 ||
+            block_kv % 32)
+            return fail(SA_ERR_INVALID_ARG, "block_q/block_kv must be multiples of 32 in [32, 1024]");
+        if (!live_pairs) return fail(SA_ERR_INVALID_ARG, "live_pairs is NULL");
+        const int64_t nqb = (n_q + block_q - 1) / block_q, nkb = (n_kv + block_kv - 1) / block_kv;
+        if (nqb > 0 && (!kv_count || (nkb > 0 && (!kv_index || !kv_partial))))
+            return fail(SA_ERR_INVALID_ARG, "kv_count/kv_index/kv_partial is NULL");
+        if (nkb > 16384) return fail(SA_ERR_UNSUPPORTED, "more than 16384 key blocks per row");
+        if (nqb > kI32Max) return fail(SA_ERR_UNSUPPORTED, "too many query blocks");
+        sa::DevPattern d;
+        sa_status st = make_pattern(pattern, n_q, d);
+        if (st != SA_OK) return st;
+        hipStream_t s = (hipStream_t)stream;
+        if (nqb == 0) return launched(sa::launch_zero_i64(live_pairs, s), "sa_build_block_mask");
+        return launched(sa::launch_block_mask(d, (int32_t)n_q, (int32_t)n_kv, block_q, block_kv,
+                                              kv_count, kv_index, kv_partial, live_pairs, s),
+                        "sa_build_block_mask");
+    } catch (...) {
+        return fail(SA_ERR_DEVICE, "sa_build_block_mask: unexpected exception");
+    }
+}
+
+sa_status sa_attn_fwd(const sa_attn_args* a, void* stream)
+{
+    try {
+        if (!a) return fail(SA_ERR_INVALID_ARG, "args is NULL");
+        if (a->batch < 0 || a->heads < 0 || a->n_q < 0 || a->n_kv < 0)
+            return fail(SA_ERR_INVALID_ARG, "batch/heads/n_q/n_kv must be >= 0");
+        if (a->head_dim != 64 && a->head_dim != 128)
+            return fail(SA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+        if (a->o_dtype != SA_DTYPE_BF16 && a->o_dtype != SA_DTYPE_F32)
+            return fail(SA_ERR_INVALID_ARG, "o_dtype must be SA_DTYPE_BF16 or SA_DTYPE_F32");
+        if (a->mode != SA_MODE_BLOCKS && a->mode != SA_MODE_GATHER)
+            return fail(SA_ERR_INVALID_ARG, "mode must be SA_MODE_BLOCKS or SA_MODE_GATHER");
+        if (a->n_q > kI32Max || a->n_kv > kI32Max || a->batch * a->heads > kI32Max)
+            return fail(SA_ERR_UNSUPPORTED, "sizes must stay below 2^31");
+        if (a->batch == 0 || a->heads == 0 || a->n_q == 0) return ok();
+        if (!a->q || !a->o || (a->n_kv > 0 && (!a->k || !a->v)))
+            return fail(SA_ERR_INVALID_ARG, "q/k/v/o is NULL");
+        if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o) ||
+            (a->lse && ((uintptr_t)a->lse & 3u)))
+            return fail(SA_ERR_INVALID_ARG, "q/k/v/o must be 16-byte aligned");
+        for (int i = 0; i < 3; ++i) {
+            if (a->q_strides[i] < 0 || a->k_strides[i] < 0 || a->v_strides[i] < 0 || a->o_strides[i] < 0)
+                return fail(SA_ERR_INVALID_ARG, "strides must be >= 0");
+            if (a->q_strides[i] % 8 || a->k_strides[i] % 8 || a->v_strides[i] % 8)
+                return fail(SA_ERR_INVALID_ARG, "q/k/v strides must be multiples of 8 elements");
+            if (a->o_strides[i] % (a->o_dtype == SA_DTYPE_F32 ? 4 : 8))
+                return fail(SA_ERR_INVALID_ARG, "o strides must keep 16-byte alignment");
+        }
+        if (a->q_strides[2] < a->head_dim || a->o_strides[2] < a->head_dim ||
+            (a->n_kv > 0 && (a->k_strides[2] < a->head_dim || a->v_strides[2] < a->head_dim)))
+            return fail(SA_ERR_INVALID_ARG, "row strides must be >= head_dim");
+        double scale = a->softmax_scale > 0 ? a->softmax_scale : 1.0 / std::sqrt((double)a->head_dim);
+
+        sa::AttnParams p{};
+        p.q = (const uint16_t*)a->q;
+        p.k = (const uint16_t*)a->k;
+        p.v = (const uint16_t*)a->v;
+        p.o = a->o;
+        p.lse = a->lse;
+        p.q_sb = a->q_strides[0]; p.q_sh = a->q_strides[1]; p.q_sn = a->q_strides[2];
+        p.k_sb = a->k_strides[0]; p.k_sh = a->k_strides[1]; p.k_sn = a->k_strides[2];
+        p.v_sb = a->v_strides[0]; p.v_sh = a->v_strides[1]; p.v_sn = a->v_strides[2];
+        p.o_sb = a->o_strides[0]; p.o_sh = a->o_strides[1]; p.o_sn = a->o_strides[2];
+        p.batch = (int32_t)a->batch;
+        p.heads = (int32_t)a->heads;
+        p.n_q = (int32_t)a->n_q;
+        p.n_kv = (int32_t)a->n_kv;
+        p.scale = (float)scale;
+        p.scale_log2 = (float)(scale * 1.4426950408889634);
+        hipStream_t s = (hipStream_t)stream;
+        const int o_f32 = a->o_dtype == SA_DTYPE_F32;
+
+        if (a->mode == SA_MODE_BLOCKS) {
+            if ((a->block_q != 64 && a->block_q != 128) || (a->block_kv != 64 && a->block_kv != 128))
+                return fail(SA_ERR_UNSUPPORTED, "block_q and block_kv must be 64 or 128");
+            if (!a->kv_count || (a->n_kv > 0 && (!a->kv_index || !a->kv_partial)))
+                return fail(SA_ERR_INVALID_ARG, "block lists are NULL");
+            sa_status st = make_pattern(&a->pattern, a->n_q, p.pat);
+            if (st != SA_OK) return st;
+            p.nqb = (int32_t)((a->n_q + a->block_q - 1) / a->block_q);
+            p.nkb = (int32_t)((a->n_kv + a->block_kv - 1) / a->block_kv);
+            if ((int64_t)p.nqb * a->batch * a->heads > kI32Max)
+                return fail(SA_ERR_UNSUPPORTED, "too many work items");
+            p.kv_count = a->kv_count;
+            p.kv_index = a->kv_index;
+            p.kv_partial = a->kv_partial;
+            return launched(sa::launch_attn_blocks(p, (int)a->head_dim, (int)a->block_q,
+                                                   (int)a->block_kv, o_f32, s),
+                            "sa_attn_fwd");
+        }
+        if (!a->gather_idx) return fail(SA_ERR_INVALID_ARG, "gather_idx is NULL");
+        if (a->topk < 1 || a->topk > 8192) return fail(SA_ERR_UNSUPPORTED, "topk must be in [1, 8192]");
+        if (a->gather_bh_stride < 0) return fail(SA_ERR_INVALID_ARG, "gather_bh_stride must be >= 0");
+        p.gidx = a->gather_idx;
+        p.topk = (int32_t)a->topk;
+        p.g_bh_stride = a->gather_bh_stride;
+        return launched(sa::launch_attn_gather(p, (int)a->head_dim, o_f32, s), "sa_attn_fwd");
+    } catch (...) {
+        return fail(SA_ERR_DEVICE, "sa_attn_fwd: unexpected exception");
+    }
+}
+
+static sa_status check_indexer(const void* q_idx, const void* k_idx, int64_t n_q, int64_t n_kv,
+                               int32_t d_idx, int64_t q_offset, const float* scores)
+{
+    if (n_q < 0 || n_kv < 0 || q_offset < 0) return fail(SA_ERR_INVALID_ARG, "negative size or offset");
+    if (n_kv > kI32Max || q_offset + n_q > kI32Max) return fail(SA_ERR_UNSUPPORTED, "sizes must stay below 2^31");
+    if (d_idx < 8 || d_idx > 256 || d_idx % 8) return fail(SA_ERR_UNSUPPORTED, "d_idx must be a multiple of 8 in [8, 256]");
+    if (n_q > 0 && n_kv > 0 && (!q_idx || !k_idx || !scores)) return fail(SA_ERR_INVALID_ARG, "NULL pointer");
+    if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(scores))
+        return fail(SA_ERR_INVALID_ARG, "q_idx/k_idx/scores must be 16-byte aligned");
+    return SA_OK;
+}
+
+static sa_status check_topk(const float* scores, int64_t n_q, int64_t n_kv, int64_t q_offset, int32_t topk,
+                            const int32_t* idx_out)
+{
+    if (n_q < 0 || n_kv < 0 || q_offset < 0) return fail(SA_ERR_INVALID_ARG, "negative size or offset");
+    if (q_offset + n_q > kI32Max) return fail(SA_ERR_UNSUPPORTED, "positions must stay below 2^31");
+    if (topk < 1 || topk > 4096) return fail(SA_ERR_UNSUPPORTED, "topk must be in [1, 4096]");
+    if (n_kv > 65536) return fail(SA_ERR_UNSUPPORTED, "n_kv must be <= 65536");
+    if (n_q > 0 && (!scores || !idx_out)) return fail(SA_ERR_INVALID_ARG, "NULL pointer");
+    if (!aligned16(scores)) return fail(SA_ERR_INVALID_ARG, "scores must be 16-byte aligned");
+    return SA_OK;
+}
+
+sa_status sa_indexer_scores(const void* q_idx, const void* k_idx, int64_t n_q, int64_t n_kv, int32_t d_idx,
+                            int64_t q_offset, float* scores, void* stream)
+{
+    try {
+        sa_status st = check_indexer(q_idx, k_idx, n_q, n_kv, d_idx, q_offset, scores);
+        if (st != SA_OK) return st;
+        if (n_q == 0 || n_kv == 0) return ok();
+        return launched(sa::launch_indexer_scores((const uint16_t*)q_idx, (const uint16_t*)k_idx, (int32_t)n_q,
+                                                  (int32_t)n_kv, d_idx, (int32_t)q_offset, scores,
+                                                  (hipStream_t)stream),
+                        "sa_indexer_scores");
+    } catch (...) {
+        return fail(SA_ERR_DEVICE, "sa_indexer_scores: unexpected exception");
+    }
+}
+
+sa_status sa_topk(const float* scores, int64_t n_q, int64_t n_kv, int64_t q_offset, int32_t topk,
+                  int32_t* idx_out, void* stream)
+{
+    try {
+        sa_status st = check_topk(scores, n_q, n_kv, q_offset, topk, idx_out);
+        if (st != SA_OK) return st;
+        if (n_q == 0) return ok();
+        return launched(sa::launch_topk(scores, (int32_t)n_q, (int32_t)n_kv, (int32_t)q_offset, topk, idx_out,
+                                        (hipStream_t)stream),
+                        "sa_topk");
+    } catch (...) {
+        return fail(SA_ERR_DEVICE, "sa_topk: unexpected exception");
+    }
+}
+
+sa_status sa_indexer_topk(const void* q_idx, const void* k_idx, int64_t n_q, int64_t n_kv, int32_t d_idx,
+                          int64_t q_offset, int32_t topk, float* scores, int32_t* idx_out, void* stream)
+{
+    try {
+        sa_status st = check_indexer(q_idx, k_idx, n_q, n_kv, d_idx, q_offset, scores);
+        if (st != SA_OK) return st;
+        st = check_topk(scores, n_q, n_kv, q_offset, topk, idx_out);
+        if (st != SA_OK) return st;
+        if (n_q == 0) return ok();
+        if (n_kv > 0) {
+            st = launched(sa::launch_indexer_scores((const uint16_t*)q_idx, (const uint16_t*)k_idx, (int32_t)n_q,
+                                                    (int32_t)n_kv, d_idx, (int32_t)q_offset, scores,
+                                                    (hipStream_t)stream),
+                          "sa_indexer_topk");
+            if (st != SA_OK) return st;
+        }
+        return launched(sa::launch_topk(scores, (int32_t)n_q, (int32_t)n_kv, (int32_t)q_offset, topk, idx_out,
+                                        (hipStream_t)stream),
+                        "sa_indexer_topk");
+    } catch (...) {
+        return fail(SA_ERR_DEVICE, "sa_indexer_topk: unexpected exception");
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,154 @@
+// sa_internal.h -- device-side pattern evaluation and launcher declarations.
+//
+// The pattern is the union of fixed terms described in the "Sparse Attention"
+// glossary (section on common sparsity patterns) and the sparse-transformer
+// blog (section on the main sparsity templates), intersected with causality;
+// its fields and their meaning are those of sa_pattern in include/sa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+// Exact unsigned division by an invariant divisor s >= 1 for 0 <= n < 2^31:
+// with l = ceil(log2 s) and M = ceil(2^(31+l) / s), floor(n / s) equals
+// (n * M) >> (31 + l).  (M*n/2^(31+l) = n/s + e*n/(s*2^(31+l)) with
+// 0 <= e < s; the excess is below 2^-l <= 1/s, so the floor is unchanged.)
+struct FastDiv {
+    uint64_t mul;
+    int32_t shift;
+    int32_t div;
+};
+
+inline FastDiv make_fastdiv(int64_t s)
+{
+    FastDiv f{};
+    if (s < 1) s = 1;
+    int l = 0;
+    while ((int64_t(1) << l) < s) ++l;
+    f.shift = 31 + l;
+    unsigned __int128 num = (unsigned __int128)1 << f.shift;
+    f.mul = (uint64_t)((num + (unsigned __int128)s - 1) / (unsigned __int128)s);
+    f.div = (int32_t)s;
+    return f;
+}
+
+__device__ __forceinline__ int32_t fdiv(int32_t n, const FastDiv& f)
+{
+    return (int32_t)(((uint64_t)(uint32_t)n * f.mul) >> f.shift);
+}
+
+__device__ __forceinline__ int32_t fmod_(int32_t n, const FastDiv& f)
+{
+    return n - fdiv(n, f) * f.div;
+}
+
+// Pattern as the kernels see it: 32-bit positions, precomputed divisors.
+struct DevPattern {
+    int32_t causal;
+    int32_t q_offset;
+    int32_t window_left;   // < 0: local term off
+    int32_t window_right;
+    int32_t sinks;
+    int32_t stride;        // <= 0: strided term off
+    int32_t stride_phase;
+    int32_t global_tokens;
+    int32_t unit;          // <= 0: unit terms off
+    int32_t unit_window;   // < 0: unit band off
+    int32_t n_rand;
+    int32_t rand_rows;
+    const int32_t *rand_units;
+    FastDiv stride_div;
+    FastDiv unit_div;
+};
+
+constexpr int kMaxRand = 8;
+
+// Per-query quantities that do not change along a query row.
+struct RowCtx {
+    int32_t q;       // absolute query position
+    int32_t qu;      // q / unit (0 if unit terms off)
+    int32_t rnd[kMaxRand];
+};
+
+__device__ __forceinline__ void row_ctx(const DevPattern& p, int32_t q, RowCtx& r)
+{
+    r.q = q;
+    r.qu = p.unit > 0 ? fdiv(q, p.unit_div) : 0;
+#pragma unroll
+    for (int i = 0; i < kMaxRand; ++i)
+        r.rnd[i] = (i < p.n_rand && p.unit > 0 && r.qu < p.rand_rows)
+                       ? p.rand_units[(int64_t)r.qu * p.n_rand + i]
+                       : -1;
+}
+
+// Per-pair predicate (one pair at a time; used on partial tiles only).
+__device__ __forceinline__ bool pair_allowed(const DevPattern& p, const RowCtx& r, int32_t kv)
+{
+    const int32_t q = r.q;
+    bool ok = (kv < p.sinks) | (q < p.global_tokens) | (kv < p.global_tokens);
+    if (p.window_left >= 0)
+        ok |= (q - kv <= p.window_left) & (kv - q <= p.window_right);
+    if (p.stride > 0) {
+        int32_t dd = q - kv;
+        ok |= (dd >= 0) && (fmod_(dd < 0 ? 0 : dd, p.stride_div) == p.stride_phase);
+    }
+    if (p.unit > 0) {
+        int32_t ku = fdiv(kv, p.unit_div);
+        if (p.unit_window >= 0) {
+            int32_t du = r.qu - ku;
+            du = du < 0 ? -du : du;
+            ok |= du <= p.unit_window;
+        }
+#pragma unroll
+        for (int i = 0; i < kMaxRand; ++i)
+            ok |= (r.rnd[i] == ku);
+    }
+    if (p.causal)
+        ok &= kv <= q;
+    return ok;
+}
+
+// ---- launchers (defined in the .hip files) --------------------------------
+
+hipError_t launch_zero_i64(int64_t* p, hipStream_t stream);
+hipError_t launch_block_mask(const DevPattern& p, int32_t n_q, int32_t n_kv, int32_t block_q,
+                             int32_t block_kv, int32_t* kv_count, int32_t* kv_index,
+                             uint8_t* kv_partial, int64_t* live_pairs, hipStream_t stream);
+
+struct AttnParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    void* o;
+    float* lse;
+    int64_t q_sb, q_sh, q_sn;
+    int64_t k_sb, k_sh, k_sn;
+    int64_t v_sb, v_sh, v_sn;
+    int64_t o_sb, o_sh, o_sn;
+    int32_t batch, heads, n_q, n_kv;
+    float scale;        // softmax scale (natural units)
+    float scale_log2;   // scale * log2(e)
+    // block mode
+    int32_t nqb, nkb;
+    const int32_t* kv_count;
+    const int32_t* kv_index;
+    const uint8_t* kv_partial;
+    DevPattern pat;
+    // gather mode
+    const int32_t* gidx;
+    int32_t topk;
+    int64_t g_bh_stride;
+};
+
+hipError_t launch_attn_blocks(const AttnParams& a, int head_dim, int block_q, int block_kv,
+                              int o_f32, hipStream_t stream);
+hipError_t launch_attn_gather(const AttnParams& a, int head_dim, int o_f32, hipStream_t stream);
+hipError_t launch_indexer_scores(const uint16_t* q_idx, const uint16_t* k_idx, int32_t n_q,
+                                 int32_t n_kv, int32_t d_idx, int32_t q_offset, float* scores,
+                                 hipStream_t stream);
+hipError_t launch_topk(const float* scores, int32_t n_q, int32_t n_kv, int32_t q_offset,
+                       int32_t topk, int32_t* idx_out, hipStream_t stream);
+
+}  // namespace sa

@@ -1,0 +1,218 @@
+/*
+ * sa.h -- C ABI of libsa.so: block-sparse attention forward on MI355X (gfx950).
+ *
+ * The method (sources cited by page title and section):
+ *  - "Sparse Attention" glossary (Ultralytics), section on common sparsity
+ *    patterns: a query scores only a chosen subset of keys -- a causal
+ *    sliding window, strided keys, global tokens, random links, attention
+ *    sinks, or keys picked by content (DeepSeek Sparse Attention: an indexer
+ *    scores every earlier token and the 2,048 best are attended).
+ *  - same page, section on turning a pattern into savings: masking a dense
+ *    score matrix still computes every score; speed comes from kernels that
+ *    skip empty tiles; the mask is split into fixed blocks (128 x 128 in the
+ *    example) and the sparsity is the share of blocks with no allowed pair.
+ *  - blog "Sparse transformers: how to cut the O(n^2) of attention"
+ *    (1gpt.online), section on how it looks in code: scores q.k^T/sqrt(d),
+ *    disallowed pairs at -inf, softmax, product with V.
+ *
+ * Conventions shared by every entry point:
+ *  - Ownership: the caller allocates and owns every buffer.  Pointers named
+ *    "device" must be device memory of the current HIP device; the library
+ *    keeps no device allocation of its own.
+ *  - Asynchrony: all work is enqueued on `stream` (a hipStream_t; NULL is the
+ *    null stream).  Nothing synchronises the host.
+ *  - Errors: invalid arguments are rejected on the host before any launch
+ *    (SA_ERR_INVALID_ARG / SA_ERR_UNSUPPORTED), so a rejected call writes
+ *    nothing.  A failed launch returns SA_ERR_DEVICE.  sa_last_error()
+ *    returns a thread-local description of the last non-OK status.  No call
+ *    aborts or lets an exception escape.
+ *  - Positions are absolute: query row r has position q_offset + r; key row
+ *    s has position s.  All sizes and positions must fit in int32 (< 2^31).
+ *  - bfloat16 tensors are passed as raw 16-bit storage.
+ */
+#ifndef SA_H
+#define SA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SA_ABI_VERSION 1
+
+typedef enum sa_status {
+    SA_OK = 0,
+    SA_ERR_INVALID_ARG = 1,
+    SA_ERR_UNSUPPORTED = 2,
+    SA_ERR_DEVICE = 3
+} sa_status;
+
+enum { SA_DTYPE_BF16 = 0, SA_DTYPE_F32 = 1 };
+enum { SA_MODE_BLOCKS = 0, SA_MODE_GATHER = 1 };
+
+/*
+ * Pattern descriptor.  A pair (q, kv) of absolute positions is allowed when
+ *
+ *     (!causal || kv <= q) && (local || sink || strided || global || unitband || random)
+ *
+ *   local    window_left >= 0 && q - kv <= window_left && kv - q <= window_right
+ *   sink     kv < sinks
+ *   strided  stride > 0 && q >= kv && (q - kv) % stride == stride_phase
+ *   global   q < global_tokens || kv < global_tokens
+ *   unitband unit > 0 && unit_window >= 0 && |q/unit - kv/unit| <= unit_window
+ *   random   unit > 0 && kv/unit is one of rand_units[(q/unit)*n_rand + 0..n_rand-1]
+ *            (rows q/unit >= rand_rows have no random units; -1 entries are empty)
+ *
+ * The terms are the glossary's fixed patterns (section on common sparsity
+ * patterns) and the blog's templates (section on the main sparsity
+ * templates; combining them is the norm, per the section that follows).
+ * The glossary's example mask (causal, q - kv <= 1024 or kv < 4) is
+ * causal=1, window_left=1024, window_right=0, sinks=4.
+ *
+ * rand_units is a DEVICE pointer (int32, rand_rows x n_rand, row-major),
+ * NULL when n_rand == 0.  n_rand <= 8.
+ */
+typedef struct sa_pattern {
+    int64_t causal;
+    int64_t q_offset;
+    int64_t window_left;
+    int64_t window_right;
+    int64_t sinks;
+    int64_t stride;
+    int64_t stride_phase;
+    int64_t global_tokens;
+    int64_t unit;
+    int64_t unit_window;
+    const int32_t *rand_units;
+    int64_t n_rand;
+    int64_t rand_rows;
+} sa_pattern;
+
+/*
+ * sa_build_block_mask -- mask to per-query-block lists of live key blocks.
+ * ("Sparse Attention" glossary, section on turning a pattern into savings:
+ * the mask split into blocks, the blocks holding no allowed pair skipped.)
+ *
+ * The score matrix n_q x n_kv is cut into tiles of block_q x block_kv (the
+ * last row/column of tiles clipped to the matrix).  For every tile the
+ * number of allowed pairs is counted; a tile is live when the count is > 0,
+ * full when it equals the clipped tile size, partial otherwise.
+ *
+ * Outputs (DEVICE pointers, caller-allocated, nqb = ceil(n_q/block_q),
+ * nkb = ceil(n_kv/block_kv)):
+ *   kv_count   int32 [nqb]         live key blocks of query block i
+ *   kv_index   int32 [nqb * nkb]   row i: live key-block ids ascending, then -1
+ *   kv_partial uint8 [nqb * nkb]   aligned with kv_index: 1 partial, 0 full/pad
+ *   live_pairs int64 [1]           total allowed pairs over the whole matrix
+ * block_q and block_kv must be multiples of 32 in [32, 1024].
+ */
+sa_status sa_build_block_mask(const sa_pattern *pattern, int64_t n_q, int64_t n_kv,
+                              int32_t block_q, int32_t block_kv, int32_t *kv_count,
+                              int32_t *kv_index, uint8_t *kv_partial, int64_t *live_pairs,
+                              void *stream);
+
+/*
+ * Arguments of sa_attn_fwd.  All tensor pointers are DEVICE pointers.
+ *
+ *   q [batch, heads, n_q, head_dim], k/v [batch, heads, n_kv, head_dim]
+ *     bfloat16, element strides {batch, head, row} in *_strides; the last
+ *     dimension is contiguous; row strides and base addresses 16-byte aligned.
+ *   o [batch, heads, n_q, head_dim] with o_strides, dtype o_dtype.
+ *   lse float32 [batch, heads, n_q] contiguous, natural-log logsumexp of the
+ *     scaled allowed scores (-inf for a row with no allowed key); may be NULL.
+ *   softmax_scale <= 0 selects 1/sqrt(head_dim) (the blog's scaling).
+ *   head_dim is 64 or 128.
+ *
+ * mode SA_MODE_BLOCKS: block lists from sa_build_block_mask for the same
+ *   pattern, n_q, n_kv, block_q, block_kv (shared by every batch and head).
+ *   Only live tiles are visited; the pattern is evaluated per pair only on
+ *   partial tiles (and on tiles clipped by n_kv).  block_q must be 64 or 128
+ *   and block_kv 64 or 128.
+ * mode SA_MODE_GATHER: per-query key lists gather_idx int32 [n_q, topk]
+ *   (row r lists key rows for query row r; entries < 0 or >= n_kv are
+ *   skipped), shared by every batch and head when gather_bh_stride == 0,
+ *   otherwise list of (b, h) starts at (b*heads + h) * gather_bh_stride.
+ *   The pattern and block fields are ignored.  (Glossary, section on common
+ *   sparsity patterns: full attention over the indexer's selected tokens.)
+ */
+typedef struct sa_attn_args {
+    const void *q;
+    const void *k;
+    const void *v;
+    void *o;
+    float *lse;
+    int64_t batch;
+    int64_t heads;
+    int64_t n_q;
+    int64_t n_kv;
+    int64_t head_dim;
+    int64_t o_dtype;
+    int64_t q_strides[3];
+    int64_t k_strides[3];
+    int64_t v_strides[3];
+    int64_t o_strides[3];
+    double softmax_scale;
+    int64_t mode;
+    int64_t block_q;
+    int64_t block_kv;
+    const int32_t *kv_count;
+    const int32_t *kv_index;
+    const uint8_t *kv_partial;
+    sa_pattern pattern;
+    const int32_t *gather_idx;
+    int64_t topk;
+    int64_t gather_bh_stride;
+} sa_attn_args;
+
+/*
+ * sa_attn_fwd -- O = softmax(Q K^T * scale restricted to allowed pairs) V, and LSE.
+ * Computed in bfloat16 MFMA products with float32 accumulation; the softmax
+ * runs in float32 (online over the visited tiles).  Returns as described in
+ * the conventions above.
+ */
+sa_status sa_attn_fwd(const sa_attn_args *args, void *stream);
+
+/*
+ * sa_indexer_scores -- indexer score of query row r (position t = q_offset + r)
+ * against every earlier key s <= t: a float32 fused-multiply-add chain over
+ * the d_idx products in index order (the glossary's DeepSeek Sparse
+ * Attention indexer, section on common sparsity patterns; the pages give no
+ * formula, the plain dot product is used).
+ *   q_idx bf16 [n_q, d_idx], k_idx bf16 [n_kv, d_idx] (DEVICE, contiguous)
+ *   scores float32 [n_q, n_kv] (DEVICE): entries s <= min(t, n_kv-1) are
+ *   written; the others are left untouched.
+ * d_idx must be a multiple of 8 in [8, 256].
+ */
+sa_status sa_indexer_scores(const void *q_idx, const void *k_idx, int64_t n_q, int64_t n_kv,
+                            int32_t d_idx, int64_t q_offset, float *scores, void *stream);
+
+/*
+ * sa_topk -- per query row, the topk candidates first in the total order
+ * (score descending, key index ascending); candidates of row r are
+ * s = 0 .. min(q_offset + r, n_kv - 1).  Output idx int32 [n_q, topk]
+ * (DEVICE): the selected key indices in ascending order, -1 padded when a
+ * row has fewer candidates.  -0.0 and +0.0 compare equal; scores must not
+ * be NaN (NaN ranks as the largest value).  topk in [1, 4096], n_kv < 2^20.
+ */
+sa_status sa_topk(const float *scores, int64_t n_q, int64_t n_kv, int64_t q_offset, int32_t topk,
+                  int32_t *idx_out, void *stream);
+
+/* sa_indexer_topk -- sa_indexer_scores into `scores` (workspace, n_q*n_kv
+ * floats, DEVICE) followed by sa_topk. */
+sa_status sa_indexer_topk(const void *q_idx, const void *k_idx, int64_t n_q, int64_t n_kv,
+                          int32_t d_idx, int64_t q_offset, int32_t topk, float *scores,
+                          int32_t *idx_out, void *stream);
+
+/* Thread-local text of the last non-OK status of this thread ("" if none). */
+const char *sa_last_error(void);
+
+/* SA_ABI_VERSION of the library. */
+int32_t sa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SA_H */

@@ -1,0 +1,157 @@
+"""GPU block-sparse attention vs the fp64 oracle (O <= 1e-2, LSE <= 1e-3)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import block_sparse_attention_sa_amd as sa
+from block_sparse_attention_sa_amd import workloads as W
+from tests.parity_util import (check_o_lse, gpu_rows, random_pattern, sample_rows, to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(pat, q, k, v, bq, bk, o_dtype=torch.float32):
+    n_q, n_kv = q.shape[2], k.shape[2]
+    bl = sa.build_block_mask(pat, n_q, n_kv, bq, bk)
+    return sa.attn_fwd(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), bl, o_dtype=o_dtype)
+
+
+def _rand(rng, B, H, nq, nkv, d):
+    f = lambda *s: W.f32_to_bf16_bits(rng.standard_normal(s, dtype=np.float32))
+    return f(B, H, nq, d), f(B, H, nkv, d), f(B, H, nkv, d)
+
+
+CASES = [(d, bq, bk, of) for d in (64, 128) for bq in (64, 128) for bk in (64, 128)
+         for of in ("f32", "bf16")]
+
+
+@pytest.mark.parametrize("d,bq,bk,of", CASES)
+def test_small_ragged_window_sinks(d, bq, bk, of):
+    rng = np.random.default_rng(d * 7 + bq + bk * 3 + (of == "bf16"))
+    n_q, n_kv = 333, 301
+    q, k, v = _rand(rng, 2, 2, n_q, n_kv, d)
+    pat = dict(causal=1, window_left=90, window_right=0, sinks=3, q_offset=10)
+    print(f"attn small d={d} bq={bq} bk={bk} o={of}", flush=True)
+    od = torch.float32 if of == "f32" else torch.bfloat16
+    o, lse = _run(pat, q, k, v, bq, bk, od)
+    o_ref, lse_ref = oracle.attn_rows(pat, q, k, v)
+    check_o_lse(o.float().cpu().numpy().reshape(-1, d), lse.cpu().numpy().reshape(-1), o_ref, lse_ref,
+                bf16_out=(of == "bf16"), ctx=f"d={d} bq={bq} bk={bk} {of}")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_patterns(seed):
+    rng = np.random.default_rng(900 + seed)
+    d = int(rng.choice([64, 128]))
+    bq, bk = int(rng.choice([64, 128])), int(rng.choice([64, 128]))
+    n_q, n_kv = int(rng.integers(1, 400)), int(rng.integers(1, 400))
+    pat = random_pattern(rng, n_q, n_kv)
+    q, k, v = _rand(rng, 1, 2, n_q, n_kv, d)
+    print(f"attn random seed={seed} d={d} bq={bq} bk={bk} n_q={n_q} n_kv={n_kv} {sorted(pat)}", flush=True)
+    o, lse = _run(pat, q, k, v, bq, bk)
+    o_ref, lse_ref = oracle.attn_rows(pat, q, k, v)
+    check_o_lse(o.cpu().numpy().reshape(-1, d), lse.cpu().numpy().reshape(-1), o_ref, lse_ref,
+                ctx=f"seed {seed}")
+
+
+def test_config1_full():
+    cfg = W.attn_config(1)
+    inp = W.attn_inputs(cfg)
+    o, lse = _run(cfg.pattern, inp["q"], inp["k"], inp["v"], cfg.block, cfg.block)
+    o_ref, lse_ref = oracle.attn_rows(cfg.pattern, inp["q"], inp["k"], inp["v"])
+    check_o_lse(o.cpu().numpy().reshape(-1, cfg.d), lse.cpu().numpy().reshape(-1), o_ref, lse_ref,
+                ctx="config 1")
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4])
+@pytest.mark.parametrize("of", ["f32", "bf16"])
+def test_full_configs_sampled_rows(cid, of):
+    """Full-size launch (the benchmark's configuration); oracle on sampled rows."""
+    cfg = W.attn_config(cid)
+    inp = W.attn_inputs(cfg)
+    print(f"attn config {cid} o={of} B={cfg.B} H={cfg.H} N={cfg.N} d={cfg.d}", flush=True)
+    od = torch.float32 if of == "f32" else torch.bfloat16
+    o, lse = _run(cfg.pattern, inp["q"], inp["k"], inp["v"], cfg.block, cfg.block, od)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(cid)
+    rows = sample_rows(rng, cfg.B, cfg.H, cfg.N, 768)
+    o_ref, lse_ref = oracle.attn_rows(cfg.pattern, inp["q"], inp["k"], inp["v"], rows=rows)
+    check_o_lse(gpu_rows(o, rows), gpu_rows(lse, rows), o_ref, lse_ref, bf16_out=(of == "bf16"),
+                ctx=f"config {cid} {of}")
+    # every row finite (no empty rows in these configurations) and no NaN anywhere
+    assert torch.isfinite(lse).all() and torch.isfinite(o.float()).all()
+
+
+def test_value_ones_give_ones_and_weights_sum():
+    cfg = W.attn_config(2)
+    inp = W.attn_inputs(cfg, heads=4)
+    ones = np.full_like(inp["v"], W.f32_to_bf16_bits(np.ones(1, np.float32))[0])
+    o, lse = _run(cfg.pattern, inp["q"], inp["k"], ones, cfg.block, cfg.block)
+    assert float((o - 1.0).abs().max()) <= 1e-2
+
+
+def test_zero_queries_closed_form():
+    """Q = 0: LSE = ln(number of allowed keys), O = mean of the allowed V rows."""
+    cfg = W.attn_config(1)
+    inp = W.attn_inputs(cfg)
+    q0 = np.zeros_like(inp["q"])
+    o, lse = _run(cfg.pattern, q0, inp["k"], inp["v"], cfg.block, cfg.block)
+    o_ref, lse_ref, cnt = oracle.attn_rows(cfg.pattern, q0, inp["k"], inp["v"], return_counts=True)
+    np.testing.assert_allclose(lse.cpu().numpy().reshape(-1), np.log(cnt), atol=1e-3, rtol=0)
+    check_o_lse(o.cpu().numpy().reshape(-1, cfg.d), lse.cpu().numpy().reshape(-1), o_ref, lse_ref)
+
+
+def test_rows_without_allowed_keys():
+    rng = np.random.default_rng(3)
+    q, k, v = _rand(rng, 1, 1, 200, 150, 64)
+    pat = dict(causal=1, window_left=5, window_right=0, q_offset=0)
+    # keys end at 150: rows q >= 156 see nothing
+    o, lse = _run(pat, q, k, v, 64, 64)
+    o_ref, lse_ref = oracle.attn_rows(pat, q, k, v)
+    assert np.isneginf(lse_ref).sum() > 0
+    check_o_lse(o.cpu().numpy().reshape(-1, 64), lse.cpu().numpy().reshape(-1), o_ref, lse_ref)
+
+
+def test_n_kv_zero():
+    rng = np.random.default_rng(4)
+    q, k, v = _rand(rng, 1, 1, 70, 0, 64)
+    o, lse = _run(dict(causal=1, window_left=5), q, k, v, 64, 64)
+    assert torch.isneginf(lse).all() and (o == 0).all()
+
+
+def test_run_to_run_bit_identical():
+    cfg = W.attn_config(2)
+    inp = W.attn_inputs(cfg, heads=4)
+    q, k, v = (to_dev_bf16(inp[t]) for t in ("q", "k", "v"))
+    bl = sa.build_block_mask(cfg.pattern, cfg.N, cfg.N, cfg.block, cfg.block)
+    o1, l1 = sa.attn_fwd(q, k, v, bl)
+    o2, l2 = sa.attn_fwd(q, k, v, bl)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_strided_layout_matches_contiguous():
+    """[B, N, H, d] storage passed through strides gives the same result."""
+    rng = np.random.default_rng(6)
+    B, H, N, d = 1, 3, 256, 128
+    q, k, v = _rand(rng, B, H, N, N, d)
+    pat = dict(causal=1, window_left=60, window_right=0, sinks=2)
+    o_ref, l_ref = _run(pat, q, k, v, 128, 64)
+    qt, kt, vt = (to_dev_bf16(np.ascontiguousarray(x.transpose(0, 2, 1, 3))).permute(0, 2, 1, 3)
+                  for x in (q, k, v))
+    bl = sa.build_block_mask(pat, N, N, 128, 64)
+    out = torch.empty((B, N, H, d), dtype=torch.float32, device="cuda").permute(0, 2, 1, 3)
+    o, l = sa.attn_fwd(qt, kt, vt, bl, out=out)
+    assert torch.equal(o, o_ref) and torch.equal(l, l_ref)
+
+
+def test_dense_pattern_matches_causal_sdpa_fp32():
+    """A window covering everything is plain causal attention (fp32 CPU reference)."""
+    rng = np.random.default_rng(8)
+    B, H, N, d = 1, 2, 384, 128
+    q, k, v = _rand(rng, B, H, N, N, d)
+    o, _ = _run(dict(causal=1, window_left=N), q, k, v, 128, 128)
+    tq, tk, tv = (torch.from_numpy(W.bf16_bits_to_f32(x)) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True)
+    assert float((o.cpu() - ref).abs().max()) <= 1e-2

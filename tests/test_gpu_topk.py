@@ -1,0 +1,150 @@
+"""GPU indexer, top-k and gather attention vs the oracle.
+
+Indexer scores and top-k indices are compared bit for bit (the indexer's
+float32 chain has one fixed order on both sides).  Gather attention is
+compared with the oracle evaluated on the GPU's own index lists, which
+isolates the attention error from the selection.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import block_sparse_attention_sa_amd as sa
+from block_sparse_attention_sa_amd import workloads as W
+from tests.parity_util import check_o_lse, gpu_rows, sample_rows, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _rbf(rng, *shape):
+    return W.f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+
+
+@pytest.mark.parametrize("n_q,n_kv,d,off", [(1, 1, 64, 0), (70, 300, 64, 230), (64, 1000, 32, 900),
+                                            (130, 4100, 128, 3970), (5, 257, 8, 0)])
+def test_indexer_bit_exact(n_q, n_kv, d, off):
+    rng = np.random.default_rng(n_q + n_kv)
+    qi, ki = _rbf(rng, n_q, d), _rbf(rng, n_kv, d)
+    print(f"indexer n_q={n_q} n_kv={n_kv} d={d} off={off}", flush=True)
+    got = torch.full((n_q, n_kv), float("nan"), device="cuda")
+    sa.indexer_scores(to_dev_bf16(qi), to_dev_bf16(ki), off, scores=got)
+    want = oracle.indexer_scores(qi, ki, off)
+    g = got.cpu().numpy()
+    for r in range(n_q):
+        nc = min(off + r + 1, n_kv)
+        assert np.array_equal(g[r, :nc].view(np.uint32), want[r, :nc].view(np.uint32)), f"row {r}"
+        assert np.all(np.isnan(g[r, nc:])), "entries beyond the candidates must be untouched"
+
+
+@pytest.mark.parametrize("n_q,n_kv,k,off", [(40, 5000, 2048, 4960), (16, 65536, 2048, 65520),
+                                            (8, 3000, 4096, 2992), (12, 777, 100, 700), (4, 9, 3, 0)])
+def test_topk_bit_exact(n_q, n_kv, k, off):
+    rng = np.random.default_rng(k + n_kv)
+    qi, ki = _rbf(rng, n_q, 64), _rbf(rng, n_kv, 64)
+    print(f"topk n_q={n_q} n_kv={n_kv} k={k} off={off}", flush=True)
+    idx, scores = sa.indexer_topk(to_dev_bf16(qi), to_dev_bf16(ki), off, k)
+    s = scores.cpu().numpy()
+    n_cand = np.minimum(np.arange(n_q) + off + 1, n_kv)
+    want = oracle.topk_rows(s, n_cand, k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), want)
+
+
+def test_topk_ties_signed_zero_and_padding():
+    rng = np.random.default_rng(77)
+    n_q, n_kv, k = 6, 6000, 2048
+    s = rng.integers(-3, 4, size=(n_q, n_kv)).astype(np.float32)  # heavy ties
+    s[1] = 0.0
+    s[1, ::2] = -0.0
+    s[2, :] = -1.0
+    scores = torch.from_numpy(s).cuda()
+    for off in (0, 1500, 5999):
+        got = sa.topk(scores, off, k).cpu().numpy()
+        want = oracle.topk_rows(s, np.minimum(np.arange(n_q) + off + 1, n_kv), k)
+        np.testing.assert_array_equal(got, want, err_msg=f"offset {off}")
+    # all-zero indexer queries: every score ties, lowest indices win
+    ki = _rbf(rng, 4000, 64)
+    idx, _ = sa.indexer_topk(torch.zeros((3, 64), dtype=torch.bfloat16, device="cuda"), to_dev_bf16(ki), 3997, 2048)
+    assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(2048, dtype=np.int32), (3, 1)))
+
+
+def test_config5_indexer_topk_sampled_rows():
+    cfg = W.topk_config(5)
+    inp = W.topk_inputs(cfg)
+    qi, ki = to_dev_bf16(inp["q_idx"]), to_dev_bf16(inp["k_idx"])
+    print("config 5 indexer+topk full size", flush=True)
+    idx, scores = sa.indexer_topk(qi, ki, cfg.q_offset, cfg.topk)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 511, 1022, 1023] + list(np.random.default_rng(5).choice(1024, 27, replace=False)))
+    rows = np.unique(rows).astype(np.int64)
+    want_s = oracle.indexer_scores(inp["q_idx"], inp["k_idx"], cfg.q_offset, rows=rows)
+    got_s = scores.cpu().numpy()[rows]
+    for i, r in enumerate(rows):
+        nc = cfg.q_offset + r + 1
+        assert np.array_equal(got_s[i, :nc].view(np.uint32), want_s[i, :nc].view(np.uint32)), f"row {r}"
+    want_idx = oracle.topk_rows(want_s, cfg.q_offset + rows + 1, cfg.topk)
+    np.testing.assert_array_equal(idx.cpu().numpy()[rows], want_idx)
+
+
+# ---------------------------------------------------------------------------
+# gather attention
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("of", ["f32", "bf16"])
+def test_gather_small_per_head_and_shared(d, of):
+    rng = np.random.default_rng(d)
+    B, H, n_q, n_kv, k = 1, 3, 50, 700, 96
+    q, kk, v = _rbf(rng, B, H, n_q, d), _rbf(rng, B, H, n_kv, d), _rbf(rng, B, H, n_kv, d)
+    od = torch.float32 if of == "f32" else torch.bfloat16
+    shared = np.stack([np.sort(rng.choice(n_kv, k, replace=False)) for _ in range(n_q)]).astype(np.int32)
+    shared[3, 50:] = -1          # padding
+    shared[4, :] = -1            # no keys at all
+    o, lse = sa.attn_fwd(to_dev_bf16(q), to_dev_bf16(kk), to_dev_bf16(v), gather_idx=torch.from_numpy(shared).cuda(),
+                         o_dtype=od)
+    o_ref, lse_ref = oracle.attn_gather_rows(q, kk, v, shared)
+    check_o_lse(o.float().cpu().numpy().reshape(-1, d), lse.cpu().numpy().reshape(-1), o_ref, lse_ref,
+                bf16_out=(of == "bf16"), ctx="shared")
+    per = np.stack([np.stack([np.sort(rng.choice(n_kv, k, replace=False)) for _ in range(n_q)])
+                    for _ in range(B * H)]).astype(np.int32)
+    o, lse = sa.attn_fwd(to_dev_bf16(q), to_dev_bf16(kk), to_dev_bf16(v),
+                         gather_idx=torch.from_numpy(per.reshape(B, H, n_q, k)).cuda(), o_dtype=od)
+    o_ref, lse_ref = oracle.attn_gather_rows(q, kk, v, per, idx_per_head=True)
+    check_o_lse(o.float().cpu().numpy().reshape(-1, d), lse.cpu().numpy().reshape(-1), o_ref, lse_ref,
+                bf16_out=(of == "bf16"), ctx="per head")
+
+
+def test_gather_of_whole_blocks_equals_block_mode():
+    """Index lists that are unions of whole key blocks reproduce the block kernel."""
+    cfg = W.attn_config(1)
+    inp = W.attn_inputs(cfg)
+    pat = dict(causal=0, unit=64, unit_window=0, global_tokens=64)  # every live tile full
+    bl = sa.build_block_mask(pat, cfg.N, cfg.N, 64, 64)
+    assert int(bl.kv_partial.sum()) == 0
+    q, k, v = (to_dev_bf16(inp[t]) for t in ("q", "k", "v"))
+    o_b, l_b = sa.attn_fwd(q, k, v, bl)
+    cnt, idx = bl.kv_count.cpu().numpy(), bl.kv_index.cpu().numpy()
+    lists = []
+    for r in range(cfg.N):
+        blocks = idx[r // 64, : cnt[r // 64]]
+        lists.append(np.concatenate([np.arange(b * 64, b * 64 + 64) for b in blocks]))
+    kmax = max(len(x) for x in lists)
+    g = np.full((cfg.N, kmax), -1, np.int32)
+    for r, x in enumerate(lists):
+        g[r, : len(x)] = x
+    o_g, l_g = sa.attn_fwd(q, k, v, gather_idx=torch.from_numpy(g).cuda())
+    assert float((o_g - o_b).abs().max()) <= 2e-3
+    assert float((l_g - l_b).abs().max()) <= 1e-4
+
+
+def test_config5_gather_sampled_rows():
+    cfg = W.topk_config(5)
+    inp = W.topk_inputs(cfg)
+    idx, _ = sa.indexer_topk(to_dev_bf16(inp["q_idx"]), to_dev_bf16(inp["k_idx"]), cfg.q_offset, cfg.topk)
+    print("config 5 gather attention full size", flush=True)
+    q, k, v = (to_dev_bf16(inp[t]) for t in ("q", "k", "v"))
+    o, lse = sa.attn_fwd(q, k, v, gather_idx=idx)
+    torch.cuda.synchronize()
+    rows = sample_rows(np.random.default_rng(55), 1, cfg.H, cfg.n_q, 256)
+    o_ref, lse_ref = oracle.attn_gather_rows(inp["q"], inp["k"], inp["v"], idx.cpu().numpy(), rows=rows)
+    check_o_lse(gpu_rows(o, rows), gpu_rows(lse, rows), o_ref, lse_ref, ctx="config 5")
