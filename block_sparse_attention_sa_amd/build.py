@@ -27,9 +27,15 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags.  The attention kernel keeps its MFMA results in
+# VGPRs (the softmax reads every score with VALU instructions); the allocator
+# then uses AGPRs as spill space instead of scratch memory.
+EXTRA = {"attn_block.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

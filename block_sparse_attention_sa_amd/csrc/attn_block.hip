@@ -10,21 +10,24 @@
 // marked partial (or clipped by the sequence end); the softmax is carried
 // online across tiles (running max, running sum, rescaled accumulator).
 //
-// gfx950 mapping.  A workgroup owns one (batch, head, query block) and has
-// BQ/32 waves of 32 query rows each.  Per live tile:
-//   * K and V tiles [BK x D] bf16 are copied HBM -> LDS with 16-byte loads
-//     (XOR-swizzled 16-byte chunks so MFMA operand reads avoid bank
-//     conflicts);
-//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the
-//     wave's Q^T held in registers).  In the accumulator layout one lane
-//     holds one query column, so row max / row sum are in-lane reductions
-//     plus one v_permlane32_swap between the two half-waves;
-//   * P^T (bf16) stays in the accumulator registers and is directly the B
-//     operand of O^T += V^T P^T; the V^T operand is read from LDS with
-//     ds_read_b64_tr_b16 (transposing 16-bit reads), so no transpose pass;
-//   * exp2 with the scale folded into one FMA; the running max is raised
-//     only when some row's tile max exceeds it by more than 8 (log2 units),
-//     which keeps every exponent <= 2^8 and skips most accumulator rescales.
+// gfx950 mapping.  A workgroup owns one (batch, head, query block of BQ rows)
+// and has BQ/64 waves; each wave owns 64 query rows as two 32-query column
+// blocks, so every K and V^T operand read from LDS feeds two MFMAs.
+//   * K and V tiles [BK x D] go HBM -> LDS by buffer loads with LDS
+//     destination (no staging registers).  Rows past the sequence end fall
+//     outside the buffer range and read as zero.  16-byte chunks are XOR
+//     swizzled per row so the operand reads hit distinct banks.
+//   * K and V phases are split so the DMA of the next K tile overlaps the
+//     softmax and P.V of the current tile, and the DMA of the next V tile
+//     overlaps the next Q.K^T.  Two workgroups share a CU (one wave per SIMD).
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T
+//     in registers).  In the accumulator layout one lane holds one query, so
+//     row max / row sum are in-lane reductions plus one v_permlane32_swap.
+//   * P^T (bf16) stays in registers as the B operand of O^T += V^T P^T; V^T
+//     is read with ds_read_b64_tr_b16 (transposing 16-bit reads).
+//   * exp2 with the scale folded into one FMA; the running max is raised only
+//     when a row's tile max exceeds it by more than 8 (log2 units), so every
+//     exponent stays <= 2^8 and most accumulator rescales are skipped.
 #include "sa_internal.h"
 
 namespace sa {
@@ -32,10 +35,12 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLazyLog2 = 8.0f;  // rescale threshold in log2 units
 
@@ -62,34 +67,55 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg)
     return base + slot;
 }
 
-__device__ __forceinline__ float wave_swap_other(float v)
+__device__ __forceinline__ float other_half(float v)
 {
-    // value of lane l ^ 32
+    // value held by lane l ^ 32
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return (threadIdx.x & 32) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
 }
 
+// Wait until at most N buffer loads of this wave are outstanding and all LDS
+// operations have completed (gfx9 s_waitcnt encoding), then barrier.  The
+// plain s_barrier keeps outstanding DMA of the other tensor in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+    __builtin_amdgcn_s_barrier();
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes)
+{
+    const int32_t n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
 template <int D, int BQ, int BK, bool OF32>
-__global__ void __launch_bounds__(BQ * 2)
+__global__ void __launch_bounds__(BQ)
 attn_block_kernel(AttnParams a)
 {
-    constexpr int NW = BQ / 32;
-    constexpr int T = NW * 64;
-    constexpr int CH = D / 8;             // 16-byte chunks per row
-    constexpr int NSB = BK / 32;          // 32-key sub-blocks per tile
-    constexpr int NDC = D / 16;           // k-steps of S^T
-    constexpr int NDB = D / 32;           // 32-wide output column blocks
-    constexpr int LOADS = BK * CH / T;    // 16-byte loads per thread per tensor
-    static_assert(BK * CH % T == 0, "tile load split");
+    constexpr int NW = BQ / 64;                   // waves, 64 query rows each
+    constexpr int NB = 2;                         // 32-query column blocks per wave
+    constexpr int KS = 64;                        // keys per sub-tile (compute and DMA unit)
+    constexpr int SUB = BK / KS;                  // sub-tiles per listed key block
+    constexpr int CH = D / 8;                     // 16-byte chunks per row
+    constexpr int NSB = KS / 32;                  // 32-key MFMA blocks per sub-tile
+    constexpr int NDC = D / 16;                   // k-steps of S^T
+    constexpr int NDB = D / 32;                   // 32-wide output column blocks
+    constexpr int ROWS_PER_KB = 1024 / (D * 2);   // sub-tile rows per 1 KB DMA instruction
+    constexpr int SUBTILE_BYTES = KS * D * 2;
+    constexpr int DMA_W = SUBTILE_BYTES / 1024 / NW;  // DMA instructions per wave per tensor
+    static_assert(SUBTILE_BYTES / 1024 % NW == 0, "DMA split");
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BK * D * 2];
-    uint8_t* const kl = smem;
-    uint8_t* const vl = smem + BK * D * 2;
+    // double-buffered K and V sub-tiles
+    __shared__ __attribute__((aligned(1024))) uint8_t kl[2][SUBTILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t vl[2][SUBTILE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int hh = lane >> 5;     // half-wave
+    const int hh = lane >> 5;  // half-wave
     const int l32 = lane & 31;
 
     const int item = xcd_remap(blockIdx.x, gridDim.x);
@@ -98,181 +124,244 @@ attn_block_kernel(AttnParams a)
     const int b = bh / a.heads, h = bh % a.heads;
 
     const uint16_t* qg = a.q + b * a.q_sb + h * a.q_sh;
-    const uint16_t* kg = a.k + b * a.k_sb + h * a.k_sh;
-    const uint16_t* vg = a.v + b * a.v_sb + h * a.v_sh;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + b * a.k_sb + h * a.k_sh, (int64_t)a.n_kv * a.k_sn * 2);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + b * a.v_sb + h * a.v_sh, (int64_t)a.n_kv * a.v_sn * 2);
+    const uint32_t krow_b = (uint32_t)(a.k_sn * 2), vrow_b = (uint32_t)(a.v_sn * 2);
 
-    const int qrow = qb * BQ + wave * 32 + l32;
-    const bool qvalid = qrow < a.n_q;
+    const int32_t* idx_row = a.kv_index + (int64_t)qb * a.nkb;
+    const uint8_t* part_row = a.kv_partial + (int64_t)qb * a.nkb;
+    const int n_sub = a.kv_count[qb] * SUB;
+    // first key of sub-tile t; a list entry that is not a key block maps past
+    // the sequence end, where the DMA reads zeros and the mask drops every key
+    auto sub_kv0 = [&](int t) {
+        const int j = idx_row[t / SUB];
+        return ((unsigned)j < (unsigned)a.nkb ? j : a.nkb) * BK + (t % SUB) * KS;
+    };
 
-    // Q^T operand: lane holds q[qrow][16*dc + 8*hh + 0..7]
-    bf16x8 qf[NDC];
+    // DMA of sub-tile t into buffer slot: lane -> (row within its 1 KB group, physical chunk)
+    const int dma_r = lane / CH;
+    const int dma_p = lane % CH;
+    auto dma = [&](int kv0, int slot) {
 #pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) {
-        u32x4 raw = {0u, 0u, 0u, 0u};
-        if (qvalid) raw = *reinterpret_cast<const u32x4*>(qg + (int64_t)qrow * a.q_sn + 16 * dc + 8 * hh);
-        qf[dc] = __builtin_bit_cast(bf16x8, raw);
+        for (int i = 0; i < DMA_W; ++i) {
+            const int g = wave + i * NW;
+            const int r = g * ROWS_PER_KB + dma_r;
+            const uint32_t koff = (uint32_t)(kv0 + r) * krow_b + (uint32_t)((dma_p ^ kswz<D>(r)) << 4);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kl[slot] + g * 1024), 16, koff, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < DMA_W; ++i) {
+            const int g = wave + i * NW;
+            const int r = g * ROWS_PER_KB + dma_r;
+            const uint32_t voff = (uint32_t)(kv0 + r) * vrow_b + (uint32_t)((dma_p ^ vswz<D>(r)) << 4);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vl[slot] + g * 1024), 16, voff, 0, 0, 0);
+        }
+    };
+    if (n_sub > 0) dma(sub_kv0(0), 0);
+
+    // Q^T operands: column block nb, lane holds q[row][16*dc + 8*hh + 0..7]
+    int qrow[NB];
+    bf16x8 qf[NB][NDC];
+    RowCtx rc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        qrow[nb] = qb * BQ + wave * 64 + nb * 32 + l32;
+        const bool ok = qrow[nb] < a.n_q;
+#pragma unroll
+        for (int dc = 0; dc < NDC; ++dc) {
+            u32x4 raw = {0u, 0u, 0u, 0u};
+            if (ok) raw = *reinterpret_cast<const u32x4*>(qg + (int64_t)qrow[nb] * a.q_sn + 16 * dc + 8 * hh);
+            qf[nb][dc] = __builtin_bit_cast(bf16x8, raw);
+        }
+        row_ctx(a.pat, qrow[nb] + a.pat.q_offset, rc[nb]);
     }
 
-    RowCtx rc;
-    row_ctx(a.pat, qrow + a.pat.q_offset, rc);
-
-    f32x16 o[NDB];
+    f32x16 o[NB][NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-        for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-    float m_run = -INFINITY;
-    float l_run = 0.f;
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[nb][db][i] = 0.f;
+    float m_run[NB] = {-INFINITY, -INFINITY};
+    float l_run[NB] = {0.f, 0.f};
     const float c = a.scale_log2;
     const float thr = kLazyLog2 / c;
 
-    const int n_tiles = a.kv_count[qb];
-    const int32_t* idx_row = a.kv_index + (int64_t)qb * a.nkb;
-    const uint8_t* part_row = a.kv_partial + (int64_t)qb * a.nkb;
+    // V^T transposed-read lane geometry
+    const int tg = lane >> 4, tj = lane & 15;
+    const int vrow_off = 4 * (tg >> 1) + (tj >> 2);
+    const int vcol_off = 16 * (tg & 1) + 4 * (tj & 3);
 
-    for (int e = 0; e < n_tiles; ++e) {
-        const int j = idx_row[e];
-        if ((unsigned)j >= (unsigned)a.nkb) continue;  // not a key block: skip (uniform)
-        const int kv0 = j * BK;
-        const bool need_mask = part_row[e] != 0 || kv0 + BK > a.n_kv;
+    for (int t = 0; t < n_sub; ++t) {
+        const int slot = t & 1;
+        const int kv0 = sub_kv0(t);
+        const int ej = idx_row[t / SUB];
+        const bool need_mask = (unsigned)ej >= (unsigned)a.nkb || part_row[t / SUB] != 0 || kv0 + KS > a.n_kv;
 
-        // ---- HBM -> registers
-        u32x4 kr[LOADS], vr[LOADS];
+        // sub-tile t has landed in every wave's share; every wave is done with t-1
+        wait_vm_barrier<0>();
+        if (t + 1 < n_sub) dma(sub_kv0(t + 1), slot ^ 1);
+        const uint8_t* kb = kl[slot];
+        const uint8_t* vb = vl[slot];
+
+        // allowed-key bits of partial / clipped sub-tiles, computed before the
+        // score registers are live; all ones on full sub-tiles
+        uint32_t mbits[NB][NSB];
 #pragma unroll
-        for (int it = 0; it < LOADS; ++it) {
-            const int u = tid + it * T;
-            const int r = u / CH, cc = u % CH;
-            const int kv = kv0 + r;
-            u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
-            if (kv < a.n_kv) {
-                zk = *reinterpret_cast<const u32x4*>(kg + (int64_t)kv * a.k_sn + cc * 8);
-                zv = *reinterpret_cast<const u32x4*>(vg + (int64_t)kv * a.v_sn + cc * 8);
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb) {
+                uint32_t bits = 0xFFFFFFFFu;
+                if (need_mask) {
+                    const int64_t k0 = kv0 + sb * 32;
+                    bits = allowed_bits32(a.pat, rc[nb], k0) & range_bits32(0, a.n_kv, k0);
+                }
+                // accumulator element i holds key k0 + 8*(i/4) + 4*hh + i%4
+                mbits[nb][sb] = bits >> (4 * hh);
             }
-            kr[it] = zk;
-            vr[it] = zv;
-        }
-        __syncthreads();  // previous tile fully consumed
-#pragma unroll
-        for (int it = 0; it < LOADS; ++it) {
-            const int u = tid + it * T;
-            const int r = u / CH, cc = u % CH;
-            *reinterpret_cast<u32x4*>(kl + r * D * 2 + ((cc ^ kswz<D>(r)) << 4)) = kr[it];
-            *reinterpret_cast<u32x4*>(vl + r * D * 2 + ((cc ^ vswz<D>(r)) << 4)) = vr[it];
-        }
-        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
 
-        // ---- S^T = K Q^T
-        f32x16 s[NSB];
+        // ---- S^T = K Q^T  (K operands fetched one k-step ahead)
+        f32x16 s[NB][NSB];
 #pragma unroll
-        for (int sb = 0; sb < NSB; ++sb)
-            for (int i = 0; i < 16; ++i) s[sb][i] = 0.f;
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int dc = 0; dc < NDC; ++dc) {
+            for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[nb][sb][i] = 0.f;
+        bf16x8 ka[2][NSB];
+        auto load_k = [&](bf16x8* dst, int dc) {
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) {
                 const int r = sb * 32 + l32;
                 const int cc = 2 * dc + hh;
-                const bf16x8 ka = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4*>(kl + r * D * 2 + ((cc ^ kswz<D>(r)) << 4)));
-                s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[dc], s[sb], 0, 0, 0);
+                dst[sb] = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4*>(kb + r * D * 2 + ((cc ^ kswz<D>(r)) << 4)));
             }
-        }
-
-        // ---- element mask on partial / clipped tiles only
-        if (need_mask) {
+        };
+        load_k(ka[0], 0);
+#pragma unroll
+        for (int dc = 0; dc < NDC; ++dc) {
+            if (dc + 1 < NDC) load_k(ka[(dc + 1) & 1], dc + 1);
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int kv = kv0 + sb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-                    const bool ok = kv < a.n_kv && pair_allowed(a.pat, rc, kv);
-                    s[sb][i] = ok ? s[sb][i] : -INFINITY;
-                }
+                for (int nb = 0; nb < NB; ++nb)
+                    s[nb][sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[dc & 1][sb], qf[nb][dc], s[nb][sb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
 
-        // ---- online softmax (row = lane's query)
-        float mx = -INFINITY;
+        // ---- element mask on partial / clipped sub-tiles only
+        if (need_mask) {
 #pragma unroll
-        for (int sb = 0; sb < NSB; ++sb)
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
-        mx = fmaxf(mx, wave_swap_other(mx));
-        const float m_new = fmaxf(m_run, mx);
-        if (__any(m_new > m_run + thr)) {
-            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
-            l_run *= alpha;
+                for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        s[nb][sb][i] = (mbits[nb][sb] >> (8 * (i >> 2) + (i & 3))) & 1u ? s[nb][sb][i] : -INFINITY;
+        }
+
+        // ---- online softmax, one query per lane and column block; P packed to bf16
+        bf16x8 pk[NB][NSB][2];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[nb][sb][i]);
+            mx = fmaxf(mx, other_half(mx));
+            const float m_new = fmaxf(m_run[nb], mx);
+            if (__any(m_new > m_run[nb] + thr)) {
+                const float alpha =
+                    m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_run[nb] - m_new) * c);
+                l_run[nb] *= alpha;
+                // one 16-register accumulator block at a time keeps the
+                // temporaries of this rarely taken path small
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) o[nb][db][i] *= alpha;
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                m_run[nb] = m_new;
+            }
+            const float mc = m_run[nb] == -INFINITY ? 0.f : m_run[nb] * c;
+            float lsum = 0.f;
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][sb][8 * cb + u], c, -mc));
+                        lsum += p;
+                        pk[nb][sb][cb][u] = (__bf16)p;
+                    }
+            l_run[nb] += lsum;
+        }
+
+        // ---- O^T += V^T P^T  (V^T operands fetched one step ahead)
+        bf16x8 va[2][NDB];
+        auto load_v = [&](bf16x8* dst, int step) {
+            const int r0 = (step >> 1) * 32 + 16 * (step & 1) + vrow_off;
+            const int r1 = r0 + 8;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const int col = 32 * db + vcol_off;
+                const int ch = col >> 3, within = (col & 7) * 2;
+                const bf16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_bf16x4*)(vb + r0 * D * 2 + ((ch ^ vswz<D>(r0)) << 4) + within));
+                const bf16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_bf16x4*)(vb + r1 * D * 2 + ((ch ^ vswz<D>(r1)) << 4) + within));
+                dst[db] = bf16x8{t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+            }
+        };
+        load_v(va[0], 0);
+#pragma unroll
+        for (int step = 0; step < 2 * NSB; ++step) {
+            if (step + 1 < 2 * NSB) load_v(va[(step + 1) & 1], step + 1);
+            const int sb = step >> 1, cb = step & 1;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-            m_run = m_new;
-        }
-        const float mc = m_run == -INFINITY ? 0.f : m_run * c;
-        float lsum = 0.f;
-#pragma unroll
-        for (int sb = 0; sb < NSB; ++sb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][i], c, -mc));
-                s[sb][i] = p;
-                lsum += p;
-            }
-        l_run += lsum;
-
-        // ---- O^T += V^T P^T
-        const int g = lane >> 4, jj = lane & 15;
-        const int vrow_off = 4 * (g >> 1) + (jj >> 2);
-        const int vcol_off = 16 * (g & 1) + 4 * (jj & 3);
-#pragma unroll
-        for (int sb = 0; sb < NSB; ++sb) {
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-                bf16x8 pb;
-#pragma unroll
-                for (int t = 0; t < 8; ++t) pb[t] = (__bf16)s[sb][8 * cb + t];
-                const int r0 = sb * 32 + 16 * cb + vrow_off;
-                const int r1 = r0 + 8;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const int col = 32 * db + vcol_off;
-                    const int ch = col >> 3, within = (col & 7) * 2;
-                    const bf16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                        (lds_bf16x4*)(vl + r0 * D * 2 + ((ch ^ vswz<D>(r0)) << 4) + within));
-                    const bf16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                        (lds_bf16x4*)(vl + r1 * D * 2 + ((ch ^ vswz<D>(r1)) << 4) + within));
-                    const bf16x8 va = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[db], 0, 0, 0);
-                }
-            }
+                for (int nb = 0; nb < NB; ++nb)
+                    o[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[step & 1][db], pk[nb][sb][cb], o[nb][db], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
     // ---- epilogue
-    const float l_tot = l_run + wave_swap_other(l_run);
-    if (qvalid) {
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        const int64_t obase = b * a.o_sb + h * a.o_sh + (int64_t)qrow * a.o_sn;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+    for (int nb = 0; nb < NB; ++nb) {
+        const float l_tot = l_run[nb] + other_half(l_run[nb]);
+        if (qrow[nb] < a.n_q) {
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            const int64_t obase = b * a.o_sb + h * a.o_sh + (int64_t)qrow[nb] * a.o_sn;
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int dv = 32 * db + 8 * r4 + 4 * hh;
-                const float x0 = o[db][4 * r4 + 0] * inv, x1 = o[db][4 * r4 + 1] * inv;
-                const float x2 = o[db][4 * r4 + 2] * inv, x3 = o[db][4 * r4 + 3] * inv;
-                if (OF32) {
-                    float* op = reinterpret_cast<float*>(a.o) + obase + dv;
-                    *reinterpret_cast<float4*>(op) = make_float4(x0, x1, x2, x3);
-                } else {
-                    uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + obase + dv;
-                    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-                    const bf16x2 p01 = {(__bf16)x0, (__bf16)x1};
-                    const bf16x2 p23 = {(__bf16)x2, (__bf16)x3};
-                    const u32x2 w = {__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
-                    *reinterpret_cast<u32x2*>(op) = w;
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int dv = 32 * db + 8 * r4 + 4 * hh;
+                    const float x0 = o[nb][db][4 * r4 + 0] * inv, x1 = o[nb][db][4 * r4 + 1] * inv;
+                    const float x2 = o[nb][db][4 * r4 + 2] * inv, x3 = o[nb][db][4 * r4 + 3] * inv;
+                    if (OF32) {
+                        float* op = reinterpret_cast<float*>(a.o) + obase + dv;
+                        *reinterpret_cast<float4*>(op) = make_float4(x0, x1, x2, x3);
+                    } else {
+                        uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + obase + dv;
+                        const bf16x2 p01 = {(__bf16)x0, (__bf16)x1};
+                        const bf16x2 p23 = {(__bf16)x2, (__bf16)x3};
+                        const u32x2 w = {__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
+                        *reinterpret_cast<u32x2*>(op) = w;
+                    }
                 }
-            }
-        if (a.lse && hh == 0)
-            a.lse[((int64_t)b * a.heads + h) * a.n_q + qrow] =
-                l_tot > 0.f ? m_run * a.scale + logf(l_tot) : -INFINITY;
+            if (a.lse && hh == 0)
+                a.lse[((int64_t)b * a.heads + h) * a.n_q + qrow[nb]] =
+                    l_tot > 0.f ? m_run[nb] * a.scale + logf(l_tot) : -INFINITY;
+        }
     }
 }
 
@@ -280,8 +369,7 @@ template <int D, int BQ, int BK, bool OF32>
 hipError_t launch_one(const AttnParams& a, hipStream_t stream)
 {
     const int64_t items = (int64_t)a.batch * a.heads * a.nqb;
-    hipLaunchKernelGGL((attn_block_kernel<D, BQ, BK, OF32>), dim3((unsigned)items), dim3(BQ * 2), 0,
-                       stream, a);
+    hipLaunchKernelGGL((attn_block_kernel<D, BQ, BK, OF32>), dim3((unsigned)items), dim3(BQ), 0, stream, a);
     return hipGetLastError();
 }
 

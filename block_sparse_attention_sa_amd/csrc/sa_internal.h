@@ -63,7 +63,7 @@ struct DevPattern {
     FastDiv unit_div;
 };
 
-constexpr int kMaxRand = 8;
+constexpr int kMaxRand = 4;
 
 // Per-query quantities that do not change along a query row.
 struct RowCtx {
@@ -108,6 +108,53 @@ __device__ __forceinline__ bool pair_allowed(const DevPattern& p, const RowCtx& 
     if (p.causal)
         ok &= kv <= q;
     return ok;
+}
+
+// Bits [lo, hi) of the 32-key chunk [k0, k0 + 32), positions clamped to it.
+__device__ __forceinline__ uint32_t range_bits32(int64_t lo, int64_t hi, int64_t k0)
+{
+    const int64_t a = lo > k0 ? lo : k0;
+    const int64_t b = hi < k0 + 32 ? hi : k0 + 32;
+    if (b <= a) return 0u;
+    const uint32_t ua = (uint32_t)(a - k0), ub = (uint32_t)(b - k0);
+    const uint32_t hi_mask = ub >= 32 ? 0xFFFFFFFFu : ((1u << ub) - 1u);
+    return hi_mask & ~((1u << ua) - 1u);
+}
+
+// Allowed keys among [k0, k0 + 32) for the query of `r`, as a bit mask (bit i
+// = key k0 + i).  Every pattern term is an interval of keys for a fixed query
+// (or, for the strided term, a progression of at most 32/stride + 1 keys), so
+// the mask costs a few shifts instead of 32 predicate evaluations.  Keys past
+// the sequence end are not clipped here.
+__device__ __forceinline__ uint32_t allowed_bits32(const DevPattern& p, const RowCtx& r, int64_t k0)
+{
+    const int64_t q = r.q;
+    uint32_t m = range_bits32(0, p.sinks, k0);
+    if (p.window_left >= 0)
+        m |= range_bits32(q - p.window_left, q + (int64_t)p.window_right + 1, k0);
+    m |= (q < p.global_tokens) ? 0xFFFFFFFFu : range_bits32(0, p.global_tokens, k0);
+    if (p.stride > 0) {
+        // keys kv <= q - phase with (q - phase - kv) % stride == 0
+        const int64_t qp = q - p.stride_phase;
+        int64_t top = qp < k0 + 31 ? qp : k0 + 31;
+        if (top >= k0) {
+            const int32_t rem = fmod_((int32_t)(qp - top), p.stride_div);
+            for (int64_t kv = top - (rem == 0 ? 0 : p.stride - rem); kv >= k0; kv -= p.stride)
+                m |= 1u << (uint32_t)(kv - k0);
+        }
+    }
+    if (p.unit > 0) {
+        if (p.unit_window >= 0)
+            m |= range_bits32((int64_t)(r.qu - p.unit_window) * p.unit,
+                              (int64_t)(r.qu + p.unit_window + 1) * p.unit, k0);
+#pragma unroll
+        for (int i = 0; i < kMaxRand; ++i)
+            if (r.rnd[i] >= 0)
+                m |= range_bits32((int64_t)r.rnd[i] * p.unit, (int64_t)(r.rnd[i] + 1) * p.unit, k0);
+    }
+    if (p.causal)
+        m &= range_bits32(0, q + 1, k0);
+    return m;
 }
 
 // ---- launchers (defined in the .hip files) --------------------------------

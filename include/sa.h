@@ -72,7 +72,7 @@ enum { SA_MODE_BLOCKS = 0, SA_MODE_GATHER = 1 };
  * causal=1, window_left=1024, window_right=0, sinks=4.
  *
  * rand_units is a DEVICE pointer (int32, rand_rows x n_rand, row-major),
- * NULL when n_rand == 0.  n_rand <= 8.
+ * NULL when n_rand == 0.  n_rand <= 4.
  */
 typedef struct sa_pattern {
     int64_t causal;
