@@ -45,12 +45,13 @@ bool aligned16(const void* p)
 }
 
 // Validates the pattern and fills the kernels' form of it.
-sa_status make_pattern(const sa_pattern* p, int64_t n_q, sa::DevPattern& d)
+sa_status make_pattern(const sa_pattern* p, int64_t n_q, int64_t n_kv, sa::DevPattern& d)
 {
     if (!p) return fail(SA_ERR_INVALID_ARG, "pattern is NULL");
     if (p->q_offset < 0) return fail(SA_ERR_INVALID_ARG, "pattern.q_offset must be >= 0");
-    if (p->q_offset + n_q > kI32Max)
-        return fail(SA_ERR_UNSUPPORTED, "query positions must stay below 2^31");
+    // kernels do position arithmetic in int32: q + n_kv must stay in range
+    if (p->q_offset + n_q + n_kv + 64 > (int64_t(1) << 29))
+        return fail(SA_ERR_UNSUPPORTED, "query positions plus n_kv must stay below 2^29");
     if (p->window_left >= 0 && p->window_right < 0)
         return fail(SA_ERR_INVALID_ARG, "pattern.window_right must be >= 0 when the window is on");
     if (p->sinks < 0 || p->global_tokens < 0)
@@ -66,20 +67,32 @@ sa_status make_pattern(const sa_pattern* p, int64_t n_q, sa::DevPattern& d)
     if (p->n_rand > 0 && (!p->rand_units || p->rand_rows < 0))
         return fail(SA_ERR_INVALID_ARG, "pattern.rand_units is NULL or rand_rows < 0");
     d = sa::DevPattern{};
+    // Values beyond the sequence extents are clamped to them: positions never
+    // exceed q_max (queries) or n_kv (keys), so the predicate is unchanged and
+    // int32 arithmetic in the kernels cannot overflow.
+    const int64_t q_max = p->q_offset + n_q;
+    const int64_t ext = (q_max > n_kv ? q_max : n_kv) + 1;
     d.causal = p->causal != 0;
     d.q_offset = (int32_t)p->q_offset;
-    d.window_left = p->window_left < 0 ? -1 : clamp32(p->window_left);
-    d.window_right = clamp32(p->window_right < 0 ? 0 : p->window_right);
-    d.sinks = clamp32(p->sinks);
-    d.stride = p->stride > 0 ? (int32_t)p->stride : 0;
+    d.window_left = p->window_left < 0 ? -1 : (int32_t)(p->window_left < ext ? p->window_left : ext);
+    d.window_right = (int32_t)(p->window_right < 0 ? 0 : (p->window_right < ext ? p->window_right : ext));
+    d.sinks = (int32_t)(p->sinks < ext ? p->sinks : ext);
+    d.stride = p->stride > 0 ? (int32_t)(p->stride < ext ? p->stride : ext) : 0;
     d.stride_phase = (int32_t)(p->stride > 0 ? p->stride_phase : 0);
-    d.global_tokens = clamp32(p->global_tokens);
-    d.unit = p->unit > 0 ? (int32_t)p->unit : 0;
-    d.unit_window = p->unit > 0 && p->unit_window >= 0 ? clamp32(p->unit_window) : -1;
-    d.n_rand = p->unit > 0 ? (int32_t)p->n_rand : 0;
+    if (d.stride > 0 && d.stride_phase >= d.stride) d.stride_phase = d.stride;  // phase beyond every distance
+    d.global_tokens = (int32_t)(p->global_tokens < ext ? p->global_tokens : ext);
+    d.unit = p->unit > 0 ? (int32_t)(p->unit < ext ? p->unit : ext) : 0;
+    d.max_unit = d.unit > 0 ? (int32_t)(ext / d.unit + 1) : 0;
+    d.unit_window = d.unit > 0 && p->unit_window >= 0
+                        ? (int32_t)(p->unit_window < d.max_unit ? p->unit_window : d.max_unit)
+                        : -1;
+    d.n_rand = d.unit > 0 ? (int32_t)p->n_rand : 0;
     d.rand_rows = d.n_rand > 0 ? clamp32(p->rand_rows) : 0;
     d.rand_units = d.n_rand > 0 ? p->rand_units : nullptr;
     d.stride_div = sa::make_fastdiv(d.stride > 0 ? d.stride : 1);
+    d.stride_bits = 0;
+    if (d.stride > 0)
+        for (int64_t b = 0; b < 64; b += d.stride) d.stride_bits |= 1ull << b;
     d.unit_div = sa::make_fastdiv(d.unit > 0 ? d.unit : 1);
     return SA_OK;
 }
@@ -121,7 +134,7 @@ sa_status sa_build_block_mask(const sa_pattern* pattern, int64_t n_q, int64_t n_
         if (nkb > 16384) return fail(SA_ERR_UNSUPPORTED, "more than 16384 key blocks per row");
         if (nqb > kI32Max) return fail(SA_ERR_UNSUPPORTED, "too many query blocks");
         sa::DevPattern d;
-        sa_status st = make_pattern(pattern, n_q, d);
+        sa_status st = make_pattern(pattern, n_q, n_kv, d);
         if (st != SA_OK) return st;
         hipStream_t s = (hipStream_t)stream;
         if (nqb == 0) return launched(sa::launch_zero_i64(live_pairs, s), "sa_build_block_mask");
@@ -190,7 +203,7 @@ sa_status sa_attn_fwd(const sa_attn_args* a, void* stream)
                 return fail(SA_ERR_UNSUPPORTED, "block_q and block_kv must be 64 or 128");
             if (!a->kv_count || (a->n_kv > 0 && (!a->kv_index || !a->kv_partial)))
                 return fail(SA_ERR_INVALID_ARG, "block lists are NULL");
-            sa_status st = make_pattern(&a->pattern, a->n_q, p.pat);
+            sa_status st = make_pattern(&a->pattern, a->n_q, a->n_kv, p.pat);
             if (st != SA_OK) return st;
             p.nqb = (int32_t)((a->n_q + a->block_q - 1) / a->block_q);
             p.nkb = (int32_t)((a->n_kv + a->block_kv - 1) / a->block_kv);

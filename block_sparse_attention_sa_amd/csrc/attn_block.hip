@@ -107,6 +107,7 @@ attn_block_kernel(AttnParams a)
     constexpr int SUBTILE_BYTES = KS * D * 2;
     constexpr int DMA_W = SUBTILE_BYTES / 1024 / NW;  // DMA instructions per wave per tensor
     static_assert(SUBTILE_BYTES / 1024 % NW == 0, "DMA split");
+    constexpr int KT = NW == 1 ? 4 : 2;           // period of the per-lane DMA offset terms
 
     // double-buffered K and V sub-tiles
     __shared__ __attribute__((aligned(1024))) uint8_t kl[2][SUBTILE_BYTES];
@@ -138,23 +139,36 @@ attn_block_kernel(AttnParams a)
         return ((unsigned)j < (unsigned)a.nkb ? j : a.nkb) * BK + (t % SUB) * KS;
     };
 
-    // DMA of sub-tile t into buffer slot: lane -> (row within its 1 KB group, physical chunk)
+    // DMA of a sub-tile into buffer slot.  Lane -> (row within its 1 KB
+    // group, physical 16-byte chunk); the DMA of group g writes LDS bytes
+    // [g*1024, g*1024 + 1024) and fetches rows g*ROWS_PER_KB + dma_r.  The
+    // swizzles depend on the row only modulo 4, and a wave's groups advance by
+    // NW, so the per-lane offset terms repeat with period KT and are computed
+    // once; the uniform parts (sub-tile start, group) stay in scalar registers.
     const int dma_r = lane / CH;
     const int dma_p = lane % CH;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t kterm[4];  // first KT entries used (a fixed bound keeps the host pass happy)
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+        const int r = (wave_u + j * NW) * ROWS_PER_KB + dma_r;
+        kterm[j] = (uint32_t)dma_r * krow_b + (uint32_t)((dma_p ^ kswz<D>(r)) << 4);
+    }
+    const uint32_t vterm = (uint32_t)dma_r * vrow_b + (uint32_t)((dma_p ^ vswz<D>(dma_r)) << 4);
     auto dma = [&](int kv0, int slot) {
 #pragma unroll
         for (int i = 0; i < DMA_W; ++i) {
-            const int g = wave + i * NW;
-            const int r = g * ROWS_PER_KB + dma_r;
-            const uint32_t koff = (uint32_t)(kv0 + r) * krow_b + (uint32_t)((dma_p ^ kswz<D>(r)) << 4);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kl[slot] + g * 1024), 16, koff, 0, 0, 0);
+            const int g = wave_u + i * NW;
+            const uint32_t rows = (uint32_t)(kv0 + g * ROWS_PER_KB);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kl[slot] + g * 1024), 16,
+                                                     kterm[i % KT] + rows * krow_b, 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < DMA_W; ++i) {
-            const int g = wave + i * NW;
-            const int r = g * ROWS_PER_KB + dma_r;
-            const uint32_t voff = (uint32_t)(kv0 + r) * vrow_b + (uint32_t)((dma_p ^ vswz<D>(r)) << 4);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vl[slot] + g * 1024), 16, voff, 0, 0, 0);
+            const int g = wave_u + i * NW;
+            const uint32_t rows = (uint32_t)(kv0 + g * ROWS_PER_KB);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vl[slot] + g * 1024), 16,
+                                                     vterm + rows * vrow_b, 0, 0, 0);
         }
     };
     if (n_sub > 0) dma(sub_kv0(0), 0);
@@ -214,7 +228,7 @@ attn_block_kernel(AttnParams a)
             for (int sb = 0; sb < NSB; ++sb) {
                 uint32_t bits = 0xFFFFFFFFu;
                 if (need_mask) {
-                    const int64_t k0 = kv0 + sb * 32;
+                    const int32_t k0 = kv0 + sb * 32;
                     bits = allowed_bits32(a.pat, rc[nb], k0) & range_bits32(0, a.n_kv, k0);
                 }
                 // accumulator element i holds key k0 + 8*(i/4) + 4*hh + i%4

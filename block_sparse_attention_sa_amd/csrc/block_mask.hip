@@ -23,7 +23,12 @@ namespace sa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kGroupChunks = 64;  // 32-key chunks per count workgroup (2048 keys)
+constexpr int kGroupChunks = 16;  // 32-key chunks per count workgroup (at least one key block)
+
+__device__ __host__ __forceinline__ int32_t group_chunks(int32_t bk)
+{
+    return bk / 32 > kGroupChunks ? bk / 32 : kGroupChunks;
+}
 
 __global__ void zero_i64(int64_t* p) { *p = 0; }
 
@@ -49,44 +54,48 @@ __device__ bool group_reachable(const DevPattern& p, int64_t qa, int64_t qb, int
     return any;
 }
 
+// Thread layout: t = row_phase * G + chunk; each thread sums the popcounts of
+// its chunk over the rows row_phase, row_phase + 256/G, ... of the block.
 __global__ void __launch_bounds__(kThreads)
 count_kernel(DevPattern p, int32_t n_q, int32_t n_kv, int32_t bq, int32_t bk, int32_t nkb,
              int32_t ngroups, int32_t* counts /* = kv_index */, int64_t* live_pairs)
 {
-    __shared__ int32_t cell[kGroupChunks];  // at most kGroupChunks key blocks per group
+    __shared__ int32_t cell[kGroupChunks];  // key blocks per group <= kGroupChunks
     const int i = blockIdx.x / ngroups;
     const int grp = blockIdx.x % ngroups;
     const int t = threadIdx.x;
     if (blockIdx.x == 0 && t == 0) *live_pairs = 0;
 
+    const int32_t G = group_chunks(bk);
+    const int32_t cpb = bk / 32;                 // chunks per key block
+    const int32_t bpg = G / cpb;                 // key blocks per group
     const int32_t nchunks = (n_kv + 31) / 32;
-    const int32_t chunks_per_block = bk / 32;
-    const int32_t blocks_per_group = kGroupChunks / chunks_per_block > 0 ? kGroupChunks / chunks_per_block : 1;
-    const int32_t j0 = grp * blocks_per_group;
-    const int32_t j1 = min(j0 + blocks_per_group, nkb);
-    const int32_t c0 = j0 * chunks_per_block;
-    const int32_t c1 = min(j1 * chunks_per_block, nchunks);
+    const int32_t j0 = grp * bpg, j1 = min(j0 + bpg, nkb);
+    const int32_t c0 = j0 * cpb, c1 = min(j1 * cpb, nchunks);
     const int32_t q0 = i * bq, q1 = min(q0 + bq, n_q);
     int32_t* out = counts + (int64_t)i * nkb;
 
-    for (int j = t; j < j1 - j0; j += kThreads) cell[j] = 0;
+    if (t < j1 - j0) cell[t] = 0;
     const bool reach = group_reachable(p, (int64_t)q0 + p.q_offset, (int64_t)q1 - 1 + p.q_offset,
                                        (int64_t)c0 * 32, min((int64_t)c1 * 32, (int64_t)n_kv) - 1);
     __syncthreads();
     if (reach) {
-        const int32_t nck = c1 - c0;
-        const int32_t pairs = (q1 - q0) * nck;
-        for (int32_t u = t; u < pairs; u += kThreads) {
-            const int32_t row = u / nck, ck = c0 + u % nck;
-            RowCtx rc;
-            row_ctx(p, q0 + row + p.q_offset, rc);
-            const int64_t k0 = (int64_t)ck * 32;
-            const uint32_t m = allowed_bits32(p, rc, k0) & range_bits32(0, n_kv, k0);
-            if (m) atomicAdd(&cell[ck / chunks_per_block - j0], __popc(m));
+        const int32_t ck = c0 + t % G;
+        const int32_t rstep = kThreads / G;
+        int32_t acc = 0;
+        if (ck < c1) {
+            const int32_t k0 = ck * 32;
+            const uint32_t clip = range_bits32(0, n_kv, k0);
+            for (int32_t row = q0 + t / G; row < q1; row += rstep) {
+                RowCtx rc;
+                row_ctx(p, row + p.q_offset, rc);
+                acc += __popc(allowed_bits32(p, rc, k0) & clip);
+            }
+            if (acc) atomicAdd(&cell[ck / cpb - j0], acc);
         }
         __syncthreads();
     }
-    for (int j = t; j < j1 - j0; j += kThreads) out[j0 + j] = cell[j];
+    if (t < j1 - j0) out[j0 + t] = cell[t];
 }
 
 __global__ void __launch_bounds__(kThreads)
@@ -167,9 +176,8 @@ hipError_t launch_block_mask(const DevPattern& p, int32_t n_q, int32_t n_kv, int
         if (e != hipSuccess) return e;
         return launch_zero_i64(live_pairs, stream);
     }
-    const int32_t chunks_per_block = block_kv / 32;
-    const int32_t blocks_per_group = kGroupChunks / chunks_per_block > 0 ? kGroupChunks / chunks_per_block : 1;
-    const int32_t ngroups = (nkb + blocks_per_group - 1) / blocks_per_group;
+    const int32_t bpg = group_chunks(block_kv) / (block_kv / 32);
+    const int32_t ngroups = (nkb + bpg - 1) / bpg;
     hipLaunchKernelGGL(count_kernel, dim3((unsigned)((int64_t)nqb * ngroups)), dim3(kThreads), 0, stream, p,
                        n_q, n_kv, block_q, block_kv, nkb, ngroups, kv_index, live_pairs);
     hipError_t e = hipGetLastError();

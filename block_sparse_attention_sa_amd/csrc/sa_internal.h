@@ -56,11 +56,13 @@ struct DevPattern {
     int32_t global_tokens;
     int32_t unit;          // <= 0: unit terms off
     int32_t unit_window;   // < 0: unit band off
+    int32_t max_unit;      // larger unit indices cannot hold a key
     int32_t n_rand;
     int32_t rand_rows;
     const int32_t *rand_units;
     FastDiv stride_div;
     FastDiv unit_div;
+    uint64_t stride_bits;  // bits at 0, stride, 2*stride, ... below 64
 };
 
 constexpr int kMaxRand = 4;
@@ -77,80 +79,58 @@ __device__ __forceinline__ void row_ctx(const DevPattern& p, int32_t q, RowCtx& 
     r.q = q;
     r.qu = p.unit > 0 ? fdiv(q, p.unit_div) : 0;
 #pragma unroll
-    for (int i = 0; i < kMaxRand; ++i)
-        r.rnd[i] = (i < p.n_rand && p.unit > 0 && r.qu < p.rand_rows)
-                       ? p.rand_units[(int64_t)r.qu * p.n_rand + i]
-                       : -1;
+    for (int i = 0; i < kMaxRand; ++i) {
+        const int32_t v = (i < p.n_rand && p.unit > 0 && r.qu < p.rand_rows)
+                              ? p.rand_units[(int64_t)r.qu * p.n_rand + i]
+                              : -1;
+        r.rnd[i] = v > p.max_unit ? -1 : v;  // beyond every key: same as empty
+    }
 }
 
-// Per-pair predicate (one pair at a time; used on partial tiles only).
-__device__ __forceinline__ bool pair_allowed(const DevPattern& p, const RowCtx& r, int32_t kv)
+// Bits [lo, hi) of the 32-key chunk [k0, k0 + 32), positions clamped to it;
+// branch-free.  Callers keep lo, hi, k0 within int32 (the host clamps the
+// pattern fields to the sequence sizes).
+__device__ __forceinline__ uint32_t range_bits32(int32_t lo, int32_t hi, int32_t k0)
 {
-    const int32_t q = r.q;
-    bool ok = (kv < p.sinks) | (q < p.global_tokens) | (kv < p.global_tokens);
-    if (p.window_left >= 0)
-        ok |= (q - kv <= p.window_left) & (kv - q <= p.window_right);
-    if (p.stride > 0) {
-        int32_t dd = q - kv;
-        ok |= (dd >= 0) && (fmod_(dd < 0 ? 0 : dd, p.stride_div) == p.stride_phase);
-    }
-    if (p.unit > 0) {
-        int32_t ku = fdiv(kv, p.unit_div);
-        if (p.unit_window >= 0) {
-            int32_t du = r.qu - ku;
-            du = du < 0 ? -du : du;
-            ok |= du <= p.unit_window;
-        }
-#pragma unroll
-        for (int i = 0; i < kMaxRand; ++i)
-            ok |= (r.rnd[i] == ku);
-    }
-    if (p.causal)
-        ok &= kv <= q;
-    return ok;
-}
-
-// Bits [lo, hi) of the 32-key chunk [k0, k0 + 32), positions clamped to it.
-__device__ __forceinline__ uint32_t range_bits32(int64_t lo, int64_t hi, int64_t k0)
-{
-    const int64_t a = lo > k0 ? lo : k0;
-    const int64_t b = hi < k0 + 32 ? hi : k0 + 32;
-    if (b <= a) return 0u;
-    const uint32_t ua = (uint32_t)(a - k0), ub = (uint32_t)(b - k0);
-    const uint32_t hi_mask = ub >= 32 ? 0xFFFFFFFFu : ((1u << ub) - 1u);
-    return hi_mask & ~((1u << ua) - 1u);
+    const int32_t ua = min(max(lo - k0, 0), 32);
+    const int32_t ub = min(max(hi - k0, 0), 32);
+    const uint64_t m = ((1ull << ub) - 1ull) & ~((1ull << ua) - 1ull);
+    return (uint32_t)m;
 }
 
 // Allowed keys among [k0, k0 + 32) for the query of `r`, as a bit mask (bit i
-// = key k0 + i).  Every pattern term is an interval of keys for a fixed query
-// (or, for the strided term, a progression of at most 32/stride + 1 keys), so
-// the mask costs a few shifts instead of 32 predicate evaluations.  Keys past
-// the sequence end are not clipped here.
-__device__ __forceinline__ uint32_t allowed_bits32(const DevPattern& p, const RowCtx& r, int64_t k0)
+// = key k0 + i).  Every pattern term is an interval of keys for a fixed query,
+// or for the strided term an arithmetic progression, so the mask costs a few
+// integer operations instead of 32 predicate evaluations.  Keys past the
+// sequence end are not clipped here.
+__device__ __forceinline__ uint32_t allowed_bits32(const DevPattern& p, const RowCtx& r, int32_t k0)
 {
-    const int64_t q = r.q;
+    const int32_t q = r.q;
     uint32_t m = range_bits32(0, p.sinks, k0);
     if (p.window_left >= 0)
-        m |= range_bits32(q - p.window_left, q + (int64_t)p.window_right + 1, k0);
+        m |= range_bits32(q - p.window_left, q + p.window_right + 1, k0);
     m |= (q < p.global_tokens) ? 0xFFFFFFFFu : range_bits32(0, p.global_tokens, k0);
     if (p.stride > 0) {
-        // keys kv <= q - phase with (q - phase - kv) % stride == 0
-        const int64_t qp = q - p.stride_phase;
-        int64_t top = qp < k0 + 31 ? qp : k0 + 31;
-        if (top >= k0) {
-            const int32_t rem = fmod_((int32_t)(qp - top), p.stride_div);
-            for (int64_t kv = top - (rem == 0 ? 0 : p.stride - rem); kv >= k0; kv -= p.stride)
-                m |= 1u << (uint32_t)(kv - k0);
-        }
+        // keys kv <= q - phase with (q - phase - kv) % stride == 0: the largest
+        // such key in the chunk is `first`; the others sit stride apart below it
+        const int32_t qp = q - p.stride_phase;
+        const int32_t top = min(qp, k0 + 31);
+        const int32_t back = fmod_(max(qp - top, 0), p.stride_div);
+        const int32_t first = top - (back == 0 ? 0 : p.stride - back);
+        const int32_t o = first - k0;  // bit of `first`
+        const int32_t base = fmod_(max(o, 0), p.stride_div);
+        const uint32_t below = (uint32_t)((2ull << max(o, 0)) - 1ull);
+        const uint32_t prog = (uint32_t)(p.stride_bits << base) & below;
+        m |= o >= 0 ? prog : 0u;
     }
     if (p.unit > 0) {
         if (p.unit_window >= 0)
-            m |= range_bits32((int64_t)(r.qu - p.unit_window) * p.unit,
-                              (int64_t)(r.qu + p.unit_window + 1) * p.unit, k0);
+            m |= range_bits32((r.qu - p.unit_window) * p.unit, (r.qu + p.unit_window + 1) * p.unit, k0);
 #pragma unroll
-        for (int i = 0; i < kMaxRand; ++i)
-            if (r.rnd[i] >= 0)
-                m |= range_bits32((int64_t)r.rnd[i] * p.unit, (int64_t)(r.rnd[i] + 1) * p.unit, k0);
+        for (int i = 0; i < kMaxRand; ++i) {
+            const uint32_t b = range_bits32(r.rnd[i] * p.unit, (r.rnd[i] + 1) * p.unit, k0);
+            m |= r.rnd[i] >= 0 ? b : 0u;
+        }
     }
     if (p.causal)
         m &= range_bits32(0, q + 1, k0);
