@@ -91,12 +91,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 
-template <int D, int BQ, int BK, bool OF32>
-__global__ void __launch_bounds__(BQ)
+template <int D, int BQ, int BK, bool OF32, int NB>
+__global__ void __launch_bounds__(BQ * 2 / NB, NB == 1 ? 2 : 1)
 attn_block_kernel(AttnParams a)
 {
-    constexpr int NW = BQ / 64;                   // waves, 64 query rows each
-    constexpr int NB = 2;                         // 32-query column blocks per wave
+    constexpr int NW = BQ / (32 * NB);            // waves, 32*NB query rows each
+    // NB: 32-query column blocks per wave
     constexpr int KS = 64;                        // keys per sub-tile (compute and DMA unit)
     constexpr int SUB = BK / KS;                  // sub-tiles per listed key block
     constexpr int CH = D / 8;                     // 16-byte chunks per row
@@ -107,7 +107,7 @@ attn_block_kernel(AttnParams a)
     constexpr int SUBTILE_BYTES = KS * D * 2;
     constexpr int DMA_W = SUBTILE_BYTES / 1024 / NW;  // DMA instructions per wave per tensor
     static_assert(SUBTILE_BYTES / 1024 % NW == 0, "DMA split");
-    constexpr int KT = NW == 1 ? 4 : 2;           // period of the per-lane DMA offset terms
+    constexpr int KT = NW >= 4 ? 1 : (NW == 2 ? 2 : 4);  // period of the per-lane DMA offset terms
 
     // double-buffered K and V sub-tiles
     __shared__ __attribute__((aligned(1024))) uint8_t kl[2][SUBTILE_BYTES];
@@ -179,7 +179,7 @@ attn_block_kernel(AttnParams a)
     RowCtx rc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-        qrow[nb] = qb * BQ + wave * 64 + nb * 32 + l32;
+        qrow[nb] = qb * BQ + wave * 32 * NB + nb * 32 + l32;
         const bool ok = qrow[nb] < a.n_q;
 #pragma unroll
         for (int dc = 0; dc < NDC; ++dc) {
@@ -197,8 +197,12 @@ attn_block_kernel(AttnParams a)
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int i = 0; i < 16; ++i) o[nb][db][i] = 0.f;
-    float m_run[NB] = {-INFINITY, -INFINITY};
-    float l_run[NB] = {0.f, 0.f};
+    float m_run[NB], l_run[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        m_run[nb] = -INFINITY;
+        l_run[nb] = 0.f;
+    }
     const float c = a.scale_log2;
     const float thr = kLazyLog2 / c;
 
@@ -382,8 +386,13 @@ attn_block_kernel(AttnParams a)
 template <int D, int BQ, int BK, bool OF32>
 hipError_t launch_one(const AttnParams& a, hipStream_t stream)
 {
+    // head_dim 128: one 32-query column block per wave, two waves per SIMD;
+    // head_dim 64: two column blocks per wave (the smaller tiles leave LDS
+    // bandwidth to spare)
+    constexpr int NB = D == 128 ? 1 : 2;
     const int64_t items = (int64_t)a.batch * a.heads * a.nqb;
-    hipLaunchKernelGGL((attn_block_kernel<D, BQ, BK, OF32>), dim3((unsigned)items), dim3(BQ), 0, stream, a);
+    hipLaunchKernelGGL((attn_block_kernel<D, BQ, BK, OF32, NB>), dim3((unsigned)items), dim3(BQ * 2 / NB), 0,
+                       stream, a);
     return hipGetLastError();
 }
 
