@@ -1,6 +1,7 @@
 // api.cpp -- the C ABI of libsa.so (declared in include/sa.h): argument
 // validation on the host, conversion to the kernels' parameter blocks, and
 // launches on the caller's stream.  No device memory is allocated here.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -212,6 +213,10 @@ sa_status sa_attn_fwd(const sa_attn_args* a, void* stream)
             p.kv_count = a->kv_count;
             p.kv_index = a->kv_index;
             p.kv_partial = a->kv_partial;
+            // key tiles are fetched with 32-bit byte offsets from the (batch, head) base
+            const int64_t row_b = 2 * std::max(a->k_strides[2], a->v_strides[2]);
+            if ((a->n_kv + 256) * row_b > kI32Max)
+                return fail(SA_ERR_UNSUPPORTED, "n_kv times the K/V row stride must stay below 2^31 bytes");
             return launched(sa::launch_attn_blocks(p, (int)a->head_dim, (int)a->block_q,
                                                    (int)a->block_kv, o_f32, s),
                             "sa_attn_fwd");

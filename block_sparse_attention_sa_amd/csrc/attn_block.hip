@@ -109,9 +109,13 @@ attn_block_kernel(AttnParams a)
     static_assert(SUBTILE_BYTES / 1024 % NW == 0, "DMA split");
     constexpr int KT = NW >= 4 ? 1 : (NW == 2 ? 2 : 4);  // period of the per-lane DMA offset terms
 
-    // double-buffered K and V sub-tiles
-    __shared__ __attribute__((aligned(1024))) uint8_t kl[2][SUBTILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t vl[2][SUBTILE_BYTES];
+    // double-buffered K and V sub-tiles, as four separate LDS objects: the
+    // compiler can then tell the buffer being filled by DMA from the one being
+    // read, and does not hold the operand reads until the prefetch lands
+    __shared__ __attribute__((aligned(1024))) uint8_t kl0[SUBTILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t kl1[SUBTILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t vl0[SUBTILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t vl1[SUBTILE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -127,16 +131,28 @@ attn_block_kernel(AttnParams a)
     const uint16_t* qg = a.q + b * a.q_sb + h * a.q_sh;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + b * a.k_sb + h * a.k_sh, (int64_t)a.n_kv * a.k_sn * 2);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + b * a.v_sb + h * a.v_sh, (int64_t)a.n_kv * a.v_sn * 2);
-    const uint32_t krow_b = (uint32_t)(a.k_sn * 2), vrow_b = (uint32_t)(a.v_sn * 2);
+    const uint32_t krow_b = (uint32_t)(a.k_sn * 2);
+    const uint32_t vrow_b = (uint32_t)(a.v_sn * 2);
 
     const int32_t* idx_row = a.kv_index + (int64_t)qb * a.nkb;
     const uint8_t* part_row = a.kv_partial + (int64_t)qb * a.nkb;
-    const int n_sub = a.kv_count[qb] * SUB;
-    // first key of sub-tile t; a list entry that is not a key block maps past
-    // the sequence end, where the DMA reads zeros and the mask drops every key
-    auto sub_kv0 = [&](int t) {
-        const int j = idx_row[t / SUB];
-        return ((unsigned)j < (unsigned)a.nkb ? j : a.nkb) * BK + (t % SUB) * KS;
+    const int cnt = min(a.kv_count[qb], a.nkb);
+    const int n_sub = cnt * SUB;
+    // The live list is held in registers, 64 entries at a time (lane j holds
+    // entry base + j) and read with readlane, so the loop issues no memory
+    // loads of its own besides the DMA.
+    int l_idx = -1, l_part = 0;
+    auto refill = [&](int base) {
+        const int e = base + lane;
+        l_idx = e < cnt ? idx_row[e] : -1;
+        l_part = e < cnt ? (int)part_row[e] : 0;
+    };
+    auto list_at = [](int v, int e) { return __builtin_amdgcn_readlane(v, e & 63); };
+    // first key of a sub-tile of list entry j; an entry that is not a key
+    // block maps past the sequence end, where the DMA reads zeros and the
+    // mask drops every key
+    auto sub_kv0 = [&](int j, int sub) {
+        return ((unsigned)j < (unsigned)a.nkb ? j : a.nkb) * BK + sub * KS;
     };
 
     // DMA of a sub-tile into buffer slot.  Lane -> (row within its 1 KB
@@ -155,23 +171,24 @@ attn_block_kernel(AttnParams a)
         kterm[j] = (uint32_t)dma_r * krow_b + (uint32_t)((dma_p ^ kswz<D>(r)) << 4);
     }
     const uint32_t vterm = (uint32_t)dma_r * vrow_b + (uint32_t)((dma_p ^ vswz<D>(dma_r)) << 4);
-    auto dma = [&](int kv0, int slot) {
+    auto dma = [&](int kv0, uint8_t* kdst, uint8_t* vdst) {
 #pragma unroll
         for (int i = 0; i < DMA_W; ++i) {
             const int g = wave_u + i * NW;
             const uint32_t rows = (uint32_t)(kv0 + g * ROWS_PER_KB);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kl[slot] + g * 1024), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kdst + g * 1024), 16,
                                                      kterm[i % KT] + rows * krow_b, 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < DMA_W; ++i) {
             const int g = wave_u + i * NW;
             const uint32_t rows = (uint32_t)(kv0 + g * ROWS_PER_KB);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vl[slot] + g * 1024), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vdst + g * 1024), 16,
                                                      vterm + rows * vrow_b, 0, 0, 0);
         }
     };
-    if (n_sub > 0) dma(sub_kv0(0), 0);
+    refill(0);
+    if (n_sub > 0) dma(sub_kv0(list_at(l_idx, 0), 0), kl0, vl0);
 
     // Q^T operands: column block nb, lane holds q[row][16*dc + 8*hh + 0..7]
     int qrow[NB];
@@ -211,17 +228,27 @@ attn_block_kernel(AttnParams a)
     const int vrow_off = 4 * (tg >> 1) + (tj >> 2);
     const int vcol_off = 16 * (tg & 1) + 4 * (tj & 3);
 
-    for (int t = 0; t < n_sub; ++t) {
-        const int slot = t & 1;
-        const int kv0 = sub_kv0(t);
-        const int ej = idx_row[t / SUB];
-        const bool need_mask = (unsigned)ej >= (unsigned)a.nkb || part_row[t / SUB] != 0 || kv0 + KS > a.n_kv;
+    // two sub-tiles per trip, so that each copy of the body names its
+    // buffers statically (even sub-tiles live in kl0/vl0, odd in kl1/vl1)
+    for (int t0 = 0; t0 < n_sub; t0 += 2)
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+        const int t = t0 + par;
+        if (t >= n_sub) break;
+        const uint8_t* kb = par ? kl1 : kl0;
+        const uint8_t* vb = par ? vl1 : vl0;
+        const int e = t / SUB;
+        const int ej = list_at(l_idx, e);
+        const int kv0 = sub_kv0(ej, t % SUB);
+        const bool need_mask = (unsigned)ej >= (unsigned)a.nkb || list_at(l_part, e) != 0 || kv0 + KS > a.n_kv;
 
         // sub-tile t has landed in every wave's share; every wave is done with t-1
         wait_vm_barrier<0>();
-        if (t + 1 < n_sub) dma(sub_kv0(t + 1), slot ^ 1);
-        const uint8_t* kb = kl[slot];
-        const uint8_t* vb = vl[slot];
+        if (t + 1 < n_sub) {
+            const int e1 = (t + 1) / SUB;
+            if (e1 != e && (e1 & 63) == 0) refill(e1);
+            dma(sub_kv0(list_at(l_idx, e1), (t + 1) % SUB), par ? kl0 : kl1, par ? vl0 : vl1);
+        }
 
         // allowed-key bits of partial / clipped sub-tiles, computed before the
         // score registers are live; all ones on full sub-tiles

@@ -150,3 +150,12 @@ def test_indexer_topk_argument_errors():
     assert L.sa_topk(None, 4, 64, 0, 16, f, None) == _lib.SA_ERR_INVALID_ARG
     assert L.sa_indexer_topk(f, f, 4, 64, 64, 0, 5000, f, f, None) == _lib.SA_ERR_UNSUPPORTED
     assert L.sa_topk(f, 0, 64, 0, 16, f, None) == _lib.SA_OK  # empty: nothing launched
+
+
+def test_attn_offset_range_error():
+    # key tiles are addressed with 32-bit byte offsets per (batch, head)
+    a = _args(n_kv=1 << 24)
+    for s in (a.k_strides, a.v_strides):
+        s[:] = [1 << 32, 1 << 32, 128]
+    assert _lib.lib().sa_attn_fwd(ctypes.byref(a), None) == _lib.SA_ERR_UNSUPPORTED
+    assert "2^31 bytes" in _err()
