@@ -46,8 +46,15 @@ def _log(msg):
 
 
 def src_hash(path=ATTN_SRC) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source with comments and blank space removed, so a
+    comment edit does not orphan the committed counters."""
+    import re
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    code = "\n".join(" ".join(line.split()) for line in text.splitlines() if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def _traffic():
@@ -70,9 +77,18 @@ def main() -> int:
     ap.add_argument("--o-dtype", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dsa", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=2,
-                    help="heads of the workload the CPU oracle runs (all 8192 rows each)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="the CPU oracle repeats whole passes over the workload until this much time has passed")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="run one plain device copy (negation) of this many MiB before the steps; "
+                         "its HBM counters calibrate FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
+                         "WRITE_SIZE) of a run with --copy-calib-mib into the committed traffic figure")
+    ap.add_argument("--calib-mib", type=int, default=256, help="size used with --copy-calib-mib")
     args = ap.parse_args()
+    if args.traffic_from:
+        return _write_traffic(args.traffic_from[0], args.traffic_from[1], args.calib_mib)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -110,6 +126,15 @@ def main() -> int:
     live_pairs = live_pairs_per_head * cfg.B * cfg.H
     flops = 4.0 * cfg.d * live_pairs
     tile_flops = 4.0 * cfg.d * cfg.block * cfg.block * live_blocks * cfg.B * cfg.H
+
+    if args.copy_calib_mib > 0:
+        n = args.copy_calib_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)  # reads and writes exactly n * 4 bytes
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         sa.build_block_mask(cfg.pattern, cfg.N, cfg.N, cfg.block, cfg.block, device=dev, out=bl)
@@ -183,7 +208,7 @@ def main() -> int:
         result["dsa_prefill"] = _bench_dsa(sa, W, np, torch, dev, dev_bf16)
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = _cpu_baseline(cfg, inp, args.cpu_heads, np)
+        result["cpu_baseline"] = _cpu_baseline(cfg, inp, args.cpu_seconds, np)
 
     print(json.dumps(result), flush=True)
     return 0
@@ -241,26 +266,84 @@ def _bench_dsa(sa, W, np, torch, dev, dev_bf16, reps=5):
     }
 
 
-def _cpu_baseline(cfg, inp, heads, np):
+def _cpu_baseline(cfg, inp, seconds, np):
+    """The fp64 oracle on the whole workload (every row of every head), repeated
+    until `seconds` have passed; rate over the live pairs it evaluated."""
     import oracle  # the CPU oracle is the baseline leg here, nothing else
-    heads = max(1, min(heads, cfg.H))
-    rows = np.arange(heads * cfg.N, dtype=np.int64)
-    _log(f"bench: cpu oracle on {heads} head(s) x {cfg.N} rows")
+    rows = np.arange(cfg.B * cfg.H * cfg.N, dtype=np.int64)
+    _log(f"bench: cpu oracle on the whole workload ({rows.size} rows), >= {seconds:.0f} s")
     t0 = time.perf_counter()
-    bl = oracle.block_lists(cfg.pattern, cfg.N, cfg.N, cfg.block, cfg.block)
+    oracle.block_lists(cfg.pattern, cfg.N, cfg.N, cfg.block, cfg.block)
     t1 = time.perf_counter()
-    _, _, cnt = oracle.attn_rows(cfg.pattern, inp["q"], inp["k"], inp["v"], rows=rows, return_counts=True)
+    passes, pairs = 0, 0
+    while True:
+        _, _, cnt = oracle.attn_rows(cfg.pattern, inp["q"], inp["k"], inp["v"], rows=rows, return_counts=True)
+        passes += 1
+        pairs += int(cnt.sum())
+        if time.perf_counter() - t1 >= seconds:
+            break
     t2 = time.perf_counter()
-    pairs = int(cnt.sum())
     value = 4.0 * cfg.d * pairs / (t2 - t1) / 1e12
     return {
         "value": round(value, 6),
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": f"fp64 oracle attention on {heads} of {cfg.H} heads (all {cfg.N} rows each, {pairs} live "
-                  f"pairs) in {t2 - t1:.2f} s; its block lists for the whole matrix took {t1 - t0:.2f} s",
+        "sample": f"fp64 oracle attention, {passes} pass(es) over the whole workload ({cfg.H} heads x "
+                  f"{cfg.N} rows, {pairs // passes} live pairs per pass) in {t2 - t1:.2f} s; its block "
+                  f"lists for the whole matrix took {t1 - t0:.2f} s",
     }
+
+
+def _counter_means(path, counter):
+    """Per-kernel mean of one counter over the dispatches in a rocprofv3 counter_collection.csv."""
+    import csv
+    sums, counts = {}, {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            k = r["Kernel_Name"]
+            sums[k] = sums.get(k, 0.0) + float(r["Counter_Value"])
+            counts[k] = counts.get(k, 0) + 1
+    return {k: (sums[k] / counts[k], counts[k]) for k in sums}
+
+
+def _write_traffic(fetch_csv, write_csv, calib_mib):
+    """HBM bytes per attention launch: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) of the attention kernel, each scaled by known bytes / counter
+    reading of the calibration copy (a negation of calib_mib MiB)."""
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+
+    def pick(table, word):
+        keys = [k for k in table if word in k]
+        if len(keys) != 1:
+            raise SystemExit(f"expected one kernel matching {word!r}, found {keys}")
+        return table[keys[0]], keys[0]
+
+    (f_attn, nf), name = pick(fetch, "attn_block_kernel<128, 128, 128")
+    (w_attn, nw), _ = pick(write, "attn_block_kernel<128, 128, 128")
+    (f_copy, _), copy_name = pick(fetch, "neg_kernel")
+    (w_copy, _), _ = pick(write, "neg_kernel")
+    known_kib = calib_mib * 1024.0
+    f_fac, w_fac = known_kib / f_copy, known_kib / w_copy
+    out = {
+        "kernel": name,
+        "kernel_source_sha256_16": src_hash(),
+        "fetch_kib_per_dispatch": round(f_attn, 1),
+        "write_kib_per_dispatch": round(w_attn, 1),
+        "dispatches": [nf, nw],
+        "calibration": {"kernel": copy_name[:80], "bytes_read_and_written": calib_mib << 20,
+                        "fetch_kib": round(f_copy, 1), "write_kib": round(w_copy, 1),
+                        "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)},
+        "hbm_bytes_per_launch": round((f_attn * f_fac + w_attn * w_fac) * 1024.0),
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+    return 0
 
 
 if __name__ == "__main__":

@@ -10,16 +10,17 @@
 // marked partial (or clipped by the sequence end); the softmax is carried
 // online across tiles (running max, running sum, rescaled accumulator).
 //
-// gfx950 mapping.  A workgroup owns one (batch, head, query block of BQ rows)
-// and has BQ/64 waves; each wave owns 64 query rows as two 32-query column
-// blocks, so every K and V^T operand read from LDS feeds two MFMAs.
-//   * K and V tiles [BK x D] go HBM -> LDS by buffer loads with LDS
-//     destination (no staging registers).  Rows past the sequence end fall
-//     outside the buffer range and read as zero.  16-byte chunks are XOR
+// gfx950 mapping.  A workgroup owns one (batch, head, query block of BQ rows).
+// At head_dim 128 each wave owns 32 query rows (two waves per SIMD); at
+// head_dim 64 each wave owns 64 rows as two 32-query column blocks, so every
+// K and V operand read from LDS feeds two MFMAs.
+//   * Live key tiles are walked in 64-key sub-tiles.  K and V sub-tiles go
+//     HBM -> LDS by buffer loads with LDS destination (no staging registers),
+//     double buffered; the loop body is unrolled over the two buffer pairs so
+//     each copy names its LDS objects statically.  Rows past the sequence end
+//     fall outside the buffer range and read as zero.  16-byte chunks are XOR
 //     swizzled per row so the operand reads hit distinct banks.
-//   * K and V phases are split so the DMA of the next K tile overlaps the
-//     softmax and P.V of the current tile, and the DMA of the next V tile
-//     overlaps the next Q.K^T.  Two workgroups share a CU (one wave per SIMD).
+//   * The live list is held in lane registers and read with readlane.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T
 //     in registers).  In the accumulator layout one lane holds one query, so
 //     row max / row sum are in-lane reductions plus one v_permlane32_swap.
