@@ -266,6 +266,16 @@ attn_block_kernel(AttnParams a)
                 // accumulator element i holds key k0 + 8*(i/4) + 4*hh + i%4
                 mbits[nb][sb] = bits >> (4 * hh);
             }
+        if (need_mask) {
+            // no row of this wave may see a key of the sub-tile: every score
+            // would be -inf and add nothing, so the wave skips the sub-tile
+            uint32_t any = 0;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int sb = 0; sb < NSB; ++sb) any |= mbits[nb][sb];
+            if (__builtin_amdgcn_ballot_w64(any != 0) == 0) continue;
+        }
         __builtin_amdgcn_sched_barrier(0);
 
         // ---- S^T = K Q^T  (K operands fetched one k-step ahead)
