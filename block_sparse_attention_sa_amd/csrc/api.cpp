@@ -84,6 +84,7 @@ sa_status make_pattern(const sa_pattern* p, int64_t n_q, int64_t n_kv, sa::DevPa
     d.global_tokens = (int32_t)(p->global_tokens < ext ? p->global_tokens : ext);
     d.unit = p->unit > 0 ? (int32_t)(p->unit < ext ? p->unit : ext) : 0;
     d.max_unit = d.unit > 0 ? (int32_t)(ext / d.unit + 1) : 0;
+    d.n_kv = (int32_t)n_kv;
     d.unit_window = d.unit > 0 && p->unit_window >= 0
                         ? (int32_t)(p->unit_window < d.max_unit ? p->unit_window : d.max_unit)
                         : -1;

@@ -75,15 +75,25 @@ __device__ __forceinline__ float other_half(float v)
     return (threadIdx.x & 32) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
 }
 
+// Workgroup barrier that also orders LDS accesses: the fences keep the
+// compiler from moving LDS reads or writes across it (s_barrier alone is not
+// a memory operation to the compiler) and cost only an lgkmcnt(0) wait.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Wait until at most N buffer loads of this wave are outstanding and all LDS
-// operations have completed (gfx9 s_waitcnt encoding), then barrier.  The
-// plain s_barrier keeps outstanding DMA of the other tensor in flight.
+// operations have completed (gfx9 s_waitcnt encoding), then barrier.  Later
+// DMA (vmcnt) stays in flight.
 template <int N>
 __device__ __forceinline__ void wait_vm_barrier()
 {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes)
@@ -251,6 +261,21 @@ attn_block_kernel(AttnParams a)
             dma(sub_kv0(list_at(l_idx, e1), (t + 1) % SUB), par ? kl0 : kl1, par ? vl0 : vl1);
         }
 
+        // K operands of the first two k-steps are requested before anything
+        // else, so the LDS latency overlaps the mask-bit arithmetic
+        bf16x8 ka[3][NSB];
+        auto load_k = [&](bf16x8* dst, int dc) {
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb) {
+                const int r = sb * 32 + l32;
+                const int cc = 2 * dc + hh;
+                dst[sb] = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4*>(kb + r * D * 2 + ((cc ^ kswz<D>(r)) << 4)));
+            }
+        };
+        load_k(ka[0], 0);
+        load_k(ka[1], 1);
+
         // allowed-key bits of partial / clipped sub-tiles, computed before the
         // score registers are live; all ones on full sub-tiles
         uint32_t mbits[NB][NSB];
@@ -261,7 +286,7 @@ attn_block_kernel(AttnParams a)
                 uint32_t bits = 0xFFFFFFFFu;
                 if (need_mask) {
                     const int32_t k0 = kv0 + sb * 32;
-                    bits = allowed_bits32(a.pat, rc[nb], k0) & range_bits32(0, a.n_kv, k0);
+                    bits = allowed_bits32(a.pat, rc[nb], k0);
                 }
                 // accumulator element i holds key k0 + 8*(i/4) + 4*hh + i%4
                 mbits[nb][sb] = bits >> (4 * hh);
@@ -278,7 +303,7 @@ attn_block_kernel(AttnParams a)
         }
         __builtin_amdgcn_sched_barrier(0);
 
-        // ---- S^T = K Q^T  (K operands fetched one k-step ahead)
+        // ---- S^T = K Q^T  (K operands fetched two k-steps ahead)
         f32x16 s[NB][NSB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
@@ -286,27 +311,38 @@ attn_block_kernel(AttnParams a)
             for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) s[nb][sb][i] = 0.f;
-        bf16x8 ka[2][NSB];
-        auto load_k = [&](bf16x8* dst, int dc) {
-#pragma unroll
-            for (int sb = 0; sb < NSB; ++sb) {
-                const int r = sb * 32 + l32;
-                const int cc = 2 * dc + hh;
-                dst[sb] = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4*>(kb + r * D * 2 + ((cc ^ kswz<D>(r)) << 4)));
-            }
-        };
-        load_k(ka[0], 0);
 #pragma unroll
         for (int dc = 0; dc < NDC; ++dc) {
-            if (dc + 1 < NDC) load_k(ka[(dc + 1) & 1], dc + 1);
+            if (dc + 2 < NDC) load_k(ka[(dc + 2) % 3], dc + 2);
+
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
-                    s[nb][sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[dc & 1][sb], qf[nb][dc], s[nb][sb], 0, 0, 0);
+                    s[nb][sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[dc % 3][sb], qf[nb][dc], s[nb][sb], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
+
+        // V^T operands of the first two P.V steps are requested now; they
+        // land while the softmax runs
+        bf16x8 va[3][NDB];
+        auto load_v = [&](bf16x8* dst, int step) {
+            const int r0 = (step >> 1) * 32 + 16 * (step & 1) + vrow_off;
+            const int r1 = r0 + 8;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const int col = 32 * db + vcol_off;
+                const int ch = col >> 3, within = (col & 7) * 2;
+                const bf16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_bf16x4*)(vb + r0 * D * 2 + ((ch ^ vswz<D>(r0)) << 4) + within));
+                const bf16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_bf16x4*)(vb + r1 * D * 2 + ((ch ^ vswz<D>(r1)) << 4) + within));
+                dst[db] = bf16x8{t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+            }
+        };
+        load_v(va[0], 0);
+        load_v(va[1], 1);
+        __builtin_amdgcn_sched_barrier(0);
 
         // ---- element mask on partial / clipped sub-tiles only
         if (need_mask) {
@@ -316,18 +352,30 @@ attn_block_kernel(AttnParams a)
                 for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
                     for (int i = 0; i < 16; ++i)
-                        s[nb][sb][i] = (mbits[nb][sb] >> (8 * (i >> 2) + (i & 3))) & 1u ? s[nb][sb][i] : -INFINITY;
+                    {
+                        // keep = all ones where the key is allowed (one bit-field
+                        // extract), then a bit-select against -inf
+                        const int32_t keep = __builtin_amdgcn_sbfe((int32_t)mbits[nb][sb], 8 * (i >> 2) + (i & 3), 1);
+                        s[nb][sb][i] = __int_as_float((__float_as_int(s[nb][sb][i]) & keep) |
+                                                      (int32_t(0xFF800000u) & ~keep));
+                    }
         }
 
         // ---- online softmax, one query per lane and column block; P packed to bf16
         bf16x8 pk[NB][NSB][2];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            float mx = -INFINITY;
+            // row max as a tree (exact in any order): short dependency chains
+            float mq[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) mq[x] = fmaxf(s[nb][0][4 * x], s[nb][0][4 * x + 1]);
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[nb][sb][i]);
+                for (int i = (sb == 0 ? 2 : 0); i < 4; ++i)
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) mq[x] = fmaxf(mq[x], s[nb][sb][4 * x + i]);
+            float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
             mx = fmaxf(mx, other_half(mx));
             const float m_new = fmaxf(m_run[nb], mx);
             if (__any(m_new > m_run[nb] + thr)) {
@@ -345,7 +393,7 @@ attn_block_kernel(AttnParams a)
                 m_run[nb] = m_new;
             }
             const float mc = m_run[nb] == -INFINITY ? 0.f : m_run[nb] * c;
-            float lsum = 0.f;
+            float ls[4] = {0.f, 0.f, 0.f, 0.f};  // four partial row sums
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
@@ -353,38 +401,22 @@ attn_block_kernel(AttnParams a)
 #pragma unroll
                     for (int u = 0; u < 8; ++u) {
                         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][sb][8 * cb + u], c, -mc));
-                        lsum += p;
+                        ls[u & 3] += p;
                         pk[nb][sb][cb][u] = (__bf16)p;
                     }
-            l_run[nb] += lsum;
+            l_run[nb] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
         }
 
-        // ---- O^T += V^T P^T  (V^T operands fetched one step ahead)
-        bf16x8 va[2][NDB];
-        auto load_v = [&](bf16x8* dst, int step) {
-            const int r0 = (step >> 1) * 32 + 16 * (step & 1) + vrow_off;
-            const int r1 = r0 + 8;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const int col = 32 * db + vcol_off;
-                const int ch = col >> 3, within = (col & 7) * 2;
-                const bf16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (lds_bf16x4*)(vb + r0 * D * 2 + ((ch ^ vswz<D>(r0)) << 4) + within));
-                const bf16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (lds_bf16x4*)(vb + r1 * D * 2 + ((ch ^ vswz<D>(r1)) << 4) + within));
-                dst[db] = bf16x8{t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
-            }
-        };
-        load_v(va[0], 0);
+        // ---- O^T += V^T P^T  (V^T operands fetched two steps ahead)
 #pragma unroll
         for (int step = 0; step < 2 * NSB; ++step) {
-            if (step + 1 < 2 * NSB) load_v(va[(step + 1) & 1], step + 1);
+            if (step + 2 < 2 * NSB) load_v(va[(step + 2) % 3], step + 2);
             const int sb = step >> 1, cb = step & 1;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
-                    o[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[step & 1][db], pk[nb][sb][cb], o[nb][db], 0, 0, 0);
+                    o[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[step % 3][db], pk[nb][sb][cb], o[nb][db], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
     }

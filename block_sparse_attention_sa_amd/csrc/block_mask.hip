@@ -85,11 +85,10 @@ count_kernel(DevPattern p, int32_t n_q, int32_t n_kv, int32_t bq, int32_t bk, in
         int32_t acc = 0;
         if (ck < c1) {
             const int32_t k0 = ck * 32;
-            const uint32_t clip = range_bits32(0, n_kv, k0);
             for (int32_t row = q0 + t / G; row < q1; row += rstep) {
                 RowCtx rc;
                 row_ctx(p, row + p.q_offset, rc);
-                acc += __popc(allowed_bits32(p, rc, k0) & clip);
+                acc += __popc(allowed_bits32(p, rc, k0));
             }
             if (acc) atomicAdd(&cell[ck / cpb - j0], acc);
         }

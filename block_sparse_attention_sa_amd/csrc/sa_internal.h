@@ -57,6 +57,7 @@ struct DevPattern {
     int32_t unit;          // <= 0: unit terms off
     int32_t unit_window;   // < 0: unit band off
     int32_t max_unit;      // larger unit indices cannot hold a key
+    int32_t n_kv;          // keys at or past n_kv do not exist
     int32_t n_rand;
     int32_t rand_rows;
     const int32_t *rand_units;
@@ -71,12 +72,18 @@ constexpr int kMaxRand = 4;
 struct RowCtx {
     int32_t q;       // absolute query position
     int32_t qu;      // q / unit (0 if unit terms off)
+    int32_t cap;     // keys >= cap are never allowed (causality, sequence end)
+    int32_t wlo;     // local window [wlo, whi), already capped
+    int32_t whi;
     int32_t rnd[kMaxRand];
 };
 
 __device__ __forceinline__ void row_ctx(const DevPattern& p, int32_t q, RowCtx& r)
 {
     r.q = q;
+    r.cap = p.causal ? min(q + 1, p.n_kv) : p.n_kv;
+    r.wlo = q - p.window_left;
+    r.whi = min(q + p.window_right + 1, r.cap);
     r.qu = p.unit > 0 ? fdiv(q, p.unit_div) : 0;
 #pragma unroll
     for (int i = 0; i < kMaxRand; ++i) {
@@ -87,29 +94,39 @@ __device__ __forceinline__ void row_ctx(const DevPattern& p, int32_t q, RowCtx& 
     }
 }
 
+// (2^w - 1) << a for w, a in [0, 31] (one v_bfm_b32)
+__device__ __forceinline__ uint32_t bit_field_mask(uint32_t w, uint32_t a)
+{
+    uint32_t r;
+    asm("v_bfm_b32 %0, %1, %2" : "=v"(r) : "v"(w), "v"(a));
+    return r;
+}
+
 // Bits [lo, hi) of the 32-key chunk [k0, k0 + 32), positions clamped to it;
 // branch-free.  Callers keep lo, hi, k0 within int32 (the host clamps the
 // pattern fields to the sequence sizes).
 __device__ __forceinline__ uint32_t range_bits32(int32_t lo, int32_t hi, int32_t k0)
 {
-    const int32_t ua = min(max(lo - k0, 0), 32);
-    const int32_t ub = min(max(hi - k0, 0), 32);
-    const uint64_t m = ((1ull << ub) - 1ull) & ~((1ull << ua) - 1ull);
-    return (uint32_t)m;
+    const int32_t a = min(max(lo - k0, 0), 32);
+    const int32_t b = min(max(hi - k0, 0), 32);
+    const int32_t w = max(b - a, 0);  // w == 32 only when a == 0
+    const uint32_t m = bit_field_mask((uint32_t)w & 31u, (uint32_t)a & 31u);
+    return w >= 32 ? 0xFFFFFFFFu : m;
 }
 
 // Allowed keys among [k0, k0 + 32) for the query of `r`, as a bit mask (bit i
-// = key k0 + i).  Every pattern term is an interval of keys for a fixed query,
-// or for the strided term an arithmetic progression, so the mask costs a few
-// integer operations instead of 32 predicate evaluations.  Keys past the
-// sequence end are not clipped here.
+// = key k0 + i), keys past the sequence end excluded.  Every pattern term is
+// an interval of keys for a fixed query, or for the strided term an
+// arithmetic progression; each is cut at the row's causal / sequence cap, so
+// the mask costs a few integer operations per term instead of 32 predicate
+// evaluations.  Terms that are off cost nothing (uniform branches).
 __device__ __forceinline__ uint32_t allowed_bits32(const DevPattern& p, const RowCtx& r, int32_t k0)
 {
     const int32_t q = r.q;
-    uint32_t m = range_bits32(0, p.sinks, k0);
-    if (p.window_left >= 0)
-        m |= range_bits32(q - p.window_left, q + p.window_right + 1, k0);
-    m |= (q < p.global_tokens) ? 0xFFFFFFFFu : range_bits32(0, p.global_tokens, k0);
+    uint32_t m = 0;
+    if (p.sinks > 0) m |= range_bits32(0, min(p.sinks, r.cap), k0);
+    if (p.window_left >= 0) m |= range_bits32(r.wlo, r.whi, k0);
+    if (p.global_tokens > 0) m |= range_bits32(0, q < p.global_tokens ? r.cap : min(p.global_tokens, r.cap), k0);
     if (p.stride > 0) {
         // keys kv <= q - phase with (q - phase - kv) % stride == 0: the largest
         // such key in the chunk is `first`; the others sit stride apart below it
@@ -121,19 +138,19 @@ __device__ __forceinline__ uint32_t allowed_bits32(const DevPattern& p, const Ro
         const int32_t base = fmod_(max(o, 0), p.stride_div);
         const uint32_t below = (uint32_t)((2ull << max(o, 0)) - 1ull);
         const uint32_t prog = (uint32_t)(p.stride_bits << base) & below;
-        m |= o >= 0 ? prog : 0u;
+        m |= o >= 0 ? prog & range_bits32(0, r.cap, k0) : 0u;
     }
     if (p.unit > 0) {
         if (p.unit_window >= 0)
-            m |= range_bits32((r.qu - p.unit_window) * p.unit, (r.qu + p.unit_window + 1) * p.unit, k0);
+            m |= range_bits32((r.qu - p.unit_window) * p.unit, min((r.qu + p.unit_window + 1) * p.unit, r.cap), k0);
 #pragma unroll
         for (int i = 0; i < kMaxRand; ++i) {
-            const uint32_t b = range_bits32(r.rnd[i] * p.unit, (r.rnd[i] + 1) * p.unit, k0);
-            m |= r.rnd[i] >= 0 ? b : 0u;
+            if (i < p.n_rand) {
+                const uint32_t b = range_bits32(r.rnd[i] * p.unit, min((r.rnd[i] + 1) * p.unit, r.cap), k0);
+                m |= r.rnd[i] >= 0 ? b : 0u;
+            }
         }
     }
-    if (p.causal)
-        m &= range_bits32(0, q + 1, k0);
     return m;
 }
 
