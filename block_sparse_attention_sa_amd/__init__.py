@@ -24,7 +24,7 @@ import numpy as np
 from . import _lib
 from ._lib import SaError  # noqa: F401
 
-__all__ = ["BlockLists", "build_block_mask", "attn_fwd", "indexer_scores", "topk", "indexer_topk",
+__all__ = ["BlockLists", "build_block_mask", "attn_fwd", "attn_workspace_bytes", "indexer_scores", "topk", "indexer_topk",
            "describe", "SaError"]
 
 
@@ -125,11 +125,15 @@ def _strides3(t) -> list:
 
 def attn_fwd(q, k, v, blocks: Optional[BlockLists] = None, gather_idx=None, *,
              o_dtype=None, softmax_scale: Optional[float] = None, out=None, lse=None,
-             want_lse: bool = True):
+             want_lse: bool = True, workspace=None, split: bool = True):
     """Block-sparse (``blocks``) or per-query gather (``gather_idx``) attention forward.
 
     q [B, H, n_q, d], k/v [B, H, n_kv, d] bfloat16 on the GPU.  ``gather_idx``
     is int32 [n_q, topk] shared by every (b, h), or [B, H, n_q, topk].
+    In gather mode over a long key range the library can take a split form
+    that needs scratch (``attn_workspace_bytes``): pass a uint8 CUDA tensor
+    as ``workspace``, or leave it None and one is allocated for the call;
+    ``split=False`` forces the single-pass form.
     Returns (O [B, H, n_q, d] in ``o_dtype`` (default float32), LSE float32
     [B, H, n_q] or None).
     """
@@ -186,8 +190,27 @@ def attn_fwd(q, k, v, blocks: Optional[BlockLists] = None, gather_idx=None, *,
         else:
             raise ValueError("gather_idx must be [n_q, topk] or [B, H, n_q, topk]")
         keep.append(g)
+        need = int(_lib.lib().sa_attn_workspace_bytes(ctypes.byref(a))) if split else 0
+        if need > 0:
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+                raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
+            a.workspace = workspace.data_ptr()
+            a.workspace_bytes = workspace.numel()
     _lib.check(_lib.lib().sa_attn_fwd(ctypes.byref(a), _stream_ptr(q.device)))
     return out, lse
+
+
+def attn_workspace_bytes(batch: int, heads: int, n_q: int, n_kv: int, head_dim: int, topk: int,
+                         per_head_lists: bool = False) -> int:
+    """Scratch bytes of the split gather form for these sizes (0 if it has none)."""
+    a = _lib.SaAttnArgs()
+    a.batch, a.heads, a.n_q, a.n_kv, a.head_dim = batch, heads, n_q, n_kv, head_dim
+    a.mode = _lib.SA_MODE_GATHER
+    a.topk = topk
+    a.gather_bh_stride = n_q * topk if per_head_lists else 0
+    return int(_lib.lib().sa_attn_workspace_bytes(ctypes.byref(a)))
 
 
 def indexer_scores(q_idx, k_idx, q_offset: int, scores=None):

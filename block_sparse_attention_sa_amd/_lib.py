@@ -17,7 +17,7 @@ SA_DTYPE_BF16, SA_DTYPE_F32 = 0, 1
 SA_MODE_BLOCKS, SA_MODE_GATHER = 0, 1
 ABI_VERSION = 1
 
-EXPORTED = ("sa_build_block_mask", "sa_attn_fwd", "sa_indexer_scores", "sa_topk",
+EXPORTED = ("sa_build_block_mask", "sa_attn_workspace_bytes", "sa_attn_fwd", "sa_indexer_scores", "sa_topk",
             "sa_indexer_topk", "sa_last_error", "sa_abi_version")
 
 _I64 = ctypes.c_int64
@@ -71,6 +71,8 @@ class SaAttnArgs(ctypes.Structure):
         ("gather_idx", _P),
         ("topk", _I64),
         ("gather_bh_stride", _I64),
+        ("workspace", _P),
+        ("workspace_bytes", _I64),
     ]
 
 
@@ -94,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.sa_build_block_mask.argtypes = [ctypes.POINTER(SaPattern), _I64, _I64, _I32, _I32, _P, _P,
                                           _P, _P, _P]
         L.sa_build_block_mask.restype = ctypes.c_int
+        L.sa_attn_workspace_bytes.argtypes = [ctypes.POINTER(SaAttnArgs)]
+        L.sa_attn_workspace_bytes.restype = ctypes.c_size_t
         L.sa_attn_fwd.argtypes = [ctypes.POINTER(SaAttnArgs), _P]
         L.sa_attn_fwd.restype = ctypes.c_int
         L.sa_indexer_scores.argtypes = [_P, _P, _I64, _I64, _I32, _I64, _P, _P]

@@ -148,6 +148,17 @@ sa_status sa_build_block_mask(const sa_pattern* pattern, int64_t n_q, int64_t n_
     }
 }
 
+size_t sa_attn_workspace_bytes(const sa_attn_args* a)
+{
+    if (!a || a->mode != SA_MODE_GATHER || a->batch <= 0 || a->heads <= 0 || a->n_q <= 0 || a->n_kv <= 0 ||
+        (a->head_dim != 64 && a->head_dim != 128) || a->topk < 1 || a->topk > 8192 || a->gather_bh_stride < 0)
+        return 0;
+    sa::GatherSplitLayout L;
+    if (!sa::gather_split_layout(a->batch, a->heads, a->n_q, a->n_kv, a->head_dim, a->topk, a->gather_bh_stride, L))
+        return 0;
+    return (size_t)L.total;
+}
+
 sa_status sa_attn_fwd(const sa_attn_args* a, void* stream)
 {
     try {
@@ -228,6 +239,23 @@ sa_status sa_attn_fwd(const sa_attn_args* a, void* stream)
         p.gidx = a->gather_idx;
         p.topk = (int32_t)a->topk;
         p.g_bh_stride = a->gather_bh_stride;
+        sa::GatherSplitLayout L;
+        if (a->workspace &&
+            sa::gather_split_layout(a->batch, a->heads, a->n_q, a->n_kv, a->head_dim, a->topk, a->gather_bh_stride, L)) {
+            if (a->workspace_bytes < L.total)
+                return fail(SA_ERR_INVALID_ARG, "workspace smaller than sa_attn_workspace_bytes (%lld bytes)",
+                            (long long)L.total);
+            if (((uintptr_t)a->workspace & 255u) != 0)
+                return fail(SA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+            uint8_t* ws = (uint8_t*)a->workspace;
+            p.g_shift = L.shift;
+            p.g_nchunk = L.nchunk;
+            p.g_lists = (int32_t*)(ws + L.lists);
+            p.g_offs = (int32_t*)(ws + L.offs);
+            p.g_po = (float*)(ws + L.po);
+            p.g_pml = (float*)(ws + L.pml);
+            return launched(sa::launch_attn_gather_split(p, (int)a->head_dim, o_f32, s), "sa_attn_fwd");
+        }
         return launched(sa::launch_attn_gather(p, (int)a->head_dim, o_f32, s), "sa_attn_fwd");
     } catch (...) {
         return fail(SA_ERR_DEVICE, "sa_attn_fwd: unexpected exception");

@@ -9,15 +9,15 @@
 // Each query has a different key set, so there is no K/V tile shared by
 // several queries and no matrix product to put on MFMA: the work is two
 // gathered matrix-vector products, about one flop per byte moved, bound by
-// the gather bandwidth.  One wave per (batch, head, query):
-//   pass 1: D/8 lanes share one key row (16 contiguous bytes each, so a key
-//           row is one coalesced 256-byte (D=128) read); partial dots are
-//           reduced across those lanes; scores go to LDS;
-//   pass 2: row max and sum of exp2 over the LDS scores;
-//   pass 3: the same lane grouping reads V rows and accumulates p * v in
-//           float32; the key groups are reduced at the end.
-// Work items are ordered head-major so that concurrently running waves share
-// one head's K/V in the caches.
+// the latency and bandwidth of the row gathers.  One wave works on one
+// query's list in blocks of 128 keys with an online softmax:
+//   * the block's key indices are read once (two per lane) and handed to the
+//     lane groups with a cross-lane shuffle;
+//   * D/8 lanes share one K or V row (16 contiguous bytes each, one
+//     coalesced row read), and eight row loads per lane are issued before
+//     any is used, so a block costs a few memory round trips, not one per key;
+//   * partial dots are reduced across the lanes of a row; scores and then
+//     probabilities sit in 128 floats of LDS per wave.
 #include "sa_internal.h"
 
 namespace sa {
@@ -28,123 +28,179 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 constexpr int kWaves = 4;
 
+// workgroup id -> work block, so that consecutive blocks (one head's key
+// range) run on the same XCD when workgroups are dealt round-robin over the
+// 8 XCDs; a bijection for any grid size
+__device__ __forceinline__ int xcd_remap(int wg, int nwg)
+{
+    const int c = nwg / 8, r = nwg % 8;
+    const int x = wg % 8, slot = wg / 8;
+    const int base = x < r ? x * (c + 1) : r * (c + 1) + (x - r) * c;
+    return base + slot;
+}
+
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-template <int D, bool OF32>
-__global__ void __launch_bounds__(kWaves * 64)
-attn_gather_kernel(AttnParams a)
+constexpr int kBlk = 128;  // keys per block of the online softmax
+constexpr int kInFlight = 8;  // row loads per lane issued before use
+
+__device__ __forceinline__ void wave_lds_sync()
 {
-    constexpr int LPK = D / 8;        // lanes per key row (8 bf16 each)
-    constexpr int KPS = 64 / LPK;     // keys per wave step
-    extern __shared__ float sc_all[];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    float* sc = sc_all + wave * a.topk;
-
-    const int64_t item = (int64_t)blockIdx.x * kWaves + wave;
-    const int64_t n_items = (int64_t)a.batch * a.heads * a.n_q;
-    if (item >= n_items) return;
-    // head-major order: item = (bh) * n_q + t
-    const int t = (int)(item % a.n_q);
-    const int bh = (int)(item / a.n_q);
-    const int b = bh / a.heads, h = bh % a.heads;
-
-    const uint16_t* kg = a.k + b * a.k_sb + h * a.k_sh;
-    const uint16_t* vg = a.v + b * a.v_sb + h * a.v_sh;
-    const int32_t* list = a.gidx + bh * a.g_bh_stride + (int64_t)t * a.topk;
-
-    const int sub = lane % LPK;      // which 8-element slice of the row
-    const int kgrp = lane / LPK;     // which key of the step
-
-    // query slice, float32
-    float qv[8];
-    {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(a.q + b * a.q_sb + h * a.q_sh +
-                                                        (int64_t)t * a.q_sn + sub * 8);
-        for (int i = 0; i < 4; ++i) {
-            qv[2 * i] = bf_lo(w[i]);
-            qv[2 * i + 1] = bf_hi(w[i]);
-        }
-    }
-
-    // pass 1: scores (log2 domain, scale folded in)
-    const float c = a.scale_log2;
-    for (int e0 = 0; e0 < a.topk; e0 += KPS * 4) {
-        float part[4];
-        int keyid[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int e = e0 + u * KPS + kgrp;
-            int s = e < a.topk ? list[e] : -1;
-            s = (s >= 0 && s < a.n_kv) ? s : -1;
-            keyid[u] = s;
-            float acc = 0.f;
-            if (s >= 0) {
-                const u32x4 w = *reinterpret_cast<const u32x4*>(kg + (int64_t)s * a.k_sn + sub * 8);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc = __builtin_fmaf(qv[2 * i], bf_lo(w[i]), acc);
-                    acc = __builtin_fmaf(qv[2 * i + 1], bf_hi(w[i]), acc);
-                }
-            }
-            part[u] = acc;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-#pragma unroll
-            for (int off = 1; off < LPK; off <<= 1) part[u] += __shfl_xor(part[u], off, 64);
-            const int e = e0 + u * KPS + kgrp;
-            if (sub == 0 && e < a.topk) sc[e] = keyid[u] >= 0 ? part[u] * c : -INFINITY;
-        }
-    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
 
-    // pass 2: max and sum
-    float mx = -INFINITY;
-    for (int e = lane; e < a.topk; e += 64) mx = fmaxf(mx, sc[e]);
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-    const float msafe = mx == -INFINITY ? 0.f : mx;
-    float sum = 0.f;
-    for (int e = lane; e < a.topk; e += 64) {
-        const float p = __builtin_amdgcn_exp2f(sc[e] - msafe);
-        sc[e] = p;
-        sum += p;
-    }
-    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-
-    // pass 3: O = sum p v
-    float acc[8];
+// Online softmax of one query over the n keys keys[0..n): m (max, log2
+// units, scale folded in), l (sum of exp2(s - m)) and acc (sum of
+// exp2(s - m) v over this lane's 8 columns, summed over all lanes of the
+// column later).  With `check`, entries outside [0, n_kv) are skipped.
+template <int D>
+__device__ __forceinline__ void gather_online(const int32_t* keys, int n, bool check, int n_kv,
+                                              const uint16_t* kg, int64_t k_sn, const uint16_t* vg, int64_t v_sn,
+                                              const float (&qv)[8], float c, float* sc, int lane,
+                                              float& m, float& l, float (&acc)[8])
+{
+    constexpr int LPK = D / 8;        // lanes per row
+    constexpr int KPS = 64 / LPK;     // rows per wave-wide load
+    constexpr int STEPS = kBlk / KPS; // loads per block and tensor
+    static_assert(STEPS % kInFlight == 0, "block split");
+    const int sub = lane % LPK, kgrp = lane / LPK;
+    m = -INFINITY;
+    l = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int e0 = 0; e0 < a.topk; e0 += KPS * 4) {
+    for (int b0 = 0; b0 < n; b0 += kBlk) {
+        const int nb = min(kBlk, n - b0);
+        int kid[2];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int e = e0 + u * KPS + kgrp;
-            if (e < a.topk) {
-                int s = list[e];
-                const float p = sc[e];
-                if (s >= 0 && s < a.n_kv && p != 0.f) {
-                    const u32x4 w = *reinterpret_cast<const u32x4*>(vg + (int64_t)s * a.v_sn + sub * 8);
+        for (int r = 0; r < 2; ++r) {
+            const int e = b0 + 64 * r + lane;
+            int s = e < n ? keys[e] : -1;
+            if (check && (s < 0 || s >= n_kv)) s = -1;
+            kid[r] = s;
+        }
+        // row index of key e = step * KPS + kgrp of the block
+        auto key_of = [&](int step) {
+            const int e = step * KPS + kgrp;
+            const int v = __shfl(step * KPS < 64 ? kid[0] : kid[1], e & 63, 64);
+            return e < nb ? v : -1;
+        };
+        // ---- scores
+        float bmax = -INFINITY;
+#pragma unroll 1
+        for (int g = 0; g < STEPS; g += kInFlight) {
+            u32x4 w[kInFlight];
+            int sk[kInFlight];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        acc[2 * i] = __builtin_fmaf(p, bf_lo(w[i]), acc[2 * i]);
-                        acc[2 * i + 1] = __builtin_fmaf(p, bf_hi(w[i]), acc[2 * i + 1]);
-                    }
+            for (int i = 0; i < kInFlight; ++i) {
+                sk[i] = key_of(g + i);
+                w[i] = u32x4{0u, 0u, 0u, 0u};
+                if (sk[i] >= 0) w[i] = *reinterpret_cast<const u32x4*>(kg + (int64_t)sk[i] * k_sn + sub * 8);
+            }
+#pragma unroll
+            for (int i = 0; i < kInFlight; ++i) {
+                float d = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    d = __builtin_fmaf(qv[2 * j], bf_lo(w[i][j]), d);
+                    d = __builtin_fmaf(qv[2 * j + 1], bf_hi(w[i][j]), d);
+                }
+#pragma unroll
+                for (int off = 1; off < LPK; off <<= 1) d += __shfl_xor(d, off, 64);
+                const float sv = sk[i] >= 0 ? d * c : -INFINITY;
+                bmax = fmaxf(bmax, sv);
+                const int e = (g + i) * KPS + kgrp;
+                if (sub == 0) sc[e] = sv;
+            }
+        }
+        for (int off = LPK; off < 64; off <<= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, off, 64));
+        const float m_new = fmaxf(m, bmax);
+        if (m_new != -INFINITY && m_new > m) {
+            const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
+            l *= alpha;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+            m = m_new;
+        }
+        wave_lds_sync();
+        // ---- probabilities (two per lane) and their sum
+        float ps = 0.f;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int e = 64 * r + lane;
+            const float sv = sc[e];
+            const float pv = (e < nb && sv != -INFINITY) ? __builtin_amdgcn_exp2f(sv - m) : 0.f;
+            sc[e] = pv;
+            ps += pv;
+        }
+        for (int off = 32; off > 0; off >>= 1) ps += __shfl_xor(ps, off, 64);
+        l += ps;
+        wave_lds_sync();
+        // ---- acc += p v
+#pragma unroll 1
+        for (int g = 0; g < STEPS; g += kInFlight) {
+            u32x4 w[kInFlight];
+            int sk[kInFlight];
+#pragma unroll
+            for (int i = 0; i < kInFlight; ++i) {
+                sk[i] = key_of(g + i);
+                w[i] = u32x4{0u, 0u, 0u, 0u};
+                if (sk[i] >= 0) w[i] = *reinterpret_cast<const u32x4*>(vg + (int64_t)sk[i] * v_sn + sub * 8);
+            }
+#pragma unroll
+            for (int i = 0; i < kInFlight; ++i) {
+                const float pv = sc[(g + i) * KPS + kgrp];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc[2 * j] = __builtin_fmaf(pv, bf_lo(w[i][j]), acc[2 * j]);
+                    acc[2 * j + 1] = __builtin_fmaf(pv, bf_hi(w[i][j]), acc[2 * j + 1]);
                 }
             }
         }
+        wave_lds_sync();
     }
+    // the rows of a step were spread over the lane groups: sum the groups
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int off = LPK; off < 64; off <<= 1) acc[i] += __shfl_xor(acc[i], off, 64);
+}
 
+template <int D>
+__device__ __forceinline__ void load_q_slice(const AttnParams& a, int b, int h, int t, int sub, float (&qv)[8])
+{
+    const u32x4 w = *reinterpret_cast<const u32x4*>(a.q + b * a.q_sb + h * a.q_sh + (int64_t)t * a.q_sn + sub * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        qv[2 * i] = bf_lo(w[i]);
+        qv[2 * i + 1] = bf_hi(w[i]);
+    }
+}
+
+template <int D, bool OF32>
+__global__ void __launch_bounds__(kWaves * 64) attn_gather_kernel(AttnParams a)
+{
+    constexpr int LPK = D / 8;
+    __shared__ float sc_all[kWaves][kBlk];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t item = (int64_t)blockIdx.x * kWaves + wave;
+    if (item >= (int64_t)a.batch * a.heads * a.n_q) return;
+    // head-major order: item = bh * n_q + t
+    const int t = (int)(item % a.n_q);
+    const int bh = (int)(item / a.n_q);
+    const int b = bh / a.heads, h = bh % a.heads;
+    const int sub = lane % LPK, kgrp = lane / LPK;
+    float qv[8];
+    load_q_slice<D>(a, b, h, t, sub, qv);
+    float m, l, acc[8];
+    gather_online<D>(a.gidx + bh * a.g_bh_stride + (int64_t)t * a.topk, a.topk, true, a.n_kv,
+                     a.k + b * a.k_sb + h * a.k_sh, a.k_sn, a.v + b * a.v_sb + h * a.v_sh, a.v_sn, qv,
+                     a.scale_log2, sc_all[wave], lane, m, l, acc);
     if (kgrp == 0) {
-        const float inv = sum > 0.f ? 1.f / sum : 0.f;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
         const int64_t obase = b * a.o_sb + h * a.o_sh + (int64_t)t * a.o_sn + sub * 8;
         if (OF32) {
             float* op = reinterpret_cast<float*>(a.o) + obase;
@@ -160,9 +216,177 @@ attn_gather_kernel(AttnParams a)
             *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.o) + obase) = w;
         }
         if (a.lse && lane == 0)
-            a.lse[(int64_t)bh * a.n_q + t] =
-                sum > 0.f ? (msafe + __log2f(sum)) * 0.69314718055994531f : -INFINITY;
+            a.lse[item] = l > 0.f ? (m + __log2f(l)) * 0.69314718055994531f : -INFINITY;
     }
+}
+
+// ---------------------------------------------------------------------------
+// Split form.  With the lists of all queries in hand, the work is regrouped
+// by key range so that the K and V rows a workgroup gathers come from one
+// 2 MB range per head, which the workgroups of one XCD share in its L2:
+//   partition: every list is reordered by key range (list order kept inside
+//              a range) and the range starts are recorded;
+//   part:      one wave per (batch*head, range, query) attends to the keys
+//              of its range and writes the unnormalised output, the max (log2
+//              units) and the sum of its partial softmax;
+//   merge:     one wave per (batch*head, query) rescales the partials to the
+//              common max and normalises.
+// Same softmax as the single pass; only float32 summation order differs.
+
+__global__ void __launch_bounds__(kWaves * 64) gather_partition_kernel(AttnParams a)
+{
+    __shared__ int32_t cnt_all[kWaves][256];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t rows = a.g_bh_stride == 0 ? (int64_t)a.n_q : (int64_t)a.batch * a.heads * a.n_q;
+    const int64_t row = (int64_t)blockIdx.x * kWaves + wave;
+    if (row >= rows) return;  // wave-level work only: no workgroup barrier below
+    const int32_t* src = a.g_bh_stride == 0
+                             ? a.gidx + row * a.topk
+                             : a.gidx + (row / a.n_q) * a.g_bh_stride + (row % a.n_q) * a.topk;
+    int32_t* dst = a.g_lists + row * a.topk;
+    int32_t* offs = a.g_offs + row * (a.g_nchunk + 1);
+    int32_t* cnt = cnt_all[wave];
+    const int nch = a.g_nchunk;
+
+    for (int i = lane; i < 256; i += 64) cnt[i] = 0;
+    wave_lds_sync();
+    for (int e = lane; e < a.topk; e += 64) {
+        const int s = src[e];
+        if (s >= 0 && s < a.n_kv) atomicAdd(&cnt[s >> a.g_shift], 1);
+    }
+    wave_lds_sync();
+    // exclusive scan of the range counts (lane owns ranges 4*lane .. 4*lane+3)
+    int v[4], tot = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = 4 * lane + k;
+        v[k] = i < nch ? cnt[i] : 0;
+        tot += v[k];
+    }
+    int incl = tot;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+    }
+    int run = incl - tot;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = 4 * lane + k;
+        if (i < nch) {
+            offs[i] = run;
+            cnt[i] = run;  // from here on: next free slot of range i
+        }
+        run += v[k];
+    }
+    if (lane == 63) offs[nch] = incl;
+    wave_lds_sync();
+    // stable scatter, 64 entries at a time: a lane's slot is its range's next
+    // free slot plus the number of lower lanes with the same range (found
+    // with one ballot per bit of the range index)
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    for (int e0 = 0; e0 < a.topk; e0 += 64) {
+        const int e = e0 + lane;
+        const int s = e < a.topk ? src[e] : -1;
+        const bool ok = s >= 0 && s < a.n_kv;
+        const int ch = ok ? (s >> a.g_shift) : 0;
+        uint64_t m = __builtin_amdgcn_ballot_w64(ok);
+#pragma unroll
+        for (int bit = 0; bit < 8; ++bit) {
+            const bool on = ((ch >> bit) & 1) != 0;
+            const uint64_t bb = __builtin_amdgcn_ballot_w64(on);
+            m &= on ? bb : ~bb;
+        }
+        const int rank = __popcll(m & below);
+        const int base = cnt[ch];
+        wave_lds_sync();
+        if (ok) {
+            dst[base + rank] = s;
+            if ((m >> lane) == 1ull) cnt[ch] = base + rank + 1;  // the group's highest lane
+        }
+        wave_lds_sync();
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kWaves * 64) gather_part_kernel(AttnParams a)
+{
+    constexpr int LPK = D / 8;
+    __shared__ float sc_all[kWaves][kBlk];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t n_items = (int64_t)a.batch * a.heads * a.g_nchunk * a.n_q;
+    const int64_t item = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * kWaves + wave;
+    if (item >= n_items) return;
+    // item = ((bh * nchunk) + range) * n_q + t: the waves working on one key
+    // range of one head are neighbours, and land on the same XCD
+    const int t = (int)(item % a.n_q);
+    const int64_t rest = item / a.n_q;
+    const int rg = (int)(rest % a.g_nchunk);
+    const int bh = (int)(rest / a.g_nchunk);
+    const int b = bh / a.heads, h = bh % a.heads;
+    const int64_t row = a.g_bh_stride == 0 ? (int64_t)t : (int64_t)bh * a.n_q + t;
+    const int32_t* offs = a.g_offs + row * (a.g_nchunk + 1);
+    const int o0 = offs[rg], o1 = offs[rg + 1];
+    const int sub = lane % LPK, kgrp = lane / LPK;
+    float qv[8];
+    load_q_slice<D>(a, b, h, t, sub, qv);
+    float m, l, acc[8];
+    gather_online<D>(a.g_lists + row * a.topk + o0, o1 - o0, false, a.n_kv, a.k + b * a.k_sb + h * a.k_sh, a.k_sn,
+                     a.v + b * a.v_sb + h * a.v_sh, a.v_sn, qv, a.scale_log2, sc_all[wave], lane, m, l, acc);
+    const int64_t pidx = ((int64_t)bh * a.n_q + t) * a.g_nchunk + rg;
+    if (kgrp == 0) {
+        float* po = a.g_po + pidx * D + sub * 8;
+        *reinterpret_cast<float4*>(po) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        *reinterpret_cast<float4*>(po + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+    if (lane == 0) {
+        a.g_pml[pidx * 2] = m;  // -inf for an empty range
+        a.g_pml[pidx * 2 + 1] = l;
+    }
+}
+
+template <int D, bool OF32>
+__global__ void __launch_bounds__(kWaves * 64) gather_merge_kernel(AttnParams a)
+{
+    constexpr int PER = D / 64;  // output columns per lane
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (item >= (int64_t)a.batch * a.heads * a.n_q) return;
+    const int t = (int)(item % a.n_q);
+    const int bh = (int)(item / a.n_q);
+    const int b = bh / a.heads, h = bh % a.heads;
+    const float* pml = a.g_pml + item * a.g_nchunk * 2;
+    const float* po = a.g_po + item * a.g_nchunk * D;
+    float m = -INFINITY;
+    for (int r = 0; r < a.g_nchunk; ++r) m = fmaxf(m, pml[2 * r]);
+    float l = 0.f, acc[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+    if (m != -INFINITY) {
+        for (int r = 0; r < a.g_nchunk; ++r) {
+            const float mr = pml[2 * r];
+            if (mr == -INFINITY) continue;
+            const float f = __builtin_amdgcn_exp2f(mr - m);
+            l = __builtin_fmaf(pml[2 * r + 1], f, l);
+#pragma unroll
+            for (int i = 0; i < PER; ++i) acc[i] = __builtin_fmaf(po[r * D + lane * PER + i], f, acc[i]);
+        }
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int64_t obase = b * a.o_sb + h * a.o_sh + (int64_t)t * a.o_sn + lane * PER;
+    if (OF32) {
+        float* op = reinterpret_cast<float*>(a.o) + obase;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) op[i] = acc[i] * inv;
+    } else {
+        uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + obase;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) op[i] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i] * inv));
+    }
+    if (a.lse && lane == 0)
+        a.lse[item] = l > 0.f ? (m + __log2f(l)) * 0.69314718055994531f : -INFINITY;
 }
 
 template <int D, bool OF32>
@@ -170,13 +394,37 @@ hipError_t launch_one(const AttnParams& a, hipStream_t stream)
 {
     const int64_t items = (int64_t)a.batch * a.heads * a.n_q;
     const int64_t wgs = (items + kWaves - 1) / kWaves;
-    const size_t lds = sizeof(float) * (size_t)kWaves * a.topk;
-    hipLaunchKernelGGL((attn_gather_kernel<D, OF32>), dim3((unsigned)wgs), dim3(kWaves * 64), lds,
+    hipLaunchKernelGGL((attn_gather_kernel<D, OF32>), dim3((unsigned)wgs), dim3(kWaves * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int D, bool OF32>
+hipError_t launch_split(const AttnParams& a, hipStream_t stream)
+{
+    const int64_t rows = a.g_bh_stride == 0 ? (int64_t)a.n_q : (int64_t)a.batch * a.heads * a.n_q;
+    hipLaunchKernelGGL(gather_partition_kernel, dim3((unsigned)((rows + kWaves - 1) / kWaves)), dim3(kWaves * 64), 0,
                        stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t parts = (int64_t)a.batch * a.heads * a.g_nchunk * a.n_q;
+    hipLaunchKernelGGL((gather_part_kernel<D>), dim3((unsigned)((parts + kWaves - 1) / kWaves)), dim3(kWaves * 64),
+                       0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t items = (int64_t)a.batch * a.heads * a.n_q;
+    hipLaunchKernelGGL((gather_merge_kernel<D, OF32>), dim3((unsigned)((items + kWaves - 1) / kWaves)),
+                       dim3(kWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_attn_gather_split(const AttnParams& a, int head_dim, int o_f32, hipStream_t stream)
+{
+    if (head_dim == 128) return o_f32 ? launch_split<128, true>(a, stream) : launch_split<128, false>(a, stream);
+    if (head_dim == 64) return o_f32 ? launch_split<64, true>(a, stream) : launch_split<64, false>(a, stream);
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_attn_gather(const AttnParams& a, int head_dim, int o_f32, hipStream_t stream)
 {

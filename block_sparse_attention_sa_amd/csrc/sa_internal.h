@@ -184,11 +184,47 @@ struct AttnParams {
     const int32_t* gidx;
     int32_t topk;
     int64_t g_bh_stride;
+    // split gather form (scratch from the caller): key ranges of 2^g_shift
+    // keys, lists partitioned by range, partial results per range
+    int32_t g_shift;
+    int32_t g_nchunk;
+    int32_t* g_lists;   // [rows][topk], rows = n_q (shared lists) or batch*heads*n_q
+    int32_t* g_offs;    // [rows][g_nchunk + 1]
+    float* g_po;        // [batch*heads*n_q][g_nchunk][head_dim]
+    float* g_pml;       // [batch*heads*n_q][g_nchunk][2]: max (log2 units), sum
 };
 
 hipError_t launch_attn_blocks(const AttnParams& a, int head_dim, int block_q, int block_kv,
                               int o_f32, hipStream_t stream);
 hipError_t launch_attn_gather(const AttnParams& a, int head_dim, int o_f32, hipStream_t stream);
+hipError_t launch_attn_gather_split(const AttnParams& a, int head_dim, int o_f32, hipStream_t stream);
+
+// Layout of the split-gather scratch (byte offsets, each 256-byte aligned).
+struct GatherSplitLayout {
+    int32_t shift, nchunk;
+    int64_t rows;
+    int64_t lists, offs, po, pml, total;
+};
+inline bool gather_split_layout(int64_t batch, int64_t heads, int64_t n_q, int64_t n_kv, int64_t head_dim,
+                                int64_t topk, int64_t bh_stride, GatherSplitLayout& L)
+{
+    // 2 MB of K and V rows per range and head
+    int32_t shift = 0;
+    while ((int64_t(1) << (shift + 1)) * 4 * head_dim <= (int64_t(1) << 21)) ++shift;
+    const int64_t nchunk = (n_kv + (int64_t(1) << shift) - 1) >> shift;
+    if (nchunk < 2 || nchunk > 256 || batch <= 0 || heads <= 0 || n_q <= 0) return false;
+    auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
+    L.shift = shift;
+    L.nchunk = (int32_t)nchunk;
+    L.rows = bh_stride == 0 ? n_q : batch * heads * n_q;
+    const int64_t items = batch * heads * n_q;
+    L.lists = 0;
+    L.offs = up(L.lists + L.rows * topk * 4);
+    L.po = up(L.offs + L.rows * (nchunk + 1) * 4);
+    L.pml = up(L.po + items * nchunk * head_dim * 4);
+    L.total = up(L.pml + items * nchunk * 2 * 4);
+    return true;
+}
 hipError_t launch_indexer_scores(const uint16_t* q_idx, const uint16_t* k_idx, int32_t n_q,
                                  int32_t n_kv, int32_t d_idx, int32_t q_offset, float* scores,
                                  hipStream_t stream);

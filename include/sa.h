@@ -164,7 +164,27 @@ typedef struct sa_attn_args {
     const int32_t *gather_idx;
     int64_t topk;
     int64_t gather_bh_stride;
+    void *workspace;            /* DEVICE scratch or NULL, see sa_attn_workspace_bytes */
+    int64_t workspace_bytes;
 } sa_attn_args;
+
+/*
+ * sa_attn_workspace_bytes -- bytes of device scratch that let sa_attn_fwd
+ * take its split form for these arguments, 0 when it has none.
+ *
+ * Gather mode over a long key range (n_kv above 2^21 / (4 * head_dim)
+ * keys) has a split form: each key list is first partitioned by key range
+ * (ranges of 2 MB of K and V per head), every range is then attended to
+ * separately by workgroups that share it in one L2 cache, and the partial
+ * results (running max, sum and unnormalised output per range) are merged.
+ * The result is the same softmax; only the order of the float32 sums
+ * differs.  The scratch holds the partitioned lists and the partial results.
+ * With workspace == NULL sa_attn_fwd uses the single-pass form instead; a
+ * non-NULL workspace smaller than this is an error.  The workspace is
+ * overwritten by the call and must not overlap any other argument; calls
+ * sharing one workspace must not run concurrently.
+ */
+size_t sa_attn_workspace_bytes(const sa_attn_args *args);
 
 /*
  * sa_attn_fwd -- O = softmax(Q K^T * scale restricted to allowed pairs) V, and LSE.

@@ -159,3 +159,23 @@ def test_attn_offset_range_error():
         s[:] = [1 << 32, 1 << 32, 128]
     assert _lib.lib().sa_attn_fwd(ctypes.byref(a), None) == _lib.SA_ERR_UNSUPPORTED
     assert "2^31 bytes" in _err()
+
+
+def test_gather_workspace_size_and_errors():
+    L = _lib.lib()
+    a = _args(mode=_lib.SA_MODE_GATHER, gather_idx=4096, topk=64, head_dim=128, n_kv=1000)
+    for s in (a.q_strides, a.k_strides, a.v_strides, a.o_strides):
+        s[:] = [1 << 24, 1 << 24, 128]
+    assert L.sa_attn_workspace_bytes(ctypes.byref(a)) == 0      # one key range: no split form
+    a.n_kv = 20000                                              # 5 ranges of 4096 keys
+    need = L.sa_attn_workspace_bytes(ctypes.byref(a))
+    rows, items, nch = 64, 64, 5
+    up = lambda x: (x + 255) // 256 * 256
+    exp = up(up(up(up(rows * 64 * 4) + rows * (nch + 1) * 4) + items * nch * 128 * 4) + items * nch * 2 * 4)
+    assert need == exp
+    a.workspace, a.workspace_bytes = 1 << 20, need - 1
+    assert L.sa_attn_fwd(ctypes.byref(a), None) == _lib.SA_ERR_INVALID_ARG and "workspace" in _err()
+    a.workspace, a.workspace_bytes = (1 << 20) + 16, need
+    assert L.sa_attn_fwd(ctypes.byref(a), None) == _lib.SA_ERR_INVALID_ARG and "aligned" in _err()
+    b = _args()
+    assert L.sa_attn_workspace_bytes(ctypes.byref(b)) == 0      # block mode needs none

@@ -148,3 +148,37 @@ def test_config5_gather_sampled_rows():
     rows = sample_rows(np.random.default_rng(55), 1, cfg.H, cfg.n_q, 256)
     o_ref, lse_ref = oracle.attn_gather_rows(inp["q"], inp["k"], inp["v"], idx.cpu().numpy(), rows=rows)
     check_o_lse(gpu_rows(o, rows), gpu_rows(lse, rows), o_ref, lse_ref, ctx="config 5")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("per_head", [False, True])
+def test_gather_split_form(d, per_head):
+    """Key ranges of 2 MB of K+V per head: n_kv spans several ranges, so the
+    split form (partition, partial softmax per range, merge) runs; unsorted
+    lists, duplicates, out-of-range entries, a list inside one range and an
+    empty list are covered."""
+    rng = np.random.default_rng(100 + d + per_head)
+    B, H, n_q, k = 2, 2, 37, 300
+    n_kv = (3 << 21) // (4 * d) + 123           # three full ranges and a ragged tail
+    q, kk, v = _rbf(rng, B, H, n_q, d), _rbf(rng, B, H, n_kv, d), _rbf(rng, B, H, n_kv, d)
+    nl = B * H if per_head else 1
+    lists = rng.integers(0, n_kv, size=(nl, n_q, k)).astype(np.int32)  # unsorted, duplicates
+    lists[:, 1, ::7] = -5                        # skipped entries
+    lists[:, 2, ::5] = n_kv + 3
+    lists[:, 3, :] = rng.integers(100, 200, size=k)   # all in the first range
+    lists[:, 4, :] = -1                           # no key at all
+    assert sa.attn_workspace_bytes(B, H, n_q, n_kv, d, k, per_head_lists=per_head) > 0
+    gi = torch.from_numpy(lists.reshape(B, H, n_q, k) if per_head else lists[0]).cuda()
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(kk), to_dev_bf16(v)
+    print(f"split gather d={d} per_head={per_head} n_kv={n_kv}", flush=True)
+    o_s, l_s = sa.attn_fwd(qd, kd, vd, gather_idx=gi)
+    o_1, l_1 = sa.attn_fwd(qd, kd, vd, gather_idx=gi, split=False)
+    if per_head:
+        o_ref, lse_ref = oracle.attn_gather_rows(q, kk, v, lists, idx_per_head=True)
+    else:
+        o_ref, lse_ref = oracle.attn_gather_rows(q, kk, v, lists[0])
+    check_o_lse(o_s.cpu().numpy().reshape(-1, d), l_s.cpu().numpy().reshape(-1), o_ref, lse_ref, ctx="split")
+    check_o_lse(o_1.cpu().numpy().reshape(-1, d), l_1.cpu().numpy().reshape(-1), o_ref, lse_ref, ctx="single")
+    # repeated call: same bits (the partition keeps list order)
+    o_s2, l_s2 = sa.attn_fwd(qd, kd, vd, gather_idx=gi)
+    assert torch.equal(o_s, o_s2) and torch.equal(l_s, l_s2)
