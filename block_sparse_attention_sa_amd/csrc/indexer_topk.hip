@@ -100,64 +100,159 @@ indexer_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict__ ki,
 }
 
 // ---------------------------------------------------------------------------
-// Top-k: one workgroup of 1024 threads per query row; the row's candidates
-// (at most 65,536) stay in registers, 64 per thread, as order-preserving
-// 32-bit keys.  Four most-significant-digit-first radix passes with 256-bin
-// LDS histograms find the key T of the k-th largest candidate and how many
-// candidates equal to T must be taken; a flag per candidate then lets each
-// thread emit a contiguous index range in ascending order after one scan.
-constexpr int KTH = 1024;
-constexpr int KPER = 64;           // candidates per thread
-constexpr int KMAXN = KTH * KPER;  // 65,536
+// Top-k: one workgroup of 256 threads per query row, several rows per CU.
+//
+// The row is read from HBM once.  A stratified sample of 8,192 candidates
+// (128 runs of 64 keys spread over the row) brackets the key T of the k-th
+// largest candidate: two 11-bit digit levels of sample histograms give keys
+// LO <= HI whose sample ranks lie a few standard deviations either side of
+// the rank k maps to.  One pass over the row then marks every candidate with
+// key >= HI as selected (bitmap in LDS), counts them, and keeps the candidates
+// in [LO, HI) -- about 1,200 for k = 2,048 of 65,536 -- in LDS.  If the
+// counts show that T lies in the bracket, an exact radix selection on the
+// kept keys (relative to LO, 11-bit digits) finds T and how many of the
+// candidates equal to T are taken; otherwise (ties, adversarial orders) the
+// same exact selection runs over the whole row from memory.  A bitmap of
+// selected positions plus one of ties then gives each thread its output slots
+// after two block scans, and the indices leave in ascending order through an
+// LDS staging buffer with coalesced stores.
+constexpr int KTH = 256;                   // threads per row
+constexpr int KWAVES = KTH / 64;
+constexpr int KMAXN = 65536;               // candidates per row at most
+constexpr int KWORDS = KMAXN / 32;         // bitmap words
+constexpr int KRUNS = 128;                 // sample runs of 64 keys
+constexpr int KSPER = KRUNS / KWAVES;      // sample keys per thread
+constexpr int KWCAP = 512;                 // kept keys per wave
+constexpr int KCAP = KWCAP * KWAVES;       // kept keys per row
+constexpr int KBINS = 2048;                // 11-bit digits
+constexpr int KBATCH = 8;                  // float4 loads in flight per thread
 
+// Order-preserving 32-bit key: larger float, larger key; -0.0 and +0.0 map to
+// one key; every NaN maps to the largest key.
 __device__ __forceinline__ uint32_t order_key(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if (u == 0x80000000u) u = 0u;  // -0 ranks equal to +0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t k = (u >> 31) ? ~u : (u | 0x80000000u);
+    k = a == 0u ? 0x80000000u : k;
+    return a > 0x7F800000u ? 0xFFFFFFFFu : k;
 }
 
-// Inclusive scan of v over the workgroup (KTH threads); returns the inclusive
-// prefix and writes the total to *total.
-__device__ int block_scan_incl(int v, int* wsum, int* total)
+struct __attribute__((aligned(16))) TopkLds {
+    uint32_t sel[KWORDS];    // bit p: candidate p is selected
+    uint32_t hist[KBINS];    // digit histogram; tie bitmap once T is known
+    uint32_t mid[2 * KCAP];  // kept keys [KCAP], their positions [KCAP]; output staging
+    uint32_t wsum[KWAVES];
+    uint32_t wcnt[KWAVES];
+    uint32_t state[4];
+};
+
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane)
 {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int x = v;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off, 64);
+        const uint32_t y = __shfl_up(x, off, 64);
         if (lane >= off) x += y;
     }
-    if (lane == 63) wsum[w] = x;
-    __syncthreads();
-    if (w == 0) {
-        int s = lane < KTH / 64 ? wsum[lane] : 0;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(s, off, 64);
-            if (lane >= off) s += y;
-        }
-        if (lane < KTH / 64) wsum[lane] = s;
-    }
-    __syncthreads();
-    const int before = w > 0 ? wsum[w - 1] : 0;
-    *total = wsum[KTH / 64 - 1];
-    __syncthreads();
-    return x + before;
+    return x;
 }
 
+// Exclusive scan over the KTH threads; *total gets the sum.
+__device__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const uint32_t x = wave_incl_scan(v, lane);
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < KWAVES; ++i) {
+        const uint32_t s = wsum[i];
+        before += i < w ? s : 0u;
+        tot += s;
+    }
+    *total = tot;
+    __syncthreads();
+    return x - v + before;
+}
+
+// For ranks r0, r1 (1-based from the largest digit down; 0 = not asked), the
+// digit whose bin holds the rank and the rank left inside that bin, into
+// state[0..1] and state[2..3].  Ends with a barrier.
+__device__ void find_digits(TopkLds& L, uint32_t r0, uint32_t r1)
+{
+    const int tid = threadIdx.x;
+    // thread t owns bins KBINS-1-8t down to KBINS-8-8t
+    const uint4 a = *reinterpret_cast<const uint4*>(&L.hist[KBINS - 8 - 8 * tid]);
+    const uint4 b = *reinterpret_cast<const uint4*>(&L.hist[KBINS - 4 - 8 * tid]);
+    const uint32_t c[8] = {b.w, b.z, b.y, b.x, a.w, a.z, a.y, a.x};
+    uint32_t sum = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sum += c[j];
+    uint32_t total;
+    const uint32_t excl = block_excl_scan(sum, L.wsum, &total);
+    const uint32_t rs[2] = {r0, r1};
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const uint32_t r = rs[q];
+        if (r > excl && r <= excl + sum) {
+            uint32_t run = excl;
+            for (int j = 0; j < 8; ++j) {
+                if (run + c[j] >= r) {
+                    L.state[2 * q] = (uint32_t)(KBINS - 1 - 8 * tid - j);
+                    L.state[2 * q + 1] = r - run;
+                    break;
+                }
+                run += c[j];
+            }
+        }
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ void zero_words(uint32_t* p, int n)
+{
+    for (int i = threadIdx.x * 4; i < n; i += KTH * 4)
+        *reinterpret_cast<uint4*>(p + i) = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Exact selection: among the keys v (of `width` significant bits) that
+// for_each(f) hands to f, the r-th largest.  Returns its value and how many
+// of the keys equal to it rank within the first r.
+template <class ForEach>
+__device__ void radix_select(TopkLds& L, ForEach&& for_each, uint32_t width, uint32_t r,
+                             uint32_t& value, uint32_t& rem)
+{
+    uint32_t P = 0, done = 0;
+    rem = r;
+    while (done < width) {
+        const uint32_t nb = min(11u, width - done);
+        const uint32_t s = width - done - nb;
+        const uint32_t top = s + nb;
+        const uint32_t msk = (1u << nb) - 1u;
+        zero_words(L.hist, KBINS);
+        __syncthreads();
+        for_each([&](uint32_t v) {
+            if (((uint64_t)v >> top) == (uint64_t)P) atomicAdd(&L.hist[(v >> s) & msk], 1u);
+        });
+        __syncthreads();
+        find_digits(L, rem, 0u);
+        P = (P << nb) | L.state[0];
+        rem = L.state[1];
+        done += nb;
+    }
+    value = P;
+}
+
+template <bool ALIGNED>
 __global__ void __launch_bounds__(KTH)
 topk_kernel(const float* __restrict__ scores, int32_t n_q, int32_t n_kv, int32_t q_offset,
             int32_t k, int32_t* __restrict__ idx_out)
 {
-    __shared__ uint32_t hist[256];
-    __shared__ int wsum[KTH / 64];
-    __shared__ uint32_t sel_state[2];  // prefix, remaining k
-    __shared__ __attribute__((aligned(16))) uint8_t flag[KMAXN];
-
+    __shared__ TopkLds L;
     const int r = blockIdx.x;
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
+    const int lane = tid & 63, w = tid >> 6;
     const int64_t t = (int64_t)q_offset + r;
     const int n_cand = (int)min((int64_t)n_kv, t + 1);
     const float* row = scores + (int64_t)r * n_kv;
@@ -168,138 +263,224 @@ topk_kernel(const float* __restrict__ scores, int32_t n_q, int32_t n_kv, int32_t
         return;
     }
 
-    // candidates: thread tid holds indices 4*tid + 4096*it + x (x < 4)
-    uint32_t key[KPER];
+    // ---- sample: run c starts at c*n_cand/128 (or c*64 for short rows) ----
+    const bool big = n_cand > KRUNS * 64;
+    const uint32_t s_n = big ? (uint32_t)(KRUNS * 64) : (uint32_t)n_cand;
+    uint32_t skey[KSPER];
+    uint32_t svalid = 0;
 #pragma unroll
-    for (int it = 0; it < KPER / 4; ++it) {
-        const int base = 4 * tid + 4096 * it;
-        if (base + 3 < n_cand && (n_kv & 3) == 0) {
-            const float4 f = *reinterpret_cast<const float4*>(row + base);
-            key[4 * it + 0] = order_key(f.x);
-            key[4 * it + 1] = order_key(f.y);
-            key[4 * it + 2] = order_key(f.z);
-            key[4 * it + 3] = order_key(f.w);
-        } else {
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-                key[4 * it + x] = base + x < n_cand ? order_key(row[base + x]) : 0u;
-        }
+    for (int i = 0; i < KSPER; ++i) {
+        const int c = i * KWAVES + w;
+        const int p = (big ? (int)(((int64_t)c * n_cand) >> 7) : c * 64) + lane;
+        skey[i] = p < n_cand ? order_key(row[p]) : 0u;
+        svalid |= (p < n_cand ? 1u : 0u) << i;
     }
+    zero_words(L.sel, KWORDS);
+    zero_words(L.hist, KBINS);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < KSPER; ++i)
+        if ((svalid >> i) & 1u) atomicAdd(&L.hist[skey[i] >> 21], 1u);
+    __syncthreads();
 
-    if (tid == 0) {
-        sel_state[0] = 0u;
-        sel_state[1] = (uint32_t)k;
+    // sample ranks a few standard deviations either side of k's image
+    const float rho = (float)k * (float)s_n / (float)n_cand;
+    const float delta = 4.0f * sqrtf(rho) + 8.0f;
+    const float fhi = floorf(rho - delta), flo = ceilf(rho + delta);
+    const uint32_t r_hi = fhi < 1.0f ? 0u : (uint32_t)fhi;
+    const uint32_t r_lo = flo > (float)s_n ? 0u : (uint32_t)flo;
+    find_digits(L, r_hi, r_lo);
+    const uint32_t b_hi = L.state[0], q_hi = L.state[1];
+    const uint32_t b_lo = L.state[2], q_lo = L.state[3];
+    uint64_t HI = uint64_t(1) << 32;  // keys >= HI: selected for sure
+    uint32_t LO = 0;                  // keys in [LO, HI): kept
+#pragma unroll
+    for (int side = 0; side < 2; ++side) {
+        const uint32_t rk = side == 0 ? r_hi : r_lo;
+        if (rk == 0) continue;  // uniform
+        const uint32_t b1 = side == 0 ? b_hi : b_lo;
+        zero_words(L.hist, KBINS);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < KSPER; ++i)
+            if (((svalid >> i) & 1u) && (skey[i] >> 21) == b1)
+                atomicAdd(&L.hist[(skey[i] >> 10) & (KBINS - 1)], 1u);
+        __syncthreads();
+        find_digits(L, side == 0 ? q_hi : q_lo, 0u);
+        const uint32_t b2 = L.state[0];
+        if (side == 0)
+            HI = ((uint64_t)b1 << 21) + ((uint64_t)(b2 + 1) << 10);
+        else
+            LO = (b1 << 21) | (b2 << 10);
     }
-    uint32_t prefix = 0;
-    uint32_t remain = (uint32_t)k;
-#pragma unroll 1
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-        for (int i = tid; i < 256; i += KTH) hist[i] = 0;
-        __syncthreads();
-        const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    const uint32_t HIm1 = (uint32_t)(HI - 1);
+
+    // ---- one pass over the row ----
+    uint32_t woff = 0;  // kept keys of this wave so far (wave-uniform)
+    uint32_t c_hi = 0;  // keys >= HI of this thread
+    uint32_t* mkey = L.mid + w * KWCAP;
+    uint32_t* midx = L.mid + KCAP + w * KWCAP;
+    auto take4 = [&](int base, const uint32_t (&u)[4]) {
+        uint32_t nib = 0;
 #pragma unroll
-        for (int it = 0; it < KPER / 4; ++it)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int idx = 4 * tid + 4096 * it + x;
-                const uint32_t kk = key[4 * it + x];
-                if (idx < n_cand && (kk & hi_mask) == prefix)
-                    atomicAdd(&hist[(kk >> shift) & 255u], 1u);
-            }
-        __syncthreads();
-        // wave 0 finds the digit: bins scanned from the top
-        if (tid < 64) {
-            // lane owns bins 255-4*lane .. 252-4*lane (descending)
-            uint32_t c4[4];
-            uint32_t sum = 0;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                c4[x] = hist[255 - 4 * lane - x];
-                sum += c4[x];
-            }
-            uint32_t incl = sum;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t y = __shfl_up(incl, off, 64);
-                if (lane >= off) incl += y;
-            }
-            const uint32_t excl = incl - sum;
-            if (excl < remain && remain <= incl) {
-                uint32_t run = excl;
-                for (int x = 0; x < 4; ++x) {
-                    if (run + c4[x] >= remain) {
-                        const uint32_t digit = 255u - 4u * lane - x;
-                        sel_state[0] = prefix | (digit << shift);
-                        sel_state[1] = remain - run;
-                        break;
-                    }
-                    run += c4[x];
+        for (int x = 0; x < 4; ++x) {
+            const bool valid = base + x < n_cand;
+            const bool gh = valid && u[x] > HIm1;
+            const bool md = valid && u[x] >= LO && u[x] <= HIm1;
+            nib |= (gh ? 1u : 0u) << x;
+            const uint64_t bm = __ballot(md);
+            if (bm) {
+                const uint32_t pos = woff + __builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
+                                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+                if (md && pos < (uint32_t)KWCAP) {
+                    mkey[pos] = u[x];
+                    midx[pos] = (uint32_t)(base + x);
                 }
+                woff += (uint32_t)__popcll(bm);
             }
         }
-        __syncthreads();
-        prefix = sel_state[0];
-        remain = sel_state[1];
-        __syncthreads();
-    }
-    const uint32_t T = prefix;  // key of the k-th largest; take `remain` of the ties
-
-    // flags: 1 = above T, 2 = equal to T, 0 = below / not a candidate
+        if (nib) {
+            atomicOr(&L.sel[base >> 5], nib << (base & 31));
+            c_hi += (uint32_t)__popc(nib);
+        }
+    };
+    const int n_it = (n_cand + 1023) >> 10;  // 1,024 positions per step
+    if (ALIGNED) {
+        float4 nxt[KBATCH];
+        auto load_batch = [&](int b0) {
 #pragma unroll
-    for (int it = 0; it < KPER / 4; ++it) {
-        const int base = 4 * tid + 4096 * it;
-        if (base < KMAXN) {
-            uint32_t w = 0;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const uint32_t kk = key[4 * it + x];
-                const uint32_t f = (base + x < n_cand) ? (kk > T ? 1u : (kk == T ? 2u : 0u)) : 0u;
-                w |= f << (8 * x);
+            for (int j = 0; j < KBATCH; ++j) {
+                const int base = ((b0 + j) << 10) + 4 * tid;
+                nxt[j] = base < n_cand ? *reinterpret_cast<const float4*>(row + base)
+                                       : make_float4(0.f, 0.f, 0.f, 0.f);
             }
-            *reinterpret_cast<uint32_t*>(flag + base) = w;
+        };
+        load_batch(0);
+        for (int b0 = 0; b0 < n_it; b0 += KBATCH) {
+            float4 cur[KBATCH];
+#pragma unroll
+            for (int j = 0; j < KBATCH; ++j) cur[j] = nxt[j];
+            if (b0 + KBATCH < n_it) load_batch(b0 + KBATCH);
+#pragma unroll
+            for (int j = 0; j < KBATCH; ++j) {
+                const int base = ((b0 + j) << 10) + 4 * tid;
+                const uint32_t u[4] = {order_key(cur[j].x), order_key(cur[j].y), order_key(cur[j].z),
+                                       order_key(cur[j].w)};
+                take4(base, u);
+            }
+        }
+    } else {
+        for (int it = 0; it < n_it; ++it) {
+            const int base = (it << 10) + 4 * tid;
+            uint32_t u[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) u[x] = base + x < n_cand ? order_key(row[base + x]) : 0u;
+            take4(base, u);
+        }
+    }
+    if (lane == 0) L.wcnt[w] = woff;
+    uint32_t n_hi;
+    (void)block_excl_scan(c_hi, L.wsum, &n_hi);  // barriers publish wcnt too
+    uint32_t n_mid = 0;
+    bool ovf = false;
+#pragma unroll
+    for (int i = 0; i < KWAVES; ++i) {
+        n_mid += L.wcnt[i];
+        ovf |= L.wcnt[i] > (uint32_t)KWCAP;
+    }
+
+    uint32_t* tie = L.hist;
+    uint32_t T, need_eq;
+    if (!ovf && n_hi < (uint32_t)k && n_hi + n_mid >= (uint32_t)k) {
+        // ---- exact selection among the kept keys ----
+        const uint64_t span = HI - LO;  // >= 1
+        const uint32_t width = span <= 1 ? 0u : 64u - (uint32_t)__clzll(span - 1);
+        auto kept = [&](auto&& f) {
+#pragma unroll
+            for (int i = 0; i < KWAVES; ++i) {
+                const uint32_t n = L.wcnt[i];
+                for (uint32_t j = tid; j < n; j += KTH) f(L.mid[i * KWCAP + j] - LO);
+            }
+        };
+        uint32_t rel;
+        radix_select(L, kept, width, (uint32_t)k - n_hi, rel, need_eq);
+        T = LO + rel;
+        zero_words(tie, KWORDS);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < KWAVES; ++i) {
+            const uint32_t n = L.wcnt[i];
+            for (uint32_t j = tid; j < n; j += KTH) {
+                const uint32_t u = L.mid[i * KWCAP + j], p = L.mid[KCAP + i * KWCAP + j];
+                if (u > T) atomicOr(&L.sel[p >> 5], 1u << (p & 31));
+                else if (u == T) atomicOr(&tie[p >> 5], 1u << (p & 31));
+            }
+        }
+    } else {
+        // ---- exact selection over the whole row ----
+        auto all = [&](auto&& f) {
+            for (int p = tid; p < n_cand; p += KTH) f(order_key(row[p]));
+        };
+        radix_select(L, all, 32u, (uint32_t)k, T, need_eq);
+        // every bitmap word is written once: 64 positions per wave step
+        for (int p0 = 0; p0 < KMAXN; p0 += KTH) {
+            const int p = p0 + tid;
+            uint32_t u = 0;
+            const bool valid = p < n_cand;
+            if (valid) u = order_key(row[p]);
+            const uint64_t g = __ballot(valid && u > T);
+            const uint64_t e = __ballot(valid && u == T);
+            if (lane == 0) {
+                const int wd = (p0 + 64 * w) >> 5;
+                L.sel[wd] = (uint32_t)g;
+                L.sel[wd + 1] = (uint32_t)(g >> 32);
+                tie[wd] = (uint32_t)e;
+                tie[wd + 1] = (uint32_t)(e >> 32);
+            }
         }
     }
     __syncthreads();
 
-    // each thread scans its contiguous 64 flags
-    const int c0 = tid * KPER;
-    int n_gt = 0, n_eq = 0;
-    for (int e = 0; e < KPER; e += 4) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(flag + c0 + e);
+    // ---- emit: thread t owns positions [256t, 256t + 256) ----
+    uint32_t sw[8], tw[8];
+    {
+        const uint4 s0 = *reinterpret_cast<const uint4*>(&L.sel[8 * tid]);
+        const uint4 s1 = *reinterpret_cast<const uint4*>(&L.sel[8 * tid + 4]);
+        const uint4 t0 = *reinterpret_cast<const uint4*>(&tie[8 * tid]);
+        const uint4 t1 = *reinterpret_cast<const uint4*>(&tie[8 * tid + 4]);
+        sw[0] = s0.x; sw[1] = s0.y; sw[2] = s0.z; sw[3] = s0.w;
+        sw[4] = s1.x; sw[5] = s1.y; sw[6] = s1.z; sw[7] = s1.w;
+        tw[0] = t0.x; tw[1] = t0.y; tw[2] = t0.z; tw[3] = t0.w;
+        tw[4] = t1.x; tw[5] = t1.y; tw[6] = t1.z; tw[7] = t1.w;
+    }
+    uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const uint32_t f = (w >> (8 * x)) & 255u;
-            n_gt += f == 1u;
-            n_eq += f == 2u;
+    for (int i = 0; i < 8; ++i) {
+        n_gt += (uint32_t)__popc(sw[i]);
+        n_eq += (uint32_t)__popc(tw[i]);
+    }
+    uint32_t tot;
+    const uint32_t eq_before = block_excl_scan(n_eq, L.wsum, &tot);
+    uint32_t take = need_eq > eq_before ? min(need_eq - eq_before, n_eq) : 0u;
+    uint32_t pos = block_excl_scan(n_gt + take, L.wsum, &tot);
+    uint32_t* stage = L.mid;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t m = sw[i], te = tw[i];
+        while (te && take) {  // lowest-index ties first
+            const uint32_t low = te & (0u - te);
+            m |= low;
+            te ^= low;
+            --take;
+        }
+        while (m) {
+            if (pos < (uint32_t)k) stage[pos] = (uint32_t)(256 * tid + 32 * i + __builtin_ctz(m));
+            ++pos;
+            m &= m - 1u;
         }
     }
-    int tot;
-    const int eq_incl = block_scan_incl(n_eq, wsum, &tot);
-    int eq_rank = eq_incl - n_eq;
-    // selected count of this thread
-    int take_eq = (int)remain - eq_rank;
-    take_eq = take_eq < 0 ? 0 : (take_eq > n_eq ? n_eq : take_eq);
-    const int mine = n_gt + take_eq;
-    const int pos_incl = block_scan_incl(mine, wsum, &tot);
-    int pos = pos_incl - mine;
-    for (int e = 0; e < KPER; e += 4) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(flag + c0 + e);
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const uint32_t f = (w >> (8 * x)) & 255u;
-            bool take = f == 1u;
-            if (f == 2u) {
-                take = eq_rank < (int)remain;
-                ++eq_rank;
-            }
-            if (take) {
-                if (pos < k) out[pos] = c0 + e + x;
-                ++pos;
-            }
-        }
-    }
-    (void)lane;
+    __syncthreads();
+    for (int e = tid; e < k; e += KTH) out[e] = (int32_t)stage[e];
 }
 
 }  // namespace
@@ -317,8 +498,12 @@ hipError_t launch_indexer_scores(const uint16_t* q_idx, const uint16_t* k_idx, i
 hipError_t launch_topk(const float* scores, int32_t n_q, int32_t n_kv, int32_t q_offset,
                        int32_t topk, int32_t* idx_out, hipStream_t stream)
 {
-    hipLaunchKernelGGL(topk_kernel, dim3(n_q), dim3(KTH), 0, stream, scores, n_q, n_kv, q_offset,
-                       topk, idx_out);
+    if ((n_kv & 3) == 0)
+        hipLaunchKernelGGL(topk_kernel<true>, dim3(n_q), dim3(KTH), 0, stream, scores, n_q, n_kv, q_offset,
+                           topk, idx_out);
+    else
+        hipLaunchKernelGGL(topk_kernel<false>, dim3(n_q), dim3(KTH), 0, stream, scores, n_q, n_kv, q_offset,
+                           topk, idx_out);
     return hipGetLastError();
 }
 

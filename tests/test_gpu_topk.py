@@ -69,6 +69,48 @@ def test_topk_ties_signed_zero_and_padding():
     assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(2048, dtype=np.int32), (3, 1)))
 
 
+def _scores_of(kind, rng, n_q, n_kv):
+    if kind == "normal":
+        return (rng.standard_normal((n_q, n_kv)) * 8).astype(np.float32)
+    if kind == "ascending":  # order carries all the structure
+        return np.tile(np.arange(n_kv, dtype=np.float32), (n_q, 1)) + rng.random((n_q, 1), dtype=np.float32)
+    if kind == "descending":
+        return np.tile(-np.arange(n_kv, dtype=np.float32), (n_q, 1))
+    if kind == "narrow":  # every score within a few ulps of 1.0
+        return (1.0 + rng.integers(0, 64, size=(n_q, n_kv)) * np.float32(2.0 ** -23)).astype(np.float32)
+    if kind == "ties":
+        return rng.integers(-2, 3, size=(n_q, n_kv)).astype(np.float32)
+    if kind == "equal":
+        return np.full((n_q, n_kv), 0.5, np.float32)
+    if kind == "wide":  # magnitudes over many octaves, both signs, signed zeros
+        s = rng.standard_normal((n_q, n_kv)).astype(np.float32) * np.float32(2.0) ** rng.integers(-60, 60, (n_q, n_kv))
+        s[:, ::97] = -0.0
+        s[:, 1::89] = 0.0
+        return s.astype(np.float32)
+    if kind == "periodic":  # the best keys sit at one offset of every 1024
+        s = rng.standard_normal((n_q, n_kv)).astype(np.float32)
+        s[:, 5::1024] += 100.0
+        s[:, 700::1024] += 50.0
+        return s
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["normal", "ascending", "descending", "narrow", "ties", "equal", "wide",
+                                  "periodic"])
+@pytest.mark.parametrize("n_kv,k", [(65536, 2048), (65535, 4096), (65536, 1), (9001, 333), (8192, 2048)])
+def test_topk_score_distributions(kind, n_kv, k):
+    """Rows whose scores defeat a sampled threshold (ties, order, narrow range)
+    must still give the exact selection; odd n_kv takes the unaligned loads."""
+    rng = np.random.default_rng(n_kv + k)
+    n_q = 3
+    s = _scores_of(kind, rng, n_q, n_kv)
+    off = n_kv - 2  # last row sees every key, the others one or two fewer
+    print(f"topk {kind} n_kv={n_kv} k={k}", flush=True)
+    got = sa.topk(torch.from_numpy(s).cuda(), off, k).cpu().numpy()
+    want = oracle.topk_rows(s, np.minimum(np.arange(n_q) + off + 1, n_kv), k)
+    np.testing.assert_array_equal(got, want)
+
+
 def test_config5_indexer_topk_sampled_rows():
     cfg = W.topk_config(5)
     inp = W.topk_inputs(cfg)
