@@ -102,8 +102,8 @@ indexer_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict__ ki,
 // ---------------------------------------------------------------------------
 // Top-k: one workgroup of 256 threads per query row, several rows per CU.
 //
-// The row is read from HBM once.  A stratified sample of 8,192 candidates
-// (128 runs of 64 keys spread over the row) brackets the key T of the k-th
+// The row is read from HBM once.  The first eighth of that pass -- 128 runs
+// of 64 keys spread evenly over the row -- is a sample that brackets the key T of the k-th
 // largest candidate: two 11-bit digit levels of sample histograms give keys
 // LO <= HI whose sample ranks lie a few standard deviations either side of
 // the rank k maps to.  One pass over the row then marks every candidate with
@@ -114,14 +114,12 @@ indexer_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict__ ki,
 // candidates equal to T are taken; otherwise (ties, adversarial orders) the
 // same exact selection runs over the whole row from memory.  A bitmap of
 // selected positions plus one of ties then gives each thread its output slots
-// after two block scans, and the indices leave in ascending order through an
+// after one block scan, and the indices leave in ascending order through an
 // LDS staging buffer with coalesced stores.
 constexpr int KTH = 256;                   // threads per row
 constexpr int KWAVES = KTH / 64;
 constexpr int KMAXN = 65536;               // candidates per row at most
 constexpr int KWORDS = KMAXN / 32;         // bitmap words
-constexpr int KRUNS = 128;                 // sample runs of 64 keys
-constexpr int KSPER = KRUNS / KWAVES;      // sample keys per thread
 constexpr int KWCAP = 512;                 // kept keys per wave
 constexpr int KCAP = KWCAP * KWAVES;       // kept keys per row
 constexpr int KBINS = 2048;                // 11-bit digits
@@ -263,26 +261,55 @@ topk_kernel(const float* __restrict__ scores, int32_t n_q, int32_t n_kv, int32_t
         return;
     }
 
-    // ---- sample: run c starts at c*n_cand/128 (or c*64 for short rows) ----
-    const bool big = n_cand > KRUNS * 64;
-    const uint32_t s_n = big ? (uint32_t)(KRUNS * 64) : (uint32_t)n_cand;
-    uint32_t skey[KSPER];
-    uint32_t svalid = 0;
+    // Thread t reads, at step `it`, the float4 of positions 4g .. 4g+3 with
+    // g = 1024*(t/16) + 16*it + t%16: each step covers 16 runs of 64 keys, one
+    // in each sixteenth of the row.  Steps are taken in the order 0, 8, ..,
+    // 56, 1, 9, .., so the first batch of eight -- keys p with p % 512 < 64,
+    // an eighth of the row spread evenly over it -- is the sample.
+    auto pos_of = [&](int it) { return 4 * (((tid >> 4) << 10) + (it << 4) + (tid & 15)); };
+    auto load1 = [&](int it) {
+        const int base = pos_of(it);
+        float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (ALIGNED) {
+            if (base < n_cand) f = *reinterpret_cast<const float4*>(row + base);
+        } else {
+            if (base + 0 < n_cand) f.x = row[base + 0];
+            if (base + 1 < n_cand) f.y = row[base + 1];
+            if (base + 2 < n_cand) f.z = row[base + 2];
+            if (base + 3 < n_cand) f.w = row[base + 3];
+        }
+        return f;
+    };
+    float4 nxt[KBATCH], cur[KBATCH];
 #pragma unroll
-    for (int i = 0; i < KSPER; ++i) {
-        const int c = i * KWAVES + w;
-        const int p = (big ? (int)(((int64_t)c * n_cand) >> 7) : c * 64) + lane;
-        skey[i] = p < n_cand ? order_key(row[p]) : 0u;
-        svalid |= (p < n_cand ? 1u : 0u) << i;
-    }
+    for (int j = 0; j < KBATCH; ++j) nxt[j] = load1(KBATCH * j);
+#pragma unroll
+    for (int j = 0; j < KBATCH; ++j) cur[j] = nxt[j];
+#pragma unroll
+    for (int j = 0; j < KBATCH; ++j) nxt[j] = load1(KBATCH * j + 1);  // in flight meanwhile
     zero_words(L.sel, KWORDS);
     zero_words(L.hist, KBINS);
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < KSPER; ++i)
-        if ((svalid >> i) & 1u) atomicAdd(&L.hist[skey[i] >> 21], 1u);
-    __syncthreads();
 
+    // ---- bracket from the sample ----
+    uint32_t skey[KBATCH][4];
+    uint32_t svalid = 0;  // bit 4j + x
+#pragma unroll
+    for (int j = 0; j < KBATCH; ++j) {
+        const int base = pos_of(KBATCH * j);
+        skey[j][0] = order_key(cur[j].x);
+        skey[j][1] = order_key(cur[j].y);
+        skey[j][2] = order_key(cur[j].z);
+        skey[j][3] = order_key(cur[j].w);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const bool v = base + x < n_cand;
+            svalid |= (v ? 1u : 0u) << (4 * j + x);
+            if (v) atomicAdd(&L.hist[skey[j][x] >> 21], 1u);
+        }
+    }
+    __syncthreads();
+    const uint32_t s_n = (uint32_t)((n_cand >> 9) * 64 + min(n_cand & 511, 64));
     // sample ranks a few standard deviations either side of k's image
     const float rho = (float)k * (float)s_n / (float)n_cand;
     const float delta = 4.0f * sqrtf(rho) + 8.0f;
@@ -302,9 +329,11 @@ topk_kernel(const float* __restrict__ scores, int32_t n_q, int32_t n_kv, int32_t
         zero_words(L.hist, KBINS);
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < KSPER; ++i)
-            if (((svalid >> i) & 1u) && (skey[i] >> 21) == b1)
-                atomicAdd(&L.hist[(skey[i] >> 10) & (KBINS - 1)], 1u);
+        for (int j = 0; j < KBATCH; ++j)
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                if (((svalid >> (4 * j + x)) & 1u) && (skey[j][x] >> 21) == b1)
+                    atomicAdd(&L.hist[(skey[j][x] >> 10) & (KBINS - 1)], 1u);
         __syncthreads();
         find_digits(L, side == 0 ? q_hi : q_lo, 0u);
         const uint32_t b2 = L.state[0];
@@ -344,38 +373,21 @@ topk_kernel(const float* __restrict__ scores, int32_t n_q, int32_t n_kv, int32_t
             c_hi += (uint32_t)__popc(nib);
         }
     };
-    const int n_it = (n_cand + 1023) >> 10;  // 1,024 positions per step
-    if (ALIGNED) {
-        float4 nxt[KBATCH];
-        auto load_batch = [&](int b0) {
 #pragma unroll
-            for (int j = 0; j < KBATCH; ++j) {
-                const int base = ((b0 + j) << 10) + 4 * tid;
-                nxt[j] = base < n_cand ? *reinterpret_cast<const float4*>(row + base)
-                                       : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-        };
-        load_batch(0);
-        for (int b0 = 0; b0 < n_it; b0 += KBATCH) {
-            float4 cur[KBATCH];
+    for (int j = 0; j < KBATCH; ++j) take4(pos_of(KBATCH * j), skey[j]);
+#pragma unroll 1
+    for (int b0 = 1; b0 < KBATCH; ++b0) {
 #pragma unroll
-            for (int j = 0; j < KBATCH; ++j) cur[j] = nxt[j];
-            if (b0 + KBATCH < n_it) load_batch(b0 + KBATCH);
+        for (int j = 0; j < KBATCH; ++j) cur[j] = nxt[j];
+        if (b0 + 1 < KBATCH) {
 #pragma unroll
-            for (int j = 0; j < KBATCH; ++j) {
-                const int base = ((b0 + j) << 10) + 4 * tid;
-                const uint32_t u[4] = {order_key(cur[j].x), order_key(cur[j].y), order_key(cur[j].z),
-                                       order_key(cur[j].w)};
-                take4(base, u);
-            }
+            for (int j = 0; j < KBATCH; ++j) nxt[j] = load1(KBATCH * j + b0 + 1);
         }
-    } else {
-        for (int it = 0; it < n_it; ++it) {
-            const int base = (it << 10) + 4 * tid;
-            uint32_t u[4];
 #pragma unroll
-            for (int x = 0; x < 4; ++x) u[x] = base + x < n_cand ? order_key(row[base + x]) : 0u;
-            take4(base, u);
+        for (int j = 0; j < KBATCH; ++j) {
+            const uint32_t u[4] = {order_key(cur[j].x), order_key(cur[j].y), order_key(cur[j].z),
+                                   order_key(cur[j].w)};
+            take4(pos_of(KBATCH * j + b0), u);
         }
     }
     if (lane == 0) L.wcnt[w] = woff;
@@ -459,10 +471,18 @@ topk_kernel(const float* __restrict__ scores, int32_t n_q, int32_t n_kv, int32_t
         n_gt += (uint32_t)__popc(sw[i]);
         n_eq += (uint32_t)__popc(tw[i]);
     }
+    // one scan of (n_gt << 16 | n_eq): neither prefix reaches 2^16.  Ties are
+    // taken in position order, so the ties taken before this thread number
+    // min(need_eq, ties before it).
     uint32_t tot;
-    const uint32_t eq_before = block_excl_scan(n_eq, L.wsum, &tot);
-    uint32_t take = need_eq > eq_before ? min(need_eq - eq_before, n_eq) : 0u;
-    uint32_t pos = block_excl_scan(n_gt + take, L.wsum, &tot);
+    const uint32_t ex = block_excl_scan((n_gt << 16) | n_eq, L.wsum, &tot);
+    // (No conditional unsigned difference here: written as need_eq > e ?
+    // need_eq - e : 0, the subtraction gets hoisted with a no-wrap flag and
+    // the minimum below folds as if need_eq >= e always held.)
+    const uint32_t eq_before = ex & 0xFFFFu;
+    const uint32_t taken_before = min(need_eq, eq_before);
+    uint32_t take = min(need_eq, eq_before + n_eq) - taken_before;
+    uint32_t pos = (ex >> 16) + taken_before;
     uint32_t* stage = L.mid;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
