@@ -29,6 +29,12 @@
 //   * exp2 with the scale folded into one FMA; the running max is raised only
 //     when a row's tile max exceeds it by more than 8 (log2 units), so every
 //     exponent stays <= 2^8 and most accumulator rescales are skipped.
+//   * Wave priorities (s_setprio): highest while a wave issues matrix
+//     instructions, middle during its softmax, lowest otherwise, so that the
+//     two waves sharing a SIMD tend to alternate matrix and vector phases.
+//   * On a sub-tile that needs the mask, a wave whose rows may all see all of
+//     its keys skips the element mask, and one whose rows may see none of
+//     them skips the sub-tile.
 #include "sa_internal.h"
 
 namespace sa {
@@ -291,19 +297,26 @@ attn_block_kernel(AttnParams a)
                 // accumulator element i holds key k0 + 8*(i/4) + 4*hh + i%4
                 mbits[nb][sb] = bits >> (4 * hh);
             }
+        bool apply_mask = need_mask;
         if (need_mask) {
             // no row of this wave may see a key of the sub-tile: every score
-            // would be -inf and add nothing, so the wave skips the sub-tile
-            uint32_t any = 0;
+            // would be -inf and add nothing, so the wave skips the sub-tile;
+            // every row may see every key: no element mask is needed
+            uint32_t any = 0, all = 0x0F0F0F0Fu;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int sb = 0; sb < NSB; ++sb) any |= mbits[nb][sb];
+                for (int sb = 0; sb < NSB; ++sb) {
+                    any |= mbits[nb][sb];
+                    all &= mbits[nb][sb];
+                }
             if (__builtin_amdgcn_ballot_w64(any != 0) == 0) continue;
+            apply_mask = __builtin_amdgcn_ballot_w64(all != 0x0F0F0F0Fu) != 0;
         }
         __builtin_amdgcn_sched_barrier(0);
 
         // ---- S^T = K Q^T  (K operands fetched two k-steps ahead)
+        __builtin_amdgcn_s_setprio(2);
         f32x16 s[NB][NSB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
@@ -323,6 +336,7 @@ attn_block_kernel(AttnParams a)
             __builtin_amdgcn_sched_barrier(0);
         }
 
+        __builtin_amdgcn_s_setprio(0);
         // V^T operands of the first two P.V steps are requested now; they
         // land while the softmax runs
         bf16x8 va[3][NDB];
@@ -344,8 +358,9 @@ attn_block_kernel(AttnParams a)
         load_v(va[1], 1);
         __builtin_amdgcn_sched_barrier(0);
 
+        __builtin_amdgcn_s_setprio(1);
         // ---- element mask on partial / clipped sub-tiles only
-        if (need_mask) {
+        if (apply_mask) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -408,6 +423,7 @@ attn_block_kernel(AttnParams a)
         }
 
         // ---- O^T += V^T P^T  (V^T operands fetched two steps ahead)
+        __builtin_amdgcn_s_setprio(2);
 #pragma unroll
         for (int step = 0; step < 2 * NSB; ++step) {
             if (step + 2 < 2 * NSB) load_v(va[(step + 2) % 3], step + 2);
@@ -419,6 +435,7 @@ attn_block_kernel(AttnParams a)
                     o[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[step % 3][db], pk[nb][sb][cb], o[nb][db], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_setprio(0);
     }
 
     // ---- epilogue
