@@ -6,7 +6,8 @@
 // give no indexer formula; the score used here is the plain dot product of
 // the indexer query and key, accumulated in float32 as one fused
 // multiply-add chain in dimension order (a fixed order makes the selection
-// reproducible bit for bit).  Ties in the selection go to the lower index.
+// reproducible bit for bit); the chain runs on the float32 matrix cores.
+// Ties in the selection go to the lower index.
 #include "sa_internal.h"
 
 namespace sa {
@@ -15,87 +16,117 @@ namespace {
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 // ---------------------------------------------------------------------------
-// Indexer: tile of 64 queries x 128 keys per workgroup, 256 threads, each
-// thread a 4 x 8 register tile.  Operands are staged in LDS as float32,
-// dimension-major, 64 dimensions at a time; every accumulator runs its own
-// sequential fma chain over the dimensions, so the result does not depend on
-// the tiling.
-constexpr int IQ = 64, IS = 128, ID = 64, ITH = 256;
+// Indexer on the float32 matrix cores.  v_mfma_f32_32x32x1_2b_f32 takes one
+// dimension per instruction: every output gets exactly one multiply-add per
+// step, and the product of two bfloat16 values is exact in float32, so a
+// chain of these instructions in dimension order rounds exactly like the
+// sequential fused-multiply-add chain (checked bit for bit, denormal sums
+// included).  Operands: A = the lane's key (lanes 0-31 keys 0-31 of the
+// tile, lanes 32-63 keys 32-63), B = the lane's query (both halves hold the
+// same 32 queries), so the two 32 x 32 blocks cover 32 queries x 64 keys.
+// Result element (reg r, lane l): query l % 32, key 32*(r/16) + 8*((r%16)/4)
+// + 4*(l/32) + r%4, i.e. runs of four consecutive keys of one query row.
+// A wave owns 32 queries and walks a 512-key chunk in 64-key tiles; the next
+// tile's key rows are loaded while the current tile's chain runs.
+typedef __attribute__((ext_vector_type(32))) float f32x32;
+constexpr int XQ = 32;    // queries per wave
+constexpr int XW = 4;     // waves per workgroup
+constexpr int XT = 64;    // keys per tile
+constexpr int XKC = 512;  // keys per workgroup
 
-__global__ void __launch_bounds__(ITH)
+__device__ __forceinline__ float bf16_at(const uint32_t (&p)[32], int j)
+{
+    return __uint_as_float((j & 1) ? (p[j >> 1] & 0xFFFF0000u) : (p[j >> 1] << 16));
+}
+
+__device__ __forceinline__ void load_row64(const uint16_t* row, bool ok, int nd, uint32_t (&p)[32])
+{
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (ok && 8 * g < nd) w = *reinterpret_cast<const u32x4*>(row + 8 * g);
+        p[4 * g + 0] = w[0];
+        p[4 * g + 1] = w[1];
+        p[4 * g + 2] = w[2];
+        p[4 * g + 3] = w[3];
+    }
+}
+
+__global__ void __launch_bounds__(64 * XW, 2)
 indexer_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict__ ki, int32_t n_q,
                int32_t n_kv, int32_t d, int32_t q_offset, float* __restrict__ scores)
 {
-    __shared__ __attribute__((aligned(16))) float qs[ID][IQ];
-    __shared__ __attribute__((aligned(16))) float ks[ID][IS];
-    const int s0 = blockIdx.x * IS;
-    const int r0 = blockIdx.y * IQ;
-    const int t_hi = q_offset + min(r0 + IQ, n_q) - 1;  // last query position of the tile
-    if (s0 > t_hi) return;                                // no candidate in this tile
-    const int tid = threadIdx.x;
-    const int tq = tid >> 4, ts = tid & 15;              // 16 x 16 thread grid
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int hh = lane >> 5, col = lane & 31;
+    const int r0 = (blockIdx.y * XW + w) * XQ;
+    if (r0 >= n_q) return;  // no barriers in this kernel: waves leave on their own
+    const int s_begin = blockIdx.x * XKC;
+    const int t_max = q_offset + min(r0 + XQ, n_q) - 1;  // last query position of the wave
+    const int s_end = min(min(s_begin + XKC, n_kv), t_max + 1);
+    if (s_begin >= s_end) return;
 
-    float acc[4][8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+    const int r = r0 + col;  // this lane's query
+    const bool r_ok = r < n_q;
+    const int t = q_offset + r;
+    const uint16_t* qrow = qi + (int64_t)(r_ok ? r : 0) * d;
+    float* orow = scores + (int64_t)(r_ok ? r : 0) * n_kv;
+    const int nch = (d + 63) >> 6;
+    const bool vec_ok = (n_kv & 3) == 0;
 
-    for (int c0 = 0; c0 < d; c0 += ID) {
-        const int dc = min(ID, d - c0);
-        __syncthreads();
-        // stage q: 64 rows x dc dims; 8 dims per 16-byte load
-        for (int u = tid; u < IQ * (ID / 8); u += ITH) {
-            const int r = u / (ID / 8), c8 = (u % (ID / 8)) * 8;
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (r0 + r < n_q && c8 < dc)
-                w = *reinterpret_cast<const u32x4*>(qi + (int64_t)(r0 + r) * d + c0 + c8);
+    uint32_t qp[32], kp[32], kn[32];
+    if (nch == 1) load_row64(qrow, r_ok, d, qp);
+    auto key_row = [&](int s0) { return ki + (int64_t)min(s0 + lane, n_kv - 1) * d; };
+    if (nch == 1) load_row64(key_row(s_begin), s_begin + lane < n_kv, d, kn);
+
+    for (int s0 = s_begin; s0 < s_end; s0 += XT) {
+        f32x32 acc;
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                qs[c8 + 2 * x][r] = __uint_as_float(w[x] << 16);
-                qs[c8 + 2 * x + 1][r] = __uint_as_float(w[x] & 0xFFFF0000u);
+        for (int i = 0; i < 32; ++i) acc[i] = 0.f;
+        if (nch == 1) {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) kp[i] = kn[i];
+            if (s0 + XT < s_end) load_row64(key_row(s0 + XT), s0 + XT + lane < n_kv, d, kn);
+#pragma unroll
+            for (int g = 0; g < 8; ++g) {
+                if (8 * g >= d) break;  // uniform
+#pragma unroll
+                for (int x = 0; x < 8; ++x)
+                    acc = __builtin_amdgcn_mfma_f32_32x32x1f32(bf16_at(kp, 8 * g + x), bf16_at(qp, 8 * g + x), acc, 0, 0, 0);
             }
-        }
-        for (int u = tid; u < IS * (ID / 8); u += ITH) {
-            const int r = u / (ID / 8), c8 = (u % (ID / 8)) * 8;
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (s0 + r < n_kv && c8 < dc)
-                w = *reinterpret_cast<const u32x4*>(ki + (int64_t)(s0 + r) * d + c0 + c8);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                ks[c8 + 2 * x][r] = __uint_as_float(w[x] << 16);
-                ks[c8 + 2 * x + 1][r] = __uint_as_float(w[x] & 0xFFFF0000u);
-            }
-        }
-        __syncthreads();
-        for (int c = 0; c < dc; ++c) {
-            const float4 qa = *reinterpret_cast<const float4*>(&qs[c][tq * 4]);
-            const float4 k0 = *reinterpret_cast<const float4*>(&ks[c][ts * 8]);
-            const float4 k1 = *reinterpret_cast<const float4*>(&ks[c][ts * 8 + 4]);
-            const float qv[4] = {qa.x, qa.y, qa.z, qa.w};
-            const float kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_fmaf(qv[i], kv[j], acc[i][j]);
-        }
-    }
-
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = r0 + tq * 4 + i;
-        if (r >= n_q) continue;
-        const int t = q_offset + r;
-        const int s = s0 + ts * 8;
-        float* dst = scores + (int64_t)r * n_kv + s;
-        if (s + 7 <= t && s + 7 < n_kv && (n_kv & 3) == 0) {
-            *reinterpret_cast<float4*>(dst) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-            *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
         } else {
+            const uint16_t* krow = key_row(s0);
+            const bool s_ok = s0 + lane < n_kv;
+            for (int c = 0; c < nch; ++c) {
+                const int c0 = 64 * c, nd = min(64, d - c0);
+                load_row64(qrow + c0, r_ok, nd, qp);
+                load_row64(krow + c0, s_ok, nd, kp);
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (s + j <= t && s + j < n_kv) dst[j] = acc[i][j];
+                for (int g = 0; g < 8; ++g) {
+                    if (8 * g >= nd) break;  // uniform
+#pragma unroll
+                    for (int x = 0; x < 8; ++x)
+                        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(bf16_at(kp, 8 * g + x), bf16_at(qp, 8 * g + x), acc, 0, 0, 0);
+                }
+            }
         }
+        if (!r_ok) continue;
+        // entries s <= t of this query row, s < n_kv
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int sk = s0 + 32 * b + 8 * m + 4 * hh;
+                const float v0 = acc[16 * b + 4 * m + 0], v1 = acc[16 * b + 4 * m + 1];
+                const float v2 = acc[16 * b + 4 * m + 2], v3 = acc[16 * b + 4 * m + 3];
+                if (vec_ok && sk + 3 <= t && sk + 3 < n_kv) {
+                    *reinterpret_cast<float4*>(orow + sk) = make_float4(v0, v1, v2, v3);
+                } else {
+                    if (sk + 0 <= t && sk + 0 < n_kv) orow[sk + 0] = v0;
+                    if (sk + 1 <= t && sk + 1 < n_kv) orow[sk + 1] = v1;
+                    if (sk + 2 <= t && sk + 2 < n_kv) orow[sk + 2] = v2;
+                    if (sk + 3 <= t && sk + 3 < n_kv) orow[sk + 3] = v3;
+                }
+            }
     }
 }
 
@@ -509,8 +540,8 @@ hipError_t launch_indexer_scores(const uint16_t* q_idx, const uint16_t* k_idx, i
                                  int32_t n_kv, int32_t d_idx, int32_t q_offset, float* scores,
                                  hipStream_t stream)
 {
-    dim3 grid((n_kv + IS - 1) / IS, (n_q + IQ - 1) / IQ);
-    hipLaunchKernelGGL(indexer_kernel, grid, dim3(ITH), 0, stream, q_idx, k_idx, n_q, n_kv, d_idx,
+    dim3 grid((n_kv + XKC - 1) / XKC, (n_q + XQ * XW - 1) / (XQ * XW));
+    hipLaunchKernelGGL(indexer_kernel, grid, dim3(64 * XW), 0, stream, q_idx, k_idx, n_q, n_kv, d_idx,
                        q_offset, scores);
     return hipGetLastError();
 }

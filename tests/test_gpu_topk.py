@@ -23,7 +23,8 @@ def _rbf(rng, *shape):
 
 
 @pytest.mark.parametrize("n_q,n_kv,d,off", [(1, 1, 64, 0), (70, 300, 64, 230), (64, 1000, 32, 900),
-                                            (130, 4100, 128, 3970), (5, 257, 8, 0)])
+                                            (130, 4100, 128, 3970), (5, 257, 8, 0), (33, 777, 256, 700),
+                                            (17, 1300, 200, 1290), (200, 2050, 64, 1900), (3, 70, 24, 5)])
 def test_indexer_bit_exact(n_q, n_kv, d, off):
     rng = np.random.default_rng(n_q + n_kv)
     qi, ki = _rbf(rng, n_q, d), _rbf(rng, n_kv, d)
