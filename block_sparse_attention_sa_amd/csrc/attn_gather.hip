@@ -39,11 +39,11 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg)
     return base + slot;
 }
 
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
 constexpr int kBlk = 128;  // keys per block of the online softmax
-constexpr int kInFlight = 8;  // row loads per lane issued before use
+constexpr int kQF = 4;     // score steps whose row loads are issued together
+constexpr int kVF = 4;     // value steps whose row loads are issued together
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 __device__ __forceinline__ void wave_lds_sync()
 {
@@ -52,21 +52,48 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
+// a.x * b.x + a.y * b.y + c on bfloat16 pairs (v_dot2c_f32_bf16)
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// The query's bfloat16 pairs of the 32 columns [32*(lane % (D/32)), +32).
+template <int D>
+__device__ __forceinline__ void load_q2(const uint16_t* qrow, int lane, uint32_t (&q2)[16])
+{
+    const int qs = lane % (D / 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 32 * qs + 8 * i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) q2[4 * i + j] = w[j];
+    }
+}
+
 // Online softmax of one query over the n keys keys[0..n): m (max, log2
 // units, scale folded in), l (sum of exp2(s - m)) and acc (sum of
-// exp2(s - m) v over this lane's 8 columns, summed over all lanes of the
-// column later).  With `check`, entries outside [0, n_kv) are skipped.
+// exp2(s - m) v over this lane's 8 columns [8*(lane % (D/8)), +8)).  With
+// `check`, entries outside [0, n_kv) are skipped.
+//   scores: D/32 lanes per key row, each a 64-byte slice, bf16 pair dot
+//           products, then a sum over the row's lanes;
+//   values: D/8 lanes per row, each 16 bytes; a lane group takes two keys
+//           per step, their values are interleaved into (key0, key1) pairs
+//           and one pair dot product with (p0, p1) adds both keys' terms.
 template <int D>
 __device__ __forceinline__ void gather_online(const int32_t* keys, int n, bool check, int n_kv,
                                               const uint16_t* kg, int64_t k_sn, const uint16_t* vg, int64_t v_sn,
-                                              const float (&qv)[8], float c, float* sc, int lane,
+                                              const uint32_t (&q2)[16], float c, float* sc, int lane,
                                               float& m, float& l, float (&acc)[8])
 {
-    constexpr int LPK = D / 8;        // lanes per row
-    constexpr int KPS = 64 / LPK;     // rows per wave-wide load
-    constexpr int STEPS = kBlk / KPS; // loads per block and tensor
-    static_assert(STEPS % kInFlight == 0, "block split");
-    const int sub = lane % LPK, kgrp = lane / LPK;
+    constexpr int LQ = D / 32, KQ = 64 / LQ;  // scores: lanes per row, rows per step
+    constexpr int QSTEPS = kBlk / KQ;
+    constexpr int LPK = D / 8, GP = 64 / LPK;  // values: lanes per row, row groups
+    constexpr int KPV = 2 * GP;                // keys per value step
+    constexpr int VSTEPS = kBlk / KPV;
+    static_assert(QSTEPS % kQF == 0 && VSTEPS % kVF == 0, "block split");
+    const int qs = lane % LQ, qg = lane / LQ;
+    const int sub = lane % LPK, vgr = lane / LPK;
     m = -INFINITY;
     l = 0.f;
 #pragma unroll
@@ -81,41 +108,46 @@ __device__ __forceinline__ void gather_online(const int32_t* keys, int n, bool c
             if (check && (s < 0 || s >= n_kv)) s = -1;
             kid[r] = s;
         }
-        // row index of key e = step * KPS + kgrp of the block
-        auto key_of = [&](int step) {
-            const int e = step * KPS + kgrp;
-            const int v = __shfl(step * KPS < 64 ? kid[0] : kid[1], e & 63, 64);
+        // key of block entry e; e < 64 or e >= 64 is uniform at every call
+        auto key_at = [&](int e) {
+            const int v = __shfl(e < 64 ? kid[0] : kid[1], e & 63, 64);
             return e < nb ? v : -1;
         };
         // ---- scores
         float bmax = -INFINITY;
 #pragma unroll 1
-        for (int g = 0; g < STEPS; g += kInFlight) {
-            u32x4 w[kInFlight];
-            int sk[kInFlight];
+        for (int g = 0; g < QSTEPS; g += kQF) {
+            u32x4 w[kQF][4];
+            int sk[kQF];
 #pragma unroll
-            for (int i = 0; i < kInFlight; ++i) {
-                sk[i] = key_of(g + i);
-                w[i] = u32x4{0u, 0u, 0u, 0u};
-                if (sk[i] >= 0) w[i] = *reinterpret_cast<const u32x4*>(kg + (int64_t)sk[i] * k_sn + sub * 8);
+            for (int i = 0; i < kQF; ++i) {
+                sk[i] = key_at((g + i) * KQ + qg);
+                const uint16_t* row = kg + (int64_t)(sk[i] >= 0 ? sk[i] : 0) * k_sn + 32 * qs;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    w[i][x] = u32x4{0u, 0u, 0u, 0u};
+                    if (sk[i] >= 0) w[i][x] = *reinterpret_cast<const u32x4*>(row + 8 * x);
+                }
             }
 #pragma unroll
-            for (int i = 0; i < kInFlight; ++i) {
-                float d = 0.f;
+            for (int i = 0; i < kQF; ++i) {
+                float d0 = 0.f, d1 = 0.f;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    d = __builtin_fmaf(qv[2 * j], bf_lo(w[i][j]), d);
-                    d = __builtin_fmaf(qv[2 * j + 1], bf_hi(w[i][j]), d);
+                for (int x = 0; x < 4; ++x) {
+                    d0 = dot2(w[i][x][0], q2[4 * x + 0], d0);
+                    d1 = dot2(w[i][x][1], q2[4 * x + 1], d1);
+                    d0 = dot2(w[i][x][2], q2[4 * x + 2], d0);
+                    d1 = dot2(w[i][x][3], q2[4 * x + 3], d1);
                 }
+                float d = d0 + d1;
 #pragma unroll
-                for (int off = 1; off < LPK; off <<= 1) d += __shfl_xor(d, off, 64);
+                for (int off = 1; off < LQ; off <<= 1) d += __shfl_xor(d, off, 64);
                 const float sv = sk[i] >= 0 ? d * c : -INFINITY;
                 bmax = fmaxf(bmax, sv);
-                const int e = (g + i) * KPS + kgrp;
-                if (sub == 0) sc[e] = sv;
+                if (qs == 0) sc[(g + i) * KQ + qg] = sv;
             }
         }
-        for (int off = LPK; off < 64; off <<= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, off, 64));
+        for (int off = LQ; off < 64; off <<= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, off, 64));
         const float m_new = fmaxf(m, bmax);
         if (m_new != -INFINITY && m_new > m) {
             const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
@@ -138,45 +170,41 @@ __device__ __forceinline__ void gather_online(const int32_t* keys, int n, bool c
         for (int off = 32; off > 0; off >>= 1) ps += __shfl_xor(ps, off, 64);
         l += ps;
         wave_lds_sync();
-        // ---- acc += p v
+        // ---- acc += p v, two keys per lane group and step
 #pragma unroll 1
-        for (int g = 0; g < STEPS; g += kInFlight) {
-            u32x4 w[kInFlight];
-            int sk[kInFlight];
+        for (int g = 0; g < VSTEPS; g += kVF) {
+            u32x4 w0[kVF], w1[kVF];
 #pragma unroll
-            for (int i = 0; i < kInFlight; ++i) {
-                sk[i] = key_of(g + i);
-                w[i] = u32x4{0u, 0u, 0u, 0u};
-                if (sk[i] >= 0) w[i] = *reinterpret_cast<const u32x4*>(vg + (int64_t)sk[i] * v_sn + sub * 8);
+            for (int i = 0; i < kVF; ++i) {
+                const int e0 = (g + i) * KPV + 2 * vgr;
+                const int s0 = key_at(e0), s1 = key_at(e0 + 1);
+                w0[i] = u32x4{0u, 0u, 0u, 0u};
+                w1[i] = u32x4{0u, 0u, 0u, 0u};
+                if (s0 >= 0) w0[i] = *reinterpret_cast<const u32x4*>(vg + (int64_t)s0 * v_sn + sub * 8);
+                if (s1 >= 0) w1[i] = *reinterpret_cast<const u32x4*>(vg + (int64_t)s1 * v_sn + sub * 8);
             }
 #pragma unroll
-            for (int i = 0; i < kInFlight; ++i) {
-                const float pv = sc[(g + i) * KPS + kgrp];
+            for (int i = 0; i < kVF; ++i) {
+                const int e0 = (g + i) * KPV + 2 * vgr;
+                const bf16x2 pp = {(__bf16)sc[e0], (__bf16)sc[e0 + 1]};
+                const uint32_t p2 = __builtin_bit_cast(uint32_t, pp);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    acc[2 * j] = __builtin_fmaf(pv, bf_lo(w[i][j]), acc[2 * j]);
-                    acc[2 * j + 1] = __builtin_fmaf(pv, bf_hi(w[i][j]), acc[2 * j + 1]);
+                    // (key0, key1) pairs of columns 2j and 2j+1
+                    const uint32_t lo = __builtin_amdgcn_perm(w1[i][j], w0[i][j], 0x05040100u);
+                    const uint32_t hi = __builtin_amdgcn_perm(w1[i][j], w0[i][j], 0x07060302u);
+                    acc[2 * j] = dot2(lo, p2, acc[2 * j]);
+                    acc[2 * j + 1] = dot2(hi, p2, acc[2 * j + 1]);
                 }
             }
         }
         wave_lds_sync();
     }
-    // the rows of a step were spread over the lane groups: sum the groups
+    // the keys of a step were spread over the lane groups: sum the groups
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int off = LPK; off < 64; off <<= 1) acc[i] += __shfl_xor(acc[i], off, 64);
-}
-
-template <int D>
-__device__ __forceinline__ void load_q_slice(const AttnParams& a, int b, int h, int t, int sub, float (&qv)[8])
-{
-    const u32x4 w = *reinterpret_cast<const u32x4*>(a.q + b * a.q_sb + h * a.q_sh + (int64_t)t * a.q_sn + sub * 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        qv[2 * i] = bf_lo(w[i]);
-        qv[2 * i + 1] = bf_hi(w[i]);
-    }
 }
 
 template <int D, bool OF32>
@@ -193,11 +221,11 @@ __global__ void __launch_bounds__(kWaves * 64) attn_gather_kernel(AttnParams a)
     const int bh = (int)(item / a.n_q);
     const int b = bh / a.heads, h = bh % a.heads;
     const int sub = lane % LPK, kgrp = lane / LPK;
-    float qv[8];
-    load_q_slice<D>(a, b, h, t, sub, qv);
+    uint32_t q2[16];
+    load_q2<D>(a.q + b * a.q_sb + h * a.q_sh + (int64_t)t * a.q_sn, lane, q2);
     float m, l, acc[8];
     gather_online<D>(a.gidx + bh * a.g_bh_stride + (int64_t)t * a.topk, a.topk, true, a.n_kv,
-                     a.k + b * a.k_sb + h * a.k_sh, a.k_sn, a.v + b * a.v_sb + h * a.v_sh, a.v_sn, qv,
+                     a.k + b * a.k_sb + h * a.k_sh, a.k_sn, a.v + b * a.v_sb + h * a.v_sh, a.v_sn, q2,
                      a.scale_log2, sc_all[wave], lane, m, l, acc);
     if (kgrp == 0) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -330,11 +358,11 @@ __global__ void __launch_bounds__(kWaves * 64) gather_part_kernel(AttnParams a)
     const int32_t* offs = a.g_offs + row * (a.g_nchunk + 1);
     const int o0 = offs[rg], o1 = offs[rg + 1];
     const int sub = lane % LPK, kgrp = lane / LPK;
-    float qv[8];
-    load_q_slice<D>(a, b, h, t, sub, qv);
+    uint32_t q2[16];
+    load_q2<D>(a.q + b * a.q_sb + h * a.q_sh + (int64_t)t * a.q_sn, lane, q2);
     float m, l, acc[8];
     gather_online<D>(a.g_lists + row * a.topk + o0, o1 - o0, false, a.n_kv, a.k + b * a.k_sb + h * a.k_sh, a.k_sn,
-                     a.v + b * a.v_sb + h * a.v_sh, a.v_sn, qv, a.scale_log2, sc_all[wave], lane, m, l, acc);
+                     a.v + b * a.v_sb + h * a.v_sh, a.v_sn, q2, a.scale_log2, sc_all[wave], lane, m, l, acc);
     const int64_t pidx = ((int64_t)bh * a.n_q + t) * a.g_nchunk + rg;
     if (kgrp == 0) {
         float* po = a.g_po + pidx * D + sub * 8;
