@@ -27,7 +27,11 @@
  *    returns a thread-local description of the last non-OK status.  No call
  *    aborts or lets an exception escape.
  *  - Positions are absolute: query row r has position q_offset + r; key row
- *    s has position s.  All sizes and positions must fit in int32 (< 2^31).
+ *    s has position s.  All sizes and positions must fit in int32 (< 2^31);
+ *    where a pattern is evaluated (sa_build_block_mask, sa_attn_fwd block
+ *    mode), q_offset + n_q + n_kv must stay below 2^29.  In sa_attn_fwd,
+ *    (n_kv + 256) times the larger K/V row stride in bytes must stay below
+ *    2^31 (rows are addressed with 32-bit byte offsets).
  *  - bfloat16 tensors are passed as raw 16-bit storage.
  */
 #ifndef SA_H
@@ -213,8 +217,9 @@ sa_status sa_indexer_scores(const void *q_idx, const void *k_idx, int64_t n_q, i
  * (score descending, key index ascending); candidates of row r are
  * s = 0 .. min(q_offset + r, n_kv - 1).  Output idx int32 [n_q, topk]
  * (DEVICE): the selected key indices in ascending order, -1 padded when a
- * row has fewer candidates.  -0.0 and +0.0 compare equal; scores must not
- * be NaN (NaN ranks as the largest value).  topk in [1, 4096], n_kv < 2^20.
+ * row has fewer candidates.  -0.0 and +0.0 compare equal; a NaN score of
+ * either sign ranks above every number, and NaNs tie with each other.
+ * topk in [1, 4096], n_kv <= 65536.
  */
 sa_status sa_topk(const float *scores, int64_t n_q, int64_t n_kv, int64_t q_offset, int32_t topk,
                   int32_t *idx_out, void *stream);
