@@ -177,7 +177,9 @@ attn_block_kernel(AttnParams a)
     // [g*1024, g*1024 + 1024) and fetches rows g*ROWS_PER_KB + dma_r.  The
     // swizzles depend on the row only modulo 4, and a wave's groups advance by
     // NW, so the per-lane offset terms repeat with period KT and are computed
-    // once; the uniform parts (sub-tile start, group) stay in scalar registers.
+    // once; the uniform parts (sub-tile start, group) go in the scalar offset
+    // operand, so the copies need no vector arithmetic or temporaries and
+    // issue back to back.
     const int dma_r = lane / CH;
     const int dma_p = lane % CH;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -193,15 +195,15 @@ attn_block_kernel(AttnParams a)
         for (int i = 0; i < DMA_W; ++i) {
             const int g = wave_u + i * NW;
             const uint32_t rows = (uint32_t)(kv0 + g * ROWS_PER_KB);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kdst + g * 1024), 16,
-                                                     kterm[i % KT] + rows * krow_b, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kdst + g * 1024), 16, kterm[i % KT],
+                                                     (int)(rows * krow_b), 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < DMA_W; ++i) {
             const int g = wave_u + i * NW;
             const uint32_t rows = (uint32_t)(kv0 + g * ROWS_PER_KB);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vdst + g * 1024), 16,
-                                                     vterm + rows * vrow_b, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vdst + g * 1024), 16, vterm,
+                                                     (int)(rows * vrow_b), 0, 0);
         }
     };
     refill(0);
