@@ -119,16 +119,25 @@ compact_kernel(int32_t n_q, int32_t n_kv, int32_t bq, int32_t bk, int32_t nkb, i
         live += cnt[j] > 0;
         pairs += cnt[j];
     }
-    scan[t] = live;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-        const int v = t >= off ? scan[t - off] : 0;
-        __syncthreads();
-        scan[t] += v;
-        __syncthreads();
+    // exclusive scan of `live` over the workgroup: within waves, then over
+    // the wave totals
+    const int lane = t & 63, w = t >> 6;
+    int x = live;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
     }
-    int pos = scan[t] - live;
-    const int total_live = scan[kThreads - 1];
+    if (lane == 63) scan[w] = x;
+    __syncthreads();
+    int before = 0, total_live = 0;
+#pragma unroll
+    for (int k = 0; k < kThreads / 64; ++k) {
+        const int v = scan[k];
+        before += k < w ? v : 0;
+        total_live += v;
+    }
+    int pos = before + x - live;
     const int32_t q0 = i * bq;
     const int64_t rows_in = min(q0 + bq, n_q) - q0;
     for (int j = j0; j < j1; ++j) {
@@ -149,7 +158,7 @@ compact_kernel(int32_t n_q, int32_t n_kv, int32_t bq, int32_t bk, int32_t nkb, i
     if (t == 0) kv_count[i] = total_live;
     // wave reduction, one atomic per wave (integers: exact in any order)
     for (int off = 32; off > 0; off >>= 1) pairs += __shfl_down(pairs, off, 64);
-    if ((t & 63) == 0 && pairs) atomicAdd(live_pairs, (unsigned long long)pairs);
+    if (lane == 0 && pairs) atomicAdd(live_pairs, (unsigned long long)pairs);
 }
 
 }  // namespace

@@ -67,3 +67,16 @@ def test_repeat_is_identical():
     b = sa.build_block_mask(cfg.pattern, cfg.N, cfg.N, cfg.block, cfg.block)
     for f in ("kv_count", "kv_index", "kv_partial", "live_pairs"):
         assert bool((getattr(a, f) == getattr(b, f)).all())
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_long_rows_two_kernel_path(seed):
+    """Rows of more than 512 key blocks take the two-kernel builder."""
+    rng = np.random.default_rng(900 + seed)
+    n_q, n_kv, bq, bk = int(rng.integers(40, 130)), int(rng.integers(16500, 21000)), 64, 32
+    assert (n_kv + bk - 1) // bk > 512
+    pat = random_pattern(rng, n_q, n_kv)
+    print(f"builder long rows seed {seed} n_q={n_q} n_kv={n_kv} {sorted(pat)}", flush=True)
+    got = sa.build_block_mask(pat, n_q, n_kv, bq, bk)
+    want = oracle.block_lists(pat, n_q, n_kv, bq, bk)
+    _compare(got, want, f"long rows seed {seed}")
