@@ -74,7 +74,12 @@ indexer_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict__ ki,
     const bool vec_ok = (n_kv & 3) == 0;
 
     uint32_t qp[32], kp[32], kn[32];
-    if (nch == 1) load_row64(qrow, r_ok, d, qp);
+    float qv[64];
+    if (nch == 1) {
+        load_row64(qrow, r_ok, d, qp);
+#pragma unroll
+        for (int j = 0; j < 64; ++j) qv[j] = bf16_at(qp, j);
+    }
     auto key_row = [&](int s0) { return ki + (int64_t)min(s0 + lane, n_kv - 1) * d; };
     if (nch == 1) load_row64(key_row(s_begin), s_begin + lane < n_kv, d, kn);
 
@@ -91,7 +96,7 @@ indexer_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict__ ki,
                 if (8 * g >= d) break;  // uniform
 #pragma unroll
                 for (int x = 0; x < 8; ++x)
-                    acc = __builtin_amdgcn_mfma_f32_32x32x1f32(bf16_at(kp, 8 * g + x), bf16_at(qp, 8 * g + x), acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x1f32(bf16_at(kp, 8 * g + x), qv[8 * g + x], acc, 0, 0, 0);
             }
         } else {
             const uint16_t* krow = key_row(s0);
