@@ -92,7 +92,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU; there is no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         return 2
 
