@@ -42,6 +42,7 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg)
 constexpr int kBlk = 128;  // keys per block of the online softmax
 constexpr int kQF = 4;     // score steps whose row loads are issued together
 constexpr int kVF = 4;     // value steps whose row loads are issued together
+constexpr int kPartItems = 4;  // (head, range, query) items per wave in the split form
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
@@ -344,34 +345,50 @@ __global__ void __launch_bounds__(kWaves * 64) gather_part_kernel(AttnParams a)
     __shared__ float sc_all[kWaves][kBlk];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t n_items = (int64_t)a.batch * a.heads * a.g_nchunk * a.n_q;
-    const int64_t item = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * kWaves + wave;
-    if (item >= n_items) return;
-    // item = ((bh * nchunk) + range) * n_q + t: the waves working on one key
-    // range of one head are neighbours, and land on the same XCD
-    const int t = (int)(item % a.n_q);
-    const int64_t rest = item / a.n_q;
-    const int rg = (int)(rest % a.g_nchunk);
-    const int bh = (int)(rest / a.g_nchunk);
-    const int b = bh / a.heads, h = bh % a.heads;
-    const int64_t row = a.g_bh_stride == 0 ? (int64_t)t : (int64_t)bh * a.n_q + t;
-    const int32_t* offs = a.g_offs + row * (a.g_nchunk + 1);
-    const int o0 = offs[rg], o1 = offs[rg + 1];
+    // sizes fit in 32 bits (the host checks batch*heads*n_q and the range count)
+    const uint32_t nq = (uint32_t)a.n_q, nch = (uint32_t)a.g_nchunk;
+    const uint32_t n_items = (uint32_t)(a.batch * a.heads) * nch * nq;
+    // kPartItems consecutive items per wave: item = ((bh * nchunk) + range) *
+    // n_q + t, so a wave's items share their head and key range, and the waves
+    // working on one key range of one head are neighbours on the same XCD
+    const uint32_t first = ((uint32_t)xcd_remap(blockIdx.x, gridDim.x) * kWaves + wave) * kPartItems;
     const int sub = lane % LPK, kgrp = lane / LPK;
-    uint32_t q2[16];
-    load_q2<D>(a.q + b * a.q_sb + h * a.q_sh + (int64_t)t * a.q_sn, lane, q2);
-    float m, l, acc[8];
-    gather_online<D>(a.g_lists + row * a.topk + o0, o1 - o0, false, a.n_kv, a.k + b * a.k_sb + h * a.k_sh, a.k_sn,
-                     a.v + b * a.v_sb + h * a.v_sh, a.v_sn, q2, a.scale_log2, sc_all[wave], lane, m, l, acc);
-    const int64_t pidx = ((int64_t)bh * a.n_q + t) * a.g_nchunk + rg;
-    if (kgrp == 0) {
-        float* po = a.g_po + pidx * D + sub * 8;
-        *reinterpret_cast<float4*>(po) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        *reinterpret_cast<float4*>(po + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
-    }
-    if (lane == 0) {
-        a.g_pml[pidx * 2] = m;  // -inf for an empty range
-        a.g_pml[pidx * 2 + 1] = l;
+    int cur_rest = -1;
+    int b = 0, h = 0, bh = 0, rg = 0;
+    const uint16_t* kg = nullptr;
+    const uint16_t* vg = nullptr;
+    for (uint32_t u = 0; u < (uint32_t)kPartItems; ++u) {
+        const uint32_t item = first + u;
+        if (item >= n_items) break;  // uniform
+        const uint32_t t = item % nq;
+        const int rest = (int)(item / nq);
+        if (rest != cur_rest) {  // uniform: head and range of this item
+            cur_rest = rest;
+            rg = rest % (int)nch;
+            bh = rest / (int)nch;
+            b = bh / a.heads;
+            h = bh % a.heads;
+            kg = a.k + b * a.k_sb + h * a.k_sh;
+            vg = a.v + b * a.v_sb + h * a.v_sh;
+        }
+        const int64_t row = a.g_bh_stride == 0 ? (int64_t)t : (int64_t)bh * nq + t;
+        const int32_t* offs = a.g_offs + row * (nch + 1);
+        const int o0 = offs[rg], o1 = offs[rg + 1];
+        uint32_t q2[16];
+        load_q2<D>(a.q + b * a.q_sb + h * a.q_sh + (int64_t)t * a.q_sn, lane, q2);
+        float m, l, acc[8];
+        gather_online<D>(a.g_lists + row * a.topk + o0, o1 - o0, false, a.n_kv, kg, a.k_sn, vg, a.v_sn, q2,
+                         a.scale_log2, sc_all[wave], lane, m, l, acc);
+        const int64_t pidx = ((int64_t)bh * nq + t) * nch + rg;
+        if (kgrp == 0) {
+            float* po = a.g_po + pidx * D + sub * 8;
+            *reinterpret_cast<float4*>(po) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            *reinterpret_cast<float4*>(po + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        }
+        if (lane == 0) {
+            a.g_pml[pidx * 2] = m;  // -inf for an empty range
+            a.g_pml[pidx * 2 + 1] = l;
+        }
     }
 }
 
@@ -435,7 +452,8 @@ hipError_t launch_split(const AttnParams& a, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t parts = (int64_t)a.batch * a.heads * a.g_nchunk * a.n_q;
-    hipLaunchKernelGGL((gather_part_kernel<D>), dim3((unsigned)((parts + kWaves - 1) / kWaves)), dim3(kWaves * 64),
+    const int64_t per_wg = (int64_t)kWaves * kPartItems;
+    hipLaunchKernelGGL((gather_part_kernel<D>), dim3((unsigned)((parts + per_wg - 1) / per_wg)), dim3(kWaves * 64),
                        0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

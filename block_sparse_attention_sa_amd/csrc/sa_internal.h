@@ -213,6 +213,7 @@ inline bool gather_split_layout(int64_t batch, int64_t heads, int64_t n_q, int64
     while ((int64_t(1) << (shift + 1)) * 4 * head_dim <= (int64_t(1) << 21)) ++shift;
     const int64_t nchunk = (n_kv + (int64_t(1) << shift) - 1) >> shift;
     if (nchunk < 2 || nchunk > 256 || batch <= 0 || heads <= 0 || n_q <= 0) return false;
+    if (batch * heads * nchunk * n_q >= (int64_t(1) << 31)) return false;  // 32-bit work items
     auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
     L.shift = shift;
     L.nchunk = (int32_t)nchunk;

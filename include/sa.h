@@ -177,7 +177,8 @@ typedef struct sa_attn_args {
  * take its split form for these arguments, 0 when it has none.
  *
  * Gather mode over a long key range (n_kv above 2^21 / (4 * head_dim)
- * keys) has a split form: each key list is first partitioned by key range
+ * keys, at most 256 ranges, batch * heads * ranges * n_q below 2^31) has a
+ * split form: each key list is first partitioned by key range
  * (ranges of 2 MB of K and V per head), every range is then attended to
  * separately by workgroups that share it in one L2 cache, and the partial
  * results (running max, sum and unnormalised output per range) are merged.
