@@ -234,6 +234,12 @@ sa_status sa_attn_fwd(const sa_attn_args* a, void* stream)
                             "sa_attn_fwd");
         }
         if (!a->gather_idx) return fail(SA_ERR_INVALID_ARG, "gather_idx is NULL");
+        {
+            // gathered rows are addressed with 32-bit byte offsets from the (batch, head) base
+            const int64_t row_b = 2 * std::max(a->k_strides[2], a->v_strides[2]);
+            if ((a->n_kv + 256) * row_b > kI32Max)
+                return fail(SA_ERR_UNSUPPORTED, "n_kv times the K/V row stride must stay below 2^31 bytes");
+        }
         if (a->topk < 1 || a->topk > 8192) return fail(SA_ERR_UNSUPPORTED, "topk must be in [1, 8192]");
         if (a->gather_bh_stride < 0) return fail(SA_ERR_INVALID_ARG, "gather_bh_stride must be >= 0");
         p.gidx = a->gather_idx;

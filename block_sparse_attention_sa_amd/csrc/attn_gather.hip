@@ -83,8 +83,8 @@ __device__ __forceinline__ void load_q2(const uint16_t* qrow, int lane, uint32_t
 //           and one pair dot product with (p0, p1) adds both keys' terms.
 template <int D>
 __device__ __forceinline__ void gather_online(const int32_t* keys, int n, bool check, int n_kv,
-                                              const uint16_t* kg, int64_t k_sn, const uint16_t* vg, int64_t v_sn,
-                                              const uint32_t (&q2)[16], float c, float* sc, int lane,
+                                              const uint16_t* kg, uint32_t krow_b, const uint16_t* vg, uint32_t vrow_b,
+                                              const uint32_t (&q2)[16], float c, float* sc, uint32_t* ro, int lane,
                                               float& m, float& l, float (&acc)[8])
 {
     constexpr int LQ = D / 32, KQ = 64 / LQ;  // scores: lanes per row, rows per step
@@ -101,34 +101,31 @@ __device__ __forceinline__ void gather_online(const int32_t* keys, int n, bool c
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     for (int b0 = 0; b0 < n; b0 += kBlk) {
         const int nb = min(kBlk, n - b0);
-        int kid[2];
+        // byte offsets of the block's K rows (bit 31 set: no key; the row
+        // read is then row 0, whose score is dropped) and V rows (row 0 for
+        // no key, whose probability is 0), two entries per lane, in LDS
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             const int e = b0 + 64 * r + lane;
-            int s = e < n ? keys[e] : -1;
-            if (check && (s < 0 || s >= n_kv)) s = -1;
-            kid[r] = s;
+            const int s = e < n ? keys[e] : -1;
+            const bool ok = e < n && !(check && (s < 0 || s >= n_kv));
+            ro[64 * r + lane] = ok ? (uint32_t)s * krow_b : 0x80000000u;
+            ro[kBlk + 64 * r + lane] = ok ? (uint32_t)s * vrow_b : 0u;
         }
-        // key of block entry e; e < 64 or e >= 64 is uniform at every call
-        auto key_at = [&](int e) {
-            const int v = __shfl(e < 64 ? kid[0] : kid[1], e & 63, 64);
-            return e < nb ? v : -1;
-        };
+        wave_lds_sync();
         // ---- scores
         float bmax = -INFINITY;
 #pragma unroll 1
         for (int g = 0; g < QSTEPS; g += kQF) {
             u32x4 w[kQF][4];
-            int sk[kQF];
+            bool okk[kQF];
 #pragma unroll
             for (int i = 0; i < kQF; ++i) {
-                sk[i] = key_at((g + i) * KQ + qg);
-                const uint16_t* row = kg + (int64_t)(sk[i] >= 0 ? sk[i] : 0) * k_sn + 32 * qs;
+                const uint32_t off = ro[(g + i) * KQ + qg];
+                okk[i] = (int32_t)off >= 0;
+                const char* row = reinterpret_cast<const char*>(kg) + (uint64_t)((off & 0x7FFFFFFFu) + 64u * qs);
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    w[i][x] = u32x4{0u, 0u, 0u, 0u};
-                    if (sk[i] >= 0) w[i][x] = *reinterpret_cast<const u32x4*>(row + 8 * x);
-                }
+                for (int x = 0; x < 4; ++x) w[i][x] = *reinterpret_cast<const u32x4*>(row + 16 * x);
             }
 #pragma unroll
             for (int i = 0; i < kQF; ++i) {
@@ -143,7 +140,7 @@ __device__ __forceinline__ void gather_online(const int32_t* keys, int n, bool c
                 float d = d0 + d1;
 #pragma unroll
                 for (int off = 1; off < LQ; off <<= 1) d += __shfl_xor(d, off, 64);
-                const float sv = sk[i] >= 0 ? d * c : -INFINITY;
+                const float sv = okk[i] ? d * c : -INFINITY;
                 bmax = fmaxf(bmax, sv);
                 if (qs == 0) sc[(g + i) * KQ + qg] = sv;
             }
@@ -178,11 +175,10 @@ __device__ __forceinline__ void gather_online(const int32_t* keys, int n, bool c
 #pragma unroll
             for (int i = 0; i < kVF; ++i) {
                 const int e0 = (g + i) * KPV + 2 * vgr;
-                const int s0 = key_at(e0), s1 = key_at(e0 + 1);
-                w0[i] = u32x4{0u, 0u, 0u, 0u};
-                w1[i] = u32x4{0u, 0u, 0u, 0u};
-                if (s0 >= 0) w0[i] = *reinterpret_cast<const u32x4*>(vg + (int64_t)s0 * v_sn + sub * 8);
-                if (s1 >= 0) w1[i] = *reinterpret_cast<const u32x4*>(vg + (int64_t)s1 * v_sn + sub * 8);
+                const u32x2 vo = *reinterpret_cast<const u32x2*>(ro + kBlk + e0);
+                const char* vb = reinterpret_cast<const char*>(vg);
+                w0[i] = *reinterpret_cast<const u32x4*>(vb + (uint64_t)(vo[0] + 16u * sub));
+                w1[i] = *reinterpret_cast<const u32x4*>(vb + (uint64_t)(vo[1] + 16u * sub));
             }
 #pragma unroll
             for (int i = 0; i < kVF; ++i) {
@@ -213,6 +209,7 @@ __global__ void __launch_bounds__(kWaves * 64) attn_gather_kernel(AttnParams a)
 {
     constexpr int LPK = D / 8;
     __shared__ float sc_all[kWaves][kBlk];
+    __shared__ __attribute__((aligned(16))) uint32_t ro_all[kWaves][2 * kBlk];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t item = (int64_t)blockIdx.x * kWaves + wave;
@@ -226,8 +223,8 @@ __global__ void __launch_bounds__(kWaves * 64) attn_gather_kernel(AttnParams a)
     load_q2<D>(a.q + b * a.q_sb + h * a.q_sh + (int64_t)t * a.q_sn, lane, q2);
     float m, l, acc[8];
     gather_online<D>(a.gidx + bh * a.g_bh_stride + (int64_t)t * a.topk, a.topk, true, a.n_kv,
-                     a.k + b * a.k_sb + h * a.k_sh, a.k_sn, a.v + b * a.v_sb + h * a.v_sh, a.v_sn, q2,
-                     a.scale_log2, sc_all[wave], lane, m, l, acc);
+                     a.k + b * a.k_sb + h * a.k_sh, (uint32_t)(2 * a.k_sn), a.v + b * a.v_sb + h * a.v_sh,
+                     (uint32_t)(2 * a.v_sn), q2, a.scale_log2, sc_all[wave], ro_all[wave], lane, m, l, acc);
     if (kgrp == 0) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
         const int64_t obase = b * a.o_sb + h * a.o_sh + (int64_t)t * a.o_sn + sub * 8;
@@ -343,6 +340,7 @@ __global__ void __launch_bounds__(kWaves * 64) gather_part_kernel(AttnParams a)
 {
     constexpr int LPK = D / 8;
     __shared__ float sc_all[kWaves][kBlk];
+    __shared__ __attribute__((aligned(16))) uint32_t ro_all[kWaves][2 * kBlk];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     // sizes fit in 32 bits (the host checks batch*heads*n_q and the range count)
@@ -377,8 +375,8 @@ __global__ void __launch_bounds__(kWaves * 64) gather_part_kernel(AttnParams a)
         uint32_t q2[16];
         load_q2<D>(a.q + b * a.q_sb + h * a.q_sh + (int64_t)t * a.q_sn, lane, q2);
         float m, l, acc[8];
-        gather_online<D>(a.g_lists + row * a.topk + o0, o1 - o0, false, a.n_kv, kg, a.k_sn, vg, a.v_sn, q2,
-                         a.scale_log2, sc_all[wave], lane, m, l, acc);
+        gather_online<D>(a.g_lists + row * a.topk + o0, o1 - o0, false, a.n_kv, kg, (uint32_t)(2 * a.k_sn), vg,
+                         (uint32_t)(2 * a.v_sn), q2, a.scale_log2, sc_all[wave], ro_all[wave], lane, m, l, acc);
         const int64_t pidx = ((int64_t)bh * nq + t) * nch + rg;
         if (kgrp == 0) {
             float* po = a.g_po + pidx * D + sub * 8;

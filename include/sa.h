@@ -29,9 +29,9 @@
  *  - Positions are absolute: query row r has position q_offset + r; key row
  *    s has position s.  All sizes and positions must fit in int32 (< 2^31);
  *    where a pattern is evaluated (sa_build_block_mask, sa_attn_fwd block
- *    mode), q_offset + n_q + n_kv must stay below 2^29.  In sa_attn_fwd
- *    block mode, (n_kv + 256) times the larger K/V row stride in bytes must
- *    stay below 2^31 (key tiles are addressed with 32-bit byte offsets).
+ *    mode), q_offset + n_q + n_kv must stay below 2^29.  In sa_attn_fwd,
+ *    (n_kv + 256) times the larger K/V row stride in bytes must stay below
+ *    2^31 (key rows are addressed with 32-bit byte offsets).
  *  - bfloat16 tensors are passed as raw 16-bit storage.
  */
 #ifndef SA_H

@@ -159,6 +159,12 @@ def test_attn_offset_range_error():
         s[:] = [1 << 32, 1 << 32, 128]
     assert _lib.lib().sa_attn_fwd(ctypes.byref(a), None) == _lib.SA_ERR_UNSUPPORTED
     assert "2^31 bytes" in _err()
+    # gathered rows too
+    g = _args(mode=_lib.SA_MODE_GATHER, gather_idx=4096, topk=64, n_kv=1 << 24)
+    for s in (g.k_strides, g.v_strides):
+        s[:] = [1 << 32, 1 << 32, 128]
+    assert _lib.lib().sa_attn_fwd(ctypes.byref(g), None) == _lib.SA_ERR_UNSUPPORTED
+    assert "2^31 bytes" in _err()
 
 
 def test_gather_workspace_size_and_errors():
