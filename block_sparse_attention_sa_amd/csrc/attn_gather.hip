@@ -53,6 +53,29 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
+// Cross-lane steps on the vector unit (DPP) instead of LDS permutes:
+// quad_perm [1,0,3,2] and [2,3,0,1] exchange with lane ^ 1 and lane ^ 2;
+// row_ror 4 and 8 rotate within 16-lane rows, which for an operation that is
+// associative and commutative, applied to values already equal within each
+// quad, combines the four quads of the row in every lane.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_sum(float x)
+{
+    x += dpp<0xB1>(x);
+    return x + dpp<0x4E>(x);
+}
+// sum over the 16-lane row, in every lane of it
+__device__ __forceinline__ float row_sum(float x)
+{
+    x = quad_sum(x);
+    x += dpp<0x124>(x);
+    return x + dpp<0x128>(x);
+}
+
 // a.x * b.x + a.y * b.y + c on bfloat16 pairs (v_dot2c_f32_bf16)
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
 {
@@ -138,14 +161,25 @@ __device__ __forceinline__ void gather_online(const int32_t* keys, int n, bool c
                     d1 = dot2(w[i][x][3], q2[4 * x + 3], d1);
                 }
                 float d = d0 + d1;
+                if (LQ == 4) {
+                    d = quad_sum(d);
+                } else {
 #pragma unroll
-                for (int off = 1; off < LQ; off <<= 1) d += __shfl_xor(d, off, 64);
+                    for (int off = 1; off < LQ; off <<= 1) d += __shfl_xor(d, off, 64);
+                }
                 const float sv = okk[i] ? d * c : -INFINITY;
                 bmax = fmaxf(bmax, sv);
                 if (qs == 0) sc[(g + i) * KQ + qg] = sv;
             }
         }
-        for (int off = LQ; off < 64; off <<= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, off, 64));
+        if (LQ == 4) {
+            // equal within quads already: fold the row's quads, then the rows
+            bmax = fmaxf(bmax, dpp<0x124>(bmax));
+            bmax = fmaxf(bmax, dpp<0x128>(bmax));
+            for (int off = 16; off < 64; off <<= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, off, 64));
+        } else {
+            for (int off = LQ; off < 64; off <<= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, off, 64));
+        }
         const float m_new = fmaxf(m, bmax);
         if (m_new != -INFINITY && m_new > m) {
             const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
@@ -165,7 +199,8 @@ __device__ __forceinline__ void gather_online(const int32_t* keys, int n, bool c
             sc[e] = pv;
             ps += pv;
         }
-        for (int off = 32; off > 0; off >>= 1) ps += __shfl_xor(ps, off, 64);
+        ps = row_sum(ps);
+        for (int off = 16; off < 64; off <<= 1) ps += __shfl_xor(ps, off, 64);
         l += ps;
         wave_lds_sync();
         // ---- acc += p v, two keys per lane group and step
