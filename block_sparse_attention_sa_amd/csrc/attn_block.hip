@@ -140,8 +140,11 @@ attn_block_kernel(AttnParams a)
     const int hh = lane >> 5;  // half-wave
     const int l32 = lane & 31;
 
+    // query blocks of a head run from the last to the first: causal rows
+    // near the start see the fewest key tiles, so the short workgroups come
+    // last and fill the gaps at the end of the launch
     const int item = xcd_remap(blockIdx.x, gridDim.x);
-    const int qb = item % a.nqb;
+    const int qb = a.nqb - 1 - item % a.nqb;
     const int bh = item / a.nqb;
     const int b = bh / a.heads, h = bh % a.heads;
 
