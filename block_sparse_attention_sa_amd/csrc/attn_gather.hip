@@ -136,10 +136,11 @@ __device__ __forceinline__ void gather_online(const int32_t* keys, int n, bool c
             ro[kBlk + 64 * r + lane] = ok ? (uint32_t)s * vrow_b : 0u;
         }
         wave_lds_sync();
-        // ---- scores
+        // ---- scores (a short last block runs only the batches that hold keys)
+        const int qlim = (nb + KQ - 1) / KQ;
         float bmax = -INFINITY;
 #pragma unroll 1
-        for (int g = 0; g < QSTEPS; g += kQF) {
+        for (int g = 0; g < qlim; g += kQF) {
             u32x4 w[kQF][4];
             bool okk[kQF];
 #pragma unroll
@@ -203,9 +204,11 @@ __device__ __forceinline__ void gather_online(const int32_t* keys, int n, bool c
         for (int off = 16; off < 64; off <<= 1) ps += __shfl_xor(ps, off, 64);
         l += ps;
         wave_lds_sync();
-        // ---- acc += p v, two keys per lane group and step
+        // ---- acc += p v, two keys per lane group and step (probabilities past
+        // nb are 0 and their offsets point at row 0)
+        const int vlim = (nb + KPV - 1) / KPV;
 #pragma unroll 1
-        for (int g = 0; g < VSTEPS; g += kVF) {
+        for (int g = 0; g < vlim; g += kVF) {
             u32x4 w0[kVF], w1[kVF];
 #pragma unroll
             for (int i = 0; i < kVF; ++i) {
