@@ -42,7 +42,7 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg)
 constexpr int kBlk = 128;  // keys per block of the online softmax
 constexpr int kQF = 4;     // score steps whose row loads are issued together
 constexpr int kVF = 4;     // value steps whose row loads are issued together
-constexpr int kPartItems = 4;  // (head, range, query) items per wave in the split form
+constexpr int kPartItems = 1;  // (head, range, query) items per wave in the split form
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
