@@ -446,13 +446,28 @@ __global__ void __launch_bounds__(kWaves * 64) gather_merge_kernel(AttnParams a)
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] = 0.f;
     if (m != -INFINITY) {
-        for (int r = 0; r < a.g_nchunk; ++r) {
-            const float mr = pml[2 * r];
-            if (mr == -INFINITY) continue;
-            const float f = __builtin_amdgcn_exp2f(mr - m);
-            l = __builtin_fmaf(pml[2 * r + 1], f, l);
+        // eight ranges at a time: their partial rows are all requested before
+        // any is used
+        constexpr int RB = 8;
+        for (int r0 = 0; r0 < a.g_nchunk; r0 += RB) {
+            float mr[RB], lr[RB], pv[RB][PER];
 #pragma unroll
-            for (int i = 0; i < PER; ++i) acc[i] = __builtin_fmaf(po[r * D + lane * PER + i], f, acc[i]);
+            for (int j = 0; j < RB; ++j) {
+                const int r = r0 + j;
+                const bool in = r < a.g_nchunk;
+                mr[j] = in ? pml[2 * r] : -INFINITY;
+                lr[j] = in ? pml[2 * r + 1] : 0.f;
+#pragma unroll
+                for (int i = 0; i < PER; ++i) pv[j][i] = in ? po[r * D + lane * PER + i] : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < RB; ++j) {
+                // an empty range has max -inf: factor 0
+                const float f = mr[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mr[j] - m);
+                l = __builtin_fmaf(lr[j], f, l);
+#pragma unroll
+                for (int i = 0; i < PER; ++i) acc[i] = __builtin_fmaf(pv[j][i], f, acc[i]);
+            }
         }
     }
     const float inv = l > 0.f ? 1.f / l : 0.f;
