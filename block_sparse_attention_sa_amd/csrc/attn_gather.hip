@@ -315,9 +315,19 @@ __global__ void __launch_bounds__(kWaves * 64) gather_partition_kernel(AttnParam
 
     for (int i = lane; i < 256; i += 64) cnt[i] = 0;
     wave_lds_sync();
-    for (int e = lane; e < a.topk; e += 64) {
-        const int s = src[e];
-        if (s >= 0 && s < a.n_kv) atomicAdd(&cnt[s >> a.g_shift], 1);
+    // list entries are read eight per lane at a time, so that a row costs a
+    // few memory latencies instead of one per 64 entries
+    constexpr int EB = 8;
+    for (int e0 = 0; e0 < a.topk; e0 += 64 * EB) {
+        int sv[EB];
+#pragma unroll
+        for (int j = 0; j < EB; ++j) {
+            const int e = e0 + 64 * j + lane;
+            sv[j] = e < a.topk ? src[e] : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < EB; ++j)
+            if (sv[j] >= 0 && sv[j] < a.n_kv) atomicAdd(&cnt[sv[j] >> a.g_shift], 1);
     }
     wave_lds_sync();
     // exclusive scan of the range counts (lane owns ranges 4*lane .. 4*lane+3)
@@ -350,9 +360,19 @@ __global__ void __launch_bounds__(kWaves * 64) gather_partition_kernel(AttnParam
     // free slot plus the number of lower lanes with the same range (found
     // with one ballot per bit of the range index)
     const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    int sv[EB];
     for (int e0 = 0; e0 < a.topk; e0 += 64) {
-        const int e = e0 + lane;
-        const int s = e < a.topk ? src[e] : -1;
+        const int jb = (e0 / 64) % EB;
+        if (jb == 0) {
+#pragma unroll
+            for (int j = 0; j < EB; ++j) {
+                const int e = e0 + 64 * j + lane;
+                sv[j] = e < a.topk ? src[e] : -1;
+            }
+        }
+        int s = sv[0];
+#pragma unroll
+        for (int j = 1; j < EB; ++j) s = jb == j ? sv[j] : s;
         const bool ok = s >= 0 && s < a.n_kv;
         const int ch = ok ? (s >> a.g_shift) : 0;
         uint64_t m = __builtin_amdgcn_ballot_w64(ok);
