@@ -176,9 +176,9 @@ sa_status sa_attn_fwd(const sa_attn_args* a, void* stream)
         if (a->batch == 0 || a->heads == 0 || a->n_q == 0) return ok();
         if (!a->q || !a->o || (a->n_kv > 0 && (!a->k || !a->v)))
             return fail(SA_ERR_INVALID_ARG, "q/k/v/o is NULL");
-        if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o) ||
-            (a->lse && ((uintptr_t)a->lse & 3u)))
+        if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
             return fail(SA_ERR_INVALID_ARG, "q/k/v/o must be 16-byte aligned");
+        if (a->lse && ((uintptr_t)a->lse & 3u)) return fail(SA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
         for (int i = 0; i < 3; ++i) {
             if (a->q_strides[i] < 0 || a->k_strides[i] < 0 || a->v_strides[i] < 0 || a->o_strides[i] < 0)
                 return fail(SA_ERR_INVALID_ARG, "strides must be >= 0");

@@ -113,6 +113,7 @@ def _args(**kw):
     (dict(mode=3), _lib.SA_ERR_INVALID_ARG, "mode"),
     (dict(q=0), _lib.SA_ERR_INVALID_ARG, "NULL"),
     (dict(k=4100), _lib.SA_ERR_INVALID_ARG, "aligned"),
+    (dict(lse=4098), _lib.SA_ERR_INVALID_ARG, "lse"),
     (dict(block_q=32), _lib.SA_ERR_UNSUPPORTED, "block"),
     (dict(kv_count=0), _lib.SA_ERR_INVALID_ARG, "block lists"),
     (dict(mode=_lib.SA_MODE_GATHER, gather_idx=0), _lib.SA_ERR_INVALID_ARG, "gather_idx"),
