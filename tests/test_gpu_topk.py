@@ -225,3 +225,29 @@ def test_gather_split_form(d, per_head):
     # repeated call: same bits (the partition keeps list order)
     o_s2, l_s2 = sa.attn_fwd(qd, kd, vd, gather_idx=gi)
     assert torch.equal(o_s, o_s2) and torch.equal(l_s, l_s2)
+
+
+@pytest.mark.parametrize("split", [False, True])
+def test_gather_list_lengths_at_batch_edges(split):
+    """Lists whose valid keys end at, just before and just after each score
+    batch (16 keys at d=128) and value batch (8 keys) edge and each 128-key
+    block edge, so that every trimmed last block length is exercised; in the
+    split form all keys of a list sit in one key range."""
+    rng = np.random.default_rng(77 + split)
+    d, B, H, k = 128, 1, 2, 300
+    n_kv = (2 << 21) // (4 * d) + 5 if split else 4096   # two ranges (split) or one short row
+    lengths = [1, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 130, 191, 192, 193, 255,
+               256, 257, 300]
+    n_q = len(lengths)
+    q, kk, v = _rbf(rng, B, H, n_q, d), _rbf(rng, B, H, n_kv, d), _rbf(rng, B, H, n_kv, d)
+    lists = np.full((n_q, k), -1, np.int32)
+    for r, n in enumerate(lengths):
+        lists[r, :n] = rng.integers(0, min(n_kv, 4000), size=n)  # first range only
+    gi = torch.from_numpy(lists).cuda()
+    if split:
+        assert sa.attn_workspace_bytes(B, H, n_q, n_kv, d, k) > 0
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(kk), to_dev_bf16(v)
+    print(f"gather list lengths split={split}", flush=True)
+    o, l = sa.attn_fwd(qd, kd, vd, gather_idx=gi, split=split)
+    o_ref, lse_ref = oracle.attn_gather_rows(q, kk, v, lists)
+    check_o_lse(o.cpu().numpy().reshape(-1, d), l.cpu().numpy().reshape(-1), o_ref, lse_ref, ctx=f"split={split}")
