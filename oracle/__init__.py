@@ -16,7 +16,8 @@ Parity status of each function (pins live in ``tests/test_oracle_pins.py``):
   counts, the area-attention pair count, dense numpy reshape-sum brute force.
 * ``attn_rows``         pinned: dense masked attention brute force (numpy),
   torch's fp64 scaled_dot_product_attention with a boolean mask and with
-  ``is_causal``, Q = 0 closed form, single-key closed form, weights sum to 1.
+  ``is_causal`` (O), torch.logsumexp of the masked scores (LSE), Q = 0 closed
+  form, single-key closed form, weights sum to 1.
 * ``attn_gather_rows``  pinned: equals ``attn_rows`` when the list is the
   allowed set; brute force on tiny inputs.
 * ``indexer_scores``    pinned: exact rational arithmetic with per-step

@@ -254,6 +254,11 @@ def test_attention_vs_torch_sdpa_boolean_mask():
     tq, tk, tv = (torch.from_numpy(_bf16_f64(inp[t])) for t in ("q", "k", "v"))
     ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask)
     np.testing.assert_allclose(o.reshape(ref.shape), ref.numpy(), rtol=0, atol=1e-12)
+    # LSE through torch's own reduction: logsumexp of the scaled scores, the
+    # disallowed ones at -inf (every row of this pattern has an allowed key)
+    sc = torch.matmul(tq, tk.transpose(-1, -2)) / np.sqrt(tq.shape[-1])
+    ref_lse = torch.logsumexp(sc.masked_fill(~mask, float("-inf")), dim=-1)
+    np.testing.assert_allclose(lse.reshape(ref_lse.shape), ref_lse.numpy(), rtol=0, atol=1e-12)
 
 
 def test_dense_window_reduces_to_causal_attention():
