@@ -9,15 +9,20 @@
 // Each query has a different key set, so there is no K/V tile shared by
 // several queries and no matrix product to put on MFMA: the work is two
 // gathered matrix-vector products, about one flop per byte moved, bound by
-// the latency and bandwidth of the row gathers.  One wave works on one
-// query's list in blocks of 128 keys with an online softmax:
-//   * the block's key indices are read once (two per lane) and handed to the
-//     lane groups with a cross-lane shuffle;
-//   * D/8 lanes share one K or V row (16 contiguous bytes each, one
-//     coalesced row read), and eight row loads per lane are issued before
-//     any is used, so a block costs a few memory round trips, not one per key;
-//   * partial dots are reduced across the lanes of a row; scores and then
-//     probabilities sit in 128 floats of LDS per wave.
+// the latency of the row gathers and the vector work per key.  One wave works
+// on one query's list (or, in the split form, on the part of it that falls in
+// one key range) in blocks of 128 keys with an online softmax:
+//   * the block's key indices are read once (two per lane) and turned into the
+//     byte offsets of their K and V rows, kept in LDS (a key out of range reads
+//     row 0 with its score forced to -inf);
+//   * scores: D/32 lanes per K row, 64 contiguous bytes each, pair dot
+//     products against the query's bfloat16 pairs, summed over the row's
+//     lanes with DPP moves; four steps of row loads are issued before any is
+//     used, so a block costs a few memory round trips, not one per key;
+//   * values: D/8 lanes per V row, 16 bytes each; a lane group takes two keys
+//     per step and adds both with one pair dot product per column pair;
+//   * scores and then probabilities sit in 128 floats of LDS per wave; a
+//     short last block runs only the load batches that hold keys.
 #include "sa_internal.h"
 
 namespace sa {
