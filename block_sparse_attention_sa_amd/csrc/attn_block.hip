@@ -26,9 +26,13 @@
 //     row max / row sum are in-lane reductions plus one v_permlane32_swap.
 //   * P^T (bf16) stays in registers as the B operand of O^T += V^T P^T; V^T
 //     is read with ds_read_b64_tr_b16 (transposing 16-bit reads).
-//   * exp2 with the scale folded into one FMA; the running max is raised only
-//     when a row's tile max exceeds it by more than 8 (log2 units), so every
-//     exponent stays <= 2^8 and most accumulator rescales are skipped.
+//   * exp2 with the scale folded into one FMA, against a per-row reference
+//     m that need not be the running max: any m gives the same softmax, as
+//     long as no exponent overflows.  The first sub-tile a row sees sets m to
+//     its max; later sub-tiles skip the row max unless some lane's sum of P
+//     over the sub-tile exceeds 2^16, and then the exact max is taken, the
+//     accumulator rescaled and P recomputed.  m is an actual score of the
+//     row, so the largest term is at least 1 and nothing important underflows.
 //   * Wave priorities (s_setprio): highest while a wave issues matrix
 //     instructions, middle during its softmax, lowest otherwise, so that the
 //     two waves sharing a SIMD tend to alternate matrix and vector phases.
@@ -49,7 +53,7 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr float kLazyLog2 = 8.0f;  // rescale threshold in log2 units
+constexpr float kSumLimit = 65536.0f;  // largest per-lane sub-tile sum taken without a row max
 
 template <int D>
 __device__ __forceinline__ int kswz(int r)
@@ -243,7 +247,7 @@ attn_block_kernel(AttnParams a)
         l_run[nb] = 0.f;
     }
     const float c = a.scale_log2;
-    const float thr = kLazyLog2 / c;
+    bool have_ref = false;  // every row of the wave has a finite reference m
 
     // V^T transposed-read lane geometry
     const int tg = lane >> 4, tj = lane & 15;
@@ -381,37 +385,14 @@ attn_block_kernel(AttnParams a)
                     }
         }
 
-        // ---- online softmax, one query per lane and column block; P packed to bf16
+        // ---- online softmax, one query per lane and column block; P packed to bf16.
+        // p = exp2(s*c - m*c) against the row's reference m.  While every row of
+        // the wave has a reference and no lane's sum over the sub-tile exceeds
+        // kSumLimit, the sub-tile needs no row max; otherwise the exact max is
+        // taken, the accumulator rescaled to it and P recomputed.
         bf16x8 pk[NB][NSB][2];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            // row max as a tree (exact in any order): short dependency chains
-            float mq[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) mq[x] = fmaxf(s[nb][0][4 * x], s[nb][0][4 * x + 1]);
-#pragma unroll
-            for (int sb = 0; sb < NSB; ++sb)
-#pragma unroll
-                for (int i = (sb == 0 ? 2 : 0); i < 4; ++i)
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) mq[x] = fmaxf(mq[x], s[nb][sb][4 * x + i]);
-            float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
-            mx = fmaxf(mx, other_half(mx));
-            const float m_new = fmaxf(m_run[nb], mx);
-            if (__any(m_new > m_run[nb] + thr)) {
-                const float alpha =
-                    m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_run[nb] - m_new) * c);
-                l_run[nb] *= alpha;
-                // one 16-register accumulator block at a time keeps the
-                // temporaries of this rarely taken path small
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) o[nb][db][i] *= alpha;
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                m_run[nb] = m_new;
-            }
+        float lt[NB];
+        auto exps = [&](int nb) {
             const float mc = m_run[nb] == -INFINITY ? 0.f : m_run[nb] * c;
             float ls[4] = {0.f, 0.f, 0.f, 0.f};  // four partial row sums
 #pragma unroll
@@ -424,8 +405,56 @@ attn_block_kernel(AttnParams a)
                         ls[u & 3] += p;
                         pk[nb][sb][cb][u] = (__bf16)p;
                     }
-            l_run[nb] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+            lt[nb] = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        };
+        bool exact = !have_ref;
+        if (!exact) {
+            bool over = false;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                exps(nb);
+                over |= lt[nb] > kSumLimit;
+            }
+            exact = __builtin_amdgcn_ballot_w64(over) != 0;
         }
+        if (exact) {
+            bool unset = false;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                // row max as a tree (exact in any order): short dependency chains
+                float mq[4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) mq[x] = fmaxf(s[nb][0][4 * x], s[nb][0][4 * x + 1]);
+#pragma unroll
+                for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+                    for (int i = (sb == 0 ? 2 : 0); i < 4; ++i)
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) mq[x] = fmaxf(mq[x], s[nb][sb][4 * x + i]);
+                float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+                mx = fmaxf(mx, other_half(mx));
+                const float m_new = fmaxf(m_run[nb], mx);
+                if (__any(m_new > m_run[nb])) {
+                    const float alpha =
+                        m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_run[nb] - m_new) * c);
+                    l_run[nb] *= alpha;
+                    // one 16-register accumulator block at a time keeps the
+                    // temporaries of this rarely taken path small
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) o[nb][db][i] *= alpha;
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    m_run[nb] = m_new;
+                }
+                exps(nb);
+                unset |= m_run[nb] == -INFINITY;
+            }
+            have_ref = __builtin_amdgcn_ballot_w64(unset) == 0;
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) l_run[nb] += lt[nb];
 
         // ---- O^T += V^T P^T  (V^T operands fetched two steps ahead)
         __builtin_amdgcn_s_setprio(2);

@@ -41,6 +41,35 @@ def test_small_ragged_window_sinks(d, bq, bk, of):
                 bf16_out=(of == "bf16"), ctx=f"d={d} bq={bq} bk={bk} {of}")
 
 
+
+@pytest.mark.parametrize("profile", ["rising", "falling", "spikes", "large_q"])
+@pytest.mark.parametrize("d,bq,bk", [(128, 128, 128), (128, 64, 64), (64, 128, 64)])
+def test_score_ranges_across_tiles(profile, d, bq, bk):
+    """Score scales that change from key tile to key tile: the row's softmax
+    reference (set on the first sub-tile it sees) must be raised and the
+    accumulator rescaled whenever later keys dominate ("rising", "spikes",
+    "large_q"), and keys far below it must still be summed correctly ("falling")."""
+    rng = np.random.default_rng(1000 * ["rising", "falling", "spikes", "large_q"].index(profile) + d + bq + 3 * bk)
+    n_q, n_kv = 333, 301
+    f = lambda *s: rng.standard_normal(s, dtype=np.float32)
+    q, k, v = f(1, 2, n_q, d), f(1, 2, n_kv, d), f(1, 2, n_kv, d)
+    j = np.arange(n_kv, dtype=np.float32)
+    if profile == "rising":
+        k *= (0.2 + j / 12.0)[None, None, :, None]
+    elif profile == "falling":
+        k *= (0.2 + (n_kv - j) / 12.0)[None, None, :, None]
+    elif profile == "spikes":
+        k[:, :, ::37] *= 25.0
+    else:
+        q *= 30.0
+    q, k, v = (W.f32_to_bf16_bits(x) for x in (q, k, v))
+    pat = dict(causal=1, window_left=200, window_right=0, sinks=2, q_offset=20)
+    print(f"attn score ranges {profile} d={d} bq={bq} bk={bk}", flush=True)
+    o, lse = _run(pat, q, k, v, bq, bk)
+    o_ref, lse_ref = oracle.attn_rows(pat, q, k, v)
+    check_o_lse(o.cpu().numpy().reshape(-1, d), lse.cpu().numpy().reshape(-1), o_ref, lse_ref,
+                ctx=f"{profile} d={d} bq={bq} bk={bk}")
+
 @pytest.mark.parametrize("seed", range(16))
 def test_random_patterns(seed):
     rng = np.random.default_rng(900 + seed)
