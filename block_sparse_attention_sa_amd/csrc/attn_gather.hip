@@ -254,7 +254,7 @@ __global__ void __launch_bounds__(kWaves * 64) attn_gather_kernel(AttnParams a)
     __shared__ float sc_all[kWaves][kBlk];
     __shared__ __attribute__((aligned(16))) uint32_t ro_all[kWaves][2 * kBlk];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int64_t item = (int64_t)blockIdx.x * kWaves + wave;
     if (item >= (int64_t)a.batch * a.heads * a.n_q) return;
     // head-major order: item = bh * n_q + t
@@ -306,7 +306,7 @@ __global__ void __launch_bounds__(kWaves * 64) gather_partition_kernel(AttnParam
 {
     __shared__ int32_t cnt_all[kWaves][256];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int64_t rows = a.g_bh_stride == 0 ? (int64_t)a.n_q : (int64_t)a.batch * a.heads * a.n_q;
     const int64_t row = (int64_t)blockIdx.x * kWaves + wave;
     if (row >= rows) return;  // wave-level work only: no workgroup barrier below
@@ -405,7 +405,8 @@ __global__ void __launch_bounds__(kWaves * 64) gather_part_kernel(AttnParams a)
     __shared__ float sc_all[kWaves][kBlk];
     __shared__ __attribute__((aligned(16))) uint32_t ro_all[kWaves][2 * kBlk];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // uniform over the wave: the item decode and addressing below run on the scalar unit
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     // sizes fit in 32 bits (the host checks batch*heads*n_q and the range count)
     const uint32_t nq = (uint32_t)a.n_q, nch = (uint32_t)a.g_nchunk;
     const uint32_t n_items = (uint32_t)(a.batch * a.heads) * nch * nq;
@@ -458,7 +459,7 @@ __global__ void __launch_bounds__(kWaves * 64) gather_merge_kernel(AttnParams a)
 {
     constexpr int PER = D / 64;  // output columns per lane
     const int lane = threadIdx.x & 63;
-    const int64_t item = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int64_t item = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     if (item >= (int64_t)a.batch * a.heads * a.n_q) return;
     const int t = (int)(item % a.n_q);
     const int bh = (int)(item / a.n_q);
