@@ -466,34 +466,43 @@ __global__ void __launch_bounds__(kWaves * 64) gather_merge_kernel(AttnParams a)
     const int b = bh / a.heads, h = bh % a.heads;
     const float* pml = a.g_pml + item * a.g_nchunk * 2;
     const float* po = a.g_po + item * a.g_nchunk * D;
-    float m = -INFINITY;
-    for (int r = 0; r < a.g_nchunk; ++r) m = fmaxf(m, pml[2 * r]);
-    float l = 0.f, acc[PER];
+    // one online pass over the ranges, sixteen at a time: a batch's partial
+    // rows, maxima and sums are all requested before any is used, then the
+    // running result is rescaled to the batch's max and the batch added
+    constexpr int RB = 16;
+    float m = -INFINITY, l = 0.f, acc[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-    if (m != -INFINITY) {
-        // eight ranges at a time: their partial rows are all requested before
-        // any is used
-        constexpr int RB = 8;
-        for (int r0 = 0; r0 < a.g_nchunk; r0 += RB) {
-            float mr[RB], lr[RB], pv[RB][PER];
+    for (int r0 = 0; r0 < a.g_nchunk; r0 += RB) {
+        float mr[RB], lr[RB], pv[RB][PER];
 #pragma unroll
-            for (int j = 0; j < RB; ++j) {
-                const int r = r0 + j;
-                const bool in = r < a.g_nchunk;
-                mr[j] = in ? pml[2 * r] : -INFINITY;
-                lr[j] = in ? pml[2 * r + 1] : 0.f;
+        for (int j = 0; j < RB; ++j) {
+            const int r = r0 + j;
+            const bool in = r < a.g_nchunk;
+            mr[j] = in ? pml[2 * r] : -INFINITY;
+            lr[j] = in ? pml[2 * r + 1] : 0.f;
 #pragma unroll
-                for (int i = 0; i < PER; ++i) pv[j][i] = in ? po[r * D + lane * PER + i] : 0.f;
-            }
+            for (int i = 0; i < PER; ++i) pv[j][i] = in ? po[r * D + lane * PER + i] : 0.f;
+        }
+        float bm = mr[0];
 #pragma unroll
-            for (int j = 0; j < RB; ++j) {
-                // an empty range has max -inf: factor 0
-                const float f = mr[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mr[j] - m);
-                l = __builtin_fmaf(lr[j], f, l);
+        for (int j = 1; j < RB; ++j) bm = fmaxf(bm, mr[j]);
+        if (bm == -INFINITY) continue;  // every range of the batch is empty
+        if (bm > m) {
+            // m == -inf: nothing accumulated yet, factor 0
+            const float g = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - bm);
+            l *= g;
 #pragma unroll
-                for (int i = 0; i < PER; ++i) acc[i] = __builtin_fmaf(pv[j][i], f, acc[i]);
-            }
+            for (int i = 0; i < PER; ++i) acc[i] *= g;
+            m = bm;
+        }
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+            // an empty range has max -inf: factor 0
+            const float f = mr[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mr[j] - m);
+            l = __builtin_fmaf(lr[j], f, l);
+#pragma unroll
+            for (int i = 0; i < PER; ++i) acc[i] = __builtin_fmaf(pv[j][i], f, acc[i]);
         }
     }
     const float inv = l > 0.f ? 1.f / l : 0.f;

@@ -227,6 +227,29 @@ def test_gather_split_form(d, per_head):
     assert torch.equal(o_s, o_s2) and torch.equal(l_s, l_s2)
 
 
+
+def test_gather_split_many_ranges():
+    """More key ranges than the merge takes in one batch (41 ranges of 4,096
+    keys at d = 128): rows whose maxima rise from batch to batch, a row with
+    no key in the first batch, a row whose keys all sit in the last range and
+    an empty row."""
+    rng = np.random.default_rng(4242)
+    B, H, n_q, k, d = 1, 2, 24, 400, 128
+    n_kv = 40 * 4096 + 77
+    q, kk, v = _rbf(rng, B, H, n_q, d), _rbf(rng, B, H, n_kv, d), _rbf(rng, B, H, n_kv, d)
+    lists = rng.integers(0, n_kv, size=(n_q, k)).astype(np.int32)
+    lists[1] = rng.integers(20 * 4096, n_kv, size=k)        # nothing in the first sixteen ranges
+    lists[2] = rng.integers(40 * 4096, n_kv, size=k)        # the ragged last range only
+    lists[3] = -1                                            # no key
+    lists[4, : k // 2] = -1                                  # half padding
+    assert sa.attn_workspace_bytes(B, H, n_q, n_kv, d, k) > 0
+    gi = torch.from_numpy(lists).cuda()
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(kk), to_dev_bf16(v)
+    print(f"split gather many ranges n_kv={n_kv}", flush=True)
+    o_s, l_s = sa.attn_fwd(qd, kd, vd, gather_idx=gi)
+    o_ref, lse_ref = oracle.attn_gather_rows(q, kk, v, lists)
+    check_o_lse(o_s.cpu().numpy().reshape(-1, d), l_s.cpu().numpy().reshape(-1), o_ref, lse_ref, ctx="many ranges")
+
 @pytest.mark.parametrize("split", [False, True])
 def test_gather_list_lengths_at_batch_edges(split):
     """Lists whose valid keys end at, just before and just after each score
