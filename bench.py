@@ -77,6 +77,7 @@ def main() -> int:
     ap.add_argument("--o-dtype", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dsa", action="store_true")
+    ap.add_argument("--no-strided", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="the CPU oracle repeats whole passes over the workload until this much time has passed")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -207,12 +208,58 @@ def main() -> int:
     if not args.no_dsa:
         result["dsa_prefill"] = _bench_dsa(sa, W, np, torch, dev, dev_bf16)
 
+    if not args.no_strided:
+        result["strided"] = _bench_strided(sa, W, np, torch, dev, dev_bf16)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = _cpu_baseline(cfg, inp, args.cpu_seconds, np)
 
     print(json.dumps(result), flush=True)
     return 0
 
+
+def _bench_strided(sa, W, np, torch, dev, dev_bf16, reps=10):
+    """The strided workload both ways: block lists of the whole pattern (every causal tile is
+    live, since the strided term touches each one), and the local band plus residue views."""
+    cfg = W.attn_config(3)
+    print("bench: generating the strided workload's inputs", file=sys.stderr, flush=True)
+    inp = W.attn_inputs(cfg)
+    q, k, v = (dev_bf16(inp[t]) for t in ("q", "k", "v"))
+    pat = cfg.pattern.as_dict()
+    stream = torch.cuda.current_stream(dev)
+    bl = sa.build_block_mask(pat, cfg.N, cfg.N, cfg.block, cfg.block, device=dev)
+    plan = sa.plan_strided(pat, cfg.N)
+    shape = (cfg.B, cfg.H, cfg.N, cfg.d)
+    o = torch.empty(shape, dtype=torch.float32, device=dev)
+    lse = torch.empty(shape[:3], dtype=torch.float32, device=dev)
+    o2 = torch.empty(shape, dtype=torch.float32, device=dev)
+    lse2 = torch.empty((cfg.B, cfg.H, plan.stride, cfg.N // plan.stride - 2), dtype=torch.float32, device=dev)
+    ways = {
+        "blocks": lambda: sa.attn_fwd(q, k, v, bl, out=o, lse=lse),
+        "split": lambda: sa.attn_fwd_strided(q, k, v, plan, out=o, lse=lse, o2=o2, lse2=lse2),
+    }
+    t = {}
+    for name, fn in ways.items():
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        t[name] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e-3
+    pairs = int(bl.live_pairs.item()) * cfg.B * cfg.H
+    flop = 4.0 * cfg.d * pairs
+    return {
+        "workload": "causal strided, stride 128 + local band of 128, B=1 H=16 N=16384 d=64",
+        "live_pairs": pairs,
+        "blocks_us": round(t["blocks"] * 1e6, 1),
+        "blocks_tflops_over_live_pairs": round(flop / t["blocks"] / 1e12, 2),
+        "split_us": round(t["split"] * 1e6, 1),
+        "split_tflops_over_live_pairs": round(flop / t["split"] / 1e12, 2),
+        "split_note": "band through block lists + one causal 128x128 tile per (head, residue) view + LSE merge",
+    }
 
 def _bench_dsa(sa, W, np, torch, dev, dev_bf16, reps=5):
     tc = W.topk_config(5)

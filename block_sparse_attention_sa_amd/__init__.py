@@ -202,6 +202,120 @@ def attn_fwd(q, k, v, blocks: Optional[BlockLists] = None, gather_idx=None, *,
     return out, lse
 
 
+
+def merge_partial(out, lse, o2, lse2, group: int = 1, q_first: int = 0, n2: Optional[int] = None):
+    """Fold a second partial result (``o2``, ``lse2``) into (``out``, ``lse``) in place
+    (``sa_merge_partial``): out/o2 float32 [B, H, n, d] views, lse float32 [B, H, n]
+    contiguous; rows q = q_first + i*group + r (i < n2) take the second part, whose LSE
+    sits at lse2[b, h, r, i]."""
+    torch = _torch()
+    for t in (out, lse, o2, lse2):
+        if t.dtype != torch.float32 or not t.is_cuda:
+            raise ValueError("merge_partial takes float32 CUDA tensors")
+    if not lse.is_contiguous() or not lse2.is_contiguous():
+        raise ValueError("lse and lse2 must be contiguous")
+    B, H, n, d = out.shape
+    if tuple(o2.shape) != (B, H, n, d) or tuple(lse.shape) != (B, H, n):
+        raise ValueError("shape mismatch")
+    if n2 is None:
+        n2 = -(-(n - q_first) // group)
+    if lse2.numel() != B * H * group * n2:
+        raise ValueError("lse2 must hold batch * heads * group * n2 values")
+    os3 = (ctypes.c_int64 * 3)(*_strides3(out))
+    o2s = (ctypes.c_int64 * 3)(*_strides3(o2))
+    _lib.check(_lib.lib().sa_merge_partial(out.data_ptr(), lse.data_ptr(), o2.data_ptr(), lse2.data_ptr(),
+                                           B, H, n, d, os3, o2s, group, q_first, n2, _stream_ptr(out.device)))
+
+
+def strided_stride(pattern, n_q: int, n_kv: int) -> int:
+    """The stride S when ``pattern`` is the strided template that ``attn_fwd_strided`` computes
+    as disjoint parts (causal; local band q - kv <= S - 1; strided keys with
+    (q - kv) % S == S - 1; no other term; q_offset 0; n_q == n_kv a multiple of S with at least
+    three groups of S rows), else 0."""
+    g = lambda key, dflt: int(_get(pattern, key, dflt) or 0)
+    S = g("stride", 0)
+    if S <= 0 or g("stride_phase", 0) != S - 1 or not g("causal", 0):
+        return 0
+    if g("window_left", -1) != S - 1 or g("window_right", 0) != 0:
+        return 0
+    if g("sinks", 0) or g("global_tokens", 0) or g("unit", 0) or g("n_rand", 0) or g("q_offset", 0):
+        return 0
+    if n_q != n_kv or n_q % S or n_q // S < 3:
+        return 0
+    return S
+
+
+@dataclasses.dataclass
+class StridedPlan:
+    """Block lists of the parts of a strided pattern (``plan_strided``)."""
+
+    stride: int
+    n: int
+    band: BlockLists
+    strided: BlockLists
+    last: BlockLists
+
+
+def plan_strided(pattern, n: int, block: int = 128, device="cuda") -> StridedPlan:
+    """Block lists for ``attn_fwd_strided``: the local band on the natural layout
+    (block x block tiles); plain causal lists shared by every (head, key residue) view;
+    and one row against every key of its view for the last query row."""
+    S = strided_stride(pattern, n, n)
+    if not S:
+        raise ValueError("not the strided template that splits into band + residue views")
+    G = n // S
+    band = build_block_mask(dict(causal=1, window_left=S - 1, window_right=0), n, n, block, block, device)
+    bs = 128 if G - 2 > 64 else 64
+    # a local term whose window covers every row (a pattern without any term allows no pair)
+    strided = build_block_mask(dict(causal=1, window_left=G, window_right=0), G - 2, G - 2, bs, bs, device)
+    last = build_block_mask(dict(causal=0, window_left=G, window_right=G), 1, G - 1, 64, bs, device)
+    return StridedPlan(S, n, band, strided, last)
+
+
+def attn_fwd_strided(q, k, v, plan: StridedPlan, *, softmax_scale: Optional[float] = None,
+                     out=None, lse=None, o2=None, lse2=None, lse3=None):
+    """The strided template as disjoint key sets per query row, merged by LSE.
+
+    * band: kv in [q - (S - 1), q], through block lists on the natural layout;
+    * strided: kv = q - (S - 1) - S*m for m >= 1, i.e. keys kv = j*S + rho of one residue
+      rho for the rows q = (i + 2)*S + rho - 1, with j <= i: for every key residue a plain
+      causal attention between strided views of the same tensors (row step S rows, residue
+      step one row; queries from row 2S - 1 on), no copy.  The views are batched as
+      [heads, S residues, n/S - 2 rows, d];
+    * the one row those views leave out, q = n - 1 (residue 0, one group further), against
+      its keys j*S, j <= n/S - 2;
+    * ``sa_merge_partial`` folds the two strided parts into the band part.
+    q, k, v bfloat16 [B, H, n, d].  Returns (O float32 [B, H, n, d], LSE [B, H, n]);
+    ``o2`` (float32 like O), ``lse2`` (float32 [B, H, S, n/S - 2]) and ``lse3`` (float32
+    [B, H, 1, 1]) are scratch, allocated when None.
+    """
+    torch = _torch()
+    B, H, n, d = q.shape
+    if n != plan.n or k.shape[2] != n:
+        raise ValueError("plan was built for another sequence length")
+    S, G = plan.stride, n // plan.stride
+    f32, dev = torch.float32, q.device
+    out = torch.empty((B, H, n, d), dtype=f32, device=dev) if out is None else out
+    lse = torch.empty((B, H, n), dtype=f32, device=dev) if lse is None else lse
+    if out.dtype != f32:
+        raise ValueError("the strided form writes a float32 O")
+    o2 = torch.empty((B, H, n, d), dtype=f32, device=dev) if o2 is None else o2
+    lse2 = torch.empty((B, H, S, G - 2), dtype=f32, device=dev) if lse2 is None else lse2
+    lse3 = torch.empty((B, H, 1, 1), dtype=f32, device=dev) if lse3 is None else lse3
+    attn_fwd(q, k, v, plan.band, softmax_scale=softmax_scale, out=out, lse=lse)
+    for b in range(B):
+        def view(t, res, rows, first):
+            st = t.stride()
+            return t.as_strided((H, res, rows, d), (st[1], st[2], S * st[2], 1),
+                                t.storage_offset() + b * st[0] + first * st[2])
+        attn_fwd(view(q, S, G - 2, 2 * S - 1), view(k, S, G - 2, 0), view(v, S, G - 2, 0), plan.strided,
+                 softmax_scale=softmax_scale, out=view(o2, S, G - 2, 2 * S - 1), lse=lse2[b])
+        attn_fwd(view(q, 1, 1, n - 1), view(k, 1, G - 1, 0), view(v, 1, G - 1, 0), plan.last,
+                 softmax_scale=softmax_scale, out=view(o2, 1, 1, n - 1), lse=lse3[b])
+    merge_partial(out, lse, o2, lse2, group=S, q_first=2 * S - 1, n2=G - 2)
+    merge_partial(out, lse, o2, lse3, group=1, q_first=n - 1, n2=1)
+    return out, lse
+
 def attn_workspace_bytes(batch: int, heads: int, n_q: int, n_kv: int, head_dim: int, topk: int,
                          per_head_lists: bool = False) -> int:
     """Scratch bytes of the split gather form for these sizes (0 if it has none)."""

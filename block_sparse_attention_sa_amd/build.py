@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libsa.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["api.cpp", "block_mask.hip", "attn_block.hip", "attn_gather.hip", "indexer_topk.hip"]
+SOURCES = ["api.cpp", "block_mask.hip", "attn_block.hip", "attn_gather.hip", "indexer_topk.hip", "merge.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

@@ -114,6 +114,44 @@ int32_t sa_abi_version(void)
     return SA_ABI_VERSION;
 }
 
+sa_status sa_merge_partial(float* o, float* lse, const float* o2, const float* lse2, int64_t batch,
+                           int64_t heads, int64_t n, int32_t head_dim, const int64_t o_strides[3],
+                           const int64_t o2_strides[3], int32_t group, int64_t q_first, int64_t n2,
+                           void* stream)
+{
+    try {
+        if (batch < 0 || heads < 0 || n < 0) return fail(SA_ERR_INVALID_ARG, "negative batch, heads or n");
+        if (head_dim != 64 && head_dim != 128) return fail(SA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+        if (group < 1) return fail(SA_ERR_INVALID_ARG, "group must be >= 1");
+        if (q_first < 0 || n2 < 0) return fail(SA_ERR_INVALID_ARG, "q_first and n2 must be >= 0");
+        if (n2 > 0 && q_first + (n2 - 1) * group >= n)
+            return fail(SA_ERR_INVALID_ARG, "rows q_first + i*group (i < n2) must stay below n");
+        const int64_t rows = batch * heads * n;
+        if (rows == 0) return ok();
+        if (!o || !lse || !o2 || !lse2 || !o_strides || !o2_strides) return fail(SA_ERR_INVALID_ARG, "NULL pointer");
+        sa::MergeParams p{};
+        p.o = o;
+        p.lse = lse;
+        p.o2 = o2;
+        p.lse2 = lse2;
+        p.rows = rows;
+        p.n = n;
+        p.n2 = n2;
+        p.q_first = q_first;
+        p.heads = heads;
+        p.o_sb = o_strides[0];
+        p.o_sh = o_strides[1];
+        p.o_sn = o_strides[2];
+        p.o2_sb = o2_strides[0];
+        p.o2_sh = o2_strides[1];
+        p.o2_sn = o2_strides[2];
+        p.group = group;
+        return launched(sa::launch_merge(p, head_dim, (hipStream_t)stream), "sa_merge_partial");
+    } catch (...) {
+        return fail(SA_ERR_DEVICE, "sa_merge_partial: unexpected exception");
+    }
+}
+
 const char* sa_last_error(void)
 {
     return g_err.c_str();

@@ -226,6 +226,24 @@ inline bool gather_split_layout(int64_t batch, int64_t heads, int64_t n_q, int64
     L.total = up(L.pml + items * nchunk * 2 * 4);
     return true;
 }
+// Second partial result folded into the first (merge.hip).  Row (b, h, q) of
+// the first part: o + b*o_sb + h*o_sh + q*o_sn (float32, head_dim columns),
+// lse[(b*heads + h)*n + q].  Row q = q_first + i*group + r (0 <= r < group,
+// 0 <= i < n2) takes the second part: o2 at the same (b, h, q) with its
+// strides, and its LSE at lse2[((b*heads + h)*group + r)*n2 + i]; the other
+// rows are left unchanged.
+struct MergeParams {
+    float* o;
+    float* lse;
+    const float* o2;
+    const float* lse2;
+    int64_t rows;  // batch * heads * n
+    int64_t n, n2, heads, q_first;
+    int64_t o_sb, o_sh, o_sn, o2_sb, o2_sh, o2_sn;
+    int32_t group;
+};
+hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t stream);
+
 hipError_t launch_indexer_scores(const uint16_t* q_idx, const uint16_t* k_idx, int32_t n_q,
                                  int32_t n_kv, int32_t d_idx, int32_t q_offset, float* scores,
                                  hipStream_t stream);

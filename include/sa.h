@@ -231,6 +231,37 @@ sa_status sa_indexer_topk(const void *q_idx, const void *k_idx, int64_t n_q, int
                           int32_t d_idx, int64_t q_offset, int32_t topk, float *scores,
                           int32_t *idx_out, void *stream);
 
+/*
+ * sa_merge_partial -- fold a second partial attention result into a first,
+ * for key sets that are split into two disjoint parts per query row:
+ *     O = (e^l1 O1 + e^l2 O2) / (e^l1 + e^l2),   LSE = log(e^l1 + e^l2)
+ * (log-sum-exp algebra on the masked softmax of the blog "Sparse
+ * transformers: how to cut the O(n^2) of attention", section on how it
+ * looks in code; its strided template, section on the main sparsity
+ * templates, splits into the local band and the strided keys).
+ *   o      float32 (DEVICE), in/out: row (b, h, q) at
+ *          o + b*o_strides[0] + h*o_strides[1] + q*o_strides[2], head_dim
+ *          contiguous columns; the first part's O on entry, the merged O on
+ *          return;
+ *   lse    float32 [batch, heads, n] (DEVICE, contiguous), in/out, natural
+ *          log; -inf marks a row without keys;
+ *   o2     float32 (DEVICE), the second part's O at (b, h, q) with o2_strides;
+ *          must not overlap o;
+ *   lse2   float32 (DEVICE): row q = q_first + i*group + r (0 <= r < group,
+ *          0 <= i < n2) has a second part, whose LSE is at
+ *          lse2[((b*heads + h)*group + r)*n2 + i]; every other row is left
+ *          unchanged (group = 1, q_first = 0, n2 = n: the natural
+ *          [batch, heads, n] layout; group = stride: the layout that
+ *          sa_attn_fwd writes for residue views of a strided pattern).
+ * head_dim 64 or 128; group >= 1; q_first + (n2 - 1)*group < n.  A row where
+ * both LSEs are -inf is left unchanged.  Asynchronous on `stream`;
+ * allocates nothing.
+ */
+sa_status sa_merge_partial(float *o, float *lse, const float *o2, const float *lse2, int64_t batch,
+                           int64_t heads, int64_t n, int32_t head_dim, const int64_t o_strides[3],
+                           const int64_t o2_strides[3], int32_t group, int64_t q_first, int64_t n2,
+                           void *stream);
+
 /* Thread-local text of the last non-OK status of this thread ("" if none). */
 const char *sa_last_error(void);
 

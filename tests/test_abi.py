@@ -186,3 +186,33 @@ def test_gather_workspace_size_and_errors():
     assert L.sa_attn_fwd(ctypes.byref(a), None) == _lib.SA_ERR_INVALID_ARG and "aligned" in _err()
     b = _args()
     assert L.sa_attn_workspace_bytes(ctypes.byref(b)) == 0      # block mode needs none
+
+
+def test_merge_partial_argument_errors():
+    L = _lib.lib()
+    f = ctypes.c_void_p(4096)
+    st3 = (ctypes.c_int64 * 3)(1 << 20, 1 << 16, 128)
+    assert L.sa_merge_partial(f, f, f, f, 1, 1, 64, 96, st3, st3, 1, 0, 64, None) == _lib.SA_ERR_UNSUPPORTED
+    assert "head_dim" in _err()
+    assert L.sa_merge_partial(f, f, f, f, 1, 1, 64, 128, st3, st3, 0, 0, 64, None) == _lib.SA_ERR_INVALID_ARG
+    assert L.sa_merge_partial(f, f, f, f, 1, 1, 64, 128, st3, st3, 16, -1, 2, None) == _lib.SA_ERR_INVALID_ARG
+    # every call below fails validation before any launch (the pointers are fake)
+    assert L.sa_merge_partial(f, f, f, f, 1, 1, 64, 128, st3, st3, 16, 31, 4, None) == _lib.SA_ERR_INVALID_ARG
+    assert "below n" in _err()                                   # 31 + 3*16 = 79 >= 64
+    assert L.sa_merge_partial(f, f, f, f, 1, 1, 64, 128, st3, st3, 16, 49, 2, None) == _lib.SA_ERR_INVALID_ARG
+    assert L.sa_merge_partial(None, f, f, f, 1, 1, 64, 128, st3, st3, 16, 31, 2, None) == _lib.SA_ERR_INVALID_ARG
+    assert "NULL" in _err()
+    assert L.sa_merge_partial(None, None, None, None, 0, 1, 64, 128, None, None, 16, 31, 2, None) == _lib.SA_OK
+
+
+def test_strided_form_detection():
+    import block_sparse_attention_sa_amd as sa
+    pat = dict(causal=1, window_left=127, window_right=0, stride=128, stride_phase=127)
+    assert sa.strided_stride(pat, 16384, 16384) == 128
+    assert sa.strided_stride(pat, 16384, 16000) == 0            # n_q != n_kv
+    assert sa.strided_stride(pat, 16300, 16300) == 0            # not a multiple of the stride
+    assert sa.strided_stride(pat, 256, 256) == 0                # fewer than three groups
+    assert sa.strided_stride(dict(pat, sinks=4), 16384, 16384) == 0
+    assert sa.strided_stride(dict(pat, stride_phase=3), 16384, 16384) == 0
+    assert sa.strided_stride(dict(pat, window_left=64), 16384, 16384) == 0
+    assert sa.strided_stride(dict(pat, causal=0), 16384, 16384) == 0

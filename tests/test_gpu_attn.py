@@ -70,6 +70,7 @@ def test_score_ranges_across_tiles(profile, d, bq, bk):
     check_o_lse(o.cpu().numpy().reshape(-1, d), lse.cpu().numpy().reshape(-1), o_ref, lse_ref,
                 ctx=f"{profile} d={d} bq={bq} bk={bk}")
 
+
 @pytest.mark.parametrize("seed", range(16))
 def test_random_patterns(seed):
     rng = np.random.default_rng(900 + seed)
