@@ -256,7 +256,7 @@ class StridedPlan:
     last: BlockLists
 
 
-def plan_strided(pattern, n: int, block: int = 128, device="cuda") -> StridedPlan:
+def plan_strided(pattern, n: int, block: int = 64, device="cuda") -> StridedPlan:
     """Block lists for ``attn_fwd_strided``: the local band on the natural layout
     (block x block tiles); plain causal lists shared by every (head, key residue) view;
     and one row against every key of its view for the last query row."""

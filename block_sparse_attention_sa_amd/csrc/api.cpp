@@ -129,6 +129,10 @@ sa_status sa_merge_partial(float* o, float* lse, const float* o2, const float* l
         const int64_t rows = batch * heads * n;
         if (rows == 0) return ok();
         if (!o || !lse || !o2 || !lse2 || !o_strides || !o2_strides) return fail(SA_ERR_INVALID_ARG, "NULL pointer");
+        if (!aligned16(o) || !aligned16(o2)) return fail(SA_ERR_INVALID_ARG, "o and o2 must be 16-byte aligned");
+        for (int j = 0; j < 3; ++j)
+            if (o_strides[j] % 4 || o2_strides[j] % 4)
+                return fail(SA_ERR_INVALID_ARG, "o and o2 strides must be multiples of 4 elements");
         sa::MergeParams p{};
         p.o = o;
         p.lse = lse;

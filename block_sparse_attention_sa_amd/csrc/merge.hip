@@ -9,22 +9,23 @@
 // templates: near neighbours plus positions at a fixed step) splits this way
 // into its local band and its strided keys.
 //
-// One wave per row (b, h, q); lanes own columns lane + 64 j, so every load
-// and store of a row is one coalesced 256-byte access per j.  The second
-// partial's LSE may be stored in residue order (see MergeParams).
+// D/4 threads per row, four columns each (16-byte loads and stores), so a
+// wave covers 64*4/D rows and every row costs one request per operand.
+// The second partial's LSE may be stored in residue order (see MergeParams).
 #include "sa_internal.h"
 
 namespace sa {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kThreads = 256;
 
 template <int D>
-__global__ void __launch_bounds__(kWaves * 64) merge_kernel(MergeParams p)
+__global__ void __launch_bounds__(kThreads) merge_kernel(MergeParams p)
 {
-    constexpr int PER = D / 64;
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    constexpr int TPR = D / 4;                 // threads per row
+    constexpr int RPB = kThreads / TPR;        // rows per workgroup
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+    const int c = (threadIdx.x % TPR) * 4;
     if (row >= p.rows) return;
     const int64_t q = row % p.n;
     const int64_t bh = row / p.n;
@@ -39,28 +40,24 @@ __global__ void __launch_bounds__(kWaves * 64) merge_kernel(MergeParams p)
     const float w1 = l1 == -INFINITY ? 0.f : expf(l1 - m);
     const float w2 = l2 == -INFINITY ? 0.f : expf(l2 - m);
     const float inv = 1.f / (w1 + w2);
-    float* o = p.o + b * p.o_sb + h * p.o_sh + q * p.o_sn;
-    const float* o2 = p.o2 + b * p.o2_sb + h * p.o2_sh + q * p.o2_sn;
-    float x1[PER], x2[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        x1[j] = o[lane + 64 * j];
-        x2[j] = o2[lane + 64 * j];
-    }
-#pragma unroll
-    for (int j = 0; j < PER; ++j) o[lane + 64 * j] = (x1[j] * w1 + x2[j] * w2) * inv;
-    if (lane == 0) p.lse[row] = m + logf(w1 + w2);
+    float4* o = reinterpret_cast<float4*>(p.o + b * p.o_sb + h * p.o_sh + q * p.o_sn + c);
+    const float4 x2 = *reinterpret_cast<const float4*>(p.o2 + b * p.o2_sb + h * p.o2_sh + q * p.o2_sn + c);
+    const float4 x1 = *o;
+    *o = make_float4((x1.x * w1 + x2.x * w2) * inv, (x1.y * w1 + x2.y * w2) * inv,
+                     (x1.z * w1 + x2.z * w2) * inv, (x1.w * w1 + x2.w * w2) * inv);
+    if (c == 0) p.lse[row] = m + logf(w1 + w2);
 }
 
 }  // namespace
 
 hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t stream)
 {
-    const unsigned grid = (unsigned)((p.rows + kWaves - 1) / kWaves);
+    const int64_t rpb = kThreads / (head_dim / 4);
+    const unsigned grid = (unsigned)((p.rows + rpb - 1) / rpb);
     if (head_dim == 128)
-        hipLaunchKernelGGL(merge_kernel<128>, dim3(grid), dim3(kWaves * 64), 0, stream, p);
+        hipLaunchKernelGGL(merge_kernel<128>, dim3(grid), dim3(kThreads), 0, stream, p);
     else if (head_dim == 64)
-        hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), dim3(kWaves * 64), 0, stream, p);
+        hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, p);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

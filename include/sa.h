@@ -253,6 +253,7 @@ sa_status sa_indexer_topk(const void *q_idx, const void *k_idx, int64_t n_q, int
  *          unchanged (group = 1, q_first = 0, n2 = n: the natural
  *          [batch, heads, n] layout; group = stride: the layout that
  *          sa_attn_fwd writes for residue views of a strided pattern).
+ * o and o2 16-byte aligned with strides that are multiples of 4 elements;
  * head_dim 64 or 128; group >= 1; q_first + (n2 - 1)*group < n.  A row where
  * both LSEs are -inf is left unchanged.  Asynchronous on `stream`;
  * allocates nothing.
