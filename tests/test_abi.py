@@ -202,6 +202,12 @@ def test_merge_partial_argument_errors():
     assert L.sa_merge_partial(f, f, f, f, 1, 1, 64, 128, st3, st3, 16, 49, 2, None) == _lib.SA_ERR_INVALID_ARG
     assert L.sa_merge_partial(None, f, f, f, 1, 1, 64, 128, st3, st3, 16, 31, 2, None) == _lib.SA_ERR_INVALID_ARG
     assert "NULL" in _err()
+    bad = (ctypes.c_int64 * 3)(1 << 20, 1 << 16, 130)          # row stride not a multiple of 4
+    assert L.sa_merge_partial(f, f, f, f, 1, 1, 64, 128, st3, bad, 16, 31, 2, None) == _lib.SA_ERR_INVALID_ARG
+    assert "multiples of 4" in _err()
+    g = ctypes.c_void_p(4100)                                     # not 16-byte aligned
+    assert L.sa_merge_partial(g, f, f, f, 1, 1, 64, 128, st3, st3, 16, 31, 2, None) == _lib.SA_ERR_INVALID_ARG
+    assert "aligned" in _err()
     assert L.sa_merge_partial(None, None, None, None, 0, 1, 64, 128, None, None, 16, 31, 2, None) == _lib.SA_OK
 
 
