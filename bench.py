@@ -258,7 +258,7 @@ def _bench_strided(sa, W, np, torch, dev, dev_bf16, reps=10):
         "blocks_tflops_over_live_pairs": round(flop / t["blocks"] / 1e12, 2),
         "split_us": round(t["split"] * 1e6, 1),
         "split_tflops_over_live_pairs": round(flop / t["split"] / 1e12, 2),
-        "split_note": "band through block lists + one causal 128x128 tile per (head, residue) view + LSE merge",
+        "split_note": "64x64 band tiles through block lists + causal 64-row tiles per (head, key residue) view + LSE merge",
     }
 
 def _bench_dsa(sa, W, np, torch, dev, dev_bf16, reps=5):
