@@ -227,6 +227,6 @@ def test_strided_form_detection():
 def test_plan_strided_rejects_other_patterns():
     import block_sparse_attention_sa_amd as sa
     pat = dict(causal=1, window_left=127, window_right=0, stride=128, stride_phase=127)
-    for bad, n in ((dict(pat, sinks=1), 16384), (pat, 16000), (dict(causal=1, window_left=127), 16384)):
+    for bad, n in ((dict(pat, sinks=1), 16384), (pat, 16300), (dict(causal=1, window_left=127), 16384)):
         with pytest.raises(ValueError):
             sa.plan_strided(bad, n)        # raises before any device work
