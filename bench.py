@@ -234,9 +234,10 @@ def _bench_strided(sa, W, np, torch, dev, dev_bf16, reps=10):
     lse = torch.empty(shape[:3], dtype=torch.float32, device=dev)
     o2 = torch.empty(shape, dtype=torch.float32, device=dev)
     lse2 = torch.empty((cfg.B, cfg.H, plan.stride, cfg.N // plan.stride - 2), dtype=torch.float32, device=dev)
+    lse3 = torch.empty((cfg.B, cfg.H, 1, 1), dtype=torch.float32, device=dev)
     ways = {
         "blocks": lambda: sa.attn_fwd(q, k, v, bl, out=o, lse=lse),
-        "split": lambda: sa.attn_fwd_strided(q, k, v, plan, out=o, lse=lse, o2=o2, lse2=lse2),
+        "split": lambda: sa.attn_fwd_strided(q, k, v, plan, out=o, lse=lse, o2=o2, lse2=lse2, lse3=lse3),
     }
     t = {}
     for name, fn in ways.items():

@@ -152,6 +152,11 @@ def attn_fwd(q, k, v, blocks: Optional[BlockLists] = None, gather_idx=None, *,
         out = torch.empty((B, H, n_q, d), dtype=o_dtype, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    if tuple(out.shape) != (B, H, n_q, d) or not out.is_cuda:
+        raise ValueError("out must be a CUDA tensor of shape [B, H, n_q, d]")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous()
+                            or lse.numel() != B * H * n_q):
+        raise ValueError("lse must be a contiguous float32 CUDA tensor of B * H * n_q values")
     a = _lib.SaAttnArgs()
     a.q, a.k, a.v, a.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()
     a.lse = lse.data_ptr() if lse is not None else None
@@ -291,8 +296,13 @@ def attn_fwd_strided(q, k, v, plan: StridedPlan, *, softmax_scale: Optional[floa
     [B, H, 1, 1]) are scratch, allocated when None.
     """
     torch = _torch()
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 4 or t.stride(-1) != 1:
+            raise ValueError("q, k, v must be 4-d bfloat16 CUDA tensors with contiguous rows")
     B, H, n, d = q.shape
-    if n != plan.n or k.shape[2] != n:
+    if tuple(k.shape) != (B, H, n, d) or tuple(v.shape) != (B, H, n, d):
+        raise ValueError("q, k and v must have the same shape [B, H, n, d]")
+    if n != plan.n:
         raise ValueError("plan was built for another sequence length")
     S, G = plan.stride, n // plan.stride
     f32, dev = torch.float32, q.device
@@ -303,6 +313,10 @@ def attn_fwd_strided(q, k, v, plan: StridedPlan, *, softmax_scale: Optional[floa
     o2 = torch.empty((B, H, n, d), dtype=f32, device=dev) if o2 is None else o2
     lse2 = torch.empty((B, H, S, G - 2), dtype=f32, device=dev) if lse2 is None else lse2
     lse3 = torch.empty((B, H, 1, 1), dtype=f32, device=dev) if lse3 is None else lse3
+    if tuple(o2.shape) != (B, H, n, d) or o2.dtype != f32:
+        raise ValueError("o2 must be float32 [B, H, n, d]")
+    if tuple(lse2.shape) != (B, H, S, G - 2) or tuple(lse3.shape) != (B, H, 1, 1):
+        raise ValueError("lse2 must be [B, H, S, n/S - 2] and lse3 [B, H, 1, 1]")
     attn_fwd(q, k, v, plan.band, softmax_scale=softmax_scale, out=out, lse=lse)
     for b in range(B):
         def view(t, res, rows, first):

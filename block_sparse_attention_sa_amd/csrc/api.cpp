@@ -123,7 +123,10 @@ sa_status sa_merge_partial(float* o, float* lse, const float* o2, const float* l
         if (batch < 0 || heads < 0 || n < 0) return fail(SA_ERR_INVALID_ARG, "negative batch, heads or n");
         if (head_dim != 64 && head_dim != 128) return fail(SA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
         if (group < 1) return fail(SA_ERR_INVALID_ARG, "group must be >= 1");
+        if (batch > kI32Max || heads > kI32Max || n > kI32Max || batch * heads > kI32Max || batch * heads * n > (int64_t(1) << 40))
+            return fail(SA_ERR_UNSUPPORTED, "batch, heads and n must stay below 2^31 and their product below 2^40");
         if (q_first < 0 || n2 < 0) return fail(SA_ERR_INVALID_ARG, "q_first and n2 must be >= 0");
+        if (n2 > n || group > n + 1) return fail(SA_ERR_INVALID_ARG, "n2 and group must not exceed n");
         if (n2 > 0 && q_first + (n2 - 1) * group >= n)
             return fail(SA_ERR_INVALID_ARG, "rows q_first + i*group (i < n2) must stay below n");
         const int64_t rows = batch * heads * n;
