@@ -11,9 +11,10 @@
 // online across tiles (running max, running sum, rescaled accumulator).
 //
 // gfx950 mapping.  A workgroup owns one (batch, head, query block of BQ rows).
-// At head_dim 128 each wave owns 32 query rows (two waves per SIMD); at
-// head_dim 64 each wave owns 64 rows as two 32-query column blocks, so every
-// K and V operand read from LDS feeds two MFMAs.
+// Each wave owns 32 query rows, two waves per SIMD.  (The kernel can also
+// give a wave NB = 2 column blocks of 32 queries, so that every K and V
+// operand read from LDS feeds two MFMAs; that measured slower at both head
+// dims, and is not launched.)
 //   * Live key tiles are walked in 64-key sub-tiles.  K and V sub-tiles go
 //     HBM -> LDS by buffer loads with LDS destination (no staging registers),
 //     double buffered; the loop body is unrolled over the two buffer pairs so
@@ -507,10 +508,9 @@ attn_block_kernel(AttnParams a)
 template <int D, int BQ, int BK, bool OF32>
 hipError_t launch_one(const AttnParams& a, hipStream_t stream)
 {
-    // head_dim 128: one 32-query column block per wave, two waves per SIMD;
-    // head_dim 64: two column blocks per wave (the smaller tiles leave LDS
-    // bandwidth to spare)
-    constexpr int NB = D == 128 ? 1 : 2;
+    // one 32-query column block per wave at both head dims (two per wave ran
+    // 15-36 % slower at head_dim 64)
+    constexpr int NB = 1;
     const int64_t items = (int64_t)a.batch * a.heads * a.nqb;
     hipLaunchKernelGGL((attn_block_kernel<D, BQ, BK, OF32, NB>), dim3((unsigned)items), dim3(BQ * 2 / NB), 0,
                        stream, a);
