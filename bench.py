@@ -336,6 +336,7 @@ def _cpu_baseline(cfg, inp, seconds, np):
         "value": round(value, 6),
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": f"fp64 oracle attention, {passes} pass(es) over the whole workload ({cfg.H} heads x "
                   f"{cfg.N} rows, {pairs // passes} live pairs per pass) in {t2 - t1:.2f} s; its block "

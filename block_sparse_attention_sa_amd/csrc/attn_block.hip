@@ -18,8 +18,9 @@
 //   * Live key tiles are walked in 64-key sub-tiles.  K and V sub-tiles go
 //     HBM -> LDS by buffer loads with LDS destination (no staging registers),
 //     double buffered; the loop body is unrolled over the two buffer pairs so
-//     each copy names its LDS objects statically.  Rows past the sequence end
-//     fall outside the buffer range and read as zero.  16-byte chunks are XOR
+//     each copy names its LDS objects statically.  A sub-tile that reaches
+//     past the last key is copied through resources that end at n_kv, so
+//     rows past the sequence end read as zero.  16-byte chunks are XOR
 //     swizzled per row so the operand reads hit distinct banks.
 //   * The live list is held in lane registers and read with readlane.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T
@@ -113,7 +114,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 
-template <int D, int BQ, int BK, bool OF32, int NB>
+// TAIL: n_kv is not a multiple of the 64-key sub-tile, so one sub-tile per
+// query block may reach past the last key (launched only then: the extra
+// copy path costs registers).
+template <int D, int BQ, int BK, bool OF32, int NB, bool TAIL>
 __global__ void __launch_bounds__(BQ * 2 / NB, NB == 1 ? 2 : 1)
 attn_block_kernel(AttnParams a)
 {
@@ -174,7 +178,7 @@ attn_block_kernel(AttnParams a)
     };
     auto list_at = [](int v, int e) { return __builtin_amdgcn_readlane(v, e & 63); };
     // first key of a sub-tile of list entry j; an entry that is not a key
-    // block maps past the sequence end, where the DMA reads zeros and the
+    // block maps past the sequence end, where the copy reads zeros and the
     // mask drops every key
     auto sub_kv0 = [&](int j, int sub) {
         return ((unsigned)j < (unsigned)a.nkb ? j : a.nkb) * BK + sub * KS;
@@ -198,7 +202,42 @@ attn_block_kernel(AttnParams a)
         kterm[j] = (uint32_t)dma_r * krow_b + (uint32_t)((dma_p ^ kswz<D>(r)) << 4);
     }
     const uint32_t vterm = (uint32_t)dma_r * vrow_b + (uint32_t)((dma_p ^ vswz<D>(dma_r)) << 4);
+    const uint16_t* kbh = a.k + b * a.k_sb + h * a.k_sh;
+    const uint16_t* vbh = a.v + b * a.v_sb + h * a.v_sh;
+    // A sub-tile that reaches past the last key (a ragged end, or a list
+    // entry that is not a key block): the buffer range check covers the
+    // per-lane offset but not the scalar one, so these copies take a resource
+    // whose base is the sub-tile's first row and whose size stops at n_kv,
+    // with the whole row offset in the per-lane operand; rows past n_kv then
+    // read as zero and nothing beyond the tensor is touched.
+    auto dma_tail = [&](int kv0, uint8_t* kdst, uint8_t* vdst) {
+        const int left = max(a.n_kv - kv0, 0);
+        const __amdgpu_buffer_rsrc_t ks = make_rsrc(kbh + (int64_t)kv0 * a.k_sn, (int64_t)left * krow_b);
+        const __amdgpu_buffer_rsrc_t vs = make_rsrc(vbh + (int64_t)kv0 * a.v_sn, (int64_t)left * vrow_b);
+#pragma unroll
+        for (int i = 0; i < DMA_W; ++i) {
+            const int g = wave_u + i * NW;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ks, (lds_void*)(kdst + g * 1024), 16,
+                                                     kterm[i % KT] + (uint32_t)(g * ROWS_PER_KB) * krow_b, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < DMA_W; ++i) {
+            const int g = wave_u + i * NW;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vs, (lds_void*)(vdst + g * 1024), 16,
+                                                     vterm + (uint32_t)(g * ROWS_PER_KB) * vrow_b, 0, 0, 0);
+        }
+    };
     auto dma = [&](int kv0, uint8_t* kdst, uint8_t* vdst) {
+        // a sub-tile wholly past the last key (a list entry that is not a key
+        // block) is not copied: the mask drops every key of it, so the wave
+        // skips it without reading its buffer
+        if (kv0 >= a.n_kv) return;
+        if (TAIL && kv0 + KS > a.n_kv) {
+            dma_tail(kv0, kdst, vdst);
+            return;
+        }
+        // every row of the sub-tile exists: one resource per tensor, the
+        // uniform row offset in the scalar operand
 #pragma unroll
         for (int i = 0; i < DMA_W; ++i) {
             const int g = wave_u + i * NW;
@@ -512,8 +551,12 @@ hipError_t launch_one(const AttnParams& a, hipStream_t stream)
     // 15-36 % slower at head_dim 64)
     constexpr int NB = 1;
     const int64_t items = (int64_t)a.batch * a.heads * a.nqb;
-    hipLaunchKernelGGL((attn_block_kernel<D, BQ, BK, OF32, NB>), dim3((unsigned)items), dim3(BQ * 2 / NB), 0,
-                       stream, a);
+    if (a.n_kv % 64)
+        hipLaunchKernelGGL((attn_block_kernel<D, BQ, BK, OF32, NB, true>), dim3((unsigned)items), dim3(BQ * 2 / NB), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((attn_block_kernel<D, BQ, BK, OF32, NB, false>), dim3((unsigned)items), dim3(BQ * 2 / NB),
+                           0, stream, a);
     return hipGetLastError();
 }
 

@@ -41,7 +41,8 @@
  *    (the pages give no formula; this fixed order is the reading adopted),
  *    plus the fp64 value of the same dot product.
  *  - orc_topk_rows: the k candidates that come first in the total order
- *    (score descending, index ascending), emitted in ascending index order.
+ *    (score descending, index ascending; a NaN score above every number),
+ *    emitted in ascending index order.
  *
  * Inputs are raw bfloat16 bit patterns (uint16); each is widened exactly.
  */
@@ -276,14 +277,22 @@ typedef struct {
     int32_t idx;
 } orc_scored;
 
-/* Total order: larger score first, then smaller index first. */
+/* Total order: larger score first, then smaller index first.  -0.0 and +0.0
+ * are equal scores.  The pages rank by score only; to make the order total on
+ * every float input, a NaN score (of either sign) ranks above every number
+ * and NaNs are equal scores (so among NaNs the smaller index comes first). */
 static int cmp_scored(const void *a, const void *b)
 {
     const orc_scored *x = (const orc_scored *)a, *y = (const orc_scored *)b;
-    if (x->key > y->key)
-        return -1;
-    if (x->key < y->key)
-        return 1;
+    int xn = isnan(x->key), yn = isnan(y->key);
+    if (xn != yn)
+        return xn ? -1 : 1;
+    if (!xn) {
+        if (x->key > y->key)
+            return -1;
+        if (x->key < y->key)
+            return 1;
+    }
     return (x->idx > y->idx) - (x->idx < y->idx);
 }
 

@@ -64,20 +64,19 @@ def random_pattern(rng, n_q, n_kv, allow_offset=True):
     return pat
 
 
-def sample_rows(rng, B, H, n_q, n):
-    """Flattened (b*H + h)*n_q + q indices: first/last rows of some heads plus random ones."""
-    total = B * H * n_q
-    fixed = [0, 1, 2, 3, n_q - 1, total - 1, total - n_q, (B * H // 2) * n_q + n_q // 2]
-    rnd = rng.choice(total, size=min(n, total), replace=False)
-    return np.unique(np.concatenate([np.array(fixed) % total, rnd]).astype(np.int64))
+_FULL_REF = {}
 
 
-def gpu_rows(t, rows):
-    """Rows of a [B, H, N, ...] device tensor at flattened indices, as numpy float64."""
-    import torch
-    flat = t.reshape(-1, *t.shape[3:]) if t.dim() > 3 else t.reshape(-1)
-    idx = torch.from_numpy(rows).to(t.device)
-    return flat.index_select(0, idx).float().cpu().numpy().astype(np.float64)
+def full_config_reference(cid):
+    """Inputs and the oracle's O and LSE over every row of attention configuration
+    ``cid`` at its full size, computed once per test process."""
+    if cid not in _FULL_REF:
+        import oracle
+        cfg = W.attn_config(cid)
+        inp = W.attn_inputs(cfg)
+        o_ref, lse_ref = oracle.attn_rows(cfg.pattern, inp["q"], inp["k"], inp["v"])
+        _FULL_REF[cid] = (cfg, inp, o_ref, lse_ref)
+    return _FULL_REF[cid]
 
 
 __all__ = ["W"]

@@ -7,7 +7,7 @@ import torch
 import oracle
 import block_sparse_attention_sa_amd as sa
 from block_sparse_attention_sa_amd import workloads as W
-from tests.parity_util import (check_o_lse, gpu_rows, random_pattern, sample_rows, to_dev_bf16)
+from tests.parity_util import check_o_lse, full_config_reference, random_pattern, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -97,21 +97,18 @@ def test_config1_full():
 
 @pytest.mark.parametrize("cid", [2, 3, 4])
 @pytest.mark.parametrize("of", ["f32", "bf16"])
-def test_full_configs_sampled_rows(cid, of):
-    """Full-size launch (the benchmark's configuration); oracle on sampled rows."""
-    cfg = W.attn_config(cid)
-    inp = W.attn_inputs(cfg)
+def test_full_configs_all_rows(cid, of):
+    """Full-size launch (the benchmark's configuration); every row of every
+    (batch, head) against the oracle."""
+    cfg, inp, o_ref, lse_ref = full_config_reference(cid)
     print(f"attn config {cid} o={of} B={cfg.B} H={cfg.H} N={cfg.N} d={cfg.d}", flush=True)
     od = torch.float32 if of == "f32" else torch.bfloat16
     o, lse = _run(cfg.pattern, inp["q"], inp["k"], inp["v"], cfg.block, cfg.block, od)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(cid)
-    rows = sample_rows(rng, cfg.B, cfg.H, cfg.N, 768)
-    o_ref, lse_ref = oracle.attn_rows(cfg.pattern, inp["q"], inp["k"], inp["v"], rows=rows)
-    check_o_lse(gpu_rows(o, rows), gpu_rows(lse, rows), o_ref, lse_ref, bf16_out=(of == "bf16"),
-                ctx=f"config {cid} {of}")
-    # every row finite (no empty rows in these configurations) and no NaN anywhere
-    assert torch.isfinite(lse).all() and torch.isfinite(o.float()).all()
+    check_o_lse(o.float().cpu().numpy().reshape(-1, cfg.d), lse.cpu().numpy().reshape(-1), o_ref, lse_ref,
+                bf16_out=(of == "bf16"), ctx=f"config {cid} {of}")
+    # no empty rows in these configurations
+    assert np.isfinite(lse_ref).all()
 
 
 def test_value_ones_give_ones_and_weights_sum():
@@ -185,3 +182,36 @@ def test_dense_pattern_matches_causal_sdpa_fp32():
     tq, tk, tv = (torch.from_numpy(W.bf16_bits_to_f32(x)) for x in (q, k, v))
     ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True)
     assert float((o.cpu() - ref).abs().max()) <= 1e-2
+
+
+@pytest.mark.parametrize("d,bq,bk,n_kv", [(128, 128, 128, 301), (128, 64, 64, 301), (64, 128, 64, 301),
+                                          (64, 64, 128, 320), (128, 128, 64, 384)])
+def test_nan_rows_past_n_kv_and_invalid_list_entries(d, bq, bk, n_kv):
+    """K and V are views into larger allocations whose rows past n_kv hold NaN
+    (a preallocated cache with an unwritten tail), and query blocks list key
+    blocks that do not exist (past the end and negative): nothing past n_kv may
+    reach O or LSE.  Ragged n_kv takes the bounds-checked copy path, a multiple
+    of 64 the fast one."""
+    rng = np.random.default_rng(d + bq + bk + n_kv)
+    B, H, n_q, pad = 1, 2, 333, 200
+    q, k, v = _rand(rng, B, H, n_q, n_kv, d)
+    nan = np.uint16(0x7FC0)
+    kf = np.full((B, H, n_kv + pad, d), nan, np.uint16)
+    vf = np.full((B, H, n_kv + pad, d), nan, np.uint16)
+    kf[:, :, :n_kv], vf[:, :, :n_kv] = k, v
+    kd, vd = to_dev_bf16(kf)[:, :, :n_kv], to_dev_bf16(vf)[:, :, :n_kv]
+    pat = dict(causal=1, window_left=90, window_right=0, sinks=3, q_offset=10)
+    bl = sa.build_block_mask(pat, n_q, n_kv, bq, bk)
+    cnt, idx = bl.kv_count.cpu().numpy(), bl.kv_index.cpu().numpy()
+    nkb = idx.shape[1]
+    for i in range(cnt.size):  # append entries that are not key blocks where a row has room
+        extra = [nkb + 3, -5, nkb][: nkb - cnt[i]]
+        idx[i, cnt[i]: cnt[i] + len(extra)] = extra
+        cnt[i] += len(extra)
+    bl.kv_count.copy_(torch.from_numpy(cnt))
+    bl.kv_index.copy_(torch.from_numpy(idx))
+    print(f"attn NaN tail d={d} bq={bq} bk={bk} n_kv={n_kv}", flush=True)
+    o, lse = sa.attn_fwd(to_dev_bf16(q), kd, vd, bl)
+    o_ref, lse_ref = oracle.attn_rows(pat, q, k, v)
+    check_o_lse(o.cpu().numpy().reshape(-1, d), lse.cpu().numpy().reshape(-1), o_ref, lse_ref,
+                ctx=f"NaN tail d={d} bq={bq} bk={bk} n_kv={n_kv}")

@@ -70,8 +70,9 @@ def test_repeat_is_identical():
 
 
 @pytest.mark.parametrize("seed", range(4))
-def test_long_rows_two_kernel_path(seed):
-    """Rows of more than 512 key blocks take the two-kernel builder."""
+def test_long_rows(seed):
+    """Rows of more than 512 key blocks (several count workgroups per query block
+    and a compaction over a long row)."""
     rng = np.random.default_rng(900 + seed)
     n_q, n_kv, bq, bk = int(rng.integers(40, 130)), int(rng.integers(16500, 21000)), 64, 32
     assert (n_kv + bk - 1) // bk > 512

@@ -13,7 +13,7 @@ import torch
 import oracle
 import block_sparse_attention_sa_amd as sa
 from block_sparse_attention_sa_amd import workloads as W
-from tests.parity_util import check_o_lse, gpu_rows, sample_rows, to_dev_bf16
+from tests.parity_util import check_o_lse, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -70,6 +70,33 @@ def test_topk_ties_signed_zero_and_padding():
     assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(2048, dtype=np.int32), (3, 1)))
 
 
+def _nan_scores(rng, n_q, n_kv, n_special):
+    """Normal scores with NaNs of both signs (quiet and signalling bit patterns),
+    +inf, -inf and signed zeros planted at random positions."""
+    s = rng.standard_normal((n_q, n_kv)).astype(np.float32)
+    u = s.view(np.uint32)
+    for r in range(n_q):
+        pos = rng.choice(n_kv, size=n_special, replace=False)
+        u[r, pos] = rng.choice(np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFFBFFFFF, 0x7F800000,
+                                         0xFF800000, 0x80000000, 0x00000000], np.uint32), size=n_special)
+    return s
+
+
+@pytest.mark.parametrize("n_kv,k,n_special", [(65536, 2048, 100), (65536, 2048, 5000), (9001, 333, 600),
+                                              (4000, 2048, 3999), (777, 100, 7)])
+def test_topk_nan_and_infinite_scores(n_kv, k, n_special):
+    """A NaN score ranks above every number and NaNs tie (lowest index first);
+    -inf ranks last; the selection matches the oracle's total order."""
+    rng = np.random.default_rng(n_kv + k + n_special)
+    n_q = 4
+    s = _nan_scores(rng, n_q, n_kv, n_special)
+    off = n_kv - 3
+    print(f"topk NaN/inf n_kv={n_kv} k={k} specials={n_special}", flush=True)
+    got = sa.topk(torch.from_numpy(s).cuda(), off, k).cpu().numpy()
+    want = oracle.topk_rows(s, np.minimum(np.arange(n_q) + off + 1, n_kv), k)
+    np.testing.assert_array_equal(got, want)
+
+
 def _scores_of(kind, rng, n_q, n_kv):
     if kind == "normal":
         return (rng.standard_normal((n_q, n_kv)) * 8).astype(np.float32)
@@ -112,22 +139,33 @@ def test_topk_score_distributions(kind, n_kv, k):
     np.testing.assert_array_equal(got, want)
 
 
-def test_config5_indexer_topk_sampled_rows():
-    cfg = W.topk_config(5)
-    inp = W.topk_inputs(cfg)
+_CFG5 = {}
+
+
+def _config5_reference():
+    """Configuration 5's inputs, the oracle's scores for every query row and its
+    top-k selection, computed once per test process."""
+    if not _CFG5:
+        cfg = W.topk_config(5)
+        inp = W.topk_inputs(cfg)
+        want_s = oracle.indexer_scores(inp["q_idx"], inp["k_idx"], cfg.q_offset)
+        want_idx = oracle.topk_rows(want_s, cfg.q_offset + np.arange(cfg.n_q) + 1, cfg.topk)
+        _CFG5.update(cfg=cfg, inp=inp, scores=want_s, idx=want_idx)
+    return _CFG5
+
+
+def test_config5_indexer_topk_all_rows():
+    ref = _config5_reference()
+    cfg, inp = ref["cfg"], ref["inp"]
     qi, ki = to_dev_bf16(inp["q_idx"]), to_dev_bf16(inp["k_idx"])
     print("config 5 indexer+topk full size", flush=True)
     idx, scores = sa.indexer_topk(qi, ki, cfg.q_offset, cfg.topk)
     torch.cuda.synchronize()
-    rows = np.array([0, 1, 511, 1022, 1023] + list(np.random.default_rng(5).choice(1024, 27, replace=False)))
-    rows = np.unique(rows).astype(np.int64)
-    want_s = oracle.indexer_scores(inp["q_idx"], inp["k_idx"], cfg.q_offset, rows=rows)
-    got_s = scores.cpu().numpy()[rows]
-    for i, r in enumerate(rows):
+    got_s = scores.cpu().numpy()
+    for r in range(cfg.n_q):
         nc = cfg.q_offset + r + 1
-        assert np.array_equal(got_s[i, :nc].view(np.uint32), want_s[i, :nc].view(np.uint32)), f"row {r}"
-    want_idx = oracle.topk_rows(want_s, cfg.q_offset + rows + 1, cfg.topk)
-    np.testing.assert_array_equal(idx.cpu().numpy()[rows], want_idx)
+        assert np.array_equal(got_s[r, :nc].view(np.uint32), ref["scores"][r, :nc].view(np.uint32)), f"row {r}"
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref["idx"])
 
 
 # ---------------------------------------------------------------------------
@@ -180,17 +218,18 @@ def test_gather_of_whole_blocks_equals_block_mode():
     assert float((l_g - l_b).abs().max()) <= 1e-4
 
 
-def test_config5_gather_sampled_rows():
-    cfg = W.topk_config(5)
-    inp = W.topk_inputs(cfg)
-    idx, _ = sa.indexer_topk(to_dev_bf16(inp["q_idx"]), to_dev_bf16(inp["k_idx"]), cfg.q_offset, cfg.topk)
+def test_config5_gather_all_rows():
+    """Gather attention of configuration 5 over the oracle's own selection, every
+    (head, query) row."""
+    ref = _config5_reference()
+    cfg, inp = ref["cfg"], ref["inp"]
     print("config 5 gather attention full size", flush=True)
     q, k, v = (to_dev_bf16(inp[t]) for t in ("q", "k", "v"))
-    o, lse = sa.attn_fwd(q, k, v, gather_idx=idx)
+    o, lse = sa.attn_fwd(q, k, v, gather_idx=torch.from_numpy(ref["idx"]).cuda())
     torch.cuda.synchronize()
-    rows = sample_rows(np.random.default_rng(55), 1, cfg.H, cfg.n_q, 256)
-    o_ref, lse_ref = oracle.attn_gather_rows(inp["q"], inp["k"], inp["v"], idx.cpu().numpy(), rows=rows)
-    check_o_lse(gpu_rows(o, rows), gpu_rows(lse, rows), o_ref, lse_ref, ctx="config 5")
+    o_ref, lse_ref = oracle.attn_gather_rows(inp["q"], inp["k"], inp["v"], ref["idx"])
+    check_o_lse(o.cpu().numpy().reshape(-1, cfg.d), lse.cpu().numpy().reshape(-1), o_ref, lse_ref,
+                ctx="config 5")
 
 
 @pytest.mark.parametrize("d", [64, 128])

@@ -438,6 +438,37 @@ def test_topk_vs_python_sort_with_ties():
         assert got[r].tolist() == _brute_topk(sig[r], int(n_cand[r]), k)
 
 
+def test_topk_nan_and_infinite_scores_python_sort():
+    """NaN scores (either sign bit) rank above +inf and tie with each other; -0.0
+    ties with +0.0.  Pinned against Python's sort on an explicit key."""
+    rng = np.random.default_rng(16)
+    n_rows, n_kv, k = 24, 200, 23
+    sig = rng.integers(-3, 4, size=(n_rows, n_kv)).astype(np.float32)
+    u = sig.view(np.uint32)
+    for r in range(n_rows):
+        pos = rng.choice(n_kv, size=int(rng.integers(0, 40)), replace=False)
+        kinds = rng.integers(0, 6, size=pos.size)
+        for p_, kd in zip(pos, kinds):
+            u[r, p_] = [0x7FC00000, 0xFFC00000, 0x7F800001, 0x7F800000, 0xFF800000, 0x80000000][kd]
+    sig[3, :] = np.nan                      # every candidate NaN
+    sig[4, :150] = np.inf                   # more +inf than k, NaN after them
+    sig[4, 190] = np.nan
+    n_cand = rng.integers(1, n_kv + 1, size=n_rows)
+    n_cand[3:5] = n_kv
+
+    def key(row, s):
+        x = float(row[s])
+        return (0 if math.isnan(x) else 1, 0.0 if math.isnan(x) else -x, s)
+
+    got = oracle.topk_rows(sig, n_cand, k)
+    for r in range(n_rows):
+        nc = int(n_cand[r])
+        sel = sorted(sorted(range(nc), key=lambda s: key(sig[r], s))[:k])
+        assert got[r].tolist() == sel + [-1] * (k - len(sel)), f"row {r}"
+    assert got[3].tolist() == list(range(k))
+    assert got[4].tolist() == sorted([190] + list(range(k - 1)))
+
+
 def test_topk_zero_queries_all_ties():
     rng = np.random.default_rng(13)
     ki = W.f32_to_bf16_bits(rng.standard_normal((3000, 64), dtype=np.float32))
