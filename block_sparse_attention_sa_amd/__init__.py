@@ -25,7 +25,7 @@ from . import _lib
 from ._lib import SaError  # noqa: F401
 
 __all__ = ["BlockLists", "build_block_mask", "attn_fwd", "attn_workspace_bytes", "indexer_scores", "topk", "indexer_topk",
-           "describe", "SaError"]
+           "indexer_topk_workspace_bytes", "describe", "SaError"]
 
 
 def _torch():
@@ -369,19 +369,42 @@ def topk(scores, q_offset: int, k: int, out=None):
     return out
 
 
-def indexer_topk(q_idx, k_idx, q_offset: int, k: int, scores=None, out=None):
-    """Indexer scores into ``scores`` (workspace) then the top-k; returns (idx, scores)."""
+def indexer_topk_workspace_bytes(n_q: int, n_kv: int, k: int) -> int:
+    """Scratch bytes of the streaming indexer + top-k (``sa_indexer_topk_workspace``)."""
+    return int(_lib.lib().sa_indexer_topk_workspace(n_q, n_kv, k))
+
+
+def indexer_topk(q_idx, k_idx, q_offset: int, k: int, out=None, scores=None, keep_scores: bool = False,
+                 workspace=None):
+    """Indexer scores and the top-k in one call (``sa_indexer_topk``); returns (idx, scores).
+
+    By default the call streams: no score matrix is written (``scores`` is None
+    on return) and the scratch is ``workspace`` (a uint8 CUDA tensor of at
+    least ``indexer_topk_workspace_bytes`` bytes, allocated for the call when
+    None).  With ``keep_scores`` (or a ``scores`` tensor) the scores are
+    written to float32 [n_q, n_kv] first and the selection reads them back.
+    """
     torch = _torch()
     n_q, d = q_idx.shape
     n_kv = k_idx.shape[0]
     _check_idx(q_idx, k_idx)
-    if scores is None:
-        scores = torch.empty((n_q, n_kv), dtype=torch.float32, device=q_idx.device)
     if out is None:
         out = torch.empty((n_q, k), dtype=torch.int32, device=q_idx.device)
+    if (keep_scores or scores is not None) and scores is None:
+        scores = torch.empty((n_q, n_kv), dtype=torch.float32, device=q_idx.device)
+    ws_ptr, ws_bytes = None, 0
+    if scores is None:
+        need = indexer_topk_workspace_bytes(n_q, n_kv, k)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q_idx.device)
+        if workspace is not None:
+            if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+                raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
     _lib.check(_lib.lib().sa_indexer_topk(q_idx.data_ptr(), k_idx.data_ptr(), n_q, n_kv, d,
-                                          int(q_offset), int(k), scores.data_ptr(),
-                                          out.data_ptr(), _stream_ptr(q_idx.device)))
+                                          int(q_offset), int(k),
+                                          scores.data_ptr() if scores is not None else None,
+                                          out.data_ptr(), ws_ptr, ws_bytes, _stream_ptr(q_idx.device)))
     return out, scores
 
 

@@ -15,10 +15,10 @@ LIB_PATH = os.path.join(_HERE, "libsa.so")
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_DEVICE = 0, 1, 2, 3
 SA_DTYPE_BF16, SA_DTYPE_F32 = 0, 1
 SA_MODE_BLOCKS, SA_MODE_GATHER = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 EXPORTED = ("sa_build_block_mask", "sa_attn_workspace_bytes", "sa_attn_fwd", "sa_indexer_scores", "sa_topk",
-            "sa_indexer_topk", "sa_merge_partial", "sa_last_error", "sa_abi_version")
+            "sa_indexer_topk_workspace", "sa_indexer_topk", "sa_merge_partial", "sa_last_error", "sa_abi_version")
 
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
@@ -104,7 +104,9 @@ def lib() -> ctypes.CDLL:
         L.sa_indexer_scores.restype = ctypes.c_int
         L.sa_topk.argtypes = [_P, _I64, _I64, _I64, _I32, _P, _P]
         L.sa_topk.restype = ctypes.c_int
-        L.sa_indexer_topk.argtypes = [_P, _P, _I64, _I64, _I32, _I64, _I32, _P, _P, _P]
+        L.sa_indexer_topk_workspace.argtypes = [_I64, _I64, _I32]
+        L.sa_indexer_topk_workspace.restype = ctypes.c_size_t
+        L.sa_indexer_topk.argtypes = [_P, _P, _I64, _I64, _I32, _I64, _I32, _P, _P, _P, ctypes.c_size_t, _P]
         L.sa_indexer_topk.restype = ctypes.c_int
         L.sa_merge_partial.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I32, ctypes.POINTER(_I64),
                                        ctypes.POINTER(_I64), _I32, _I64, _I64, _P]

@@ -319,7 +319,7 @@ static sa_status check_indexer(const void* q_idx, const void* k_idx, int64_t n_q
     if (n_q < 0 || n_kv < 0 || q_offset < 0) return fail(SA_ERR_INVALID_ARG, "negative size or offset");
     if (n_kv > kI32Max || q_offset + n_q > kI32Max) return fail(SA_ERR_UNSUPPORTED, "sizes must stay below 2^31");
     if (d_idx < 8 || d_idx > 256 || d_idx % 8) return fail(SA_ERR_UNSUPPORTED, "d_idx must be a multiple of 8 in [8, 256]");
-    if (n_q > 0 && n_kv > 0 && (!q_idx || !k_idx || !scores)) return fail(SA_ERR_INVALID_ARG, "NULL pointer");
+    if (n_q > 0 && n_kv > 0 && (!q_idx || !k_idx)) return fail(SA_ERR_INVALID_ARG, "NULL pointer");
     if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(scores))
         return fail(SA_ERR_INVALID_ARG, "q_idx/k_idx/scores must be 16-byte aligned");
     return SA_OK;
@@ -343,6 +343,7 @@ sa_status sa_indexer_scores(const void* q_idx, const void* k_idx, int64_t n_q, i
     try {
         sa_status st = check_indexer(q_idx, k_idx, n_q, n_kv, d_idx, q_offset, scores);
         if (st != SA_OK) return st;
+        if (n_q > 0 && n_kv > 0 && !scores) return fail(SA_ERR_INVALID_ARG, "scores is NULL");
         if (n_q == 0 || n_kv == 0) return ok();
         return launched(sa::launch_indexer_scores((const uint16_t*)q_idx, (const uint16_t*)k_idx, (int32_t)n_q,
                                                   (int32_t)n_kv, d_idx, (int32_t)q_offset, scores,
@@ -368,24 +369,57 @@ sa_status sa_topk(const float* scores, int64_t n_q, int64_t n_kv, int64_t q_offs
     }
 }
 
+size_t sa_indexer_topk_workspace(int64_t n_q, int64_t n_kv, int32_t topk)
+{
+    sa::StreamTopkLayout L;
+    if (topk < 1 || topk > 4096 || !sa::stream_topk_layout(n_q, n_kv, L)) return 0;
+    return (size_t)L.total;
+}
+
 sa_status sa_indexer_topk(const void* q_idx, const void* k_idx, int64_t n_q, int64_t n_kv, int32_t d_idx,
-                          int64_t q_offset, int32_t topk, float* scores, int32_t* idx_out, void* stream)
+                          int64_t q_offset, int32_t topk, float* scores_out, int32_t* idx_out, void* workspace,
+                          size_t workspace_bytes, void* stream)
 {
     try {
-        sa_status st = check_indexer(q_idx, k_idx, n_q, n_kv, d_idx, q_offset, scores);
-        if (st != SA_OK) return st;
-        st = check_topk(scores, n_q, n_kv, q_offset, topk, idx_out);
-        if (st != SA_OK) return st;
-        if (n_q == 0) return ok();
-        if (n_kv > 0) {
-            st = launched(sa::launch_indexer_scores((const uint16_t*)q_idx, (const uint16_t*)k_idx, (int32_t)n_q,
-                                                    (int32_t)n_kv, d_idx, (int32_t)q_offset, scores,
-                                                    (hipStream_t)stream),
-                          "sa_indexer_topk");
+        if (scores_out) {
+            // two steps through the caller's score matrix
+            sa_status st = check_indexer(q_idx, k_idx, n_q, n_kv, d_idx, q_offset, scores_out);
             if (st != SA_OK) return st;
+            st = check_topk(scores_out, n_q, n_kv, q_offset, topk, idx_out);
+            if (st != SA_OK) return st;
+            if (n_q == 0) return ok();
+            if (n_kv > 0) {
+                st = launched(sa::launch_indexer_scores((const uint16_t*)q_idx, (const uint16_t*)k_idx, (int32_t)n_q,
+                                                        (int32_t)n_kv, d_idx, (int32_t)q_offset, scores_out,
+                                                        (hipStream_t)stream),
+                              "sa_indexer_topk");
+                if (st != SA_OK) return st;
+            }
+            return launched(sa::launch_topk(scores_out, (int32_t)n_q, (int32_t)n_kv, (int32_t)q_offset, topk,
+                                            idx_out, (hipStream_t)stream),
+                            "sa_indexer_topk");
         }
-        return launched(sa::launch_topk(scores, (int32_t)n_q, (int32_t)n_kv, (int32_t)q_offset, topk, idx_out,
-                                        (hipStream_t)stream),
+        // streaming: no score matrix, scratch from the caller
+        sa_status st = check_indexer(q_idx, k_idx, n_q, n_kv, d_idx, q_offset, nullptr);
+        if (st != SA_OK) return st;
+        if (topk < 1 || topk > 4096) return fail(SA_ERR_UNSUPPORTED, "topk must be in [1, 4096]");
+        if (n_kv > sa::kStreamMaxKv) return fail(SA_ERR_UNSUPPORTED, "n_kv must be <= 65536");
+        if (n_q > 0 && !idx_out) return fail(SA_ERR_INVALID_ARG, "idx_out is NULL");
+        if (n_q == 0) return ok();
+        if (n_kv == 0) return launched(sa::launch_topk(nullptr, (int32_t)n_q, 0, (int32_t)q_offset, topk, idx_out,
+                                                       (hipStream_t)stream),
+                                       "sa_indexer_topk");
+        sa::StreamTopkLayout L;
+        sa::stream_topk_layout(n_q, n_kv, L);
+        if (!workspace) return fail(SA_ERR_INVALID_ARG, "workspace is NULL (sa_indexer_topk_workspace: %lld bytes)",
+                                    (long long)L.total);
+        if (workspace_bytes < (size_t)L.total)
+            return fail(SA_ERR_INVALID_ARG, "workspace smaller than sa_indexer_topk_workspace (%lld bytes)",
+                        (long long)L.total);
+        if (((uintptr_t)workspace & 255u) != 0) return fail(SA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+        return launched(sa::launch_indexer_topk_stream((const uint16_t*)q_idx, (const uint16_t*)k_idx, (int32_t)n_q,
+                                                       (int32_t)n_kv, d_idx, (int32_t)q_offset, topk, idx_out,
+                                                       (uint8_t*)workspace, L, (hipStream_t)stream),
                         "sa_indexer_topk");
     } catch (...) {
         return fail(SA_ERR_DEVICE, "sa_indexer_topk: unexpected exception");

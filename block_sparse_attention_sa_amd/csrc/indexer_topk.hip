@@ -52,26 +52,21 @@ __device__ __forceinline__ void load_row64(const uint16_t* row, bool ok, int nd,
     }
 }
 
-__global__ void __launch_bounds__(64 * XW, 2)
-indexer_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict__ ki, int32_t n_q,
-               int32_t n_kv, int32_t d, int32_t q_offset, float* __restrict__ scores)
+// The chain over the tiles [s_begin, s_end) (64 keys each) for the wave's 32
+// query rows r0 .. r0 + 31: emit(s0, acc) receives each tile's 32 x 64
+// scores in the layout above.  Key rows past n_kv read as row n_kv - 1 (the
+// caller drops those entries).
+template <class Emit>
+__device__ __forceinline__ void indexer_walk(const uint16_t* __restrict__ qi, const uint16_t* __restrict__ ki,
+                                             int32_t n_q, int32_t n_kv, int32_t d, int r0, int s_begin,
+                                             int s_end, Emit&& emit)
 {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int hh = lane >> 5, col = lane & 31;
-    const int r0 = (blockIdx.y * XW + w) * XQ;
-    if (r0 >= n_q) return;  // no barriers in this kernel: waves leave on their own
-    const int s_begin = blockIdx.x * XKC;
-    const int t_max = q_offset + min(r0 + XQ, n_q) - 1;  // last query position of the wave
-    const int s_end = min(min(s_begin + XKC, n_kv), t_max + 1);
-    if (s_begin >= s_end) return;
-
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 31;
     const int r = r0 + col;  // this lane's query
     const bool r_ok = r < n_q;
-    const int t = q_offset + r;
     const uint16_t* qrow = qi + (int64_t)(r_ok ? r : 0) * d;
-    float* orow = scores + (int64_t)(r_ok ? r : 0) * n_kv;
     const int nch = (d + 63) >> 6;
-    const bool vec_ok = (n_kv & 3) == 0;
 
     uint32_t qp[32], kp[32], kn[32];
     float qv[64];
@@ -114,7 +109,31 @@ indexer_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict__ ki,
                 }
             }
         }
-        if (!r_ok) continue;
+        emit(s0, acc);
+    }
+}
+
+__global__ void __launch_bounds__(64 * XW, 2)
+indexer_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict__ ki, int32_t n_q,
+               int32_t n_kv, int32_t d, int32_t q_offset, float* __restrict__ scores)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int hh = lane >> 5, col = lane & 31;
+    const int r0 = (blockIdx.y * XW + w) * XQ;
+    if (r0 >= n_q) return;  // no barriers in this kernel: waves leave on their own
+    const int s_begin = blockIdx.x * XKC;
+    const int t_max = q_offset + min(r0 + XQ, n_q) - 1;  // last query position of the wave
+    const int s_end = min(min(s_begin + XKC, n_kv), t_max + 1);
+    if (s_begin >= s_end) return;
+
+    const int r = r0 + col;  // this lane's query
+    const bool r_ok = r < n_q;
+    const int t = q_offset + r;
+    float* orow = scores + (int64_t)(r_ok ? r : 0) * n_kv;
+    const bool vec_ok = (n_kv & 3) == 0;
+
+    indexer_walk(qi, ki, n_q, n_kv, d, r0, s_begin, s_end, [&](int s0, const f32x32& acc) {
+        if (!r_ok) return;
         // entries s <= t of this query row, s < n_kv
 #pragma unroll
         for (int b = 0; b < 2; ++b)
@@ -132,7 +151,7 @@ indexer_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict__ ki,
                     if (sk + 3 <= t && sk + 3 < n_kv) orow[sk + 3] = v3;
                 }
             }
-    }
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -210,10 +229,26 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total)
     return x - v + before;
 }
 
+// Maximum over the KTH threads (every thread gets it).
+__device__ uint32_t block_max(uint32_t v, uint32_t* wmax)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor(v, off, 64));
+    if (lane == 0) wmax[w] = v;
+    __syncthreads();
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < KWAVES; ++i) m = max(m, wmax[i]);
+    __syncthreads();
+    return m;
+}
+
 // For ranks r0, r1 (1-based from the largest digit down; 0 = not asked), the
 // digit whose bin holds the rank and the rank left inside that bin, into
 // state[0..1] and state[2..3].  Ends with a barrier.
-__device__ void find_digits(TopkLds& L, uint32_t r0, uint32_t r1)
+template <class Lds>
+__device__ void find_digits(Lds& L, uint32_t r0, uint32_t r1)
 {
     const int tid = threadIdx.x;
     // thread t owns bins KBINS-1-8t down to KBINS-8-8t
@@ -253,8 +288,8 @@ __device__ __forceinline__ void zero_words(uint32_t* p, int n)
 // Exact selection: among the keys v (of `width` significant bits) that
 // for_each(f) hands to f, the r-th largest.  Returns its value and how many
 // of the keys equal to it rank within the first r.
-template <class ForEach>
-__device__ void radix_select(TopkLds& L, ForEach&& for_each, uint32_t width, uint32_t r,
+template <class Lds, class ForEach>
+__device__ void radix_select(Lds& L, ForEach&& for_each, uint32_t width, uint32_t r,
                              uint32_t& value, uint32_t& rem)
 {
     uint32_t P = 0, done = 0;
@@ -276,6 +311,64 @@ __device__ void radix_select(TopkLds& L, ForEach&& for_each, uint32_t width, uin
         done += nb;
     }
     value = P;
+}
+
+// The selected keys leave in ascending position order: every position whose
+// bit is set in `sel`, plus the first need_eq positions (lowest first) whose
+// bit is set in `tie` (bitmaps of KMAXN positions).  Thread t owns positions
+// [256t, 256t + 256); `stage` (k words of LDS) orders the output so the
+// stores are coalesced.
+template <class Lds>
+__device__ void emit_ascending(Lds& L, const uint32_t* sel, const uint32_t* tie, uint32_t need_eq, int32_t k,
+                               uint32_t* stage, int32_t* __restrict__ out)
+{
+    const int tid = threadIdx.x;
+    uint32_t sw[8], tw[8];
+    {
+        const uint4 s0 = *reinterpret_cast<const uint4*>(&sel[8 * tid]);
+        const uint4 s1 = *reinterpret_cast<const uint4*>(&sel[8 * tid + 4]);
+        const uint4 t0 = *reinterpret_cast<const uint4*>(&tie[8 * tid]);
+        const uint4 t1 = *reinterpret_cast<const uint4*>(&tie[8 * tid + 4]);
+        sw[0] = s0.x; sw[1] = s0.y; sw[2] = s0.z; sw[3] = s0.w;
+        sw[4] = s1.x; sw[5] = s1.y; sw[6] = s1.z; sw[7] = s1.w;
+        tw[0] = t0.x; tw[1] = t0.y; tw[2] = t0.z; tw[3] = t0.w;
+        tw[4] = t1.x; tw[5] = t1.y; tw[6] = t1.z; tw[7] = t1.w;
+    }
+    uint32_t n_gt = 0, n_eq = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        n_gt += (uint32_t)__popc(sw[i]);
+        n_eq += (uint32_t)__popc(tw[i]);
+    }
+    // one scan of (n_gt << 16 | n_eq): neither prefix reaches 2^16.  Ties are
+    // taken in position order, so the ties taken before this thread number
+    // min(need_eq, ties before it).
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan((n_gt << 16) | n_eq, L.wsum, &tot);
+    // (No conditional unsigned difference here: written as need_eq > e ?
+    // need_eq - e : 0, the subtraction gets hoisted with a no-wrap flag and
+    // the minimum below folds as if need_eq >= e always held.)
+    const uint32_t eq_before = ex & 0xFFFFu;
+    const uint32_t taken_before = min(need_eq, eq_before);
+    uint32_t take = min(need_eq, eq_before + n_eq) - taken_before;
+    uint32_t pos = (ex >> 16) + taken_before;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t m = sw[i], te = tw[i];
+        while (te && take) {  // lowest-index ties first
+            const uint32_t low = te & (0u - te);
+            m |= low;
+            te ^= low;
+            --take;
+        }
+        while (m) {
+            if (pos < (uint32_t)k) stage[pos] = (uint32_t)(256 * tid + 32 * i + __builtin_ctz(m));
+            ++pos;
+            m &= m - 1u;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < k; e += KTH) out[e] = (int32_t)stage[e];
 }
 
 template <bool ALIGNED>
@@ -489,54 +582,391 @@ topk_kernel(const float* __restrict__ scores, int32_t n_q, int32_t n_kv, int32_t
     }
     __syncthreads();
 
-    // ---- emit: thread t owns positions [256t, 256t + 256) ----
-    uint32_t sw[8], tw[8];
-    {
-        const uint4 s0 = *reinterpret_cast<const uint4*>(&L.sel[8 * tid]);
-        const uint4 s1 = *reinterpret_cast<const uint4*>(&L.sel[8 * tid + 4]);
-        const uint4 t0 = *reinterpret_cast<const uint4*>(&tie[8 * tid]);
-        const uint4 t1 = *reinterpret_cast<const uint4*>(&tie[8 * tid + 4]);
-        sw[0] = s0.x; sw[1] = s0.y; sw[2] = s0.z; sw[3] = s0.w;
-        sw[4] = s1.x; sw[5] = s1.y; sw[6] = s1.z; sw[7] = s1.w;
-        tw[0] = t0.x; tw[1] = t0.y; tw[2] = t0.z; tw[3] = t0.w;
-        tw[4] = t1.x; tw[5] = t1.y; tw[6] = t1.z; tw[7] = t1.w;
-    }
-    uint32_t n_gt = 0, n_eq = 0;
+    emit_ascending(L, L.sel, tie, need_eq, k, L.mid, out);
+}
+
+// ---------------------------------------------------------------------------
+// Streaming indexer + top-k: the selection without the score matrix.
+//
+// 1. stream_sample_kernel scores one 64-key tile in every SPERIOD keys (a
+//    1/32 sample spread over the row) on the same matrix-core chain and
+//    stores their order keys (0 where a key is not a candidate).
+// 2. stream_bracket_kernel picks, per query row, the order key LO of the
+//    sample rank rho + 6 sqrt(rho) + 8, rho = k * sample size / candidates:
+//    LO sits well below the k-th largest candidate, so about 1.9 k
+//    candidates have keys >= LO.  LO = 0 marks a row that goes the direct
+//    way in step 4 (too few candidates for a sample).
+// 3. stream_filter_kernel walks every candidate like indexer_kernel and, in
+//    place of the score store, keeps the (key, position) of every candidate
+//    with key >= LO in a region of SCAP slots per (row, 512-key chunk) that
+//    the two half-waves holding the row fill from either end, counting on
+//    without storing once their counts add up to more than SCAP.
+// 4. stream_select_kernel, one workgroup per row: if no region overflowed
+//    and at least k candidates were kept, every candidate with key < LO
+//    ranks below the k-th kept one, so the exact selection among the kept
+//    keys is the row's top-k: one 11-bit histogram pass finds the bin of the
+//    k-th key and the few keys of that bin are ranked directly (more radix
+//    passes only when the bin is crowded); each thread then emits its
+//    region's selected positions, ties taken in position order.
+// 5. stream_direct_kernel takes the other rows -- an adversarial order that
+//    fooled the sample: their scores are recomputed with the same float32
+//    chain (vector FMA in dimension order) at each pass of an exact
+//    selection over the whole row.  Every other row's workgroup exits at once.
+constexpr int SPERIOD = kStreamPeriod;  // keys per sample tile
+constexpr int SCAP = kStreamCap;        // kept slots per (row, chunk)
+static_assert(kStreamChunk == XKC, "filter regions are the indexer's key chunks");
+static_assert(SCAP % 8 == 0, "regions are loaded in 16-byte pieces");
+static_assert(64 * (KMAXN / SPERIOD) <= KTH * 8, "sample row fits the bracket kernel's registers");
+
+__global__ void __launch_bounds__(64 * XW, 2)
+stream_sample_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict__ ki, int32_t n_q, int32_t n_kv,
+                     int32_t d, int32_t q_offset, uint32_t* __restrict__ samp, int32_t s_max)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int hh = lane >> 5, col = lane & 31;
+    const int r0 = (blockIdx.y * XW + w) * XQ;
+    if (r0 >= n_q) return;
+    const int s_begin = blockIdx.x * SPERIOD;
+    const int r = r0 + col;
+    const bool r_ok = r < n_q;
+    const int t = q_offset + r;
+    uint32_t* srow = samp + (int64_t)(r_ok ? r : 0) * s_max + blockIdx.x * XT;
+    auto store = [&](int s0, const f32x32* acc) {
+        if (!r_ok) return;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        n_gt += (uint32_t)__popc(sw[i]);
-        n_eq += (uint32_t)__popc(tw[i]);
-    }
-    // one scan of (n_gt << 16 | n_eq): neither prefix reaches 2^16.  Ties are
-    // taken in position order, so the ties taken before this thread number
-    // min(need_eq, ties before it).
-    uint32_t tot;
-    const uint32_t ex = block_excl_scan((n_gt << 16) | n_eq, L.wsum, &tot);
-    // (No conditional unsigned difference here: written as need_eq > e ?
-    // need_eq - e : 0, the subtraction gets hoisted with a no-wrap flag and
-    // the minimum below folds as if need_eq >= e always held.)
-    const uint32_t eq_before = ex & 0xFFFFu;
-    const uint32_t taken_before = min(need_eq, eq_before);
-    uint32_t take = min(need_eq, eq_before + n_eq) - taken_before;
-    uint32_t pos = (ex >> 16) + taken_before;
-    uint32_t* stage = L.mid;
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint32_t m = sw[i], te = tw[i];
-        while (te && take) {  // lowest-index ties first
-            const uint32_t low = te & (0u - te);
-            m |= low;
-            te ^= low;
-            --take;
+            for (int m = 0; m < 4; ++m) {
+                const int j = 32 * b + 8 * m + 4 * hh;
+                uint32_t u[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int sk = s0 + j + i;
+                    u[i] = (acc && sk <= t && sk < n_kv) ? order_key((*acc)[16 * b + 4 * m + i]) : 0u;
+                }
+                *reinterpret_cast<uint4*>(srow + j) = make_uint4(u[0], u[1], u[2], u[3]);
+            }
+    };
+    if (s_begin > q_offset + min(r0 + XQ, n_q) - 1) {  // no candidate of the wave in this tile
+        store(s_begin, nullptr);
+        return;
+    }
+    indexer_walk(qi, ki, n_q, n_kv, d, r0, s_begin, s_begin + XT,
+                 [&](int s0, const f32x32& acc) { store(s0, &acc); });
+}
+
+struct __attribute__((aligned(16))) BracketLds {
+    uint32_t hist[KBINS];
+    uint32_t wsum[KWAVES];
+    uint32_t state[4];
+};
+
+__global__ void __launch_bounds__(KTH)
+stream_bracket_kernel(const uint32_t* __restrict__ samp, int32_t s_max, int32_t n_kv, int32_t q_offset, int32_t k,
+                      uint32_t* __restrict__ lo)
+{
+    __shared__ BracketLds L;
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const int64_t t = (int64_t)q_offset + r;
+    const int n_cand = (int)min((int64_t)n_kv, t + 1);
+    // sample positions among the candidates: the first XT of every SPERIOD
+    const int s_n = (n_cand / SPERIOD) * XT + min(n_cand % SPERIOD, XT);
+    const float rho = (float)k * (float)s_n / (float)max(n_cand, 1);
+    const float frank = ceilf(rho + 6.0f * sqrtf(rho) + 8.0f);
+    if (n_cand <= k || frank > (float)s_n) {
+        if (tid == 0) lo[r] = 0u;  // selected directly
+        return;
+    }
+    constexpr int PER = 8;  // s_max <= 64 * 32 = KTH * PER
+    uint32_t v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int j = tid + KTH * i;
+        v[i] = j < s_max ? samp[(int64_t)r * s_max + j] : 0u;
+    }
+    auto each = [&](auto&& f) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) f(v[i]);
+    };
+    uint32_t value, rem;
+    radix_select(L, each, 32u, (uint32_t)frank, value, rem);
+    // >= 1, since 0 is no float's key; a NaN threshold (so many NaN scores) goes
+    // the direct way
+    if (tid == 0) lo[r] = value == 0xFFFFFFFFu ? 0u : value;
+}
+
+// The float whose order key is `key` (key < 0xFFFFFFFF, i.e. not a NaN):
+// for every float v that is not a NaN, order_key(v) >= key exactly when
+// v >= key_float(key), and a NaN v passes !(v < key_float(key)) as well.
+__device__ __forceinline__ float key_float(uint32_t key)
+{
+    return __uint_as_float(key >= 0x80000000u ? key & 0x7FFFFFFFu : ~key);
+}
+
+__global__ void __launch_bounds__(64 * XW, 2)
+stream_filter_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict__ ki, int32_t n_q, int32_t n_kv,
+                     int32_t d, int32_t q_offset, const uint32_t* __restrict__ lo, int32_t nchunk,
+                     uint32_t* __restrict__ ccnt, uint32_t* __restrict__ ckey, uint16_t* __restrict__ cpos)
+{
+    // a lane's 32 scores of the current tile, so that the few kept ones can be
+    // fetched by a per-lane index: [wave][score group of 4][lane][4]
+    __shared__ float4 stage[XW][8][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int hh = lane >> 5, col = lane & 31;
+    const int r0 = (blockIdx.y * XW + w) * XQ;
+    if (r0 >= n_q) return;
+    const int s_begin = blockIdx.x * XKC;
+    const int t_max = q_offset + min(r0 + XQ, n_q) - 1;
+    const int s_end = min(min(s_begin + XKC, n_kv), t_max + 1);
+    if (s_begin >= s_end) return;  // no row of the wave reads this chunk's counts
+    const int t_min = q_offset + r0;  // first query position of the wave
+
+    const int r = r0 + col;
+    const bool r_ok = r < n_q;
+    const int t = q_offset + r;
+    const uint32_t lo_r = r_ok ? lo[r] : 0u;
+    const float lo_f = key_float(lo_r);
+    // the region of (row, chunk): half-wave 0 fills it from the front, half-wave
+    // 1 from the back; it overflows when the two counts add up to more than SCAP
+    const int64_t region = (int64_t)(r_ok ? r : 0) * nchunk + blockIdx.x;
+    uint32_t* kdst = ckey + region * SCAP;
+    uint16_t* pdst = cpos + region * SCAP;
+    const float* my = reinterpret_cast<const float*>(&stage[w][0][lane]);  // score e at my[(e >> 2) * 256 + (e & 3)]
+    uint32_t cnt = 0;
+    indexer_walk(qi, ki, n_q, n_kv, d, r0, s_begin, s_end, [&](int s0, const f32x32& acc) {
+        // bit e = 16*b + 4*m + i: score e (key s0 + 32b + 8m + 4hh + i) is kept
+        uint32_t keep = 0;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) keep |= (!(acc[e] < lo_f) ? 1u : 0u) << e;
+        if (s0 + XT - 1 > min(t_min, n_kv - 1)) {  // a tile past some row's last candidate
+            uint32_t ok = 0;
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+                const int sk = s0 + 32 * (e >> 4) + 8 * ((e >> 2) & 3) + 4 * hh + (e & 3);
+                ok |= (sk <= t && sk < n_kv ? 1u : 0u) << e;
+            }
+            keep &= ok;
         }
-        while (m) {
-            if (pos < (uint32_t)k) stage[pos] = (uint32_t)(256 * tid + 32 * i + __builtin_ctz(m));
-            ++pos;
-            m &= m - 1u;
+        if (lo_r == 0u) keep = 0;  // row selected directly (or not a row)
+        if (!keep) return;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) stage[w][g][lane] = make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+        while (keep) {
+            const int e = __builtin_ctz(keep);
+            keep &= keep - 1u;
+            if (cnt < (uint32_t)SCAP) {
+                const int slot = hh ? SCAP - 1 - (int)cnt : (int)cnt;
+                kdst[slot] = order_key(my[(e >> 2) * 256 + (e & 3)]);
+                pdst[slot] = (uint16_t)(s0 - s_begin + 32 * (e >> 4) + 8 * ((e >> 2) & 3) + 4 * hh + (e & 3));
+            }
+            ++cnt;
+        }
+    });
+    if (r_ok) ccnt[region * 2 + hh] = cnt;
+}
+
+constexpr int SKC = 6144;   // kept candidates a row may carry into the select
+constexpr int SMALL = 256;  // keys in the rank's histogram bin that are ranked directly
+
+struct __attribute__((aligned(16))) SelectLds {
+    uint32_t sel[KWORDS];   // bit p: candidate p is selected
+    uint32_t hist[KBINS];   // digit histogram; the keys of the rank's bin; tie bitmap
+    uint32_t key[SKC];      // kept keys - LO; output staging
+    uint32_t wsum[KWAVES];
+    uint32_t wmax[KWAVES];
+    uint32_t state[4];
+};
+
+// Exact top-k of row r from its kept candidates.  A row that cannot be
+// selected this way (threshold 0, a region overflowed, fewer than k or more
+// than SKC candidates kept) gets lo[r] = 0 and is left to
+// stream_direct_kernel.
+__global__ void __launch_bounds__(KTH)
+stream_select_kernel(int32_t n_kv, int32_t q_offset, int32_t k, uint32_t* __restrict__ lo, int32_t nchunk,
+                     const uint32_t* __restrict__ ccnt, const uint32_t* __restrict__ ckey,
+                     const uint16_t* __restrict__ cpos, int32_t* __restrict__ idx_out)
+{
+    __shared__ SelectLds L;
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const int64_t t = (int64_t)q_offset + r;
+    const int n_cand = (int)min((int64_t)n_kv, t + 1);
+    int32_t* out = idx_out + (int64_t)r * k;
+    if (n_cand <= k) {
+        for (int e = tid; e < k; e += KTH) out[e] = e < n_cand ? e : -1;
+        return;
+    }
+    const uint32_t lo_r = lo[r];
+    // thread tid owns region tid, the row's 512-key chunk tid
+    const int n_reg = (n_cand + XKC - 1) / XKC;  // <= KTH
+    const bool mine = lo_r != 0u && tid < n_reg;
+    const int64_t reg = (int64_t)r * nchunk + tid;
+    uint32_t c0 = 0, c1 = 0;
+    if (mine) {
+        c0 = ccnt[2 * reg];
+        c1 = ccnt[2 * reg + 1];
+    }
+    const bool ovf = __syncthreads_or(c0 + c1 > (uint32_t)SCAP) != 0;
+    uint32_t total;
+    const uint32_t before = block_excl_scan(ovf ? 0u : c0 + c1, L.wsum, &total);
+    if (lo_r == 0u || ovf || total < (uint32_t)k || total > (uint32_t)SKC) {
+        if (tid == 0) lo[r] = 0u;
+        return;
+    }
+    // ---- the owner loads all slots of its region (independent 16-byte loads)
+    // and keeps them in registers; the filled ones -- the first c0 and the
+    // last c1 -- go to LDS as keys relative to LO ----
+    u32x4 kw[SCAP / 4], pw[SCAP / 8];
+    uint32_t fm[3];  // filled slots, 32 per word
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+        auto below = [](int64_t n) { return n <= 0 ? 0u : (n >= 32 ? 0xFFFFFFFFu : (1u << n) - 1u); };
+        const int64_t base = 32 * x;
+        fm[x] = mine ? (below((int64_t)c0 - base) |
+                        (~below((int64_t)SCAP - (int64_t)c1 - base) & below((int64_t)SCAP - base)))
+                     : 0u;
+    }
+    auto filled = [&](int j) { return ((fm[j >> 5] >> (j & 31)) & 1u) != 0u; };
+    uint32_t kmax = 0;
+    if (mine) {
+        const u32x4* ks = reinterpret_cast<const u32x4*>(ckey + reg * SCAP);
+        const u32x4* ps = reinterpret_cast<const u32x4*>(cpos + reg * SCAP);
+#pragma unroll
+        for (int i = 0; i < SCAP / 4; ++i) kw[i] = ks[i];
+#pragma unroll
+        for (int i = 0; i < SCAP / 8; ++i) pw[i] = ps[i];
+        uint32_t n = before;
+#pragma unroll
+        for (int j = 0; j < SCAP; ++j) {
+            if (filled(j)) {
+                const uint32_t u = kw[j >> 2][j & 3] - lo_r;
+                L.key[n++] = u;
+                kmax = max(kmax, u);
+            }
+        }
+    }
+    // The kept keys lie in [LO, max]: selecting on key - LO with only the bits
+    // that span needs spreads the digits over the histogram bins.
+    kmax = block_max(kmax, L.wmax);  // (its barriers publish the keys)
+    const uint32_t width = kmax == 0u ? 0u : 32u - (uint32_t)__clz(kmax);
+    auto kept = [&](auto&& f) {
+        for (uint32_t j = tid; j < total; j += KTH) f(L.key[j]);
+    };
+    // ---- T (relative) and how many keys equal to it are taken ----
+    uint32_t T, need_eq;
+    const uint32_t nb = min(11u, width), shift = width - nb;
+    zero_words(L.hist, KBINS);
+    __syncthreads();
+    kept([&](uint32_t v) { atomicAdd(&L.hist[v >> shift], 1u); });
+    __syncthreads();
+    find_digits(L, (uint32_t)k, 0u);
+    const uint32_t bin = L.state[0], rem = L.state[1];
+    const uint32_t m = L.hist[bin];
+    __syncthreads();
+    if (m <= (uint32_t)SMALL && shift > 0u) {
+        // rank the bin's keys directly: the rem-th largest of them is T
+        uint32_t* bk = L.hist;
+        if (tid == 0) L.state[2] = 0u;
+        __syncthreads();
+        kept([&](uint32_t v) {
+            if ((v >> shift) == bin) bk[atomicAdd(&L.state[2], 1u)] = v;
+        });
+        __syncthreads();
+        if ((uint32_t)tid < m) {
+            const uint32_t x = bk[tid];
+            uint32_t gt = 0, ge = 0;
+            for (uint32_t j = 0; j < m; ++j) {
+                const uint32_t y = bk[j];
+                gt += y > x ? 1u : 0u;
+                ge += y >= x ? 1u : 0u;
+            }
+            if (gt < rem && rem <= ge) {  // x is T (every thread holding T writes the same)
+                L.state[0] = x;
+                L.state[1] = rem - gt;
+            }
+        }
+        __syncthreads();
+        T = L.state[0];
+        need_eq = L.state[1];
+    } else {
+        radix_select(L, kept, width, (uint32_t)k, T, need_eq);
+    }
+    // ---- selected (> T) and tied (== T) positions as bitmaps, then emitted
+    // in ascending order ----
+    uint32_t* tie = L.hist;
+    __syncthreads();
+    zero_words(L.sel, KWORDS);
+    zero_words(tie, KWORDS);
+    __syncthreads();
+    if (mine) {
+        const uint32_t pbase = (uint32_t)tid * XKC;
+#pragma unroll
+        for (int j = 0; j < SCAP; ++j) {
+            if (filled(j)) {
+                const uint32_t u = kw[j >> 2][j & 3] - lo_r;
+                const uint32_t w2 = pw[j >> 3][(j >> 1) & 3];
+                const uint32_t p = pbase + ((j & 1) ? w2 >> 16 : w2 & 0xFFFFu);
+                if (u > T) atomicOr(&L.sel[p >> 5], 1u << (p & 31));
+                else if (u == T) atomicOr(&tie[p >> 5], 1u << (p & 31));
+            }
         }
     }
     __syncthreads();
-    for (int e = tid; e < k; e += KTH) out[e] = (int32_t)stage[e];
+    emit_ascending(L, L.sel, tie, need_eq, k, L.key, out);
+}
+
+// The rows stream_select_kernel left (lo[r] == 0 with more than k
+// candidates): the scores are recomputed with the indexer's float32 chain
+// (vector FMA in dimension order, the same bits) at each pass of an exact
+// selection over the whole row.
+__global__ void __launch_bounds__(KTH)
+stream_direct_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict__ ki, int32_t n_kv, int32_t d,
+                     int32_t q_offset, int32_t k, const uint32_t* __restrict__ lo, int32_t* __restrict__ idx_out)
+{
+    __shared__ TopkLds L;
+    __shared__ float qf[256];
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int64_t t = (int64_t)q_offset + r;
+    const int n_cand = (int)min((int64_t)n_kv, t + 1);
+    if (n_cand <= k || lo[r] != 0u) return;
+    for (int i = tid; i < d; i += KTH) qf[i] = __uint_as_float((uint32_t)qi[(int64_t)r * d + i] << 16);
+    __syncthreads();
+    auto score_key = [&](int p) {
+        const uint16_t* kr = ki + (int64_t)p * d;
+        float acc = 0.f;
+        for (int i = 0; i < d; i += 8) {
+            const u32x4 kw = *reinterpret_cast<const u32x4*>(kr + i);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                acc = __builtin_fmaf(qf[i + 2 * x], __uint_as_float(kw[x] << 16), acc);
+                acc = __builtin_fmaf(qf[i + 2 * x + 1], __uint_as_float(kw[x] & 0xFFFF0000u), acc);
+            }
+        }
+        return order_key(acc);
+    };
+    auto all = [&](auto&& f) {
+        for (int p = tid; p < n_cand; p += KTH) f(score_key(p));
+    };
+    uint32_t T, need_eq;
+    radix_select(L, all, 32u, (uint32_t)k, T, need_eq);
+    uint32_t* tie = L.hist;
+    // every bitmap word is written once: 64 positions per wave step
+    for (int p0 = 0; p0 < KMAXN; p0 += KTH) {
+        const int p = p0 + tid;
+        const bool valid = p < n_cand;
+        const uint32_t u = valid ? score_key(p) : 0u;
+        const uint64_t g = __ballot(valid && u > T);
+        const uint64_t e = __ballot(valid && u == T);
+        if (lane == 0) {
+            const int wd = (p0 + 64 * w) >> 5;
+            L.sel[wd] = (uint32_t)g;
+            L.sel[wd + 1] = (uint32_t)(g >> 32);
+            tie[wd] = (uint32_t)e;
+            tie[wd + 1] = (uint32_t)(e >> 32);
+        }
+    }
+    __syncthreads();
+    emit_ascending(L, L.sel, tie, need_eq, k, L.mid, idx_out + (int64_t)r * k);
 }
 
 }  // namespace
@@ -560,6 +990,33 @@ hipError_t launch_topk(const float* scores, int32_t n_q, int32_t n_kv, int32_t q
     else
         hipLaunchKernelGGL(topk_kernel<false>, dim3(n_q), dim3(KTH), 0, stream, scores, n_q, n_kv, q_offset,
                            topk, idx_out);
+    return hipGetLastError();
+}
+
+}  // namespace sa
+
+namespace sa {
+
+hipError_t launch_indexer_topk_stream(const uint16_t* q_idx, const uint16_t* k_idx, int32_t n_q, int32_t n_kv,
+                                      int32_t d_idx, int32_t q_offset, int32_t topk, int32_t* idx_out,
+                                      uint8_t* ws, const StreamTopkLayout& L, hipStream_t stream)
+{
+    uint32_t* samp = reinterpret_cast<uint32_t*>(ws + L.samp);
+    uint32_t* lo = reinterpret_cast<uint32_t*>(ws + L.lo);
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + L.cnt);
+    uint32_t* key = reinterpret_cast<uint32_t*>(ws + L.key);
+    uint16_t* pos = reinterpret_cast<uint16_t*>(ws + L.pos);
+    const unsigned qgroups = (unsigned)((n_q + XQ * XW - 1) / (XQ * XW));
+    hipLaunchKernelGGL(stream_sample_kernel, dim3((unsigned)(L.s_max / XT), qgroups), dim3(64 * XW), 0, stream, q_idx,
+                       k_idx, n_q, n_kv, d_idx, q_offset, samp, L.s_max);
+    hipLaunchKernelGGL(stream_bracket_kernel, dim3((unsigned)n_q), dim3(KTH), 0, stream, samp, L.s_max, n_kv, q_offset,
+                       topk, lo);
+    hipLaunchKernelGGL(stream_filter_kernel, dim3((unsigned)L.nchunk, qgroups), dim3(64 * XW), 0, stream, q_idx, k_idx,
+                       n_q, n_kv, d_idx, q_offset, lo, L.nchunk, cnt, key, pos);
+    hipLaunchKernelGGL(stream_select_kernel, dim3((unsigned)n_q), dim3(KTH), 0, stream, n_kv, q_offset, topk, lo,
+                       L.nchunk, cnt, key, pos, idx_out);
+    hipLaunchKernelGGL(stream_direct_kernel, dim3((unsigned)n_q), dim3(KTH), 0, stream, q_idx, k_idx, n_kv, d_idx,
+                       q_offset, topk, lo, idx_out);
     return hipGetLastError();
 }
 

@@ -244,6 +244,41 @@ struct MergeParams {
 };
 hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t stream);
 
+// Streaming indexer + top-k (indexer_topk.hip): no score matrix.  Scratch
+// layout (byte offsets, each 256-byte aligned):
+//   samp  uint32 [n_q][s_max]            order keys of the sampled tiles
+//   lo    uint32 [n_q]                   per-row keep threshold (0: direct)
+//   cnt   uint32 [n_q][nchunk][2]        kept candidates per (row, chunk) and half-wave
+//   key   uint32 [n_q][nchunk][cap]      their order keys (half-wave 0 from the
+//                                        front, half-wave 1 from the back)
+//   pos   uint16 [n_q][nchunk][cap]      their positions within the chunk
+constexpr int kStreamPeriod = 2048;  // one 64-key sample tile per this many keys
+constexpr int kStreamChunk = 512;    // keys per filter chunk
+constexpr int kStreamCap = 72;       // kept slots per (row, chunk)
+constexpr int64_t kStreamMaxKv = 65536;
+struct StreamTopkLayout {
+    int32_t s_max, nchunk;
+    int64_t samp, lo, cnt, key, pos, total;
+};
+inline bool stream_topk_layout(int64_t n_q, int64_t n_kv, StreamTopkLayout& L)
+{
+    if (n_q <= 0 || n_kv <= 0 || n_kv > kStreamMaxKv) return false;
+    auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
+    L.s_max = (int32_t)(64 * ((n_kv + kStreamPeriod - 1) / kStreamPeriod));
+    L.nchunk = (int32_t)((n_kv + kStreamChunk - 1) / kStreamChunk);
+    const int64_t regions = n_q * L.nchunk;
+    L.samp = 0;
+    L.lo = up(L.samp + n_q * L.s_max * 4);
+    L.cnt = up(L.lo + n_q * 4);
+    L.key = up(L.cnt + regions * 2 * 4);
+    L.pos = up(L.key + regions * kStreamCap * 4);
+    L.total = up(L.pos + regions * kStreamCap * 2);
+    return true;
+}
+hipError_t launch_indexer_topk_stream(const uint16_t* q_idx, const uint16_t* k_idx, int32_t n_q, int32_t n_kv,
+                                      int32_t d_idx, int32_t q_offset, int32_t topk, int32_t* idx_out,
+                                      uint8_t* ws, const StreamTopkLayout& L, hipStream_t stream);
+
 hipError_t launch_indexer_scores(const uint16_t* q_idx, const uint16_t* k_idx, int32_t n_q,
                                  int32_t n_kv, int32_t d_idx, int32_t q_offset, float* scores,
                                  hipStream_t stream);

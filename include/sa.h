@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 1
+#define SA_ABI_VERSION 2
 
 typedef enum sa_status {
     SA_OK = 0,
@@ -225,11 +225,41 @@ sa_status sa_indexer_scores(const void *q_idx, const void *k_idx, int64_t n_q, i
 sa_status sa_topk(const float *scores, int64_t n_q, int64_t n_kv, int64_t q_offset, int32_t topk,
                   int32_t *idx_out, void *stream);
 
-/* sa_indexer_topk -- sa_indexer_scores into `scores` (workspace, n_q*n_kv
- * floats, DEVICE) followed by sa_topk. */
+/*
+ * sa_indexer_topk_workspace -- bytes of DEVICE scratch that sa_indexer_topk
+ * needs when it streams (scores_out == NULL), 0 when these sizes have no
+ * streaming form (n_q <= 0, n_kv <= 0, n_kv > 65536, topk outside
+ * [1, 4096]).  At n_q = 1024, n_kv = 65536 it is about 66 MB, against 268 MB
+ * for the score matrix the two-step form writes.
+ */
+size_t sa_indexer_topk_workspace(int64_t n_q, int64_t n_kv, int32_t topk);
+
+/*
+ * sa_indexer_topk -- the indexer and the top-k of DeepSeek Sparse Attention
+ * ("Sparse Attention" glossary, section on common sparsity patterns: every
+ * earlier token is scored, the topk best are attended) in one call.  Scores
+ * and the order are exactly those of sa_indexer_scores and sa_topk, so the
+ * selection is bit for bit the same either way.
+ *
+ *   scores_out != NULL: two steps, sa_indexer_scores into scores_out (float32
+ *     [n_q, n_kv], DEVICE) followed by sa_topk; workspace is ignored.
+ *   scores_out == NULL: streaming, no score matrix.  A 1/32 sample of each
+ *     row's scores sets a threshold below the k-th best; one pass over the
+ *     keys keeps the (score, index) of every candidate above it in the
+ *     workspace; an exact selection among the kept candidates gives the
+ *     top-k.  A row whose sample misleads (an adversarial order) is selected
+ *     exactly from recomputed scores instead, so the result never depends on
+ *     the data's order, only the time does.  workspace: DEVICE scratch of at
+ *     least sa_indexer_topk_workspace(n_q, n_kv, topk) bytes, 256-byte
+ *     aligned, owned by the caller, overwritten by the call; calls sharing
+ *     one workspace must not run concurrently.
+ * idx_out int32 [n_q, topk] (DEVICE): as sa_topk.  Limits: those of
+ * sa_indexer_scores and sa_topk (d_idx a multiple of 8 in [8, 256], topk in
+ * [1, 4096], n_kv <= 65536).
+ */
 sa_status sa_indexer_topk(const void *q_idx, const void *k_idx, int64_t n_q, int64_t n_kv,
-                          int32_t d_idx, int64_t q_offset, int32_t topk, float *scores,
-                          int32_t *idx_out, void *stream);
+                          int32_t d_idx, int64_t q_offset, int32_t topk, float *scores_out,
+                          int32_t *idx_out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * sa_merge_partial -- fold a second partial attention result into a first,

@@ -149,8 +149,41 @@ def test_indexer_topk_argument_errors():
     assert L.sa_topk(f, 4, 64, 0, 0, f, None) == _lib.SA_ERR_UNSUPPORTED
     assert L.sa_topk(f, 4, 70000, 0, 16, f, None) == _lib.SA_ERR_UNSUPPORTED
     assert L.sa_topk(None, 4, 64, 0, 16, f, None) == _lib.SA_ERR_INVALID_ARG
-    assert L.sa_indexer_topk(f, f, 4, 64, 64, 0, 5000, f, f, None) == _lib.SA_ERR_UNSUPPORTED
+    assert L.sa_indexer_topk(f, f, 4, 64, 64, 0, 5000, f, f, None, 0, None) == _lib.SA_ERR_UNSUPPORTED
     assert L.sa_topk(f, 0, 64, 0, 16, f, None) == _lib.SA_OK  # empty: nothing launched
+    # streaming form (scores_out NULL): the workspace is checked before any launch
+    need = L.sa_indexer_topk_workspace(4, 64, 16)
+    assert need > 0
+    assert L.sa_indexer_topk(f, f, 4, 64, 64, 0, 16, None, f, None, 0, None) == _lib.SA_ERR_INVALID_ARG
+    assert "workspace" in _err()
+    assert L.sa_indexer_topk(f, f, 4, 64, 64, 0, 16, None, f, f, need - 1, None) == _lib.SA_ERR_INVALID_ARG
+    assert L.sa_indexer_topk(f, f, 4, 64, 64, 0, 16, None, f, ctypes.c_void_p(4096 + 16), need,
+                             None) == _lib.SA_ERR_INVALID_ARG
+    assert "aligned" in _err()
+    assert L.sa_indexer_topk(f, f, 4, 70000, 64, 0, 16, None, f, f, need, None) == _lib.SA_ERR_UNSUPPORTED
+    assert L.sa_indexer_topk(f, f, 4, 64, 64, 0, 16, None, None, f, need, None) == _lib.SA_ERR_INVALID_ARG
+    assert L.sa_indexer_topk(f, f, 0, 64, 64, 0, 16, None, None, None, 0, None) == _lib.SA_OK
+
+
+def test_indexer_topk_workspace_sizes():
+    """The streaming scratch: per row a 1/32 sample (64 keys of every 2,048), a
+    threshold, and per 512-key chunk two counts and 72 kept slots of a 4-byte key
+    and a 2-byte position, each array 256-byte aligned."""
+    L = _lib.lib()
+    up = lambda x: (x + 255) // 256 * 256
+
+    def expect(n_q, n_kv):
+        s_max = 64 * -(-n_kv // 2048)
+        reg = n_q * -(-n_kv // 512)
+        return up(up(up(up(up(n_q * s_max * 4) + n_q * 4) + reg * 2 * 4) + reg * 72 * 4) + reg * 72 * 2)
+
+    for n_q, n_kv in ((1024, 65536), (1, 1), (77, 5000), (3, 65535)):
+        assert L.sa_indexer_topk_workspace(n_q, n_kv, 2048) == expect(n_q, n_kv)
+    assert L.sa_indexer_topk_workspace(1024, 65536, 2048) < 64 << 20
+    assert L.sa_indexer_topk_workspace(0, 100, 16) == 0
+    assert L.sa_indexer_topk_workspace(4, 65537, 16) == 0
+    assert L.sa_indexer_topk_workspace(4, 100, 0) == 0
+    assert L.sa_indexer_topk_workspace(4, 100, 4097) == 0
 
 
 def test_attn_offset_range_error():

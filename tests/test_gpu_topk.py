@@ -40,16 +40,76 @@ def test_indexer_bit_exact(n_q, n_kv, d, off):
 
 
 @pytest.mark.parametrize("n_q,n_kv,k,off", [(40, 5000, 2048, 4960), (16, 65536, 2048, 65520),
-                                            (8, 3000, 4096, 2992), (12, 777, 100, 700), (4, 9, 3, 0)])
+                                            (8, 3000, 4096, 2992), (12, 777, 100, 700), (4, 9, 3, 0),
+                                            (300, 65536, 2048, 65236), (70, 40000, 1000, 39000),
+                                            (33, 2100, 2048, 2060), (5, 65536, 4096, 0)])
 def test_topk_bit_exact(n_q, n_kv, k, off):
+    """Both forms of sa_indexer_topk (through the score matrix, and streaming)
+    against the oracle's selection from its own scores."""
     rng = np.random.default_rng(k + n_kv)
     qi, ki = _rbf(rng, n_q, 64), _rbf(rng, n_kv, 64)
     print(f"topk n_q={n_q} n_kv={n_kv} k={k} off={off}", flush=True)
-    idx, scores = sa.indexer_topk(to_dev_bf16(qi), to_dev_bf16(ki), off, k)
-    s = scores.cpu().numpy()
     n_cand = np.minimum(np.arange(n_q) + off + 1, n_kv)
-    want = oracle.topk_rows(s, n_cand, k)
+    want = oracle.topk_rows(oracle.indexer_scores(qi, ki, off), n_cand, k)
+    idx2, scores = sa.indexer_topk(to_dev_bf16(qi), to_dev_bf16(ki), off, k, keep_scores=True)
+    idx1, none = sa.indexer_topk(to_dev_bf16(qi), to_dev_bf16(ki), off, k)
+    assert none is None and scores is not None
+    np.testing.assert_array_equal(idx2.cpu().numpy(), want)
+    np.testing.assert_array_equal(idx1.cpu().numpy(), want)
+
+
+def _one_hot_queries(n_q, d=64):
+    q = np.zeros((n_q, d), np.uint16)
+    q[:, 0] = W.f32_to_bf16_bits(np.ones(1, np.float32))[0]
+    return q
+
+
+@pytest.mark.parametrize("kind", ["sample_high", "sample_low", "all_equal", "few_distinct", "ascending"])
+@pytest.mark.parametrize("n_kv,k", [(65536, 2048), (32768, 2048), (20000, 333)])
+def test_streaming_topk_adversarial_orders(kind, n_kv, k):
+    """One-hot indexer queries make every score equal a chosen key value, laid
+    out so that the 1/32 sample misleads the threshold: sampled keys above all
+    others (too few kept), below all others (every region overflows), all
+    equal, few distinct values, or rising with the index.  The streaming form
+    must fall back to the exact selection and still match the oracle."""
+    rng = np.random.default_rng(n_kv + k + len(kind))
+    n_q = 6
+    p = np.arange(n_kv)
+    sampled = (p % 2048) < 64
+    if kind == "sample_high":
+        v = np.where(sampled, 4.0 + rng.random(n_kv), rng.random(n_kv))
+    elif kind == "sample_low":
+        v = np.where(sampled, -4.0 - rng.random(n_kv), rng.random(n_kv))
+    elif kind == "all_equal":
+        v = np.full(n_kv, 0.75)
+    elif kind == "few_distinct":
+        v = rng.integers(-2, 3, size=n_kv).astype(np.float64)
+    else:
+        v = p / n_kv * 8.0
+    ki = np.zeros((n_kv, 64), np.uint16)
+    ki[:, 0] = W.f32_to_bf16_bits(v.astype(np.float32))
+    ki[:, 1:] = _rbf(rng, n_kv, 63)        # never reaches the score: the query is zero there
+    qi = _one_hot_queries(n_q)
+    off = n_kv - n_q
+    print(f"streaming top-k {kind} n_kv={n_kv} k={k}", flush=True)
+    idx, _ = sa.indexer_topk(to_dev_bf16(qi), to_dev_bf16(ki), off, k)
+    want = oracle.topk_rows(oracle.indexer_scores(qi, ki, off), np.arange(n_q) + off + 1, k)
     np.testing.assert_array_equal(idx.cpu().numpy(), want)
+
+
+def test_streaming_topk_reused_workspace_and_short_rows():
+    """Rows from fewer candidates than k (padding) up to the whole key range in
+    one call, and a workspace reused by a second, smaller call."""
+    rng = np.random.default_rng(99)
+    n_kv, k = 12000, 1500
+    qi, ki = _rbf(rng, 400, 64), _rbf(rng, n_kv, 64)
+    ws = torch.empty(sa.indexer_topk_workspace_bytes(400, n_kv, k), dtype=torch.uint8, device="cuda")
+    for n_q, off in ((400, 0), (300, 11700), (37, 1400)):
+        print(f"streaming top-k reuse n_q={n_q} off={off}", flush=True)
+        got, _ = sa.indexer_topk(to_dev_bf16(qi[:n_q]), to_dev_bf16(ki), off, k, workspace=ws)
+        n_cand = np.minimum(np.arange(n_q) + off + 1, n_kv)
+        want = oracle.topk_rows(oracle.indexer_scores(qi[:n_q], ki, off), n_cand, k)
+        np.testing.assert_array_equal(got.cpu().numpy(), want)
 
 
 def test_topk_ties_signed_zero_and_padding():
@@ -155,17 +215,21 @@ def _config5_reference():
 
 
 def test_config5_indexer_topk_all_rows():
+    """Configuration 5 at full size: the streaming selection and the two-step one
+    (scores bit for bit too) on every query row."""
     ref = _config5_reference()
     cfg, inp = ref["cfg"], ref["inp"]
     qi, ki = to_dev_bf16(inp["q_idx"]), to_dev_bf16(inp["k_idx"])
     print("config 5 indexer+topk full size", flush=True)
-    idx, scores = sa.indexer_topk(qi, ki, cfg.q_offset, cfg.topk)
+    idx1, _ = sa.indexer_topk(qi, ki, cfg.q_offset, cfg.topk)
+    idx2, scores = sa.indexer_topk(qi, ki, cfg.q_offset, cfg.topk, keep_scores=True)
     torch.cuda.synchronize()
     got_s = scores.cpu().numpy()
     for r in range(cfg.n_q):
         nc = cfg.q_offset + r + 1
         assert np.array_equal(got_s[r, :nc].view(np.uint32), ref["scores"][r, :nc].view(np.uint32)), f"row {r}"
-    np.testing.assert_array_equal(idx.cpu().numpy(), ref["idx"])
+    np.testing.assert_array_equal(idx2.cpu().numpy(), ref["idx"])
+    np.testing.assert_array_equal(idx1.cpu().numpy(), ref["idx"])
 
 
 # ---------------------------------------------------------------------------
