@@ -25,7 +25,7 @@ from . import _lib
 from ._lib import SaError  # noqa: F401
 
 __all__ = ["BlockLists", "build_block_mask", "attn_fwd", "attn_workspace_bytes", "indexer_scores", "topk", "indexer_topk",
-           "indexer_topk_workspace_bytes", "describe", "SaError"]
+           "indexer_topk_workspace_bytes", "indexer_topk_noalloc", "describe", "SaError"]
 
 
 def _torch():
@@ -406,6 +406,21 @@ def indexer_topk(q_idx, k_idx, q_offset: int, k: int, out=None, scores=None, kee
                                           scores.data_ptr() if scores is not None else None,
                                           out.data_ptr(), ws_ptr, ws_bytes, _stream_ptr(q_idx.device)))
     return out, scores
+
+
+def indexer_topk_noalloc(q_idx, k_idx, q_offset: int, k: int, out=None):
+    """The streaming indexer + top-k on the library's fixed per-device scratch
+    (``sa_indexer_topk_noalloc``): the C call allocates nothing.  Calls that
+    overlap on one device race on that scratch.  Returns idx int32 [n_q, k]."""
+    torch = _torch()
+    n_q, d = q_idx.shape
+    n_kv = k_idx.shape[0]
+    _check_idx(q_idx, k_idx)
+    if out is None:
+        out = torch.empty((n_q, k), dtype=torch.int32, device=q_idx.device)
+    _lib.check(_lib.lib().sa_indexer_topk_noalloc(q_idx.data_ptr(), k_idx.data_ptr(), n_q, n_kv, d, int(q_offset),
+                                                  int(k), out.data_ptr(), _stream_ptr(q_idx.device)))
+    return out
 
 
 def _check_idx(q_idx, k_idx):

@@ -18,7 +18,8 @@ SA_MODE_BLOCKS, SA_MODE_GATHER = 0, 1
 ABI_VERSION = 2
 
 EXPORTED = ("sa_build_block_mask", "sa_attn_workspace_bytes", "sa_attn_fwd", "sa_indexer_scores", "sa_topk",
-            "sa_indexer_topk_workspace", "sa_indexer_topk", "sa_merge_partial", "sa_last_error", "sa_abi_version")
+            "sa_indexer_topk_workspace", "sa_indexer_topk", "sa_indexer_topk_noalloc", "sa_merge_partial",
+            "sa_last_error", "sa_abi_version")
 
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
@@ -108,6 +109,8 @@ def lib() -> ctypes.CDLL:
         L.sa_indexer_topk_workspace.restype = ctypes.c_size_t
         L.sa_indexer_topk.argtypes = [_P, _P, _I64, _I64, _I32, _I64, _I32, _P, _P, _P, ctypes.c_size_t, _P]
         L.sa_indexer_topk.restype = ctypes.c_int
+        L.sa_indexer_topk_noalloc.argtypes = [_P, _P, _I64, _I64, _I32, _I64, _I32, _P, _P]
+        L.sa_indexer_topk_noalloc.restype = ctypes.c_int
         L.sa_merge_partial.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I32, ctypes.POINTER(_I64),
                                        ctypes.POINTER(_I64), _I32, _I64, _I64, _P]
         L.sa_merge_partial.restype = ctypes.c_int

@@ -426,4 +426,27 @@ sa_status sa_indexer_topk(const void* q_idx, const void* k_idx, int64_t n_q, int
     }
 }
 
+sa_status sa_indexer_topk_noalloc(const void* q_idx, const void* k_idx, int64_t n_q, int64_t n_kv, int32_t d_idx,
+                                  int64_t q_offset, int32_t topk, int32_t* idx_out, void* stream)
+{
+    try {
+        sa::StreamTopkLayout L;
+        if (n_q > 0 && n_kv > 0 && n_kv <= sa::kStreamMaxKv && sa::stream_topk_layout(n_q, n_kv, L) &&
+            L.total > sa::kNoAllocScratchBytes)
+            return fail(SA_ERR_UNSUPPORTED,
+                        "sa_indexer_topk_noalloc: these sizes need %lld bytes of scratch, above the fixed %lld",
+                        (long long)L.total, (long long)sa::kNoAllocScratchBytes);
+        uint8_t* ws = nullptr;
+        if (n_q > 0 && n_kv > 0) {
+            const hipError_t e = sa::noalloc_scratch(&ws);
+            if (e != hipSuccess)
+                return fail(SA_ERR_DEVICE, "sa_indexer_topk_noalloc: scratch address: %s", hipGetErrorString(e));
+        }
+        return sa_indexer_topk(q_idx, k_idx, n_q, n_kv, d_idx, q_offset, topk, nullptr, idx_out, ws,
+                               (size_t)sa::kNoAllocScratchBytes, stream);
+    } catch (...) {
+        return fail(SA_ERR_DEVICE, "sa_indexer_topk_noalloc: unexpected exception");
+    }
+}
+
 }  // extern "C"

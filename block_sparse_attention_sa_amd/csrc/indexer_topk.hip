@@ -10,6 +10,8 @@
 // Ties in the selection go to the lower index.
 #include "sa_internal.h"
 
+#include <mutex>
+
 namespace sa {
 namespace {
 
@@ -1018,6 +1020,40 @@ hipError_t launch_indexer_topk_stream(const uint16_t* q_idx, const uint16_t* k_i
     hipLaunchKernelGGL(stream_direct_kernel, dim3((unsigned)n_q), dim3(KTH), 0, stream, q_idx, k_idx, n_kv, d_idx,
                        q_offset, topk, lo, idx_out);
     return hipGetLastError();
+}
+
+}  // namespace sa
+
+namespace sa {
+namespace {
+
+// Scratch of sa_indexer_topk_noalloc, for callers that cannot allocate: one
+// copy of this array per device, held until the process ends.  In host code
+// the name is a stand-in, not a device address: launches take the address
+// that noalloc_scratch looks up per device.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+hipError_t noalloc_scratch(uint8_t** ptr)
+{
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = static_cast<uint8_t*>(addr[dev]);
+    return hipSuccess;
 }
 
 }  // namespace sa

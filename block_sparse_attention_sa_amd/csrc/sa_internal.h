@@ -279,6 +279,11 @@ hipError_t launch_indexer_topk_stream(const uint16_t* q_idx, const uint16_t* k_i
                                       int32_t d_idx, int32_t q_offset, int32_t topk, int32_t* idx_out,
                                       uint8_t* ws, const StreamTopkLayout& L, hipStream_t stream);
 
+// The fixed per-device scratch of sa_indexer_topk_noalloc (its address on
+// the current device; looked up once per device).
+constexpr int64_t kNoAllocScratchBytes = int64_t(64) << 20;
+hipError_t noalloc_scratch(uint8_t** ptr);
+
 hipError_t launch_indexer_scores(const uint16_t* q_idx, const uint16_t* k_idx, int32_t n_q,
                                  int32_t n_kv, int32_t d_idx, int32_t q_offset, float* scores,
                                  hipStream_t stream);

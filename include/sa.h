@@ -262,6 +262,25 @@ sa_status sa_indexer_topk(const void *q_idx, const void *k_idx, int64_t n_q, int
                           int32_t *idx_out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * sa_indexer_topk_noalloc -- the streaming sa_indexer_topk (scores_out NULL)
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Its
+ * scratch is a fixed array of SA_NOALLOC_SCRATCH_BYTES bytes inside the
+ * library, one per device, held until the process ends; its address is
+ * looked up on the first call on each device.  The call allocates nothing.
+ * Sizes whose sa_indexer_topk_workspace exceeds the array are rejected with
+ * SA_ERR_UNSUPPORTED (n_q = 1024, n_kv = 65536 fits).  Every call on one
+ * device uses that device's one array and leaves its contents behind: calls
+ * that overlap on a device (several streams or threads) race, so the caller
+ * must order them.  Arguments, outputs and limits otherwise as
+ * sa_indexer_topk.
+ */
+#define SA_NOALLOC_SCRATCH_BYTES (64ll << 20)
+sa_status sa_indexer_topk_noalloc(const void *q_idx, const void *k_idx, int64_t n_q, int64_t n_kv,
+                                  int32_t d_idx, int64_t q_offset, int32_t topk, int32_t *idx_out,
+                                  void *stream);
+
+/*
  * sa_merge_partial -- fold a second partial attention result into a first,
  * for key sets that are split into two disjoint parts per query row:
  *     O = (e^l1 O1 + e^l2 O2) / (e^l1 + e^l2),   LSE = log(e^l1 + e^l2)
