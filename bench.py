@@ -228,16 +228,13 @@ def _bench_strided(sa, W, np, torch, dev, dev_bf16, reps=10):
     pat = cfg.pattern.as_dict()
     stream = torch.cuda.current_stream(dev)
     bl = sa.build_block_mask(pat, cfg.N, cfg.N, cfg.block, cfg.block, device=dev)
-    plan = sa.plan_strided(pat, cfg.N)
     shape = (cfg.B, cfg.H, cfg.N, cfg.d)
     o = torch.empty(shape, dtype=torch.float32, device=dev)
     lse = torch.empty(shape[:3], dtype=torch.float32, device=dev)
-    o2 = torch.empty(shape, dtype=torch.float32, device=dev)
-    lse2 = torch.empty((cfg.B, cfg.H, plan.stride, cfg.N // plan.stride - 2), dtype=torch.float32, device=dev)
-    lse3 = torch.empty((cfg.B, cfg.H, 1, 1), dtype=torch.float32, device=dev)
+    ws = sa.strided_plan(pat, cfg.B, cfg.H, cfg.N, cfg.d, dev)
     ways = {
         "blocks": lambda: sa.attn_fwd(q, k, v, bl, out=o, lse=lse),
-        "split": lambda: sa.attn_fwd_strided(q, k, v, plan, out=o, lse=lse, o2=o2, lse2=lse2, lse3=lse3),
+        "split": lambda: sa.attn_fwd_strided(q, k, v, pat, out=o, lse=lse, workspace=ws),
     }
     t = {}
     for name, fn in ways.items():
@@ -259,7 +256,9 @@ def _bench_strided(sa, W, np, torch, dev, dev_bf16, reps=10):
         "blocks_tflops_over_live_pairs": round(flop / t["blocks"] / 1e12, 2),
         "split_us": round(t["split"] * 1e6, 1),
         "split_tflops_over_live_pairs": round(flop / t["split"] / 1e12, 2),
-        "split_note": "64x64 band tiles through block lists + causal 64-row tiles per (head, key residue) view + LSE merge",
+        "split_note": "one sa_attn_fwd call (SA_MODE_STRIDED) on a plan built once by sa_attn_strided_plan: "
+                      "64x64 band tiles, causal 64-row tiles per (head, key residue) view and the last row, the "
+                      "later parts merged by log-sum-exp in the kernel epilogue",
     }
 
 def _bench_dsa(sa, W, np, torch, dev, dev_bf16, reps=10):

@@ -24,7 +24,8 @@ import numpy as np
 from . import _lib
 from ._lib import SaError  # noqa: F401
 
-__all__ = ["BlockLists", "build_block_mask", "attn_fwd", "attn_workspace_bytes", "indexer_scores", "topk", "indexer_topk",
+__all__ = ["BlockLists", "build_block_mask", "attn_fwd", "attn_workspace_bytes", "attn_fwd_strided",
+           "attn_workspace_bytes_strided", "strided_plan", "merge_partial", "indexer_scores", "topk", "indexer_topk",
            "indexer_topk_workspace_bytes", "indexer_topk_noalloc", "describe", "SaError"]
 
 
@@ -232,69 +233,51 @@ def merge_partial(out, lse, o2, lse2, group: int = 1, q_first: int = 0, n2: Opti
                                            B, H, n, d, os3, o2s, group, q_first, n2, _stream_ptr(out.device)))
 
 
-def strided_stride(pattern, n_q: int, n_kv: int) -> int:
-    """The stride S when ``pattern`` is the strided template that ``attn_fwd_strided`` computes
-    as disjoint parts (causal; local band q - kv <= S - 1; strided keys with
-    (q - kv) % S == S - 1; no other term; q_offset 0; n_q == n_kv a multiple of S with at least
-    three groups of S rows), else 0."""
-    g = lambda key, dflt: int(_get(pattern, key, dflt) or 0)
-    S = g("stride", 0)
-    if S <= 0 or g("stride_phase", 0) != S - 1 or not g("causal", 0):
-        return 0
-    if g("window_left", -1) != S - 1 or g("window_right", 0) != 0:
-        return 0
-    if g("sinks", 0) or g("global_tokens", 0) or g("unit", 0) or g("n_rand", 0) or g("q_offset", 0):
-        return 0
-    if n_q != n_kv or n_q % S or n_q // S < 3:
-        return 0
-    return S
+def _strided_args(q, k, v, pattern, out, lse, softmax_scale):
+    a = _lib.SaAttnArgs()
+    B, H, n, d = q.shape
+    a.q, a.k, a.v, a.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()
+    a.lse = lse.data_ptr()
+    a.batch, a.heads, a.n_q, a.n_kv, a.head_dim = B, H, n, n, d
+    a.o_dtype = _lib.SA_DTYPE_F32
+    a.q_strides[:] = _strides3(q)
+    a.k_strides[:] = _strides3(k)
+    a.v_strides[:] = _strides3(v)
+    a.o_strides[:] = _strides3(out)
+    a.softmax_scale = float(softmax_scale) if softmax_scale else 0.0
+    a.mode = _lib.SA_MODE_STRIDED
+    a.pattern = _template_struct(pattern)
+    return a
 
 
-@dataclasses.dataclass
-class StridedPlan:
-    """Block lists of the parts of a strided pattern (``plan_strided``)."""
-
-    stride: int
-    n: int
-    band: BlockLists
-    strided: BlockLists
-    last: BlockLists
-
-
-def plan_strided(pattern, n: int, block: int = 64, device="cuda",
-                 residue_block: Optional[int] = None) -> StridedPlan:
-    """Block lists for ``attn_fwd_strided``: the local band on the natural layout
-    (block x block tiles); plain causal lists shared by every (head, key residue) view;
-    and one row against every key of its view for the last query row."""
-    S = strided_stride(pattern, n, n)
-    if not S:
+def strided_plan(pattern, batch: int, heads: int, n: int, head_dim: int, device="cuda"):
+    """The workspace of ``attn_fwd_strided`` with the block lists of its parts built in it
+    (``sa_attn_strided_plan``); reusable by every call with the same pattern and length."""
+    torch = _torch()
+    need = attn_workspace_bytes_strided(pattern, batch, heads, n, head_dim)
+    if need == 0:
         raise ValueError("not the strided template that splits into band + residue views")
-    G = n // S
-    band = build_block_mask(dict(causal=1, window_left=S - 1, window_right=0), n, n, block, block, device)
-    bs = residue_block or 64  # 64-row tiles: twice the workgroups of 128-row ones, 3 % faster
-    # a local term whose window covers every row (a pattern without any term allows no pair)
-    strided = build_block_mask(dict(causal=1, window_left=G, window_right=0), G - 2, G - 2, bs, bs, device)
-    last = build_block_mask(dict(causal=0, window_left=G, window_right=G), 1, G - 1, 64, bs, device)
-    return StridedPlan(S, n, band, strided, last)
+    ws = torch.empty(need, dtype=torch.uint8, device=device)
+    a = _lib.SaAttnArgs()
+    a.batch, a.heads, a.n_q, a.n_kv, a.head_dim = batch, heads, n, n, head_dim
+    a.mode = _lib.SA_MODE_STRIDED
+    a.pattern = _template_struct(pattern)
+    a.k_strides[:] = a.v_strides[:] = [heads * n * head_dim, n * head_dim, head_dim]
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    _lib.check(_lib.lib().sa_attn_strided_plan(ctypes.byref(a), _stream_ptr(torch.device(device))))
+    return ws
 
 
-def attn_fwd_strided(q, k, v, plan: StridedPlan, *, softmax_scale: Optional[float] = None,
-                     out=None, lse=None, o2=None, lse2=None, lse3=None):
-    """The strided template as disjoint key sets per query row, merged by LSE.
-
-    * band: kv in [q - (S - 1), q], through block lists on the natural layout;
-    * strided: kv = q - (S - 1) - S*m for m >= 1, i.e. keys kv = j*S + rho of one residue
-      rho for the rows q = (i + 2)*S + rho - 1, with j <= i: for every key residue a plain
-      causal attention between strided views of the same tensors (row step S rows, residue
-      step one row; queries from row 2S - 1 on), no copy.  The views are batched as
-      [heads, S residues, n/S - 2 rows, d];
-    * the one row those views leave out, q = n - 1 (residue 0, one group further), against
-      its keys j*S, j <= n/S - 2;
-    * ``sa_merge_partial`` folds the two strided parts into the band part.
-    q, k, v bfloat16 [B, H, n, d].  Returns (O float32 [B, H, n, d], LSE [B, H, n]);
-    ``o2`` (float32 like O), ``lse2`` (float32 [B, H, S, n/S - 2]) and ``lse3`` (float32
-    [B, H, 1, 1]) are scratch, allocated when None.
-    """
+def attn_fwd_strided(q, k, v, pattern, *, softmax_scale: Optional[float] = None, out=None, lse=None,
+                     workspace=None):
+    """The strided template as disjoint key sets per row (``sa_attn_fwd``, ``SA_MODE_STRIDED``):
+    the local band through block lists, the strided keys as causal attention between
+    strided views (one per head and key residue) and the last row, merged by log-sum-exp in
+    the kernels.  q, k, v bfloat16 [B, H, n, d]; ``pattern`` must be the template (causal,
+    window_left = stride - 1, stride_phase = stride - 1, no other term; n a multiple of the
+    stride, at least three groups), else the library rejects it.  ``workspace`` is a plan
+    from ``strided_plan`` (made for the call when None).  Returns (O float32 [B, H, n, d],
+    LSE [B, H, n])."""
     torch = _torch()
     for t in (q, k, v):
         if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 4 or t.stride(-1) != 1:
@@ -302,34 +285,40 @@ def attn_fwd_strided(q, k, v, plan: StridedPlan, *, softmax_scale: Optional[floa
     B, H, n, d = q.shape
     if tuple(k.shape) != (B, H, n, d) or tuple(v.shape) != (B, H, n, d):
         raise ValueError("q, k and v must have the same shape [B, H, n, d]")
-    if n != plan.n:
-        raise ValueError("plan was built for another sequence length")
-    S, G = plan.stride, n // plan.stride
-    f32, dev = torch.float32, q.device
-    out = torch.empty((B, H, n, d), dtype=f32, device=dev) if out is None else out
-    lse = torch.empty((B, H, n), dtype=f32, device=dev) if lse is None else lse
-    if out.dtype != f32:
-        raise ValueError("the strided form writes a float32 O")
-    o2 = torch.empty((B, H, n, d), dtype=f32, device=dev) if o2 is None else o2
-    lse2 = torch.empty((B, H, S, G - 2), dtype=f32, device=dev) if lse2 is None else lse2
-    lse3 = torch.empty((B, H, 1, 1), dtype=f32, device=dev) if lse3 is None else lse3
-    if tuple(o2.shape) != (B, H, n, d) or o2.dtype != f32:
-        raise ValueError("o2 must be float32 [B, H, n, d]")
-    if tuple(lse2.shape) != (B, H, S, G - 2) or tuple(lse3.shape) != (B, H, 1, 1):
-        raise ValueError("lse2 must be [B, H, S, n/S - 2] and lse3 [B, H, 1, 1]")
-    attn_fwd(q, k, v, plan.band, softmax_scale=softmax_scale, out=out, lse=lse)
-    for b in range(B):
-        def view(t, res, rows, first):
-            st = t.stride()
-            return t.as_strided((H, res, rows, d), (st[1], st[2], S * st[2], 1),
-                                t.storage_offset() + b * st[0] + first * st[2])
-        attn_fwd(view(q, S, G - 2, 2 * S - 1), view(k, S, G - 2, 0), view(v, S, G - 2, 0), plan.strided,
-                 softmax_scale=softmax_scale, out=view(o2, S, G - 2, 2 * S - 1), lse=lse2[b])
-        attn_fwd(view(q, 1, 1, n - 1), view(k, 1, G - 1, 0), view(v, 1, G - 1, 0), plan.last,
-                 softmax_scale=softmax_scale, out=view(o2, 1, 1, n - 1), lse=lse3[b])
-    merge_partial(out, lse, o2, lse2, group=S, q_first=2 * S - 1, n2=G - 2)
-    merge_partial(out, lse, o2, lse3, group=1, q_first=n - 1, n2=1)
+    out = torch.empty((B, H, n, d), dtype=torch.float32, device=q.device) if out is None else out
+    lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device) if lse is None else lse
+    if out.dtype != torch.float32 or tuple(out.shape) != (B, H, n, d):
+        raise ValueError("out must be float32 [B, H, n, d]")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * H * n:
+        raise ValueError("lse must be a contiguous float32 tensor of B * H * n values")
+    if workspace is None:
+        workspace = strided_plan(pattern, B, H, n, d, q.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
+    a = _strided_args(q, k, v, pattern, out, lse, softmax_scale)
+    a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    _lib.check(_lib.lib().sa_attn_fwd(ctypes.byref(a), _stream_ptr(q.device)))
     return out, lse
+
+
+def _template_struct(pattern):
+    g = lambda key, dflt: int(_get(pattern, key, dflt) or 0)
+    return _lib.SaPattern(causal=g("causal", 0), q_offset=g("q_offset", 0), window_left=g("window_left", -1),
+                          window_right=g("window_right", 0), sinks=g("sinks", 0), stride=g("stride", 0),
+                          stride_phase=g("stride_phase", 0), global_tokens=g("global_tokens", 0),
+                          unit=g("unit", 0), unit_window=g("unit_window", -1), rand_units=None,
+                          n_rand=g("n_rand", 0), rand_rows=0)
+
+
+def attn_workspace_bytes_strided(pattern, batch: int, heads: int, n: int, head_dim: int) -> int:
+    """Scratch bytes of ``attn_fwd_strided`` (0: ``pattern`` is not the strided template).
+    Touches no device."""
+    a = _lib.SaAttnArgs()
+    a.batch, a.heads, a.n_q, a.n_kv, a.head_dim = batch, heads, n, n, head_dim
+    a.mode = _lib.SA_MODE_STRIDED
+    a.pattern = _template_struct(pattern)
+    return int(_lib.lib().sa_attn_workspace_bytes(ctypes.byref(a)))
+
 
 def attn_workspace_bytes(batch: int, heads: int, n_q: int, n_kv: int, head_dim: int, topk: int,
                          per_head_lists: bool = False) -> int:

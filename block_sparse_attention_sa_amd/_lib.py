@@ -14,10 +14,10 @@ LIB_PATH = os.path.join(_HERE, "libsa.so")
 
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_DEVICE = 0, 1, 2, 3
 SA_DTYPE_BF16, SA_DTYPE_F32 = 0, 1
-SA_MODE_BLOCKS, SA_MODE_GATHER = 0, 1
+SA_MODE_BLOCKS, SA_MODE_GATHER, SA_MODE_STRIDED = 0, 1, 2
 ABI_VERSION = 2
 
-EXPORTED = ("sa_build_block_mask", "sa_attn_workspace_bytes", "sa_attn_fwd", "sa_indexer_scores", "sa_topk",
+EXPORTED = ("sa_build_block_mask", "sa_attn_workspace_bytes", "sa_attn_strided_plan", "sa_attn_fwd", "sa_indexer_scores", "sa_topk",
             "sa_indexer_topk_workspace", "sa_indexer_topk", "sa_indexer_topk_noalloc", "sa_merge_partial",
             "sa_last_error", "sa_abi_version")
 
@@ -99,6 +99,8 @@ def lib() -> ctypes.CDLL:
         L.sa_build_block_mask.restype = ctypes.c_int
         L.sa_attn_workspace_bytes.argtypes = [ctypes.POINTER(SaAttnArgs)]
         L.sa_attn_workspace_bytes.restype = ctypes.c_size_t
+        L.sa_attn_strided_plan.argtypes = [ctypes.POINTER(SaAttnArgs), _P]
+        L.sa_attn_strided_plan.restype = ctypes.c_int
         L.sa_attn_fwd.argtypes = [ctypes.POINTER(SaAttnArgs), _P]
         L.sa_attn_fwd.restype = ctypes.c_int
         L.sa_indexer_scores.argtypes = [_P, _P, _I64, _I64, _I32, _I64, _P, _P]

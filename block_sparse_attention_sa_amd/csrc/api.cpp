@@ -105,6 +105,189 @@ sa_status launched(hipError_t e, const char* what)
     return ok();
 }
 
+// The strided template that sa_attn_fwd's SA_MODE_STRIDED computes as
+// disjoint key sets (causal; local band q - kv <= S - 1; strided keys
+// (q - kv) % S == S - 1; no other term; q_offset 0; n_q == n_kv a multiple of
+// S with at least three groups of S rows): S, else 0.
+int64_t strided_template(const sa_attn_args* a)
+{
+    const sa_pattern& p = a->pattern;
+    const int64_t S = p.stride;
+    if (S <= 0 || p.stride_phase != S - 1 || !p.causal || p.window_left != S - 1 || p.window_right != 0) return 0;
+    if (p.sinks || p.global_tokens || p.unit > 0 || p.n_rand || p.q_offset) return 0;
+    if (a->n_q != a->n_kv || a->n_q % S || a->n_q / S < 3) return 0;
+    return S;
+}
+
+// Scratch of the strided form: the block lists of its three parts (band on
+// the natural layout; the (n/S - 2)-row residue views against all n/S key
+// groups -- the causal mask drops the groups past each row, and a key range
+// that is a multiple of the sub-tile keeps the copies on the fast path; the
+// last query row, as position n/S - 2 of a causal row over the same n/S
+// groups).
+struct StridedLayout {
+    struct Lists {
+        int64_t n_q, n_kv, nqb, nkb, count, index, partial, live;
+    } band, res, last;
+    int64_t total;
+};
+constexpr int kStridedBlock = 64;
+
+StridedLayout strided_layout(int64_t n, int64_t S)
+{
+    auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
+    StridedLayout L{};
+    const int64_t G = n / S;
+    int64_t at = 0;
+    auto lists = [&](StridedLayout::Lists& l, int64_t n_q, int64_t n_kv) {
+        l.n_q = n_q;
+        l.n_kv = n_kv;
+        l.nqb = (n_q + kStridedBlock - 1) / kStridedBlock;
+        l.nkb = (n_kv + kStridedBlock - 1) / kStridedBlock;
+        l.count = at;
+        l.index = up(l.count + 4 * l.nqb);
+        l.partial = up(l.index + 4 * l.nqb * l.nkb);
+        l.live = up(l.partial + l.nqb * l.nkb);
+        at = up(l.live + 8);
+    };
+    lists(L.band, n, n);
+    lists(L.res, G - 2, G);
+    lists(L.last, 1, G);
+    L.total = at;
+    return L;
+}
+
+// SA_MODE_STRIDED: the strided template as three disjoint key sets per
+// query row (the blog "Sparse transformers: how to cut the O(n^2) of
+// attention", section on the main sparsity templates; the masked softmax's
+// log-sum-exp splits over disjoint key sets):
+//   band     kv in [q - (S - 1), q], block lists on the natural layout;
+//   residue  kv = q - (S - 1) - S*m (m >= 1): for each key residue rho the
+//            rows q = (i + 2)*S + rho - 1 against keys j*S + rho, j <= i --
+//            plain causal attention between strided views of the same
+//            tensors (no copy), one view per (head, residue);
+//   last     query row n - 1 (residue 0, one group past the views) against
+//            keys j*S, j <= n/S - 2.
+// The second and third parts are folded into the band's O and LSE in the
+// attention kernel's epilogue.  The block lists of all three (the plan) are
+// built into the workspace by sa_attn_strided_plan.
+struct StridedParts {
+    int64_t S, G;
+    StridedLayout W;
+    sa_pattern pat[3];
+    sa::DevPattern dev[3];
+};
+
+sa_status strided_check(const sa_attn_args* a, StridedParts& P)
+{
+    P.S = strided_template(a);
+    if (!P.S)
+        return fail(SA_ERR_INVALID_ARG, "SA_MODE_STRIDED: the pattern is not the strided template "
+                                        "(causal, window_left = stride - 1, stride_phase = stride - 1, "
+                                        "no other term, n_q == n_kv a multiple of stride >= 3 * stride)");
+    const int64_t n = a->n_q;
+    P.G = n / P.S;
+    P.W = strided_layout(n, P.S);
+    if (!a->workspace || a->workspace_bytes < P.W.total)
+        return fail(SA_ERR_INVALID_ARG, "SA_MODE_STRIDED needs a workspace of sa_attn_workspace_bytes (%lld bytes)",
+                    (long long)P.W.total);
+    if (((uintptr_t)a->workspace & 255u) != 0) return fail(SA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    // residue views step S rows per key: their 32-bit DMA offsets
+    const int64_t row_b = 2 * std::max(a->k_strides[2], a->v_strides[2]);
+    if ((n + 256 * P.S) * row_b > kI32Max)
+        return fail(SA_ERR_UNSUPPORTED, "n_kv times the K/V row stride must stay below 2^31 bytes");
+    const StridedLayout::Lists* ls[3] = {&P.W.band, &P.W.res, &P.W.last};
+    for (int i = 0; i < 3; ++i) P.pat[i] = sa_pattern{};
+    P.pat[0].causal = 1; P.pat[0].window_left = P.S - 1; P.pat[0].unit_window = -1;
+    P.pat[1].causal = 1; P.pat[1].window_left = P.G; P.pat[1].unit_window = -1;
+    P.pat[2].causal = 1; P.pat[2].window_left = P.G; P.pat[2].unit_window = -1; P.pat[2].q_offset = P.G - 2;
+    for (int i = 0; i < 3; ++i) {
+        const sa_status st = make_pattern(&P.pat[i], ls[i]->n_q, ls[i]->n_kv, P.dev[i]);
+        if (st != SA_OK) return st;
+    }
+    return SA_OK;
+}
+
+sa_status strided_plan(const sa_attn_args* a, hipStream_t s)
+{
+    StridedParts P;
+    const sa_status st0 = strided_check(a, P);
+    if (st0 != SA_OK) return st0;
+    uint8_t* ws = (uint8_t*)a->workspace;
+    const StridedLayout::Lists* ls[3] = {&P.W.band, &P.W.res, &P.W.last};
+    for (int i = 0; i < 3; ++i) {
+        const sa_status st = launched(sa::launch_block_mask(P.dev[i], (int32_t)ls[i]->n_q, (int32_t)ls[i]->n_kv,
+                                                            kStridedBlock, kStridedBlock, (int32_t*)(ws + ls[i]->count),
+                                                            (int32_t*)(ws + ls[i]->index), ws + ls[i]->partial,
+                                                            (int64_t*)(ws + ls[i]->live), s),
+                                      "sa_attn_strided_plan");
+        if (st != SA_OK) return st;
+    }
+    return ok();
+}
+
+sa_status strided_fwd(const sa_attn_args* a, const sa::AttnParams& base, hipStream_t s)
+{
+    StridedParts P;
+    const sa_status st0 = strided_check(a, P);
+    if (st0 != SA_OK) return st0;
+    if (a->o_dtype != SA_DTYPE_F32) return fail(SA_ERR_UNSUPPORTED, "SA_MODE_STRIDED writes a float32 O");
+    if (!a->lse) return fail(SA_ERR_INVALID_ARG, "SA_MODE_STRIDED needs lse (the parts are merged through it)");
+    const int64_t n = a->n_q, S = P.S, G = P.G, B = a->batch, H = a->heads;
+    uint8_t* ws = (uint8_t*)a->workspace;
+    auto with_lists = [&](sa::AttnParams& p, int part, const StridedLayout::Lists& l) {
+        p.pat = P.dev[part];
+        p.nqb = (int32_t)l.nqb;
+        p.nkb = (int32_t)l.nkb;
+        p.kv_count = (const int32_t*)(ws + l.count);
+        p.kv_index = (const int32_t*)(ws + l.index);
+        p.kv_partial = ws + l.partial;
+    };
+    // band: the natural layout
+    {
+        sa::AttnParams p = base;
+        with_lists(p, 0, P.W.band);
+        const sa_status st =
+            launched(sa::launch_attn_blocks(p, (int)a->head_dim, kStridedBlock, kStridedBlock, 1, s), "sa_attn_fwd");
+        if (st != SA_OK) return st;
+    }
+    for (int64_t b = 0; b < B; ++b) {
+        // residue views: "batch" = head, "head" = residue, row i; merged in place
+        sa::AttnParams p = base;
+        with_lists(p, 1, P.W.res);
+        p.q = base.q + b * a->q_strides[0] + (2 * S - 1) * a->q_strides[2];
+        p.k = base.k + b * a->k_strides[0];
+        p.v = base.v + b * a->v_strides[0];
+        p.o = (float*)base.o + b * a->o_strides[0] + (2 * S - 1) * a->o_strides[2];
+        p.q_sb = a->q_strides[1]; p.q_sh = a->q_strides[2]; p.q_sn = S * a->q_strides[2];
+        p.k_sb = a->k_strides[1]; p.k_sh = a->k_strides[2]; p.k_sn = S * a->k_strides[2];
+        p.v_sb = a->v_strides[1]; p.v_sh = a->v_strides[2]; p.v_sn = S * a->v_strides[2];
+        p.o_sb = a->o_strides[1]; p.o_sh = a->o_strides[2]; p.o_sn = S * a->o_strides[2];
+        p.lse = a->lse + b * H * n + (2 * S - 1);
+        p.lse_sb = n; p.lse_sh = 1; p.lse_sn = S;
+        p.batch = (int32_t)H;
+        p.heads = (int32_t)S;
+        p.n_q = (int32_t)(G - 2);
+        p.n_kv = (int32_t)G;
+        p.merge = 1;
+        sa_status st =
+            launched(sa::launch_attn_blocks(p, (int)a->head_dim, kStridedBlock, kStridedBlock, 1, s), "sa_attn_fwd");
+        if (st != SA_OK) return st;
+        // the last row: position G - 2 of a causal row over the key groups j*S
+        sa::AttnParams l = p;
+        with_lists(l, 2, P.W.last);
+        l.q = base.q + b * a->q_strides[0] + (n - 1) * a->q_strides[2];
+        l.o = (float*)base.o + b * a->o_strides[0] + (n - 1) * a->o_strides[2];
+        l.heads = 1;
+        l.n_q = 1;
+        l.lse = a->lse + b * H * n + (n - 1);
+        l.lse_sb = n; l.lse_sh = 0; l.lse_sn = 0;
+        st = launched(sa::launch_attn_blocks(l, (int)a->head_dim, kStridedBlock, kStridedBlock, 1, s), "sa_attn_fwd");
+        if (st != SA_OK) return st;
+    }
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -195,6 +378,10 @@ sa_status sa_build_block_mask(const sa_pattern* pattern, int64_t n_q, int64_t n_
 
 size_t sa_attn_workspace_bytes(const sa_attn_args* a)
 {
+    if (a && a->mode == SA_MODE_STRIDED) {
+        const int64_t S = strided_template(a);
+        return S > 0 && a->n_q <= kI32Max ? (size_t)strided_layout(a->n_q, S).total : 0;
+    }
     if (!a || a->mode != SA_MODE_GATHER || a->batch <= 0 || a->heads <= 0 || a->n_q <= 0 || a->n_kv <= 0 ||
         (a->head_dim != 64 && a->head_dim != 128) || a->topk < 1 || a->topk > 8192 || a->gather_bh_stride < 0)
         return 0;
@@ -214,8 +401,8 @@ sa_status sa_attn_fwd(const sa_attn_args* a, void* stream)
             return fail(SA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
         if (a->o_dtype != SA_DTYPE_BF16 && a->o_dtype != SA_DTYPE_F32)
             return fail(SA_ERR_INVALID_ARG, "o_dtype must be SA_DTYPE_BF16 or SA_DTYPE_F32");
-        if (a->mode != SA_MODE_BLOCKS && a->mode != SA_MODE_GATHER)
-            return fail(SA_ERR_INVALID_ARG, "mode must be SA_MODE_BLOCKS or SA_MODE_GATHER");
+        if (a->mode != SA_MODE_BLOCKS && a->mode != SA_MODE_GATHER && a->mode != SA_MODE_STRIDED)
+            return fail(SA_ERR_INVALID_ARG, "mode must be SA_MODE_BLOCKS, SA_MODE_GATHER or SA_MODE_STRIDED");
         if (a->n_q > kI32Max || a->n_kv > kI32Max || a->batch * a->heads > kI32Max)
             return fail(SA_ERR_UNSUPPORTED, "sizes must stay below 2^31");
         if (a->batch == 0 || a->heads == 0 || a->n_q == 0) return ok();
@@ -247,6 +434,10 @@ sa_status sa_attn_fwd(const sa_attn_args* a, void* stream)
         p.k_sb = a->k_strides[0]; p.k_sh = a->k_strides[1]; p.k_sn = a->k_strides[2];
         p.v_sb = a->v_strides[0]; p.v_sh = a->v_strides[1]; p.v_sn = a->v_strides[2];
         p.o_sb = a->o_strides[0]; p.o_sh = a->o_strides[1]; p.o_sn = a->o_strides[2];
+        p.lse_sb = a->heads * a->n_q;
+        p.lse_sh = a->n_q;
+        p.lse_sn = 1;
+        p.merge = 0;
         p.batch = (int32_t)a->batch;
         p.heads = (int32_t)a->heads;
         p.n_q = (int32_t)a->n_q;
@@ -256,6 +447,7 @@ sa_status sa_attn_fwd(const sa_attn_args* a, void* stream)
         hipStream_t s = (hipStream_t)stream;
         const int o_f32 = a->o_dtype == SA_DTYPE_F32;
 
+        if (a->mode == SA_MODE_STRIDED) return strided_fwd(a, p, s);
         if (a->mode == SA_MODE_BLOCKS) {
             if ((a->block_q != 64 && a->block_q != 128) || (a->block_kv != 64 && a->block_kv != 128))
                 return fail(SA_ERR_UNSUPPORTED, "block_q and block_kv must be 64 or 128");
@@ -423,6 +615,18 @@ sa_status sa_indexer_topk(const void* q_idx, const void* k_idx, int64_t n_q, int
                         "sa_indexer_topk");
     } catch (...) {
         return fail(SA_ERR_DEVICE, "sa_indexer_topk: unexpected exception");
+    }
+}
+
+sa_status sa_attn_strided_plan(const sa_attn_args* a, void* stream)
+{
+    try {
+        if (!a) return fail(SA_ERR_INVALID_ARG, "args is NULL");
+        if (a->mode != SA_MODE_STRIDED) return fail(SA_ERR_INVALID_ARG, "mode must be SA_MODE_STRIDED");
+        if (a->n_q < 0 || a->n_q > kI32Max) return fail(SA_ERR_UNSUPPORTED, "n_q must be in [0, 2^31)");
+        return strided_plan(a, (hipStream_t)stream);
+    } catch (...) {
+        return fail(SA_ERR_DEVICE, "sa_attn_strided_plan: unexpected exception");
     }
 }
 

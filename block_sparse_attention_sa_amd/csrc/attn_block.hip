@@ -517,29 +517,56 @@ attn_block_kernel(AttnParams a)
     for (int nb = 0; nb < NB; ++nb) {
         const float l_tot = l_run[nb] + other_half(l_run[nb]);
         if (qrow[nb] < a.n_q) {
-            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            const float lse = l_tot > 0.f ? m_run[nb] * a.scale + logf(l_tot) : -INFINITY;
             const int64_t obase = b * a.o_sb + h * a.o_sh + (int64_t)qrow[nb] * a.o_sn;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const int dv = 32 * db + 8 * r4 + 4 * hh;
-                    const float x0 = o[nb][db][4 * r4 + 0] * inv, x1 = o[nb][db][4 * r4 + 1] * inv;
-                    const float x2 = o[nb][db][4 * r4 + 2] * inv, x3 = o[nb][db][4 * r4 + 3] * inv;
-                    if (OF32) {
-                        float* op = reinterpret_cast<float*>(a.o) + obase + dv;
-                        *reinterpret_cast<float4*>(op) = make_float4(x0, x1, x2, x3);
-                    } else {
-                        uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + obase + dv;
-                        const bf16x2 p01 = {(__bf16)x0, (__bf16)x1};
-                        const bf16x2 p23 = {(__bf16)x2, (__bf16)x3};
-                        const u32x2 w = {__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
-                        *reinterpret_cast<u32x2*>(op) = w;
-                    }
+            float* lp = a.lse ? a.lse + b * a.lse_sb + h * a.lse_sh + (int64_t)qrow[nb] * a.lse_sn : nullptr;
+            // Merge mode: O and LSE already hold this row's attention over a
+            // disjoint key set; fold this part in with log-sum-exp weights,
+            // O = (e^l1 O1 + e^l2 O2) / (e^l1 + e^l2), LSE = log(e^l1 + e^l2).
+            // A part without keys leaves the row as it is.
+            float w1 = 0.f, lse_out = lse;
+            bool write = true;
+            if (OF32 && a.merge) {
+                const float l1 = *lp;
+                write = lse != -INFINITY;
+                if (write && l1 != -INFINITY) {
+                    const float m = fmaxf(l1, lse);
+                    const float e1 = __expf(l1 - m), e2 = __expf(lse - m);
+                    const float rs = 1.f / (e1 + e2);
+                    lse_out = m + logf(e1 + e2);
+                    w1 = e1 * rs;
+                    inv *= e2 * rs;
                 }
-            if (a.lse && hh == 0)
-                a.lse[((int64_t)b * a.heads + h) * a.n_q + qrow[nb]] =
-                    l_tot > 0.f ? m_run[nb] * a.scale + logf(l_tot) : -INFINITY;
+            }
+            if (write) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int dv = 32 * db + 8 * r4 + 4 * hh;
+                        float x0 = o[nb][db][4 * r4 + 0] * inv, x1 = o[nb][db][4 * r4 + 1] * inv;
+                        float x2 = o[nb][db][4 * r4 + 2] * inv, x3 = o[nb][db][4 * r4 + 3] * inv;
+                        if (OF32) {
+                            float* op = reinterpret_cast<float*>(a.o) + obase + dv;
+                            if (w1 != 0.f) {
+                                const float4 o1 = *reinterpret_cast<const float4*>(op);
+                                x0 += w1 * o1.x;
+                                x1 += w1 * o1.y;
+                                x2 += w1 * o1.z;
+                                x3 += w1 * o1.w;
+                            }
+                            *reinterpret_cast<float4*>(op) = make_float4(x0, x1, x2, x3);
+                        } else {
+                            uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + obase + dv;
+                            const bf16x2 p01 = {(__bf16)x0, (__bf16)x1};
+                            const bf16x2 p23 = {(__bf16)x2, (__bf16)x3};
+                            const u32x2 w = {__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
+                            *reinterpret_cast<u32x2*>(op) = w;
+                        }
+                    }
+                if (lp && hh == 0) *lp = lse_out;
+            }
         }
     }
 }

@@ -171,7 +171,9 @@ struct AttnParams {
     int64_t k_sb, k_sh, k_sn;
     int64_t v_sb, v_sh, v_sn;
     int64_t o_sb, o_sh, o_sn;
+    int64_t lse_sb, lse_sh, lse_sn;  // element strides of LSE (b, h, row)
     int32_t batch, heads, n_q, n_kv;
+    int32_t merge;      // block mode, float32 O: fold into the O and LSE already there
     float scale;        // softmax scale (natural units)
     float scale_log2;   // scale * log2(e)
     // block mode

@@ -54,7 +54,7 @@ typedef enum sa_status {
 } sa_status;
 
 enum { SA_DTYPE_BF16 = 0, SA_DTYPE_F32 = 1 };
-enum { SA_MODE_BLOCKS = 0, SA_MODE_GATHER = 1 };
+enum { SA_MODE_BLOCKS = 0, SA_MODE_GATHER = 1, SA_MODE_STRIDED = 2 };
 
 /*
  * Pattern descriptor.  A pair (q, kv) of absolute positions is allowed when
@@ -140,6 +140,23 @@ sa_status sa_build_block_mask(const sa_pattern *pattern, int64_t n_q, int64_t n_
  *   otherwise list of (b, h) starts at (b*heads + h) * gather_bh_stride.
  *   The pattern and block fields are ignored.  (Glossary, section on common
  *   sparsity patterns: full attention over the indexer's selected tokens.)
+ * mode SA_MODE_STRIDED: the strided template of the blog "Sparse
+ *   transformers: how to cut the O(n^2) of attention" (section on the main
+ *   sparsity templates: near neighbours plus keys at a fixed step) --
+ *   pattern causal, window_left = stride - 1, window_right = 0,
+ *   stride_phase = stride - 1 and no other term, q_offset 0, n_q == n_kv a
+ *   multiple of stride with n_q >= 3 * stride -- computed as three disjoint
+ *   key sets per row: the local band through block lists, the strided keys
+ *   as plain causal attention between strided views of the same tensors
+ *   (one per head and key residue), and the last row; the later parts are
+ *   merged into the first with log-sum-exp weights.  O must be float32 and
+ *   lse non-NULL; block_q, block_kv and the list pointers are ignored: the
+ *   block lists of the parts are read from `workspace` (at least
+ *   sa_attn_workspace_bytes bytes, 256-byte aligned), where
+ *   sa_attn_strided_plan has built them for the same pattern and n_q
+ *   (batch, heads, head_dim, strides and tensors may differ between calls).
+ *   Other patterns are rejected (SA_ERR_INVALID_ARG); they run in
+ *   SA_MODE_BLOCKS.
  */
 typedef struct sa_attn_args {
     const void *q;
@@ -173,8 +190,10 @@ typedef struct sa_attn_args {
 } sa_attn_args;
 
 /*
- * sa_attn_workspace_bytes -- bytes of device scratch that let sa_attn_fwd
- * take its split form for these arguments, 0 when it has none.
+ * sa_attn_workspace_bytes -- bytes of device scratch that sa_attn_fwd needs
+ * (SA_MODE_STRIDED: the block lists of its parts; 0 if the pattern is not
+ * the strided template) or that let it take its split form (gather mode),
+ * 0 when it has none.
  *
  * Gather mode over a long key range (n_kv above 2^21 / (4 * head_dim)
  * keys, at most 256 ranges, batch * heads * ranges * n_q below 2^31) has a
@@ -190,6 +209,16 @@ typedef struct sa_attn_args {
  * sharing one workspace must not run concurrently.
  */
 size_t sa_attn_workspace_bytes(const sa_attn_args *args);
+
+/*
+ * sa_attn_strided_plan -- the block lists of SA_MODE_STRIDED's three parts
+ * (band, residue views, last row) into args->workspace, built once for a
+ * pattern and length and read by every later sa_attn_fwd in that mode.  Uses
+ * mode (must be SA_MODE_STRIDED), pattern, n_q, n_kv, the K/V row strides
+ * (for the offset limit), workspace and workspace_bytes of `args`; rejects
+ * what sa_attn_fwd would reject for these fields.  Asynchronous on `stream`.
+ */
+sa_status sa_attn_strided_plan(const sa_attn_args *args, void *stream);
 
 /*
  * sa_attn_fwd -- O = softmax(Q K^T * scale restricted to allowed pairs) V, and LSE.

@@ -244,22 +244,54 @@ def test_merge_partial_argument_errors():
     assert L.sa_merge_partial(None, None, None, None, 0, 1, 64, 128, None, None, 16, 31, 2, None) == _lib.SA_OK
 
 
-def test_strided_form_detection():
+def test_strided_form_detection_and_workspace():
+    """SA_MODE_STRIDED accepts only the strided template (its workspace query is 0
+    otherwise) and its scratch holds the three parts' block lists, 64 x 64 tiles."""
     import block_sparse_attention_sa_amd as sa
     pat = dict(causal=1, window_left=127, window_right=0, stride=128, stride_phase=127)
-    assert sa.strided_stride(pat, 16384, 16384) == 128
-    assert sa.strided_stride(pat, 16384, 16000) == 0            # n_q != n_kv
-    assert sa.strided_stride(pat, 16300, 16300) == 0            # not a multiple of the stride
-    assert sa.strided_stride(pat, 256, 256) == 0                # fewer than three groups
-    assert sa.strided_stride(dict(pat, sinks=4), 16384, 16384) == 0
-    assert sa.strided_stride(dict(pat, stride_phase=3), 16384, 16384) == 0
-    assert sa.strided_stride(dict(pat, window_left=64), 16384, 16384) == 0
-    assert sa.strided_stride(dict(pat, causal=0), 16384, 16384) == 0
+    up = lambda x: (x + 255) // 256 * 256
+
+    def lists(at, nq, nkv):
+        nqb, nkb = -(-nq // 64), -(-nkv // 64)
+        return up(up(up(up(at + 4 * nqb) + 4 * nqb * nkb) + nqb * nkb) + 8)
+
+    n, S = 16384, 128
+    G = n // S
+    exp = lists(lists(lists(0, n, n), G - 2, G), 1, G)
+    assert sa.attn_workspace_bytes_strided(pat, 1, 16, n, 64) == exp
+    assert sa.attn_workspace_bytes_strided(pat, 1, 16, 16300, 64) == 0           # not a multiple of the stride
+    assert sa.attn_workspace_bytes_strided(pat, 1, 16, 256, 64) == 0             # fewer than three groups
+    for bad in (dict(pat, sinks=4), dict(pat, stride_phase=3), dict(pat, window_left=64), dict(pat, causal=0),
+                dict(pat, global_tokens=1), dict(pat, q_offset=5)):
+        assert sa.attn_workspace_bytes_strided(bad, 1, 16, n, 64) == 0, bad
 
 
-def test_plan_strided_rejects_other_patterns():
-    import block_sparse_attention_sa_amd as sa
-    pat = dict(causal=1, window_left=127, window_right=0, stride=128, stride_phase=127)
-    for bad, n in ((dict(pat, sinks=1), 16384), (pat, 16300), (dict(causal=1, window_left=127), 16384)):
-        with pytest.raises(ValueError):
-            sa.plan_strided(bad, n)        # raises before any device work
+def test_strided_mode_argument_errors():
+    L = _lib.lib()
+    a = _args(mode=_lib.SA_MODE_STRIDED, n_q=1024, n_kv=1024, o_dtype=_lib.SA_DTYPE_F32, lse=8192)
+    a.pattern = _lib.SaPattern(causal=1, window_left=127, window_right=0, stride=128, stride_phase=127,
+                               unit_window=-1)
+    for st in (a.q_strides, a.k_strides, a.v_strides, a.o_strides):
+        st[:] = [1 << 20, 1 << 16, 64]
+    need = L.sa_attn_workspace_bytes(ctypes.byref(a))
+    assert need > 0
+    assert L.sa_attn_fwd(ctypes.byref(a), None) == _lib.SA_ERR_INVALID_ARG and "workspace" in _err()
+    a.workspace, a.workspace_bytes = 1 << 20, need - 1
+    assert L.sa_attn_fwd(ctypes.byref(a), None) == _lib.SA_ERR_INVALID_ARG
+    a.workspace, a.workspace_bytes = (1 << 20) + 16, need
+    assert L.sa_attn_fwd(ctypes.byref(a), None) == _lib.SA_ERR_INVALID_ARG and "aligned" in _err()
+    a.workspace = 1 << 20
+    a.o_dtype = _lib.SA_DTYPE_BF16
+    assert L.sa_attn_fwd(ctypes.byref(a), None) == _lib.SA_ERR_UNSUPPORTED and "float32" in _err()
+    a.o_dtype = _lib.SA_DTYPE_F32
+    a.lse = None
+    assert L.sa_attn_fwd(ctypes.byref(a), None) == _lib.SA_ERR_INVALID_ARG and "lse" in _err()
+    a.lse = 8192
+    a.pattern.sinks = 2
+    assert L.sa_attn_fwd(ctypes.byref(a), None) == _lib.SA_ERR_INVALID_ARG and "template" in _err()
+    assert L.sa_attn_strided_plan(ctypes.byref(a), None) == _lib.SA_ERR_INVALID_ARG and "template" in _err()
+    a.pattern.sinks = 0
+    a.workspace_bytes = need - 1
+    assert L.sa_attn_strided_plan(ctypes.byref(a), None) == _lib.SA_ERR_INVALID_ARG and "workspace" in _err()
+    a.mode = _lib.SA_MODE_BLOCKS
+    assert L.sa_attn_strided_plan(ctypes.byref(a), None) == _lib.SA_ERR_INVALID_ARG and "mode" in _err()

@@ -1,5 +1,6 @@
-"""The strided template computed as local band + residue views, merged by LSE,
-vs the fp64 oracle of the whole pattern (O <= 1e-2, LSE <= 1e-3)."""
+"""The strided template computed as local band + residue views, merged by LSE in
+the kernels' epilogues (sa_attn_fwd, SA_MODE_STRIDED), vs the fp64 oracle of the
+whole pattern (O <= 1e-2, LSE <= 1e-3)."""
 
 import numpy as np
 import pytest
@@ -29,10 +30,9 @@ def test_strided_small_vs_oracle(B, H, S, G, d):
     n = S * G
     q, k, v = _rand(rng, B, H, n, d)
     pat = _pattern(S)
-    assert sa.strided_stride(pat, n, n) == S
+    assert sa.attn_workspace_bytes_strided(pat, B, H, n, d) > 0
     print(f"strided small B={B} H={H} S={S} n={n} d={d}", flush=True)
-    plan = sa.plan_strided(pat, n)
-    o, lse = sa.attn_fwd_strided(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), plan)
+    o, lse = sa.attn_fwd_strided(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), pat)
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attn_rows(pat, q, k, v)
     check_o_lse(o.cpu().numpy().reshape(-1, d), lse.cpu().numpy().reshape(-1), o_ref, lse_ref,
@@ -47,9 +47,8 @@ def test_strided_noncontiguous_layout():
     q, k, v = _rand(rng, B, H, n, d)
     dev = [to_dev_bf16(np.ascontiguousarray(t.transpose(0, 2, 1, 3))).transpose(1, 2) for t in (q, k, v)]
     assert not dev[0].is_contiguous()
-    plan = sa.plan_strided(_pattern(S), n)
     print("strided non-contiguous layout", flush=True)
-    o, lse = sa.attn_fwd_strided(*dev, plan)
+    o, lse = sa.attn_fwd_strided(*dev, _pattern(S))
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attn_rows(_pattern(S), q, k, v)
     check_o_lse(o.cpu().numpy().reshape(-1, d), lse.cpu().numpy().reshape(-1), o_ref, lse_ref, ctx="bnhd")
@@ -59,14 +58,30 @@ def test_strided_full_size_all_rows():
     """The 16,384-token strided workload (stride 128, H = 16, d = 64): every row."""
     cfg, inp, o_ref, lse_ref = full_config_reference(3)
     pat = cfg.pattern.as_dict()
-    assert sa.strided_stride(pat, cfg.N, cfg.N) == 128
     q, k, v = (to_dev_bf16(inp[t]) for t in ("q", "k", "v"))
     print("strided full size", flush=True)
-    plan = sa.plan_strided(pat, cfg.N)
-    o, lse = sa.attn_fwd_strided(q, k, v, plan)
+    o, lse = sa.attn_fwd_strided(q, k, v, pat)
     torch.cuda.synchronize()
     check_o_lse(o.cpu().numpy().reshape(-1, cfg.d), lse.cpu().numpy().reshape(-1), o_ref, lse_ref,
                 ctx="config 3 strided form")
+
+
+def test_strided_rejects_other_patterns_and_reuses_workspace():
+    """Patterns that are not the template are rejected before any work; a workspace
+    is reused by a second call on other inputs with the same shape."""
+    rng = np.random.default_rng(9)
+    B, H, S, G, d = 1, 2, 64, 5, 128
+    n = S * G
+    q, k, v = _rand(rng, B, H, n, d)
+    with pytest.raises(ValueError):
+        sa.attn_fwd_strided(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), dict(_pattern(S), sinks=2))
+    ws = sa.strided_plan(_pattern(S), B, H, n, d)
+    for seed in (1, 2):
+        q, k, v = _rand(np.random.default_rng(seed), B, H, n, d)
+        print(f"strided workspace reuse {seed}", flush=True)
+        o, lse = sa.attn_fwd_strided(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), _pattern(S), workspace=ws)
+        o_ref, lse_ref = oracle.attn_rows(_pattern(S), q, k, v)
+        check_o_lse(o.cpu().numpy().reshape(-1, d), lse.cpu().numpy().reshape(-1), o_ref, lse_ref, ctx=f"reuse {seed}")
 
 
 def test_merge_partial_closed_form():
