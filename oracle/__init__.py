@@ -23,7 +23,15 @@ Parity status of each function (pins live in ``tests/test_oracle_pins.py``):
 * ``indexer_scores``    pinned: exact rational arithmetic with per-step
   float32 rounding on tiny inputs; fp64 part against numpy fp64 dot.
 * ``topk_rows``         pinned: brute-force Python sort on tiny rows, all-ties
-  (zero queries) gives 0..k-1, k >= candidates gives every candidate.
+  (zero queries) gives 0..k-1, k >= candidates gives every candidate; NaN
+  order against Python's sort on an explicit key.
+* ``select_blocks``     pinned: numpy brute force of the block means and
+  scores (another summation order) with a sort; zero queries (all ties: the
+  lowest reachable blocks); planted one-hot keys with a known ranking;
+  n_select >= reachable blocks gives every causal block.
+* ``attn_sel_rows``     pinned: dense masked attention brute force with the
+  mask built from the lists (numpy); every causal block selected equals
+  causal attention (torch fp64 SDPA).
 """
 
 from __future__ import annotations
@@ -93,6 +101,11 @@ def _load():
         lib.orc_indexer_scores.restype = None
         lib.orc_topk_rows.argtypes = [_P, _P, _I64, _I64, _I32, _P]
         lib.orc_topk_rows.restype = None
+        lib.orc_select_blocks.argtypes = [_P, _P, _I64, _I64, _I64, _I32, _I64, _I32, _I32, _I32, _P, _P, _P, _P]
+        lib.orc_select_blocks.restype = None
+        lib.orc_attn_sel_rows.argtypes = [_P, _P, _P, _I64, _I64, _I32, ctypes.c_double, _I64, _I32, _I32, _P, _P,
+                                          _P, _I64, _P, _P]
+        lib.orc_attn_sel_rows.restype = None
         lib.orc_num_threads.argtypes = []
         lib.orc_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -230,3 +243,43 @@ def topk_rows(sigma: np.ndarray, n_cand, k: int) -> np.ndarray:
     idx = np.zeros((n_rows, k), np.int32)
     _load().orc_topk_rows(_ptr(sigma), _ptr(n_cand), n_rows, n_kv, int(k), _ptr(idx))
     return idx
+
+
+def select_blocks(q: np.ndarray, k: np.ndarray, q_offset: int, bq: int, bk: int, n_select: int):
+    """Content-selected key blocks of q [B, H, n_q, d], k [B, H, n_kv, d] (bf16 bits).
+
+    Returns dict(kv_count [B*H, nqb], kv_index [B*H, nqb, nkb], kv_partial, live_pairs)."""
+    q = np.ascontiguousarray(q, np.uint16)
+    k = np.ascontiguousarray(k, np.uint16)
+    B, H, n_q, d = q.shape
+    n_kv = k.shape[2]
+    nqb, nkb = -(-n_q // bq), -(-n_kv // bk)
+    kv_count = np.zeros((B * H, nqb), np.int32)
+    kv_index = np.zeros((B * H, nqb, nkb), np.int32)
+    kv_partial = np.zeros((B * H, nqb, nkb), np.uint8)
+    live = np.zeros(1, np.int64)
+    _load().orc_select_blocks(_ptr(q), _ptr(k), B * H, n_q, n_kv, d, int(q_offset), bq, bk, int(n_select),
+                              _ptr(kv_count), _ptr(kv_index), _ptr(kv_partial), _ptr(live))
+    return dict(kv_count=kv_count, kv_index=kv_index, kv_partial=kv_partial, live_pairs=int(live[0]))
+
+
+def attn_sel_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_offset: int, bq: int, bk: int, kv_count,
+                  kv_index, rows=None, scale: float | None = None):
+    """fp64 attention of rows over their query block's selected key blocks, causal."""
+    q = np.ascontiguousarray(q, np.uint16)
+    k = np.ascontiguousarray(k, np.uint16)
+    v = np.ascontiguousarray(v, np.uint16)
+    kv_count = np.ascontiguousarray(kv_count, np.int32)
+    kv_index = np.ascontiguousarray(kv_index, np.int32)
+    B, H, n_q, d = q.shape
+    n_kv = k.shape[2]
+    if rows is None:
+        rows = np.arange(B * H * n_q, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, np.int64)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    o = np.zeros((rows.size, d), np.float64)
+    lse = np.zeros(rows.size, np.float64)
+    _load().orc_attn_sel_rows(_ptr(q), _ptr(k), _ptr(v), n_q, n_kv, d, float(scale), int(q_offset), bq, bk,
+                              _ptr(kv_count), _ptr(kv_index), _ptr(rows), rows.size, _ptr(o), _ptr(lse))
+    return o, lse

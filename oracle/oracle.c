@@ -43,6 +43,15 @@
  *  - orc_topk_rows: the k candidates that come first in the total order
  *    (score descending, index ascending; a NaN score above every number),
  *    emitted in ascending index order.
+ *  - orc_select_blocks: content-selected key blocks per (batch*head, query
+ *    block), the "selection of the most relevant blocks" of [G]'s common
+ *    sparsity patterns (Native Sparse Attention), read as: the block's own
+ *    (diagonal) key blocks, plus the n_select causally reachable key blocks
+ *    of highest score <mean query of the block, mean key of the block>
+ *    (ties to the lower block), means taken over the block size in fp64.
+ *  - orc_attn_sel_rows: attention of each row over the keys of its query
+ *    block's selected key blocks, causally ([B] masked attention with the
+ *    mask given by the selected blocks).
  *
  * Inputs are raw bfloat16 bit patterns (uint16); each is widened exactly.
  */
@@ -327,6 +336,135 @@ void orc_topk_rows(const float *sigma, const int64_t *n_cand, int64_t n_rows, in
                 out[e] = -1;
         }
         free(buf);
+    }
+}
+
+/* Content-selected key blocks.  q [BH, n_q, d], k [BH, n_kv, d] contiguous
+ * bf16 bits; query row r has position q_offset + r.  For every (bh, query
+ * block i) with rows [i*bq, min((i+1)*bq, n_q)) and positions [p0, p1]:
+ *   qm[c] = (sum over the block's rows, in row order, of q[r][c]) / bq
+ *   km_j[c] = (sum over key block j's rows of k[s][c]) / bk
+ * (rows past the end count as zero; bq, bk are powers of two, so the
+ * division is exact), both in fp64;
+ *   score(i, j) = qm . km_j, an fp64 fused multiply-add chain over c;
+ *   reachable: j*bk <= p1 (some key of the block is causally visible);
+ *   own: the key blocks holding positions p0 .. p1;
+ *   selected = own  +  the n_sel reachable, not-own blocks first in the
+ *   order (score descending, block ascending).
+ * Output per (bh, i): kv_count, kv_index (ascending, -1 padded), kv_partial
+ * (1 when some pair of the clipped tile is not causal), and live_pairs = the
+ * causal pairs over all selected tiles. */
+void orc_select_blocks(const uint16_t *q, const uint16_t *k, int64_t BH, int64_t n_q, int64_t n_kv, int32_t d,
+                       int64_t q_offset, int32_t bq, int32_t bk, int32_t n_sel, int32_t *kv_count,
+                       int32_t *kv_index, uint8_t *kv_partial, int64_t *live_pairs)
+{
+    int64_t nqb = (n_q + bq - 1) / bq, nkb = (n_kv + bk - 1) / bk;
+    int64_t total = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : total)
+    for (int64_t item = 0; item < BH * nqb; ++item) {
+        int64_t bh = item / nqb, i = item % nqb;
+        int64_t r0 = i * bq, r1 = r0 + bq < n_q ? r0 + bq : n_q;
+        int64_t p0 = q_offset + r0, p1 = q_offset + r1 - 1;
+        double *qm = (double *)malloc(sizeof(double) * (size_t)d);
+        double *km = (double *)malloc(sizeof(double) * (size_t)d);
+        double *score = (double *)malloc(sizeof(double) * (size_t)(nkb > 0 ? nkb : 1));
+        unsigned char *sel = (unsigned char *)calloc((size_t)(nkb > 0 ? nkb : 1), 1);
+        for (int32_t c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int64_t r = r0; r < r1; ++r)
+                acc += bf16_to_f64(q[(bh * n_q + r) * d + c]);
+            qm[c] = acc / bq;
+        }
+        for (int64_t j = 0; j < nkb; ++j) {
+            int64_t s0 = j * bk, s1 = s0 + bk < n_kv ? s0 + bk : n_kv;
+            for (int32_t c = 0; c < d; ++c) {
+                double acc = 0.0;
+                for (int64_t s = s0; s < s1; ++s)
+                    acc += bf16_to_f64(k[(bh * n_kv + s) * d + c]);
+                km[c] = acc / bk;
+            }
+            double dot = 0.0;
+            for (int32_t c = 0; c < d; ++c)
+                dot = fma(qm[c], km[c], dot);
+            score[j] = dot;
+            int own = s0 <= p1 && s1 - 1 >= p0;
+            if (own)
+                sel[j] = 1;
+        }
+        /* n_sel times: the best reachable block not taken yet */
+        for (int32_t t = 0; t < n_sel; ++t) {
+            int64_t best = -1;
+            for (int64_t j = 0; j < nkb; ++j) {
+                if (sel[j] || j * bk > p1)
+                    continue;
+                if (best < 0 || score[j] > score[best])
+                    best = j;
+            }
+            if (best < 0)
+                break;
+            sel[best] = 2;
+        }
+        int32_t n_live = 0;
+        for (int64_t j = 0; j < nkb; ++j) {
+            if (!sel[j])
+                continue;
+            int64_t s0 = j * bk, s1 = s0 + bk < n_kv ? s0 + bk : n_kv;
+            int64_t cnt = 0;
+            for (int64_t qp = p0; qp <= p1; ++qp)
+                for (int64_t s = s0; s < s1; ++s)
+                    cnt += s <= qp;
+            total += cnt;
+            kv_index[item * nkb + n_live] = (int32_t)j;
+            kv_partial[item * nkb + n_live] = (uint8_t)(cnt != (p1 - p0 + 1) * (s1 - s0));
+            ++n_live;
+        }
+        kv_count[item] = n_live;
+        for (int64_t e = n_live; e < nkb; ++e) {
+            kv_index[item * nkb + e] = -1;
+            kv_partial[item * nkb + e] = 0;
+        }
+        free(qm);
+        free(km);
+        free(score);
+        free(sel);
+    }
+    *live_pairs = total;
+}
+
+/* Attention of rows over content-selected blocks: row (bh, r) attends to the
+ * keys s <= q_offset + r whose block s / bk is listed for (bh, r / bq) in
+ * kv_count / kv_index ([BH, nqb] / [BH, nqb, nkb], as orc_select_blocks
+ * writes them).  rows[] as in orc_attn_rows. */
+void orc_attn_sel_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t n_q, int64_t n_kv,
+                       int32_t d, double scale, int64_t q_offset, int32_t bq, int32_t bk, const int32_t *kv_count,
+                       const int32_t *kv_index, const int64_t *rows, int64_t n_rows, double *o, double *lse)
+{
+    int64_t nqb = (n_q + bq - 1) / bq, nkb = (n_kv + bk - 1) / bk;
+#pragma omp parallel
+    {
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_kv > 0 ? n_kv : 1));
+        double *s_buf = (double *)malloc(sizeof(double) * (size_t)(n_kv > 0 ? n_kv : 1));
+        unsigned char *in = (unsigned char *)malloc((size_t)(nkb > 0 ? nkb : 1));
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < n_rows; ++r) {
+            int64_t bh = rows[r] / n_q, qi = rows[r] % n_q;
+            int64_t item = bh * nqb + qi / bq;
+            memset(in, 0, (size_t)(nkb > 0 ? nkb : 1));
+            for (int32_t e = 0; e < kv_count[item]; ++e) {
+                int32_t j = kv_index[item * nkb + e];
+                if (j >= 0 && j < nkb)
+                    in[j] = 1;
+            }
+            int64_t nk = 0;
+            for (int64_t s = 0; s < n_kv; ++s)
+                if (s <= q_offset + qi && in[s / bk])
+                    keys[nk++] = s;
+            attend_list(q + (bh * n_q + qi) * (int64_t)d, k + bh * n_kv * (int64_t)d,
+                        v + bh * n_kv * (int64_t)d, d, scale, keys, nk, s_buf, o + r * (int64_t)d, lse + r);
+        }
+        free(keys);
+        free(s_buf);
+        free(in);
     }
 }
 

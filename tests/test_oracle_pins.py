@@ -502,3 +502,137 @@ def test_topk_against_full_sort_on_indexer_scores():
         nc = int(n_cand[r])
         order = np.lexsort((np.arange(nc), -sig[r, :nc].astype(np.float64)))
         assert got[r].tolist() == sorted(order[:k].tolist())
+
+
+# ----------------------------------------------------------------------------
+# content-selected blocks (the glossary's NSA block selection)
+# ----------------------------------------------------------------------------
+
+def _numpy_selection(q, k, q_offset, bq, bk, n_sel):
+    """Block means (rows past the end as zero), scores and the selection with
+    numpy's own reductions; returns per (bh, i) the selected block set and the
+    gap between the last chosen and the first rejected score."""
+    B, H, n_q, d = q.shape
+    n_kv = k.shape[2]
+    nqb, nkb = -(-n_q // bq), -(-n_kv // bk)
+    qf = np.zeros((B * H, nqb * bq, d))
+    kf = np.zeros((B * H, nkb * bk, d))
+    qf[:, :n_q] = _bf16_f64(q).reshape(B * H, n_q, d)
+    kf[:, :n_kv] = _bf16_f64(k).reshape(B * H, n_kv, d)
+    qm = qf.reshape(B * H, nqb, bq, d).mean(axis=2)
+    km = kf.reshape(B * H, nkb, bk, d).mean(axis=2)
+    scores = np.einsum("bid,bjd->bij", qm, km)
+    out = {}
+    for bh in range(B * H):
+        for i in range(nqb):
+            p0, p1 = q_offset + i * bq, q_offset + min((i + 1) * bq, n_q) - 1
+            own = {j for j in range(nkb) if j * bk <= p1 and min((j + 1) * bk, n_kv) - 1 >= p0}
+            cand = sorted((j for j in range(nkb) if j * bk <= p1 and j not in own),
+                          key=lambda j: (-scores[bh, i, j], j))
+            chosen = cand[:n_sel]
+            gap = np.inf
+            if len(cand) > n_sel and n_sel > 0:
+                gap = scores[bh, i, cand[n_sel - 1]] - scores[bh, i, cand[n_sel]]
+            out[(bh, i)] = (sorted(own | set(chosen)), gap)
+    return out
+
+
+def _lists_as_sets(sel):
+    res = {}
+    BH, nqb, _ = sel["kv_index"].shape
+    for bh in range(BH):
+        for i in range(nqb):
+            res[(bh, i)] = sel["kv_index"][bh, i, : sel["kv_count"][bh, i]].tolist()
+    return res
+
+
+@pytest.mark.parametrize("n_q,n_kv,q_offset,bq,bk,n_sel", [(300, 300, 0, 64, 64, 2), (256, 512, 256, 128, 64, 3),
+                                                           (200, 333, 133, 64, 128, 1), (130, 130, 0, 64, 64, 5)])
+def test_select_blocks_vs_numpy_brute_force(n_q, n_kv, q_offset, bq, bk, n_sel):
+    """The selection against numpy's means and scores (a different summation
+    order; rows whose kept/rejected gap is within rounding are not compared)."""
+    rng = np.random.default_rng(n_q + n_kv + bq + n_sel)
+    f = lambda *s: W.f32_to_bf16_bits(rng.standard_normal(s, dtype=np.float32))
+    q, k = f(1, 3, n_q, 32), f(1, 3, n_kv, 32)
+    got = oracle.select_blocks(q, k, q_offset, bq, bk, n_sel)
+    want = _numpy_selection(q, k, q_offset, bq, bk, n_sel)
+    sets = _lists_as_sets(got)
+    compared = 0
+    for key, (blocks, gap) in want.items():
+        if gap > 1e-9:
+            assert sets[key] == blocks, key
+            compared += 1
+    assert compared >= len(want) - 1
+    # partial flags and pair counts from the causal rule inside the chosen tiles
+    lists = {}
+    total = 0
+    for (bh, i), blocks in sets.items():
+        p0, p1 = q_offset + i * bq, q_offset + min((i + 1) * bq, n_q) - 1
+        for e, j in enumerate(blocks):
+            s0, s1 = j * bk, min((j + 1) * bk, n_kv)
+            cnt = sum(max(0, min(s1, qp + 1) - s0) for qp in range(p0, p1 + 1))
+            total += cnt
+            assert got["kv_partial"][bh, i, e] == int(cnt != (p1 - p0 + 1) * (s1 - s0))
+        assert np.all(got["kv_index"][bh, i, len(blocks):] == -1)
+    assert got["live_pairs"] == total
+
+
+def test_select_blocks_zero_queries_take_the_lowest_blocks():
+    """Q = 0: every score is 0, so the ties go to the lowest reachable blocks."""
+    rng = np.random.default_rng(21)
+    n, bq, n_sel = 640, 64, 3
+    k = W.f32_to_bf16_bits(rng.standard_normal((1, 2, n, 16), dtype=np.float32))
+    q = np.zeros((1, 2, n, 16), np.uint16)
+    got = _lists_as_sets(oracle.select_blocks(q, k, 0, bq, bq, n_sel))
+    for (bh, i), blocks in got.items():
+        assert blocks == sorted(set(range(min(i, n_sel))) | {i}), (bh, i)
+
+
+def test_select_blocks_planted_ranking():
+    """Keys of block j all equal v_j * e_0 and queries e_0: block j scores v_j,
+    so the chosen blocks are the n_sel reachable ones of largest v_j."""
+    n, bq, n_sel, d = 1024, 64, 4, 16
+    nkb = n // bq
+    vals = np.random.default_rng(22).permutation(nkb).astype(np.float32) + 1.0  # distinct, exact in bf16
+    k = np.zeros((1, 1, n, d), np.uint16)
+    k[0, 0, :, 0] = W.f32_to_bf16_bits(np.repeat(vals, bq))
+    q = np.zeros((1, 1, n, d), np.uint16)
+    q[0, 0, :, 0] = W.f32_to_bf16_bits(np.ones(1, np.float32))[0]
+    got = _lists_as_sets(oracle.select_blocks(q, k, 0, bq, bq, n_sel))
+    for i in range(nkb):
+        best = sorted(range(i), key=lambda j: -vals[j])[:n_sel]
+        assert got[(0, i)] == sorted(set(best) | {i}), i
+
+
+def test_select_every_block_is_causal_attention():
+    """n_select above the reachable blocks keeps every causal block: attention
+    over the selection is causal attention (torch fp64 SDPA)."""
+    rng = np.random.default_rng(23)
+    n, d = 320, 64
+    q, k, v = _rand_qkv(rng, 1, 2, n, n, d)
+    sel = oracle.select_blocks(q, k, 0, 64, 64, 99)
+    o, lse = oracle.attn_sel_rows(q, k, v, 0, 64, 64, sel["kv_count"], sel["kv_index"])
+    tq, tk, tv = (torch.from_numpy(_bf16_f64(x)) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True)
+    np.testing.assert_allclose(o.reshape(ref.shape), ref.numpy(), rtol=0, atol=1e-12)
+    assert sel["live_pairs"] == 2 * n * (n + 1) // 2
+
+
+def test_attn_sel_rows_vs_dense_brute_force():
+    """Attention over the selected blocks against the dense masked brute force
+    with the mask built from the lists (causal inside the chosen tiles)."""
+    rng = np.random.default_rng(24)
+    n_q, n_kv, q_offset, bq, bk, d = 150, 230, 80, 64, 32, 16
+    q, k, v = _rand_qkv(rng, 1, 2, n_q, n_kv, d)
+    sel = oracle.select_blocks(q, k, q_offset, bq, bk, 2)
+    o, lse = oracle.attn_sel_rows(q, k, v, q_offset, bq, bk, sel["kv_count"], sel["kv_index"])
+    for h in range(2):
+        mask = np.zeros((n_q, n_kv), bool)
+        for r in range(n_q):
+            i = r // bq
+            for j in sel["kv_index"][h, i, : sel["kv_count"][h, i]]:
+                cols = np.arange(j * bk, min((j + 1) * bk, n_kv))
+                mask[r, cols[cols <= q_offset + r]] = True
+        bo, blse = brute.masked_attention(_bf16_f64(q[0, h]), _bf16_f64(k[0, h]), _bf16_f64(v[0, h]), mask)
+        np.testing.assert_allclose(o[h * n_q:(h + 1) * n_q], bo, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[h * n_q:(h + 1) * n_q], blse, rtol=0, atol=1e-12)
