@@ -78,6 +78,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dsa", action="store_true")
     ap.add_argument("--no-strided", action="store_true")
+    ap.add_argument("--no-select", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="the CPU oracle repeats whole passes over the workload until this much time has passed")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -211,6 +212,9 @@ def main() -> int:
     if not args.no_strided:
         result["strided"] = _bench_strided(sa, W, np, torch, dev, dev_bf16)
 
+    if not args.no_select:
+        result["content_selected"] = _bench_select(sa, W, np, torch, dev, dev_bf16)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = _cpu_baseline(cfg, inp, args.cpu_seconds, np)
 
@@ -260,6 +264,46 @@ def _bench_strided(sa, W, np, torch, dev, dev_bf16, reps=10):
                       "64x64 band tiles, causal 64-row tiles per (head, key residue) view and the last row, the "
                       "later parts merged by log-sum-exp in the kernel epilogue",
     }
+
+def _bench_select(sa, W, np, torch, dev, dev_bf16, reps=20):
+    """Content-selected key blocks (workload 6): the selection (block means, scores,
+    top-n per query block and head) and the block kernel over the per-head lists."""
+    cfg = W.select_config()
+    _log("bench: generating the content-selected workload's inputs")
+    inp = W.select_inputs(cfg)
+    q, k, v = (dev_bf16(inp[t]) for t in ("q", "k", "v"))
+    sel = sa.select_blocks(q, k, cfg.block, cfg.block, cfg.n_select)
+    o = torch.empty((cfg.B, cfg.H, cfg.N, cfg.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((cfg.B, cfg.H, cfg.N), dtype=torch.float32, device=dev)
+    ws = torch.empty(1 << 22, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    steps = [("select", lambda: sa.select_blocks(q, k, cfg.block, cfg.block, cfg.n_select, workspace=ws, out=sel)),
+             ("attention", lambda: sa.attn_fwd(q, k, v, sel, out=o, lse=lse))]
+    for _, fn in steps:
+        fn()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for e in ev:
+        for j, (_, fn) in enumerate(steps):
+            e[j].record(stream)
+            fn()
+        e[-1].record(stream)
+    torch.cuda.synchronize()
+    t = {name: float(np.median([e[j].elapsed_time(e[j + 1]) for e in ev])) * 1e-3 for j, (name, _) in enumerate(steps)}
+    pairs = int(sel.live_pairs.item())
+    tiles = int(sel.kv_count.sum().item())
+    flop = 4.0 * cfg.d * pairs
+    return {
+        "workload": "content-selected key blocks (own block + top-8 by mean-query . mean-key per query block and "
+                    "head), causal, B=1 H=32 N=8192 d=128, 128x128 blocks",
+        "live_pairs": pairs, "tiles": tiles,
+        "select_us": round(t["select"] * 1e6, 1),
+        "attention_us": round(t["attention"] * 1e6, 1),
+        "attention_tflops_over_live_pairs": round(flop / t["attention"] / 1e12, 2),
+        "attention_tflops_over_live_tiles": round(4.0 * cfg.d * cfg.block * cfg.block * tiles / t["attention"] / 1e12, 2),
+        "total_tflops_over_live_pairs": round(flop / (t["select"] + t["attention"]) / 1e12, 2),
+    }
+
 
 def _bench_dsa(sa, W, np, torch, dev, dev_bf16, reps=10):
     """The content-selected workload: the streaming indexer + top-k (no score

@@ -24,7 +24,7 @@ import numpy as np
 from . import _lib
 from ._lib import SaError  # noqa: F401
 
-__all__ = ["BlockLists", "build_block_mask", "attn_fwd", "attn_workspace_bytes", "attn_fwd_strided",
+__all__ = ["BlockLists", "build_block_mask", "select_blocks", "attn_fwd", "attn_workspace_bytes", "attn_fwd_strided",
            "attn_workspace_bytes_strided", "strided_plan", "merge_partial", "indexer_scores", "topk", "indexer_topk",
            "indexer_topk_workspace_bytes", "indexer_topk_noalloc", "describe", "SaError"]
 
@@ -82,15 +82,16 @@ def device_pattern(pattern, device) -> DevicePattern:
 class BlockLists:
     """Output of :func:`build_block_mask` (device tensors)."""
 
-    kv_count: object    # int32 [nqb]
-    kv_index: object    # int32 [nqb, nkb]
-    kv_partial: object  # uint8 [nqb, nkb]
+    kv_count: object    # int32 [nqb] (per_head: [B*H, nqb])
+    kv_index: object    # int32 [nqb, nkb] (per_head: [B*H, nqb, nkb])
+    kv_partial: object  # uint8 like kv_index
     live_pairs: object  # int64 [1]
     n_q: int
     n_kv: int
     block_q: int
     block_kv: int
     pattern: DevicePattern
+    per_head: bool = False
 
 
 def build_block_mask(pattern, n_q: int, n_kv: int, block_q: int, block_kv: int,
@@ -111,6 +112,46 @@ def build_block_mask(pattern, n_q: int, n_kv: int, block_q: int, block_kv: int,
         ctypes.byref(out.pattern.struct), n_q, n_kv, block_q, block_kv,
         out.kv_count.data_ptr(), out.kv_index.data_ptr(), out.kv_partial.data_ptr(),
         out.live_pairs.data_ptr(), _stream_ptr(device)))
+    return out
+
+
+def select_blocks(q, k, block_q: int, block_kv: int, n_select: int, q_offset: int = 0, workspace=None,
+                  out: Optional[BlockLists] = None) -> BlockLists:
+    """Content-selected key blocks per (b, h, query block) (``sa_select_blocks``): the
+    block's own key blocks plus the ``n_select`` causally reachable ones whose mean key
+    scores highest against the block's mean query.  q [B, H, n_q, d], k [B, H, n_kv, d]
+    bfloat16.  The result drives :func:`attn_fwd` with a causal element mask."""
+    torch = _torch()
+    for t in (q, k):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 4:
+            raise ValueError("q and k must be 4-d bfloat16 CUDA tensors")
+    B, H, n_q, d = q.shape
+    n_kv = k.shape[2]
+    nqb, nkb = -(-n_q // block_q), -(-n_kv // block_kv)
+    dev = q.device
+    if out is None:
+        out = BlockLists(
+            kv_count=torch.empty((B * H, nqb), dtype=torch.int32, device=dev),
+            kv_index=torch.empty((B * H, nqb, nkb), dtype=torch.int32, device=dev),
+            kv_partial=torch.empty((B * H, nqb, nkb), dtype=torch.uint8, device=dev),
+            live_pairs=torch.empty(1, dtype=torch.int64, device=dev),
+            n_q=n_q, n_kv=n_kv, block_q=block_q, block_kv=block_kv,
+            pattern=device_pattern(dict(causal=1, q_offset=q_offset, window_left=n_kv + q_offset), dev),
+            per_head=True)
+    a = _lib.SaSelectArgs()
+    a.q, a.k = q.data_ptr(), k.data_ptr()
+    a.batch, a.heads, a.n_q, a.n_kv, a.head_dim = B, H, n_q, n_kv, d
+    a.q_strides[:] = _strides3(q)
+    a.k_strides[:] = _strides3(k)
+    a.q_offset, a.block_q, a.block_kv, a.n_select = int(q_offset), block_q, block_kv, int(n_select)
+    a.kv_count, a.kv_index = out.kv_count.data_ptr(), out.kv_index.data_ptr()
+    a.kv_partial, a.live_pairs = out.kv_partial.data_ptr(), out.live_pairs.data_ptr()
+    need = int(_lib.lib().sa_select_blocks_workspace(ctypes.byref(a)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    _lib.check(_lib.lib().sa_select_blocks(ctypes.byref(a), _stream_ptr(dev)))
     return out
 
 
@@ -180,6 +221,9 @@ def attn_fwd(q, k, v, blocks: Optional[BlockLists] = None, gather_idx=None, *,
         a.kv_index = blocks.kv_index.data_ptr()
         a.kv_partial = blocks.kv_partial.data_ptr()
         a.pattern = blocks.pattern.struct
+        a.per_head_lists = 1 if blocks.per_head else 0
+        if blocks.per_head and tuple(blocks.kv_count.shape) != (B * H, -(-n_q // blocks.block_q)):
+            raise ValueError("per-head block lists were built for another batch * heads")
     else:
         g = gather_idx
         if g.dtype != torch.int32 or not g.is_cuda or not g.is_contiguous():

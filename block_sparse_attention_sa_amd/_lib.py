@@ -19,6 +19,7 @@ ABI_VERSION = 2
 
 EXPORTED = ("sa_build_block_mask", "sa_attn_workspace_bytes", "sa_attn_strided_plan", "sa_attn_fwd", "sa_indexer_scores", "sa_topk",
             "sa_indexer_topk_workspace", "sa_indexer_topk", "sa_indexer_topk_noalloc", "sa_merge_partial",
+            "sa_select_blocks_workspace", "sa_select_blocks",
             "sa_last_error", "sa_abi_version")
 
 _I64 = ctypes.c_int64
@@ -74,6 +75,31 @@ class SaAttnArgs(ctypes.Structure):
         ("gather_bh_stride", _I64),
         ("workspace", _P),
         ("workspace_bytes", _I64),
+        ("per_head_lists", _I64),
+    ]
+
+
+class SaSelectArgs(ctypes.Structure):
+    _fields_ = [
+        ("q", _P),
+        ("k", _P),
+        ("batch", _I64),
+        ("heads", _I64),
+        ("n_q", _I64),
+        ("n_kv", _I64),
+        ("head_dim", _I64),
+        ("q_strides", _I64 * 3),
+        ("k_strides", _I64 * 3),
+        ("q_offset", _I64),
+        ("block_q", _I64),
+        ("block_kv", _I64),
+        ("n_select", _I64),
+        ("kv_count", _P),
+        ("kv_index", _P),
+        ("kv_partial", _P),
+        ("live_pairs", _P),
+        ("workspace", _P),
+        ("workspace_bytes", _I64),
     ]
 
 
@@ -113,6 +139,10 @@ def lib() -> ctypes.CDLL:
         L.sa_indexer_topk.restype = ctypes.c_int
         L.sa_indexer_topk_noalloc.argtypes = [_P, _P, _I64, _I64, _I32, _I64, _I32, _P, _P]
         L.sa_indexer_topk_noalloc.restype = ctypes.c_int
+        L.sa_select_blocks_workspace.argtypes = [ctypes.POINTER(SaSelectArgs)]
+        L.sa_select_blocks_workspace.restype = ctypes.c_size_t
+        L.sa_select_blocks.argtypes = [ctypes.POINTER(SaSelectArgs), _P]
+        L.sa_select_blocks.restype = ctypes.c_int
         L.sa_merge_partial.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I32, ctypes.POINTER(_I64),
                                        ctypes.POINTER(_I64), _I32, _I64, _I64, _P]
         L.sa_merge_partial.restype = ctypes.c_int

@@ -462,6 +462,9 @@ sa_status sa_attn_fwd(const sa_attn_args* a, void* stream)
             p.kv_count = a->kv_count;
             p.kv_index = a->kv_index;
             p.kv_partial = a->kv_partial;
+            if (a->per_head_lists != 0 && a->per_head_lists != 1)
+                return fail(SA_ERR_INVALID_ARG, "per_head_lists must be 0 or 1");
+            p.per_head_lists = (int32_t)a->per_head_lists;
             // key tiles are fetched with 32-bit byte offsets from the (batch, head) base
             const int64_t row_b = 2 * std::max(a->k_strides[2], a->v_strides[2]);
             if ((a->n_kv + 256) * row_b > kI32Max)
@@ -615,6 +618,80 @@ sa_status sa_indexer_topk(const void* q_idx, const void* k_idx, int64_t n_q, int
                         "sa_indexer_topk");
     } catch (...) {
         return fail(SA_ERR_DEVICE, "sa_indexer_topk: unexpected exception");
+    }
+}
+
+static sa_status check_select(const sa_select_args* a, sa::SelectParams& p)
+{
+    if (!a) return fail(SA_ERR_INVALID_ARG, "args is NULL");
+    if (a->batch < 0 || a->heads < 0 || a->n_q < 0 || a->n_kv < 0 || a->q_offset < 0 || a->n_select < 0)
+        return fail(SA_ERR_INVALID_ARG, "negative size, offset or n_select");
+    if (a->head_dim != 64 && a->head_dim != 128) return fail(SA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    if ((a->block_q != 64 && a->block_q != 128) || (a->block_kv != 64 && a->block_kv != 128))
+        return fail(SA_ERR_UNSUPPORTED, "block_q and block_kv must be 64 or 128");
+    if (a->n_q > kI32Max || a->n_kv > kI32Max || a->q_offset + a->n_q > kI32Max || a->batch * a->heads > 65535)
+        return fail(SA_ERR_UNSUPPORTED, "sizes must stay below 2^31 and batch*heads below 65536");
+    const int64_t nqb = (a->n_q + a->block_q - 1) / a->block_q, nkb = (a->n_kv + a->block_kv - 1) / a->block_kv;
+    if (nkb > sa::kSelectMaxBlocks) return fail(SA_ERR_UNSUPPORTED, "more than %d key blocks", sa::kSelectMaxBlocks);
+    if (nqb > 65535) return fail(SA_ERR_UNSUPPORTED, "more than 65535 query blocks");
+    for (int i = 0; i < 3; ++i)
+        if (a->q_strides[i] < 0 || a->k_strides[i] < 0) return fail(SA_ERR_INVALID_ARG, "strides must be >= 0");
+    p = sa::SelectParams{};
+    p.q = (const uint16_t*)a->q;
+    p.k = (const uint16_t*)a->k;
+    p.q_sb = a->q_strides[0]; p.q_sh = a->q_strides[1]; p.q_sn = a->q_strides[2];
+    p.k_sb = a->k_strides[0]; p.k_sh = a->k_strides[1]; p.k_sn = a->k_strides[2];
+    p.batch = (int32_t)a->batch;
+    p.heads = (int32_t)a->heads;
+    p.n_q = (int32_t)a->n_q;
+    p.n_kv = (int32_t)a->n_kv;
+    p.d = (int32_t)a->head_dim;
+    p.q_offset = (int32_t)a->q_offset;
+    p.bq = (int32_t)a->block_q;
+    p.bk = (int32_t)a->block_kv;
+    p.nqb = (int32_t)nqb;
+    p.nkb = (int32_t)nkb;
+    p.n_sel = (int32_t)std::min<int64_t>(a->n_select, nkb);
+    p.kv_count = a->kv_count;
+    p.kv_index = a->kv_index;
+    p.kv_partial = a->kv_partial;
+    p.live_pairs = a->live_pairs;
+    return SA_OK;
+}
+
+size_t sa_select_blocks_workspace(const sa_select_args* a)
+{
+    sa::SelectParams p;
+    const std::string keep = g_err;  // a size query leaves the last error alone
+    const sa_status st = check_select(a, p);
+    g_err = keep;
+    if (st != SA_OK || a->batch * a->heads == 0 || p.nqb == 0 || p.nkb == 0) return 0;
+    return (size_t)sa::select_workspace_bytes(a->batch * a->heads, p.nqb, p.nkb, p.d);
+}
+
+sa_status sa_select_blocks(const sa_select_args* a, void* stream)
+{
+    try {
+        sa::SelectParams p;
+        sa_status st = check_select(a, p);
+        if (st != SA_OK) return st;
+        if (!a->live_pairs) return fail(SA_ERR_INVALID_ARG, "live_pairs is NULL");
+        hipStream_t s = (hipStream_t)stream;
+        if (a->batch * a->heads == 0 || p.nqb == 0 || p.nkb == 0)
+            return launched(sa::launch_zero_i64(a->live_pairs, s), "sa_select_blocks");
+        if (!a->q || !a->k || !a->kv_count || !a->kv_index || !a->kv_partial)
+            return fail(SA_ERR_INVALID_ARG, "NULL pointer");
+        const int64_t need = sa::select_workspace_bytes(a->batch * a->heads, p.nqb, p.nkb, p.d);
+        if (!a->workspace || a->workspace_bytes < need)
+            return fail(SA_ERR_INVALID_ARG, "workspace smaller than sa_select_blocks_workspace (%lld bytes)",
+                        (long long)need);
+        if (((uintptr_t)a->workspace & 255u) != 0) return fail(SA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+        auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
+        p.qm = (double*)a->workspace;
+        p.km = (double*)((uint8_t*)a->workspace + up(a->batch * a->heads * p.nqb * p.d * 8));
+        return launched(sa::launch_select_blocks(p, s), "sa_select_blocks");
+    } catch (...) {
+        return fail(SA_ERR_DEVICE, "sa_select_blocks: unexpected exception");
     }
 }
 

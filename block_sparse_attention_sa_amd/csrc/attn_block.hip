@@ -163,9 +163,10 @@ attn_block_kernel(AttnParams a)
     const uint32_t krow_b = (uint32_t)(a.k_sn * 2);
     const uint32_t vrow_b = (uint32_t)(a.v_sn * 2);
 
-    const int32_t* idx_row = a.kv_index + (int64_t)qb * a.nkb;
-    const uint8_t* part_row = a.kv_partial + (int64_t)qb * a.nkb;
-    const int cnt = min(a.kv_count[qb], a.nkb);
+    const int64_t lrow = (a.per_head_lists ? (int64_t)bh * a.nqb : 0) + qb;  // list row of this work item
+    const int32_t* idx_row = a.kv_index + lrow * a.nkb;
+    const uint8_t* part_row = a.kv_partial + lrow * a.nkb;
+    const int cnt = min(a.kv_count[lrow], a.nkb);
     const int n_sub = cnt * SUB;
     // The live list is held in registers, 64 entries at a time (lane j holds
     // entry base + j) and read with readlane, so the loop issues no memory

@@ -181,6 +181,7 @@ struct AttnParams {
     const int32_t* kv_count;
     const int32_t* kv_index;
     const uint8_t* kv_partial;
+    int32_t per_head_lists;  // lists of (b, h) at (b*heads + h) * nqb [* nkb]
     DevPattern pat;
     // gather mode
     const int32_t* gidx;
@@ -285,6 +286,28 @@ hipError_t launch_indexer_topk_stream(const uint16_t* q_idx, const uint16_t* k_i
 // the current device; looked up once per device).
 constexpr int64_t kNoAllocScratchBytes = int64_t(64) << 20;
 hipError_t noalloc_scratch(uint8_t** ptr);
+
+// Content-selected key blocks (block_select.hip).  Scratch: the fp64 mean
+// query of every (b, h, query block) and mean key of every (b, h, key block).
+constexpr int kSelectMaxBlocks = 1024;  // key blocks per row
+struct SelectParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    int64_t q_sb, q_sh, q_sn, k_sb, k_sh, k_sn;
+    int32_t batch, heads, n_q, n_kv, d, q_offset, bq, bk, nqb, nkb, n_sel;
+    int32_t* kv_count;
+    int32_t* kv_index;
+    uint8_t* kv_partial;
+    int64_t* live_pairs;
+    double* qm;  // [batch*heads][nqb][d]
+    double* km;  // [batch*heads][d][nkb]
+};
+inline int64_t select_workspace_bytes(int64_t bh, int64_t nqb, int64_t nkb, int64_t d)
+{
+    auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
+    return up(bh * nqb * d * 8) + up(bh * nkb * d * 8);
+}
+hipError_t launch_select_blocks(const SelectParams& p, hipStream_t stream);
 
 hipError_t launch_indexer_scores(const uint16_t* q_idx, const uint16_t* k_idx, int32_t n_q,
                                  int32_t n_kv, int32_t d_idx, int32_t q_offset, float* scores,

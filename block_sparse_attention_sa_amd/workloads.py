@@ -192,3 +192,35 @@ def topk_inputs(cfg: TopkConfig, n_q: Optional[int] = None, n_kv: Optional[int] 
         "v": randn_bf16((1, H, nkv, cfg.d), seed_for(cfg.cid, "v")),
     }
     return out
+
+
+@dataclasses.dataclass
+class SelectConfig:
+    """Content-selected key blocks (the glossary's Native Sparse Attention block
+    selection): each (b, h, query block) keeps its own key block plus the
+    ``n_select`` causally reachable key blocks of highest mean-query . mean-key."""
+    cid: int
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    block: int
+    n_select: int
+
+
+def select_config(cid: int = 6) -> SelectConfig:
+    if cid != 6:
+        raise ValueError("only workload 6 is a content-selected block workload")
+    return SelectConfig(6, "nsa_select8_n8192_h32_d128", 1, 32, 8192, 128, 128, 8)
+
+
+def select_inputs(cfg: SelectConfig, n: Optional[int] = None, heads: Optional[int] = None,
+                  batch: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Q, K, V bf16 bits [B, H, N, d] for the content-selected workload (seeds of
+    workload ``cfg.cid``)."""
+    B = cfg.B if batch is None else batch
+    H = cfg.H if heads is None else heads
+    N = cfg.N if n is None else n
+    shape = (B, H, N, cfg.d)
+    return {t: randn_bf16(shape, seed_for(cfg.cid, t)) for t in ("q", "k", "v")}

@@ -133,7 +133,11 @@ sa_status sa_build_block_mask(const sa_pattern *pattern, int64_t n_q, int64_t n_
  *   pattern, n_q, n_kv, block_q, block_kv (shared by every batch and head).
  *   Only live tiles are visited; the pattern is evaluated per pair only on
  *   partial tiles (and on tiles clipped by n_kv).  block_q must be 64 or 128
- *   and block_kv 64 or 128.
+ *   and block_kv 64 or 128.  With per_head_lists = 1 every (b, h) has lists
+ *   of its own (as sa_select_blocks writes them): kv_count at
+ *   (b*heads + h)*nqb, kv_index and kv_partial at (b*heads + h)*nqb*nkb;
+ *   a pair is then attended when its tile is listed for the row's (b, h,
+ *   query block) and, on a tile marked partial, the pattern allows it.
  * mode SA_MODE_GATHER: per-query key lists gather_idx int32 [n_q, topk]
  *   (row r lists key rows for query row r; entries < 0 or >= n_kv are
  *   skipped), shared by every batch and head when gather_bh_stride == 0,
@@ -187,7 +191,66 @@ typedef struct sa_attn_args {
     int64_t gather_bh_stride;
     void *workspace;            /* DEVICE scratch or NULL, see sa_attn_workspace_bytes */
     int64_t workspace_bytes;
+    int64_t per_head_lists;     /* SA_MODE_BLOCKS: 0 shared lists, 1 lists per (b, h) */
 } sa_attn_args;
+
+/*
+ * Arguments of sa_select_blocks: content-selected key blocks, the glossary's
+ * Native Sparse Attention "selection of the most relevant blocks" ("Sparse
+ * Attention", section on common sparsity patterns), with a list per (b, h)
+ * since heads differ in what they attend to (blog "Sparse transformers: how
+ * to cut the O(n^2) of attention", section on combining templates).  The
+ * pages give no formula; per (b, h, query block i) with query positions
+ * p0 .. p1 (row r at q_offset + r):
+ *   mean query qm_i and mean key km_j of key block j: fp64 sums of the
+ *   block's rows in row order divided by the block size (rows past the end
+ *   count as zero);  score(i, j) = qm_i . km_j, an fp64 fma chain over the
+ *   head dim;
+ *   kept: the key blocks holding positions p0 .. p1, plus the n_select
+ *   blocks j with j*block_kv <= p1 (causally reachable) first in the order
+ *   (score descending, block ascending).
+ * Outputs (DEVICE, caller-allocated; nqb = ceil(n_q/block_q), nkb =
+ * ceil(n_kv/block_kv) <= 1024):
+ *   kv_count   int32 [batch*heads, nqb]
+ *   kv_index   int32 [batch*heads, nqb, nkb]  kept blocks ascending, -1 pad
+ *   kv_partial uint8 [batch*heads, nqb, nkb]  1: some pair of the clipped
+ *              tile is not causal (key position > query position)
+ *   live_pairs int64 [1]  causal pairs over all kept tiles
+ * q, k: bfloat16 [batch, heads, n, head_dim] with element strides (b, h,
+ * row), head_dim 64 or 128; block_q, block_kv 64 or 128.  workspace: at
+ * least sa_select_blocks_workspace bytes, 256-byte aligned.  Attention over
+ * the result: sa_attn_fwd, SA_MODE_BLOCKS, per_head_lists = 1, the same
+ * block sizes and the pattern {causal = 1, q_offset, window_left = n_kv}.
+ */
+typedef struct sa_select_args {
+    const void *q;
+    const void *k;
+    int64_t batch;
+    int64_t heads;
+    int64_t n_q;
+    int64_t n_kv;
+    int64_t head_dim;
+    int64_t q_strides[3];
+    int64_t k_strides[3];
+    int64_t q_offset;
+    int64_t block_q;
+    int64_t block_kv;
+    int64_t n_select;
+    int32_t *kv_count;
+    int32_t *kv_index;
+    uint8_t *kv_partial;
+    int64_t *live_pairs;
+    void *workspace;
+    int64_t workspace_bytes;
+} sa_select_args;
+
+/* Bytes of DEVICE scratch sa_select_blocks needs (the fp64 block means); 0
+ * for sizes it does not take. */
+size_t sa_select_blocks_workspace(const sa_select_args *args);
+
+/* sa_select_blocks -- the content-selected lists above.  Asynchronous on
+ * `stream`; invalid arguments are rejected before any launch. */
+sa_status sa_select_blocks(const sa_select_args *args, void *stream);
 
 /*
  * sa_attn_workspace_bytes -- bytes of device scratch that sa_attn_fwd needs

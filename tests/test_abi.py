@@ -43,8 +43,12 @@ def test_struct_layout_matches_header(tmp_path):
     probe = tmp_path / "layout.c"
     fields_p = [f for f, _ in _lib.SaPattern._fields_]
     fields_a = [f for f, _ in _lib.SaAttnArgs._fields_]
+    fields_s = [f for f, _ in _lib.SaSelectArgs._fields_]
     lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void){",
-             'printf("P %zu\\n", sizeof(sa_pattern));', 'printf("A %zu\\n", sizeof(sa_attn_args));']
+             'printf("P %zu\\n", sizeof(sa_pattern));', 'printf("A %zu\\n", sizeof(sa_attn_args));',
+             'printf("S %zu\\n", sizeof(sa_select_args));']
+    for f in fields_s:
+        lines.append(f'printf("s.{f} %zu\\n", offsetof(sa_select_args, {f}));')
     for f in fields_p:
         lines.append(f'printf("p.{f} %zu\\n", offsetof(sa_pattern, {f}));')
     for f in fields_a:
@@ -60,6 +64,9 @@ def test_struct_layout_matches_header(tmp_path):
         assert int(out[f"p.{f}"]) == getattr(_lib.SaPattern, f).offset, f
     for f in fields_a:
         assert int(out[f"a.{f}"]) == getattr(_lib.SaAttnArgs, f).offset, f
+    for f in fields_s:
+        assert int(out[f"s.{f}"]) == getattr(_lib.SaSelectArgs, f).offset, f
+    assert int(out["S"]) == ctypes.sizeof(_lib.SaSelectArgs)
 
 
 def _err():
@@ -295,3 +302,39 @@ def test_strided_mode_argument_errors():
     assert L.sa_attn_strided_plan(ctypes.byref(a), None) == _lib.SA_ERR_INVALID_ARG and "workspace" in _err()
     a.mode = _lib.SA_MODE_BLOCKS
     assert L.sa_attn_strided_plan(ctypes.byref(a), None) == _lib.SA_ERR_INVALID_ARG and "mode" in _err()
+
+
+def _sel_args(**kw):
+    a = _lib.SaSelectArgs()
+    a.q = a.k = 4096
+    a.batch, a.heads, a.n_q, a.n_kv, a.head_dim = 1, 2, 512, 512, 64
+    a.q_strides[:] = a.k_strides[:] = [2 * 512 * 64, 512 * 64, 64]
+    a.block_q = a.block_kv = 64
+    a.n_select = 2
+    a.kv_count = a.kv_index = a.kv_partial = a.live_pairs = 4096
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+def test_select_blocks_workspace_and_errors():
+    L = _lib.lib()
+    a = _sel_args()
+    assert L.sa_select_blocks_workspace(ctypes.byref(a)) == 2 * 8 * 64 * 8 * 2   # fp64 means of q and k blocks
+    for kw, status, word in ((dict(head_dim=96), _lib.SA_ERR_UNSUPPORTED, "head_dim"),
+                             (dict(block_q=32), _lib.SA_ERR_UNSUPPORTED, "block"),
+                             (dict(n_kv=64 * 1025), _lib.SA_ERR_UNSUPPORTED, "key blocks"),
+                             (dict(n_select=-1), _lib.SA_ERR_INVALID_ARG, "negative"),
+                             (dict(live_pairs=None), _lib.SA_ERR_INVALID_ARG, "live_pairs"),
+                             (dict(), _lib.SA_ERR_INVALID_ARG, "workspace")):
+        b = _sel_args(**kw)
+        assert L.sa_select_blocks(ctypes.byref(b), None) == status, kw
+        assert word in _err(), (kw, _err())
+    b = _sel_args(workspace=4096 + 16, workspace_bytes=1 << 20)
+    assert L.sa_select_blocks(ctypes.byref(b), None) == _lib.SA_ERR_INVALID_ARG and "aligned" in _err()
+    assert L.sa_select_blocks_workspace(ctypes.byref(_sel_args(head_dim=96))) == 0
+
+
+def test_attn_per_head_lists_flag_checked():
+    a = _args(per_head_lists=2)
+    assert _lib.lib().sa_attn_fwd(ctypes.byref(a), None) == _lib.SA_ERR_INVALID_ARG and "per_head_lists" in _err()
