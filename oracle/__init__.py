@@ -32,6 +32,10 @@ Parity status of each function (pins live in ``tests/test_oracle_pins.py``):
 * ``attn_sel_rows``     pinned: dense masked attention brute force with the
   mask built from the lists (numpy); every causal block selected equals
   causal attention (torch fp64 SDPA).
+* ``attn_bwd``          pinned: torch fp64 autograd of the dense masked
+  attention (a library routine), central finite differences of the oracle's
+  own forward on tiny inputs, dQ = 0 and dK = 0 for rows with one allowed key,
+  dV columns summing to the columns of dO (each row's weights sum to 1).
 """
 
 from __future__ import annotations
@@ -106,6 +110,9 @@ def _load():
         lib.orc_attn_sel_rows.argtypes = [_P, _P, _P, _I64, _I64, _I32, ctypes.c_double, _I64, _I32, _I32, _P, _P,
                                           _P, _I64, _P, _P]
         lib.orc_attn_sel_rows.restype = None
+        lib.orc_attn_bwd.argtypes = [ctypes.POINTER(OrcPattern), _P, _P, _P, _P, _I64, _I64, _I32, ctypes.c_double,
+                                     _P, _I64, _P, _P, _P]
+        lib.orc_attn_bwd.restype = None
         lib.orc_num_threads.argtypes = []
         lib.orc_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -283,3 +290,26 @@ def attn_sel_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_offset: int, bq
     _load().orc_attn_sel_rows(_ptr(q), _ptr(k), _ptr(v), n_q, n_kv, d, float(scale), int(q_offset), bq, bk,
                               _ptr(kv_count), _ptr(kv_index), _ptr(rows), rows.size, _ptr(o), _ptr(lse))
     return o, lse
+
+
+def attn_bwd(pattern, q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, heads=None,
+             scale: float | None = None):
+    """fp64 gradients (dQ, dK, dV) of the masked attention for the slices ``heads``
+    (flattened b*H + h indices; default all) of [B, H, N, d] bf16-bit tensors and
+    an upstream gradient ``dout`` (bf16 bits like q).  Shapes [n_heads, N, d]."""
+    h = _PatternHolder(pattern)
+    q = np.ascontiguousarray(q, np.uint16)
+    k = np.ascontiguousarray(k, np.uint16)
+    v = np.ascontiguousarray(v, np.uint16)
+    dout = np.ascontiguousarray(dout, np.uint16)
+    B, H, n_q, d = q.shape
+    n_kv = k.shape[2]
+    bh = np.arange(B * H, dtype=np.int64) if heads is None else np.ascontiguousarray(heads, np.int64)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    dq = np.zeros((bh.size, n_q, d), np.float64)
+    dk = np.zeros((bh.size, n_kv, d), np.float64)
+    dv = np.zeros((bh.size, n_kv, d), np.float64)
+    _load().orc_attn_bwd(ctypes.byref(h.s), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), n_q, n_kv, d, float(scale),
+                         _ptr(bh), bh.size, _ptr(dq), _ptr(dk), _ptr(dv))
+    return dq, dk, dv

@@ -52,6 +52,12 @@
  *  - orc_attn_sel_rows: attention of each row over the keys of its query
  *    block's selected key blocks, causally ([B] masked attention with the
  *    mask given by the selected blocks).
+ *  - orc_attn_bwd: the gradient of the masked attention ([B]'s scores, -inf
+ *    fill, softmax, times V -- [G] notes NSA is trained end to end) with
+ *    respect to Q, K and V for an upstream gradient dO, by the chain rule on
+ *    the definition: P = softmax over the allowed keys, dV = P^T dO,
+ *    dP = dO V^T, dS = P * (dP - rowsum(P * dP)), dQ = scale dS K,
+ *    dK = scale dS^T Q.
  *
  * Inputs are raw bfloat16 bit patterns (uint16); each is widened exactly.
  */
@@ -466,6 +472,101 @@ void orc_attn_sel_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, 
         free(s_buf);
         free(in);
     }
+}
+
+/* Gradients of the masked attention of the (b*H + h) slices listed in bh[]
+ * (all their rows), fp64.  q, dout [BH, n_q, d], k, v [BH, n_kv, d] bf16
+ * bits; dq [n_bh, n_q, d], dk, dv [n_bh, n_kv, d] in the order of bh[].
+ * Pass 1, per query row: the allowed keys, P = exp(s - LSE), dq.
+ * Pass 2, per key row: the queries that may see it, dk and dv. */
+void orc_attn_bwd(const orc_pattern *p, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                  const uint16_t *dout, int64_t n_q, int64_t n_kv, int32_t d, double scale, const int64_t *bh,
+                  int64_t n_bh, double *dq, double *dk, double *dv)
+{
+    double *lse = (double *)malloc(sizeof(double) * (size_t)(n_bh * n_q > 0 ? n_bh * n_q : 1));
+    double *dsum = (double *)malloc(sizeof(double) * (size_t)(n_bh * n_q > 0 ? n_bh * n_q : 1));
+    /* pass 1: per query row */
+#pragma omp parallel
+    {
+        double *s_buf = (double *)malloc(sizeof(double) * (size_t)(n_kv > 0 ? n_kv : 1));
+        double *dp_buf = (double *)malloc(sizeof(double) * (size_t)(n_kv > 0 ? n_kv : 1));
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_kv > 0 ? n_kv : 1));
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < n_bh * n_q; ++r) {
+            int64_t t = r / n_q, qi = r % n_q, g = bh[t];
+            const uint16_t *qrow = q + (g * n_q + qi) * d, *grow = dout + (g * n_q + qi) * d;
+            const uint16_t *kb = k + g * n_kv * d, *vb = v + g * n_kv * d;
+            int64_t nk = 0;
+            for (int64_t kv = 0; kv < n_kv; ++kv)
+                if (orc_allowed(p, qi + p->q_offset, kv))
+                    keys[nk++] = kv;
+            double *dqr = dq + r * d;
+            for (int32_t c = 0; c < d; ++c)
+                dqr[c] = 0.0;
+            if (nk == 0) {
+                lse[r] = -INFINITY;
+                dsum[r] = 0.0;
+                continue;
+            }
+            double m = -INFINITY;
+            for (int64_t e = 0; e < nk; ++e) {
+                double acc = 0.0, acc2 = 0.0;
+                for (int32_t c = 0; c < d; ++c) {
+                    acc += bf16_to_f64(qrow[c]) * bf16_to_f64(kb[keys[e] * d + c]);
+                    acc2 += bf16_to_f64(grow[c]) * bf16_to_f64(vb[keys[e] * d + c]);
+                }
+                s_buf[e] = acc * scale;
+                dp_buf[e] = acc2;
+                if (s_buf[e] > m)
+                    m = s_buf[e];
+            }
+            double sum = 0.0;
+            for (int64_t e = 0; e < nk; ++e)
+                sum += exp(s_buf[e] - m);
+            double L = m + log(sum), D = 0.0;
+            for (int64_t e = 0; e < nk; ++e)
+                D += exp(s_buf[e] - L) * dp_buf[e];
+            lse[r] = L;
+            dsum[r] = D;
+            for (int64_t e = 0; e < nk; ++e) {
+                double ds = exp(s_buf[e] - L) * (dp_buf[e] - D);
+                for (int32_t c = 0; c < d; ++c)
+                    dqr[c] += scale * ds * bf16_to_f64(kb[keys[e] * d + c]);
+            }
+        }
+        free(s_buf);
+        free(dp_buf);
+        free(keys);
+    }
+    /* pass 2: per key row */
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < n_bh * n_kv; ++r) {
+        int64_t t = r / n_kv, kv = r % n_kv, g = bh[t];
+        const uint16_t *krow = k + (g * n_kv + kv) * d, *vrow = v + (g * n_kv + kv) * d;
+        double *dkr = dk + r * d, *dvr = dv + r * d;
+        for (int32_t c = 0; c < d; ++c) {
+            dkr[c] = 0.0;
+            dvr[c] = 0.0;
+        }
+        for (int64_t qi = 0; qi < n_q; ++qi) {
+            if (!orc_allowed(p, qi + p->q_offset, kv))
+                continue;
+            const uint16_t *qrow = q + (g * n_q + qi) * d, *grow = dout + (g * n_q + qi) * d;
+            double acc = 0.0, acc2 = 0.0;
+            for (int32_t c = 0; c < d; ++c) {
+                acc += bf16_to_f64(qrow[c]) * bf16_to_f64(krow[c]);
+                acc2 += bf16_to_f64(grow[c]) * bf16_to_f64(vrow[c]);
+            }
+            double P = exp(acc * scale - lse[t * n_q + qi]);
+            double ds = P * (acc2 - dsum[t * n_q + qi]);
+            for (int32_t c = 0; c < d; ++c) {
+                dvr[c] += P * bf16_to_f64(grow[c]);
+                dkr[c] += scale * ds * bf16_to_f64(qrow[c]);
+            }
+        }
+    }
+    free(lse);
+    free(dsum);
 }
 
 int orc_num_threads(void)

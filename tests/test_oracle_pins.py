@@ -636,3 +636,73 @@ def test_attn_sel_rows_vs_dense_brute_force():
         bo, blse = brute.masked_attention(_bf16_f64(q[0, h]), _bf16_f64(k[0, h]), _bf16_f64(v[0, h]), mask)
         np.testing.assert_allclose(o[h * n_q:(h + 1) * n_q], bo, rtol=0, atol=1e-12)
         np.testing.assert_allclose(lse[h * n_q:(h + 1) * n_q], blse, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# backward (gradients of the masked attention)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(6))
+def test_backward_vs_torch_autograd(seed):
+    """dQ, dK, dV against torch fp64 autograd of the dense masked attention
+    (loss = sum(O * dO)); rows with no allowed key included."""
+    rng = np.random.default_rng(3000 + seed)
+    nq, nkv, d = int(rng.integers(1, 70)), int(rng.integers(1, 70)), int(rng.choice([4, 16, 64]))
+    pat = _random_pattern(rng, nq, nkv)
+    q, k, v = _rand_qkv(rng, 1, 2, nq, nkv, d)
+    g = W.f32_to_bf16_bits(rng.standard_normal((1, 2, nq, d), dtype=np.float32))
+    dq, dk, dv = oracle.attn_bwd(pat, q, k, v, g)
+    mask = torch.from_numpy(_dense_mask(pat, nq, nkv))
+    tq, tk, tv = (torch.from_numpy(_bf16_f64(x)).requires_grad_(True) for x in (q, k, v))
+    sc = torch.matmul(tq, tk.transpose(-1, -2)) / math.sqrt(d)
+    sc = sc.masked_fill(~mask, float("-inf"))
+    w = torch.softmax(sc, dim=-1).nan_to_num(0.0)   # rows without keys: weights 0
+    o = torch.matmul(w, tv)
+    (o * torch.from_numpy(_bf16_f64(g))).sum().backward()
+    np.testing.assert_allclose(dq, tq.grad.numpy()[0], rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.numpy()[0], rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.numpy()[0], rtol=0, atol=1e-11)
+
+
+def test_backward_finite_differences():
+    """Central differences of the oracle's own forward: d(sum(O * dO)) / dx."""
+    rng = np.random.default_rng(31)
+    n, d = 12, 4
+    pat = dict(causal=1, window_left=4, window_right=0, sinks=1)
+    q, k, v = _rand_qkv(rng, 1, 1, n, n, d)
+    g = W.f32_to_bf16_bits(rng.standard_normal((1, 1, n, d), dtype=np.float32))
+    dq, dk, dv = oracle.attn_bwd(pat, q, k, v, g)
+    gf = _bf16_f64(g)[0, 0]
+    allowed = _dense_mask(pat, n, n)
+    base = {t: _bf16_f64(x)[0, 0] for t, x in (("q", q), ("k", k), ("v", v))}
+
+    def loss(qq, kk, vv):
+        o, _ = brute.masked_attention(qq, kk, vv, allowed)
+        return float((o * gf).sum())
+
+    eps = 1e-6
+    for name, grad in (("q", dq[0]), ("k", dk[0]), ("v", dv[0])):
+        for (r, c) in ((0, 0), (5, 2), (11, 3), (7, 1)):
+            plus = {t: x.copy() for t, x in base.items()}
+            minus = {t: x.copy() for t, x in base.items()}
+            plus[name][r, c] += eps
+            minus[name][r, c] -= eps
+            fd = (loss(plus["q"], plus["k"], plus["v"]) - loss(minus["q"], minus["k"], minus["v"])) / (2 * eps)
+            assert abs(fd - grad[r, c]) < 1e-7, (name, r, c, fd, grad[r, c])
+
+
+def test_backward_closed_forms():
+    """A row that sees one key: its P is 1, so dS = 0 there (no dQ from it) and
+    dV of that key gets the row's dO; with the diagonal-only pattern dQ = dK = 0
+    and dV = dO.  Every column of dV sums to the column sums of dO (the weights
+    of each row sum to 1)."""
+    rng = np.random.default_rng(32)
+    n, d = 40, 16
+    q, k, v = _rand_qkv(rng, 1, 1, n, n, d)
+    g = W.f32_to_bf16_bits(rng.standard_normal((1, 1, n, d), dtype=np.float32))
+    dq, dk, dv = oracle.attn_bwd(dict(causal=1, window_left=0, window_right=0), q, k, v, g)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    np.testing.assert_array_equal(dv[0], _bf16_f64(g)[0, 0])
+    pat = dict(causal=1, window_left=9, window_right=0, sinks=2)
+    dq, dk, dv = oracle.attn_bwd(pat, q, k, v, g)
+    np.testing.assert_allclose(dv[0].sum(0), _bf16_f64(g)[0, 0].sum(0), rtol=0, atol=1e-10)
