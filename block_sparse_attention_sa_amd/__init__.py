@@ -24,7 +24,7 @@ import numpy as np
 from . import _lib
 from ._lib import SaError  # noqa: F401
 
-__all__ = ["BlockLists", "build_block_mask", "select_blocks", "attn_fwd", "attn_workspace_bytes", "attn_fwd_strided",
+__all__ = ["BlockLists", "build_block_mask", "select_blocks", "attn_fwd", "attn_bwd", "attn_workspace_bytes", "attn_fwd_strided",
            "attn_workspace_bytes_strided", "strided_plan", "merge_partial", "indexer_scores", "topk", "indexer_topk",
            "indexer_topk_workspace_bytes", "indexer_topk_noalloc", "describe", "SaError"]
 
@@ -251,6 +251,48 @@ def attn_fwd(q, k, v, blocks: Optional[BlockLists] = None, gather_idx=None, *,
     _lib.check(_lib.lib().sa_attn_fwd(ctypes.byref(a), _stream_ptr(q.device)))
     return out, lse
 
+
+
+def attn_bwd(q, k, v, o, lse, dout, blocks: BlockLists, *, softmax_scale: Optional[float] = None,
+             dq=None, dk=None, dv=None, workspace=None):
+    """Gradients (dQ, dK, dV) of the block-sparse attention (``sa_attn_bwd``) for the
+    upstream gradient ``dout``.  q, k, v, dout bfloat16 contiguous [B, H, n, d]; o float32
+    and lse float32 are the forward's outputs for the same ``blocks``.  Returns float32
+    (dq [B, H, n_q, d], dk, dv [B, H, n_kv, d])."""
+    torch = _torch()
+    for t in (q, k, v, dout):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError("q, k, v, dout must be contiguous 4-d bfloat16 CUDA tensors")
+    B, H, n_q, d = q.shape
+    n_kv = k.shape[2]
+    if tuple(dout.shape) != (B, H, n_q, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch")
+    if o.dtype != torch.float32 or not o.is_contiguous() or tuple(o.shape) != (B, H, n_q, d):
+        raise ValueError("o must be the forward's contiguous float32 output")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * H * n_q:
+        raise ValueError("lse must be the forward's contiguous float32 logsumexp")
+    if blocks.n_q != n_q or blocks.n_kv != n_kv:
+        raise ValueError("block lists were built for another n_q / n_kv")
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty((B, H, n_q, d), **f32) if dq is None else dq
+    dk = torch.empty((B, H, n_kv, d), **f32) if dk is None else dk
+    dv = torch.empty((B, H, n_kv, d), **f32) if dv is None else dv
+    a = _lib.SaAttnBwdArgs()
+    a.q, a.k, a.v, a.o, a.lse, a.dout = (t.data_ptr() for t in (q, k, v, o, lse, dout))
+    a.dq, a.dk, a.dv = dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    a.batch, a.heads, a.n_q, a.n_kv, a.head_dim = B, H, n_q, n_kv, d
+    a.softmax_scale = float(softmax_scale) if softmax_scale else 0.0
+    a.block_q, a.block_kv = blocks.block_q, blocks.block_kv
+    a.kv_count, a.kv_index, a.kv_partial = (t.data_ptr() for t in (blocks.kv_count, blocks.kv_index,
+                                                                    blocks.kv_partial))
+    a.per_head_lists = 1 if blocks.per_head else 0
+    a.pattern = blocks.pattern.struct
+    need = int(_lib.lib().sa_attn_bwd_workspace(ctypes.byref(a)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    _lib.check(_lib.lib().sa_attn_bwd(ctypes.byref(a), _stream_ptr(q.device)))
+    return dq, dk, dv
 
 
 def merge_partial(out, lse, o2, lse2, group: int = 1, q_first: int = 0, n2: Optional[int] = None):

@@ -19,7 +19,7 @@ ABI_VERSION = 2
 
 EXPORTED = ("sa_build_block_mask", "sa_attn_workspace_bytes", "sa_attn_strided_plan", "sa_attn_fwd", "sa_indexer_scores", "sa_topk",
             "sa_indexer_topk_workspace", "sa_indexer_topk", "sa_indexer_topk_noalloc", "sa_merge_partial",
-            "sa_select_blocks_workspace", "sa_select_blocks",
+            "sa_select_blocks_workspace", "sa_select_blocks", "sa_attn_bwd_workspace", "sa_attn_bwd",
             "sa_last_error", "sa_abi_version")
 
 _I64 = ctypes.c_int64
@@ -103,6 +103,35 @@ class SaSelectArgs(ctypes.Structure):
     ]
 
 
+class SaAttnBwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("q", _P),
+        ("k", _P),
+        ("v", _P),
+        ("o", _P),
+        ("lse", _P),
+        ("dout", _P),
+        ("dq", _P),
+        ("dk", _P),
+        ("dv", _P),
+        ("batch", _I64),
+        ("heads", _I64),
+        ("n_q", _I64),
+        ("n_kv", _I64),
+        ("head_dim", _I64),
+        ("softmax_scale", ctypes.c_double),
+        ("block_q", _I64),
+        ("block_kv", _I64),
+        ("kv_count", _P),
+        ("kv_index", _P),
+        ("kv_partial", _P),
+        ("per_head_lists", _I64),
+        ("pattern", SaPattern),
+        ("workspace", _P),
+        ("workspace_bytes", _I64),
+    ]
+
+
 class SaError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"libsa status {status}: {msg}")
@@ -143,6 +172,10 @@ def lib() -> ctypes.CDLL:
         L.sa_select_blocks_workspace.restype = ctypes.c_size_t
         L.sa_select_blocks.argtypes = [ctypes.POINTER(SaSelectArgs), _P]
         L.sa_select_blocks.restype = ctypes.c_int
+        L.sa_attn_bwd_workspace.argtypes = [ctypes.POINTER(SaAttnBwdArgs)]
+        L.sa_attn_bwd_workspace.restype = ctypes.c_size_t
+        L.sa_attn_bwd.argtypes = [ctypes.POINTER(SaAttnBwdArgs), _P]
+        L.sa_attn_bwd.restype = ctypes.c_int
         L.sa_merge_partial.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I32, ctypes.POINTER(_I64),
                                        ctypes.POINTER(_I64), _I32, _I64, _I64, _P]
         L.sa_merge_partial.restype = ctypes.c_int

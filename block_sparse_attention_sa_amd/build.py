@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libsa.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 SOURCES = ["api.cpp", "block_mask.hip", "attn_block.hip", "attn_gather.hip", "indexer_topk.hip", "merge.hip",
-           "block_select.hip"]
+           "block_select.hip", "attn_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

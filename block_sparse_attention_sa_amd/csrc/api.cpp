@@ -695,6 +695,89 @@ sa_status sa_select_blocks(const sa_select_args* a, void* stream)
     }
 }
 
+static sa_status check_bwd(const sa_attn_bwd_args* a, sa::BwdParams& p, sa::BwdLayout& L)
+{
+    if (!a) return fail(SA_ERR_INVALID_ARG, "args is NULL");
+    if (a->batch < 0 || a->heads < 0 || a->n_q < 0 || a->n_kv < 0)
+        return fail(SA_ERR_INVALID_ARG, "batch/heads/n_q/n_kv must be >= 0");
+    if (a->head_dim != 64 && a->head_dim != 128) return fail(SA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    if ((a->block_q != 64 && a->block_q != 128) || (a->block_kv != 64 && a->block_kv != 128))
+        return fail(SA_ERR_UNSUPPORTED, "block_q and block_kv must be 64 or 128");
+    if (a->per_head_lists != 0 && a->per_head_lists != 1) return fail(SA_ERR_INVALID_ARG, "per_head_lists must be 0 or 1");
+    if (a->n_q > kI32Max || a->n_kv > kI32Max || a->batch * a->heads > kI32Max)
+        return fail(SA_ERR_UNSUPPORTED, "sizes must stay below 2^31");
+    p = sa::BwdParams{};
+    const sa_status st = make_pattern(&a->pattern, a->n_q, a->n_kv, p.pat);
+    if (st != SA_OK) return st;
+    p.batch = (int32_t)a->batch;
+    p.heads = (int32_t)a->heads;
+    p.n_q = (int32_t)a->n_q;
+    p.n_kv = (int32_t)a->n_kv;
+    const double scale = a->softmax_scale > 0 ? a->softmax_scale : 1.0 / std::sqrt((double)a->head_dim);
+    p.scale = (float)scale;
+    p.scale_log2 = (float)(scale * 1.4426950408889634);
+    p.nqb = (int32_t)((a->n_q + a->block_q - 1) / a->block_q);
+    p.nkb = (int32_t)((a->n_kv + a->block_kv - 1) / a->block_kv);
+    p.per_head_lists = (int32_t)a->per_head_lists;
+    p.n_lists = a->per_head_lists ? (int32_t)(a->batch * a->heads) : 1;
+    if ((int64_t)p.nqb * a->batch * a->heads > kI32Max || (int64_t)p.nkb * a->batch * a->heads > kI32Max)
+        return fail(SA_ERR_UNSUPPORTED, "too many work items");
+    L = sa::bwd_layout(a->batch * a->heads * a->n_q, p.n_lists, p.nqb, p.nkb);
+    return SA_OK;
+}
+
+size_t sa_attn_bwd_workspace(const sa_attn_bwd_args* a)
+{
+    sa::BwdParams p;
+    sa::BwdLayout L;
+    const std::string keep = g_err;  // a size query leaves the last error alone
+    const sa_status st = check_bwd(a, p, L);
+    g_err = keep;
+    return st == SA_OK ? (size_t)L.total : 0;
+}
+
+sa_status sa_attn_bwd(const sa_attn_bwd_args* a, void* stream)
+{
+    try {
+        sa::BwdParams p;
+        sa::BwdLayout L;
+        sa_status st = check_bwd(a, p, L);
+        if (st != SA_OK) return st;
+        if (a->batch == 0 || a->heads == 0 || (a->n_q == 0 && a->n_kv == 0)) return ok();
+        if (!a->q || !a->k || !a->v || !a->o || !a->lse || !a->dout || !a->dq || !a->dk || !a->dv || !a->kv_count ||
+            (p.nkb > 0 && (!a->kv_index || !a->kv_partial)))
+            return fail(SA_ERR_INVALID_ARG, "NULL pointer");
+        if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->dout))
+            return fail(SA_ERR_INVALID_ARG, "q/k/v/dout must be 16-byte aligned");
+        if (!a->workspace || a->workspace_bytes < L.total)
+            return fail(SA_ERR_INVALID_ARG, "workspace smaller than sa_attn_bwd_workspace (%lld bytes)",
+                        (long long)L.total);
+        if (((uintptr_t)a->workspace & 255u) != 0) return fail(SA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+        p.q = (const uint16_t*)a->q;
+        p.k = (const uint16_t*)a->k;
+        p.v = (const uint16_t*)a->v;
+        p.dout = (const uint16_t*)a->dout;
+        p.o = a->o;
+        p.lse = a->lse;
+        p.dq = a->dq;
+        p.dk = a->dk;
+        p.dv = a->dv;
+        p.kv_count = a->kv_count;
+        p.kv_index = a->kv_index;
+        p.kv_partial = a->kv_partial;
+        uint8_t* ws = (uint8_t*)a->workspace;
+        p.dsum = (float*)(ws + L.dsum);
+        p.q_count = (int32_t*)(ws + L.q_count);
+        p.q_index = (int32_t*)(ws + L.q_index);
+        p.q_partial = ws + L.q_partial;
+        return launched(sa::launch_attn_bwd(p, (int)a->head_dim, (int)a->block_q, (int)a->block_kv,
+                                            (hipStream_t)stream),
+                        "sa_attn_bwd");
+    } catch (...) {
+        return fail(SA_ERR_DEVICE, "sa_attn_bwd: unexpected exception");
+    }
+}
+
 sa_status sa_attn_strided_plan(const sa_attn_args* a, void* stream)
 {
     try {

@@ -309,6 +309,47 @@ inline int64_t select_workspace_bytes(int64_t bh, int64_t nqb, int64_t nkb, int6
 }
 hipError_t launch_select_blocks(const SelectParams& p, hipStream_t stream);
 
+// Backward (attn_bwd.hip).  Tensors contiguous [batch, heads, n, head_dim];
+// scratch: D [batch*heads*n_q] and the block lists transposed (per key block,
+// the query blocks that list it).
+struct BwdParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* dout;
+    const float* o;
+    const float* lse;
+    float* dq;
+    float* dk;
+    float* dv;
+    int32_t batch, heads, n_q, n_kv;
+    float scale, scale_log2;
+    int32_t nqb, nkb, per_head_lists, n_lists;
+    const int32_t* kv_count;
+    const int32_t* kv_index;
+    const uint8_t* kv_partial;
+    DevPattern pat;
+    float* dsum;        // [batch*heads*n_q]
+    int32_t* q_count;   // [n_lists][nkb]
+    int32_t* q_index;   // [n_lists][nkb][nqb]
+    uint8_t* q_partial; // [n_lists][nkb][nqb]
+};
+struct BwdLayout {
+    int64_t dsum, q_count, q_index, q_partial, total;
+};
+inline BwdLayout bwd_layout(int64_t rows, int64_t n_lists, int64_t nqb, int64_t nkb)
+{
+    auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
+    BwdLayout L;
+    L.dsum = 0;
+    L.q_count = up(rows * 4);
+    L.q_index = up(L.q_count + n_lists * nkb * 4);
+    L.q_partial = up(L.q_index + n_lists * nkb * nqb * 4);
+    L.total = up(L.q_partial + n_lists * nkb * nqb);
+    return L;
+}
+hipError_t launch_attn_bwd(const BwdParams& a, int head_dim, int block_q, int block_kv, hipStream_t stream);
+
 hipError_t launch_indexer_scores(const uint16_t* q_idx, const uint16_t* k_idx, int32_t n_q,
                                  int32_t n_kv, int32_t d_idx, int32_t q_offset, float* scores,
                                  hipStream_t stream);

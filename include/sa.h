@@ -404,6 +404,60 @@ sa_status sa_merge_partial(float *o, float *lse, const float *o2, const float *l
                            const int64_t o2_strides[3], int32_t group, int64_t q_first, int64_t n2,
                            void *stream);
 
+/*
+ * Arguments of sa_attn_bwd: the gradients of sa_attn_fwd's block mode with
+ * respect to Q, K and V for an upstream gradient dO, by the chain rule on
+ * the blog's masked attention ("Sparse transformers: how to cut the O(n^2)
+ * of attention", section on how it looks in code; the "Sparse Attention"
+ * glossary notes Native Sparse Attention is trained end to end):
+ *   P = exp(s*scale - LSE) on allowed pairs,  D = rowsum(dO * O),
+ *   dS = P * (dO . v - D),  dV = P^T dO,  dQ = scale dS K,  dK = scale dS^T Q.
+ * Every tensor is a contiguous DEVICE array [batch, heads, n, head_dim]:
+ *   q, dout bfloat16 (n = n_q); k, v bfloat16 (n = n_kv);
+ *   o float32 and lse float32 [batch, heads, n_q]: the forward's outputs for
+ *   the same inputs, lists and pattern;
+ *   dq float32 (n_q), dk, dv float32 (n_kv): written, every row (rows that
+ *   no allowed pair touches get 0).
+ * The block lists, pattern, block sizes and per_head_lists are those of the
+ * forward call (block_q, block_kv 64 or 128; head_dim 64 or 128).  P and dS
+ * enter the matrix products as bfloat16, products accumulate in float32.
+ * workspace: at least sa_attn_bwd_workspace bytes, 256-byte aligned.
+ */
+typedef struct sa_attn_bwd_args {
+    const void *q;
+    const void *k;
+    const void *v;
+    const float *o;
+    const float *lse;
+    const void *dout;
+    float *dq;
+    float *dk;
+    float *dv;
+    int64_t batch;
+    int64_t heads;
+    int64_t n_q;
+    int64_t n_kv;
+    int64_t head_dim;
+    double softmax_scale;
+    int64_t block_q;
+    int64_t block_kv;
+    const int32_t *kv_count;
+    const int32_t *kv_index;
+    const uint8_t *kv_partial;
+    int64_t per_head_lists;
+    sa_pattern pattern;
+    void *workspace;
+    int64_t workspace_bytes;
+} sa_attn_bwd_args;
+
+/* Bytes of DEVICE scratch sa_attn_bwd needs (D per row and the block lists
+ * transposed); 0 for sizes it does not take. */
+size_t sa_attn_bwd_workspace(const sa_attn_bwd_args *args);
+
+/* sa_attn_bwd -- dQ, dK, dV as above.  Asynchronous on `stream`; invalid
+ * arguments are rejected before any launch. */
+sa_status sa_attn_bwd(const sa_attn_bwd_args *args, void *stream);
+
 /* Thread-local text of the last non-OK status of this thread ("" if none). */
 const char *sa_last_error(void);
 

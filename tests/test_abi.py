@@ -44,9 +44,12 @@ def test_struct_layout_matches_header(tmp_path):
     fields_p = [f for f, _ in _lib.SaPattern._fields_]
     fields_a = [f for f, _ in _lib.SaAttnArgs._fields_]
     fields_s = [f for f, _ in _lib.SaSelectArgs._fields_]
+    fields_b = [f for f, _ in _lib.SaAttnBwdArgs._fields_]
     lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void){",
              'printf("P %zu\\n", sizeof(sa_pattern));', 'printf("A %zu\\n", sizeof(sa_attn_args));',
-             'printf("S %zu\\n", sizeof(sa_select_args));']
+             'printf("S %zu\\n", sizeof(sa_select_args));', 'printf("B %zu\\n", sizeof(sa_attn_bwd_args));']
+    for f in fields_b:
+        lines.append(f'printf("b.{f} %zu\\n", offsetof(sa_attn_bwd_args, {f}));')
     for f in fields_s:
         lines.append(f'printf("s.{f} %zu\\n", offsetof(sa_select_args, {f}));')
     for f in fields_p:
@@ -67,6 +70,9 @@ def test_struct_layout_matches_header(tmp_path):
     for f in fields_s:
         assert int(out[f"s.{f}"]) == getattr(_lib.SaSelectArgs, f).offset, f
     assert int(out["S"]) == ctypes.sizeof(_lib.SaSelectArgs)
+    for f in fields_b:
+        assert int(out[f"b.{f}"]) == getattr(_lib.SaAttnBwdArgs, f).offset, f
+    assert int(out["B"]) == ctypes.sizeof(_lib.SaAttnBwdArgs)
 
 
 def _err():
@@ -338,3 +344,32 @@ def test_select_blocks_workspace_and_errors():
 def test_attn_per_head_lists_flag_checked():
     a = _args(per_head_lists=2)
     assert _lib.lib().sa_attn_fwd(ctypes.byref(a), None) == _lib.SA_ERR_INVALID_ARG and "per_head_lists" in _err()
+
+
+def test_attn_bwd_workspace_and_errors():
+    L = _lib.lib()
+
+    def bwd(**kw):
+        a = _lib.SaAttnBwdArgs()
+        a.q = a.k = a.v = a.o = a.lse = a.dout = a.dq = a.dk = a.dv = 4096
+        a.batch, a.heads, a.n_q, a.n_kv, a.head_dim = 1, 2, 300, 300, 64
+        a.block_q = a.block_kv = 64
+        a.kv_count = a.kv_index = a.kv_partial = 4096
+        a.pattern = _lib.SaPattern(causal=1, window_left=50, window_right=0, unit_window=-1)
+        for k_, v_ in kw.items():
+            setattr(a, k_, v_)
+        return a
+
+    up = lambda x: (x + 255) // 256 * 256
+    nqb = nkb = 5
+    exp = up(up(up(2 * 300 * 4) + nkb * 4) + nkb * nqb * 4) + nkb * nqb
+    assert L.sa_attn_bwd_workspace(ctypes.byref(bwd())) == up(exp)
+    for kw, status, word in ((dict(head_dim=96), _lib.SA_ERR_UNSUPPORTED, "head_dim"),
+                             (dict(block_kv=32), _lib.SA_ERR_UNSUPPORTED, "block"),
+                             (dict(per_head_lists=3), _lib.SA_ERR_INVALID_ARG, "per_head_lists"),
+                             (dict(dq=None), _lib.SA_ERR_INVALID_ARG, "NULL"),
+                             (dict(k=4100), _lib.SA_ERR_INVALID_ARG, "aligned"),
+                             (dict(), _lib.SA_ERR_INVALID_ARG, "workspace")):
+        assert L.sa_attn_bwd(ctypes.byref(bwd(**kw)), None) == status, kw
+        assert word in _err(), (kw, _err())
+    assert L.sa_attn_bwd_workspace(ctypes.byref(bwd(head_dim=96))) == 0

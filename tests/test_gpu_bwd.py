@@ -1,0 +1,130 @@
+"""Backward of the block-sparse attention (sa_attn_bwd) against the fp64 oracle's
+gradients.
+
+Tolerance: every gradient entry within 1e-2 of the reference scaled by the
+tensor's own magnitude, |err| <= 1e-2 * max(1, max |ref|).  The products take
+bf16 operands (Q, K, V, dO as given; P and dS rounded to bf16, relative error
+2^-9 each) with float32 accumulation, as in the forward, whose O tolerance is
+1e-2 for outputs of unit scale; dK and dV sum over every query that sees a key,
+so their scale grows with the number of such queries and the bound follows it.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import block_sparse_attention_sa_amd as sa
+from block_sparse_attention_sa_amd import workloads as W
+from tests.parity_util import random_pattern, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+REL = 1e-2
+
+
+def _check(name, got, ref, ctx):
+    got = np.asarray(got, np.float64)
+    bound = REL * max(1.0, float(np.abs(ref).max()) if ref.size else 1.0)
+    err = float(np.abs(got - ref).max()) if ref.size else 0.0
+    print(f"{ctx} {name}: max err {err:.3e} bound {bound:.3e}", flush=True)
+    assert err <= bound, f"{ctx} {name}: max err {err:.3e} > {bound:.3e}"
+
+
+def _rand(rng, *shape):
+    return W.f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+
+
+def _run(pat, q, k, v, g, bq, bk, heads=None):
+    n_q, n_kv = q.shape[2], k.shape[2]
+    qd, kd, vd, gd = (to_dev_bf16(x) for x in (q, k, v, g))
+    bl = sa.build_block_mask(pat, n_q, n_kv, bq, bk)
+    o, lse = sa.attn_fwd(qd, kd, vd, bl)
+    dq, dk, dv = sa.attn_bwd(qd, kd, vd, o, lse, gd, bl)
+    torch.cuda.synchronize()
+    B, H = q.shape[:2]
+    sel = np.arange(B * H) if heads is None else np.asarray(heads)
+    f = lambda t: t.reshape(B * H, t.shape[2], t.shape[3]).cpu().numpy()[sel]
+    return f(dq), f(dk), f(dv)
+
+
+@pytest.mark.parametrize("d,bq,bk", [(64, 64, 64), (128, 128, 128), (64, 128, 64), (128, 64, 128)])
+def test_bwd_window_sinks_ragged(d, bq, bk):
+    rng = np.random.default_rng(d + bq + 2 * bk)
+    n_q, n_kv = 333, 301
+    pat = dict(causal=1, window_left=90, window_right=0, sinks=3, q_offset=10)
+    q, k, v, g = _rand(rng, 2, 2, n_q, d), _rand(rng, 2, 2, n_kv, d), _rand(rng, 2, 2, n_kv, d), _rand(rng, 2, 2, n_q, d)
+    print(f"bwd window d={d} bq={bq} bk={bk}", flush=True)
+    dq, dk, dv = _run(pat, q, k, v, g, bq, bk)
+    rq, rk, rv = oracle.attn_bwd(pat, q, k, v, g)
+    for name, a, b in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        _check(name, a, b, f"d={d} bq={bq} bk={bk}")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_bwd_random_patterns(seed):
+    rng = np.random.default_rng(700 + seed)
+    d = int(rng.choice([64, 128]))
+    bq, bk = int(rng.choice([64, 128])), int(rng.choice([64, 128]))
+    n_q, n_kv = int(rng.integers(1, 300)), int(rng.integers(1, 300))
+    pat = random_pattern(rng, n_q, n_kv)
+    q, k, v, g = _rand(rng, 1, 2, n_q, d), _rand(rng, 1, 2, n_kv, d), _rand(rng, 1, 2, n_kv, d), _rand(rng, 1, 2, n_q, d)
+    print(f"bwd random seed={seed} d={d} bq={bq} bk={bk} n_q={n_q} n_kv={n_kv} {sorted(pat)}", flush=True)
+    dq, dk, dv = _run(pat, q, k, v, g, bq, bk)
+    rq, rk, rv = oracle.attn_bwd(pat, q, k, v, g)
+    for name, a, b in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        _check(name, a, b, f"seed {seed}")
+
+
+def test_bwd_config1_whole():
+    cfg = W.attn_config(1)
+    inp = W.attn_inputs(cfg)
+    g = _rand(np.random.default_rng(41), cfg.B, cfg.H, cfg.N, cfg.d)
+    pat = cfg.pattern.as_dict()
+    dq, dk, dv = _run(pat, inp["q"], inp["k"], inp["v"], g, cfg.block, cfg.block)
+    rq, rk, rv = oracle.attn_bwd(pat, inp["q"], inp["k"], inp["v"], g)
+    for name, a, b in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        _check(name, a, b, "config 1")
+
+
+def test_bwd_config2_full_size_two_heads():
+    """The glossary's worked pattern at full size (B=1, H=32, N=8192, d=128); every
+    row of two heads against the oracle."""
+    cfg = W.attn_config(2)
+    inp = W.attn_inputs(cfg)
+    g = _rand(np.random.default_rng(42), cfg.B, cfg.H, cfg.N, cfg.d)
+    pat = cfg.pattern.as_dict()
+    heads = [0, 31]
+    print("bwd config 2 full size", flush=True)
+    dq, dk, dv = _run(pat, inp["q"], inp["k"], inp["v"], g, cfg.block, cfg.block, heads=heads)
+    rq, rk, rv = oracle.attn_bwd(pat, inp["q"], inp["k"], inp["v"], g, heads=heads)
+    for name, a, b in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        _check(name, a, b, "config 2")
+
+
+def test_bwd_content_selected_per_head_lists():
+    """Per-(b, h) lists from sa_select_blocks: every head's gradients."""
+    rng = np.random.default_rng(43)
+    B, H, n, d, bs = 1, 3, 640, 128, 64
+    q, k, v, g = (_rand(rng, B, H, n, d) for _ in range(4))
+    qd, kd, vd, gd = (to_dev_bf16(x) for x in (q, k, v, g))
+    sel = sa.select_blocks(qd, kd, bs, bs, 3)
+    o, lse = sa.attn_fwd(qd, kd, vd, sel)
+    dq, dk, dv = sa.attn_bwd(qd, kd, vd, o, lse, gd, sel)
+    torch.cuda.synchronize()
+    want = oracle.select_blocks(q, k, 0, bs, bs, 3)
+    # reference: torch fp64 autograd of the dense attention masked by the oracle's
+    # selection (the routine that pins the oracle's own backward)
+    for h in range(H):
+        mask = np.zeros((n, n), bool)
+        for i in range(n // bs):
+            for j in want["kv_index"][h, i, : want["kv_count"][h, i]]:
+                mask[i * bs:(i + 1) * bs, j * bs:(j + 1) * bs] = True
+        mask &= np.tril(np.ones((n, n), bool))
+        tq, tk, tv = (torch.from_numpy(W.bf16_bits_to_f32(x[0, h]).astype(np.float64)).requires_grad_(True)
+                      for x in (q, k, v))
+        sc = torch.matmul(tq, tk.T) / np.sqrt(d)
+        w = torch.softmax(sc.masked_fill(~torch.from_numpy(mask), float("-inf")), dim=-1)
+        (torch.matmul(w, tv) * torch.from_numpy(W.bf16_bits_to_f32(g[0, h]).astype(np.float64))).sum().backward()
+        for name, a, b in (("dq", dq[0, h], tq.grad), ("dk", dk[0, h], tk.grad), ("dv", dv[0, h], tv.grad)):
+            _check(name, a.cpu().numpy(), b.numpy(), f"selected head {h}")
