@@ -79,6 +79,8 @@ def main() -> int:
     ap.add_argument("--no-dsa", action="store_true")
     ap.add_argument("--no-strided", action="store_true")
     ap.add_argument("--no-select", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--no-other", action="store_true", help="skip the tiny and BigBird-style block workloads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="the CPU oracle repeats whole passes over the workload until this much time has passed")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -170,6 +172,30 @@ def main() -> int:
     _log(f"bench: step {ms_per_step * 1e3:.1f} us (builder {builder_ms * 1e3:.1f} us, attention "
          f"{attn_ms * 1e3:.1f} us) -> {value:.1f} TFLOP/s over live pairs")
 
+    # the attention kernel alone, median over at least 50 launches, warm (L2 and
+    # MALL as the previous launch left them) and cold (a 1 GiB buffer written
+    # between launches)
+    reps = max(50, args.steps)
+    warm, cold = [], []
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        sa.attn_fwd(q, k, v, bl, out=out, lse=lse)
+        e1.record(stream)
+        warm.append((e0, e1))
+    for _ in range(reps):
+        flush.fill_(1.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        sa.attn_fwd(q, k, v, bl, out=out, lse=lse)
+        e1.record(stream)
+        cold.append((e0, e1))
+    torch.cuda.synchronize()
+    del flush
+    attn_med_ms = float(np.median([a.elapsed_time(b) for a, b in warm]))
+    attn_cold_ms = float(np.median([a.elapsed_time(b) for a, b in cold]))
+
     traffic = _traffic()
     result = {
         "metric": "effective TFLOP/s over live pairs (and % bf16 MFMA peak), 1x MI355X",
@@ -193,6 +219,11 @@ def main() -> int:
             "pct_bf16_peak_over_live_pairs": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
             "builder_us": round(builder_ms * 1e3, 2), "attention_us": round(attn_ms * 1e3, 2),
             "attention_tflops_over_live_tiles": round(tile_flops / (attn_ms * 1e-3) / 1e12, 2),
+            "attention_us_median_warm": round(attn_med_ms * 1e3, 2),
+            "attention_us_median_cold": round(attn_cold_ms * 1e3, 2),
+            "attention_median_reps": reps,
+            "attention_tflops_over_live_pairs_median_warm": round(flops / (attn_med_ms * 1e-3) / 1e12, 2),
+            "attention_tflops_over_live_tiles_median_warm": round(tile_flops / (attn_med_ms * 1e-3) / 1e12, 2),
         },
         "roofline": {
             "kernel": "attn_block_kernel<128,128,128>",
@@ -214,6 +245,13 @@ def main() -> int:
 
     if not args.no_select:
         result["content_selected"] = _bench_select(sa, W, np, torch, dev, dev_bf16)
+
+    if not args.no_bwd:
+        result["backward"] = _bench_bwd(sa, np, torch, dev, cfg, q, k, v, bl, out, lse, live_pairs, live_blocks)
+
+    if not args.no_other:
+        result["window128_sinks4_n512"] = _bench_blocks(sa, W, np, torch, dev, dev_bf16, 1)
+        result["bigbird_n16384"] = _bench_blocks(sa, W, np, torch, dev, dev_bf16, 4)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = _cpu_baseline(cfg, inp, args.cpu_seconds, np)
@@ -264,6 +302,71 @@ def _bench_strided(sa, W, np, torch, dev, dev_bf16, reps=10):
                       "64x64 band tiles, causal 64-row tiles per (head, key residue) view and the last row, the "
                       "later parts merged by log-sum-exp in the kernel epilogue",
     }
+
+def _bench_bwd(sa, np, torch, dev, cfg, q, k, v, bl, out, lse, live_pairs, live_blocks, reps=20):
+    """The backward at the headline workload: dQ, dK, dV from the forward's O and LSE.
+    Algorithmic work: 5 products per live pair (S, dP, dV, dQ, dK), 10 * d flop."""
+    g = torch.randn(q.shape, device=dev).to(torch.bfloat16)
+    sa.attn_fwd(q, k, v, bl, out=out, lse=lse)
+    dq, dk, dv = sa.attn_bwd(q, k, v, out, lse, g, bl)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        sa.attn_bwd(q, k, v, out, lse, g, bl, dq=dq, dk=dk, dv=dv)
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    t = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    flop = 10.0 * cfg.d * live_pairs
+    tile_flop = 10.0 * cfg.d * cfg.block * cfg.block * live_blocks * cfg.B * cfg.H
+    return {
+        "workload": "backward (dQ, dK, dV) of the headline workload, from its O and LSE",
+        "us_median": round(t * 1e6, 1),
+        "tflops_over_live_pairs": round(flop / t / 1e12, 2),
+        "tflops_over_live_tiles": round(tile_flop / t / 1e12, 2),
+        "pct_bf16_peak_over_live_pairs": round(100.0 * flop / t / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "flop_note": "10 * head_dim per live pair (S, dP, dV, dQ, dK products)",
+    }
+
+
+def _bench_blocks(sa, W, np, torch, dev, dev_bf16, cid, reps=50):
+    """Block-list attention on another block workload (builder + attention timed apart)."""
+    cfg = W.attn_config(cid)
+    _log(f"bench: generating inputs for {cfg.name}")
+    inp = W.attn_inputs(cfg)
+    q, k, v = (dev_bf16(inp[t]) for t in ("q", "k", "v"))
+    bl = sa.build_block_mask(cfg.pattern, cfg.N, cfg.N, cfg.block, cfg.block, device=dev)
+    o = torch.empty((cfg.B, cfg.H, cfg.N, cfg.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((cfg.B, cfg.H, cfg.N), dtype=torch.float32, device=dev)
+    sa.attn_fwd(q, k, v, bl, out=o, lse=lse)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = []
+    for _ in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        sa.build_block_mask(cfg.pattern, cfg.N, cfg.N, cfg.block, cfg.block, device=dev, out=bl)
+        e[1].record(stream)
+        sa.attn_fwd(q, k, v, bl, out=o, lse=lse)
+        e[2].record(stream)
+        ev.append(e)
+    torch.cuda.synchronize()
+    tb = float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+    ta = float(np.median([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    pairs = int(bl.live_pairs.item()) * cfg.B * cfg.H
+    tiles = int(bl.kv_count.sum().item()) * cfg.B * cfg.H
+    return {
+        "workload": f"{cfg.name}: B={cfg.B} H={cfg.H} N={cfg.N} d={cfg.d}, {cfg.block}x{cfg.block} blocks",
+        "live_pairs": pairs,
+        "builder_us_median": round(tb * 1e6, 2),
+        "attention_us_median": round(ta * 1e6, 2),
+        "attention_tflops_over_live_pairs": round(4.0 * cfg.d * pairs / ta / 1e12, 2),
+        "attention_tflops_over_live_tiles": round(4.0 * cfg.d * cfg.block * cfg.block * tiles / ta / 1e12, 2),
+    }
+
 
 def _bench_select(sa, W, np, torch, dev, dev_bf16, reps=20):
     """Content-selected key blocks (workload 6): the selection (block means, scores,

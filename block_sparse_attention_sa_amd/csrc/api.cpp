@@ -770,6 +770,8 @@ sa_status sa_attn_bwd(const sa_attn_bwd_args* a, void* stream)
         p.q_count = (int32_t*)(ws + L.q_count);
         p.q_index = (int32_t*)(ws + L.q_index);
         p.q_partial = ws + L.q_partial;
+        p.order_q = (int32_t*)(ws + L.order_q);
+        p.order_k = (int32_t*)(ws + L.order_k);
         return launched(sa::launch_attn_bwd(p, (int)a->head_dim, (int)a->block_q, (int)a->block_kv,
                                             (hipStream_t)stream),
                         "sa_attn_bwd");

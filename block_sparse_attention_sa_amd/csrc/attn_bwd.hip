@@ -14,15 +14,24 @@
 //
 // gfx950 mapping: every product is a v_mfma_f32_32x32x16_bf16 on 32 x 32
 // tiles with bf16 operands (P and dS rounded to bf16) and float32
-// accumulation.
-//   * bwd_dq_kernel: a wave owns 32 queries and walks their live key tiles in
-//     32-key steps (K, K^T and V staged in LDS by the workgroup); S^T and
-//     dP^T come out with one query per lane, so the row's LSE and D are one
-//     register each; dS goes through a per-wave LDS tile into dQ += dS K.
-//   * bwd_dkdv_kernel: a wave owns 32 keys and walks the query tiles whose
-//     lists hold its key block (lists transposed by bwd_transpose_kernel);
-//     S and dP come out with one key per lane; P^T and dS^T go through
-//     per-wave LDS tiles into dV += P^T dO and dK += dS^T Q.
+// accumulation.  The contraction index of an MFMA may be permuted freely as
+// long as both operands use the same order; the backward uses this so that
+// P and dS feed the second product straight from the accumulator registers
+// of the first: lane half h of an output tile holds rows 8m + 4h + c
+// (m, c < 4), so the k-slots 8h .. 8h+7 of chunk ks carry rows
+// 16ks + 4h + {0..3} and 16ks + 8 + 4h + {0..3}, and the other operand is
+// read with the same order from a transposed LDS copy (two 8-byte reads).
+//   * bwd_dq_kernel: a wave owns 32 queries (Q and dO in registers) and walks
+//     the live key tiles 32 keys at a time; the workgroup stages K (row-major
+//     and transposed) and V in LDS, double-buffered, the next tile's loads in
+//     flight while the current one is computed, one barrier per step.  It
+//     also forms D = rowsum(dO * O) for its queries.
+//   * bwd_dkdv_kernel: a wave owns 32 keys (K and V in registers) and walks
+//     the query tiles whose lists hold its key block (the lists transposed by
+//     bwd_transpose_kernel), staging Q and dO the same way.
+//   * Work items start longest list first (bwd_order_kernel), so that key
+//     blocks every query sees (attention sinks, global tokens) do not finish
+//     last.
 #include "sa_internal.h"
 
 namespace sa {
@@ -30,133 +39,233 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 constexpr float kLog2e = 1.4426950408889634f;
+// u16 stride of a transposed [dim][32 rows] tile: 18 dwords, so the 8-byte
+// reads of 32 lanes at 32 consecutive dims cover the 64 banks once, and the
+// transposing u32 stores of a wave (16 row pairs x 4 chunks) do as well
+constexpr int kTS = 36;
 
 __device__ __forceinline__ bf16x8 lds8(const uint16_t* p)
 {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
-__device__ __forceinline__ uint16_t bf16_bits(float x)
+// B operand with the permuted contraction order: rows r0 .. r0+3 and
+// r0+8 .. r0+11 of column `dim` of a transposed tile
+__device__ __forceinline__ bf16x8 tr_op(const uint16_t* tr, int dim, int r0)
 {
-    return __builtin_bit_cast(uint16_t, (__bf16)x);
+    const u32x2 lo = *reinterpret_cast<const u32x2*>(tr + dim * kTS + r0);
+    const u32x2 hi = *reinterpret_cast<const u32x2*>(tr + dim * kTS + r0 + 8);
+    const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
+    return __builtin_bit_cast(bf16x8, w);
 }
 
-// The pair predicate of the pattern for one (query position, key) pair: the
-// same terms as allowed_bits32, one pair at a time.
-__device__ bool allowed_pair(const DevPattern& p, int32_t q, int32_t kv)
+// A operand from accumulator elements base .. base+7 (bf16, nearest even)
+__device__ __forceinline__ bf16x8 pack8(const f32x16& v, int base)
 {
-    if (kv >= p.n_kv || (p.causal && kv > q)) return false;
-    if (p.window_left >= 0 && q - kv <= p.window_left && kv - q <= p.window_right) return true;
-    if (kv < p.sinks) return true;
-    if (p.stride > 0 && q >= kv && fmod_(q - kv, p.stride_div) == p.stride_phase) return true;
-    if (q < p.global_tokens || kv < p.global_tokens) return true;
-    if (p.unit > 0) {
-        const int32_t qu = fdiv(q, p.unit_div), ku = fdiv(kv, p.unit_div);
-        if (p.unit_window >= 0 && abs(qu - ku) <= p.unit_window) return true;
-        if (qu < p.rand_rows)
-            for (int i = 0; i < p.n_rand; ++i)
-                if (p.rand_units[(int64_t)qu * p.n_rand + i] == ku) return true;
-    }
-    return false;
-}
-
-// D[row] = sum_c dO[row][c] * O[row][c]; 16 lanes per row
-__global__ void __launch_bounds__(256) bwd_dsum_kernel(const uint16_t* __restrict__ dout, const float* __restrict__ o,
-                                                       int64_t rows, int32_t d, float* __restrict__ dsum)
-{
-    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int l = threadIdx.x & 15;
-    float acc = 0.f;
-    if (row < rows)
-        for (int c = l; c < d; c += 16)
-            acc += __uint_as_float((uint32_t)dout[row * d + c] << 16) * o[row * d + c];
+    bf16x8 r;
 #pragma unroll
-    for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);
-    if (row < rows && l == 0) dsum[row] = acc;
+    for (int j = 0; j < 8; ++j) r[j] = (__bf16)v[base + j];
+    return r;
 }
 
-// For every list row L and key block j: the query blocks whose list holds j,
-// ascending, with the list's partial flag.
-__global__ void bwd_transpose_kernel(const int32_t* __restrict__ kv_count, const int32_t* __restrict__ kv_index,
-                                     const uint8_t* __restrict__ kv_partial, int32_t n_lists, int32_t nqb,
-                                     int32_t nkb, int32_t* __restrict__ q_count, int32_t* __restrict__ q_index,
-                                     uint8_t* __restrict__ q_partial)
-{
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= (int64_t)n_lists * nkb) return;
-    const int64_t L = t / nkb;
-    const int j = (int)(t % nkb);
-    int n = 0;
-    for (int i = 0; i < nqb; ++i) {
-        const int64_t row = L * nqb + i;
-        const int cnt = min(kv_count[row], nkb);
-        for (int e = 0; e < cnt; ++e)
-            if (kv_index[row * nkb + e] == j) {
-                q_index[t * nqb + n] = i;
-                q_partial[t * nqb + n] = kv_partial[row * nkb + e];
-                ++n;
-                break;
-            }
-    }
-    q_count[t] = n;
-}
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
-// Rows [r0, r0 + 32) of a [.., n, D] bf16 tensor into LDS: row-major `rm`
-// ([32][D]) and, when T, transposed `tr` ([D][32]); rows at or past n are zero.
-template <int D, bool T>
-__device__ __forceinline__ void stage32(const uint16_t* __restrict__ src, int r0, int n, uint16_t* rm, uint16_t* tr,
-                                        int tid, int nthreads)
-{
-    constexpr int CH = D / 8;  // 16-byte chunks per row
-    for (int idx = tid; idx < 32 * CH; idx += nthreads) {
-        const int r = idx / CH, ch = idx % CH;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (r0 + r < n) w = *reinterpret_cast<const u32x4*>(src + (int64_t)(r0 + r) * D + 8 * ch);
-        *reinterpret_cast<u32x4*>(rm + r * D + 8 * ch) = w;
-        if (T) {
+// 32 rows [row0, row0 + 32) of a [n, D] bf16 tensor, staged through
+// registers: load() issues the global reads (rows at or past n read as zero),
+// store() writes the row-major copy ([32][D + 8], 16-byte rows padded so that
+// 16 lanes reading one chunk of 16 rows hit distinct banks) and, when T, the
+// transposed copy ([D][kTS]).  A thread moves row pairs (2p, 2p + 1) of one
+// 8-column chunk so that the transposed stores are whole dwords.
+template <int D, int NT, bool T>
+struct Stage32 {
+    static constexpr int CH = D / 8, ITEMS = 16 * CH, PER = (ITEMS + NT - 1) / NT, RS = D + 8;
+    u32x4 r0[PER], r1[PER];
+
+    __device__ __forceinline__ void clear()
+    {
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                tr[(8 * ch + 2 * x) * 32 + r] = (uint16_t)(w[x] & 0xFFFFu);
-                tr[(8 * ch + 2 * x + 1) * 32 + r] = (uint16_t)(w[x] >> 16);
+        for (int i = 0; i < PER; ++i) r0[i] = r1[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+    __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int row0, int n, int tid)
+    {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int it = tid + i * NT;
+            const int p = it & 15, ch = it >> 4;
+            const int64_t r = (int64_t)row0 + 2 * p;
+            r0[i] = r1[i] = u32x4{0u, 0u, 0u, 0u};
+            if (it < ITEMS) {
+                if (r < n) r0[i] = *reinterpret_cast<const u32x4*>(src + r * D + 8 * ch);
+                if (r + 1 < n) r1[i] = *reinterpret_cast<const u32x4*>(src + (r + 1) * D + 8 * ch);
             }
         }
+    }
+    __device__ __forceinline__ void store(uint16_t* rm, uint16_t* tr, int tid) const
+    {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int it = tid + i * NT;
+            if (it >= ITEMS) continue;
+            const int p = it & 15, ch = it >> 4;
+            *reinterpret_cast<u32x4*>(rm + (2 * p) * RS + 8 * ch) = r0[i];
+            *reinterpret_cast<u32x4*>(rm + (2 * p + 1) * RS + 8 * ch) = r1[i];
+            if (T) {
+                uint32_t* t32 = reinterpret_cast<uint32_t*>(tr);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int dim = 8 * ch + 2 * x;
+                    t32[dim * (kTS / 2) + p] = (r0[i][x] & 0xFFFFu) | (r1[i][x] << 16);
+                    t32[(dim + 1) * (kTS / 2) + p] = (r0[i][x] >> 16) | (r1[i][x] & 0xFFFF0000u);
+                }
+            }
+        }
+    }
+};
+
+// For every list row L and key block j: the query blocks whose list holds j,
+// ascending, with the list's partial flag.  One wave per (L, j); lane i
+// binary-searches row i's ascending list, a ballot keeps the order.
+__global__ void __launch_bounds__(256) bwd_transpose_kernel(const int32_t* __restrict__ kv_count,
+                                                            const int32_t* __restrict__ kv_index,
+                                                            const uint8_t* __restrict__ kv_partial, int32_t n_lists,
+                                                            int32_t nqb, int32_t nkb, int32_t* __restrict__ q_count,
+                                                            int32_t* __restrict__ q_index,
+                                                            uint8_t* __restrict__ q_partial)
+{
+    const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (wv >= (int64_t)n_lists * nkb) return;
+    const int64_t L = wv / nkb;
+    const int j = (int)(wv % nkb);
+    int n = 0;
+    for (int i0 = 0; i0 < nqb; i0 += 64) {
+        const int i = i0 + lane;
+        bool found = false;
+        uint8_t part = 0;
+        if (i < nqb) {
+            const int64_t row = L * nqb + i;
+            const int cnt = max(0, min(kv_count[row], nkb));
+            const int32_t* ix = kv_index + row * nkb;
+            int lo = 0, hi = cnt;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (ix[mid] < j) lo = mid + 1;
+                else hi = mid;
+            }
+            if (lo < cnt && ix[lo] == j) {
+                found = true;
+                part = kv_partial[row * nkb + lo];
+            }
+        }
+        const uint64_t m = __ballot(found);
+        if (found) {
+            const int pos = n + __popcll(m & ((1ull << lane) - 1ull));
+            q_index[wv * nqb + pos] = i;
+            q_partial[wv * nqb + pos] = part;
+        }
+        n += __popcll(m);
+    }
+    if (lane == 0) q_count[wv] = n;
+}
+
+__device__ __forceinline__ int order_bucket(int32_t c, int32_t maxc)
+{
+    c = max(0, min(c, maxc));
+    return (int)(((int64_t)c * 1023) / max(maxc, 1));
+}
+
+// order[rank] = item, items by list length descending (equal lengths in any
+// order): a schedule only, every item writes its own outputs.  Block 0 orders
+// the query-block lists, block 1 the transposed key-block lists.
+__global__ void __launch_bounds__(1024) bwd_order_kernel(const int32_t* __restrict__ cq, int32_t nq_items,
+                                                         int32_t maxq, int32_t* __restrict__ oq,
+                                                         const int32_t* __restrict__ ck, int32_t nk_items,
+                                                         int32_t maxk, int32_t* __restrict__ ok)
+{
+    const int32_t* cnt = blockIdx.x ? ck : cq;
+    const int32_t T = blockIdx.x ? nk_items : nq_items;
+    const int32_t maxc = blockIdx.x ? maxk : maxq;
+    int32_t* order = blockIdx.x ? ok : oq;
+    __shared__ int32_t slot[1024];
+    __shared__ int32_t wsum[16];
+    const int tid = threadIdx.x;
+    slot[tid] = 0;
+    __syncthreads();
+    for (int32_t t = tid; t < T; t += 1024) atomicAdd(&slot[1023 - order_bucket(cnt[t], maxc)], 1);
+    __syncthreads();
+    const int v = slot[tid];
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if ((tid & 63) >= off) x += y;
+    }
+    if ((tid & 63) == 63) wsum[tid >> 6] = x;
+    __syncthreads();
+    int before = 0;
+    for (int i = 0; i < (tid >> 6); ++i) before += wsum[i];
+    slot[tid] = before + x - v;
+    __syncthreads();
+    for (int32_t t = tid; t < T; t += 1024) {
+        const int pos = atomicAdd(&slot[1023 - order_bucket(cnt[t], maxc)], 1);
+        order[pos] = t;
     }
 }
 
 template <int D, int BQ, int BK>
-__global__ void __launch_bounds__(BQ * 2)
+__global__ void __launch_bounds__(BQ * 2, 2)
 bwd_dq_kernel(BwdParams a)
 {
-    constexpr int NW = BQ / 32, NT = BQ * 2, NDC = D / 16, NDB = D / 32;
-    __shared__ __attribute__((aligned(16))) uint16_t kt[32 * D];
-    __shared__ __attribute__((aligned(16))) uint16_t ktt[D * 32];
-    __shared__ __attribute__((aligned(16))) uint16_t vt[32 * D];
-    __shared__ __attribute__((aligned(16))) uint16_t dst[NW][32 * 32];
+    constexpr int NT = BQ * 2, NDC = D / 16, NDB = D / 32, RS = D + 8, SUB = BK / 32;
+    using KStage = Stage32<D, NT, true>;
+    using VStage = Stage32<D, NT, false>;
+    __shared__ __attribute__((aligned(16))) uint16_t k_rm[2][32 * RS];
+    __shared__ __attribute__((aligned(16))) uint16_t k_tr[2][D * kTS];
+    __shared__ __attribute__((aligned(16))) uint16_t v_rm[2][32 * RS];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
-    const int qb = blockIdx.x % a.nqb, bh = blockIdx.x / a.nqb;
+    const int BH = a.batch * a.heads;
+    int bh, qb;
+    int64_t lrow;
+    if (a.per_head_lists) {
+        const int t = a.order_q[blockIdx.x];
+        bh = t / a.nqb;
+        qb = t % a.nqb;
+        lrow = t;
+    } else {
+        bh = (int)(blockIdx.x % (unsigned)BH);
+        qb = a.order_q[blockIdx.x / (unsigned)BH];
+        lrow = qb;
+    }
     const int q = qb * BQ + 32 * w + l32;  // this lane's query row
     const bool q_ok = q < a.n_q;
-    const uint16_t* qg = a.q + (int64_t)bh * a.n_q * D;
-    const uint16_t* gg = a.dout + (int64_t)bh * a.n_q * D;
-    const uint16_t* kg = a.k + (int64_t)bh * a.n_kv * D;
-    const uint16_t* vg = a.v + (int64_t)bh * a.n_kv * D;
-    // B operands Q^T and dO^T: lane holds row q, dims 16s + 8hh .. + 7
+    const int64_t qrow = (int64_t)bh * a.n_q + q;
+    // B operands Q^T and dO^T: lane holds row q, dims 16s + 8hh .. + 7; and
+    // the row's D = dO . O from the same dims plus the other half's
     bf16x8 qop[NDC], gop[NDC];
+    float dpart = 0.f;
 #pragma unroll
     for (int s = 0; s < NDC; ++s) {
         u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
         if (q_ok) {
-            x = *reinterpret_cast<const u32x4*>(qg + (int64_t)q * D + 16 * s + 8 * hh);
-            y = *reinterpret_cast<const u32x4*>(gg + (int64_t)q * D + 16 * s + 8 * hh);
+            x = *reinterpret_cast<const u32x4*>(a.q + qrow * D + 16 * s + 8 * hh);
+            y = *reinterpret_cast<const u32x4*>(a.dout + qrow * D + 16 * s + 8 * hh);
+            const f32x4 o0 = *reinterpret_cast<const f32x4*>(a.o + qrow * D + 16 * s + 8 * hh);
+            const f32x4 o1 = *reinterpret_cast<const f32x4*>(a.o + qrow * D + 16 * s + 8 * hh + 4);
+            dpart += bf16_lo(y.x) * o0.x + bf16_hi(y.x) * o0.y + bf16_lo(y.y) * o0.z + bf16_hi(y.y) * o0.w;
+            dpart += bf16_lo(y.z) * o1.x + bf16_hi(y.z) * o1.y + bf16_lo(y.w) * o1.z + bf16_hi(y.w) * o1.w;
         }
         qop[s] = __builtin_bit_cast(bf16x8, x);
         gop[s] = __builtin_bit_cast(bf16x8, y);
     }
-    const float lse = q_ok ? a.lse[(int64_t)bh * a.n_q + q] : INFINITY;
-    const float dsum = q_ok ? a.dsum[(int64_t)bh * a.n_q + q] : 0.f;
+    const float dsum = dpart + __shfl_xor(dpart, 32);
+    if (q_ok && hh == 0) a.dsum[qrow] = dsum;
+    const float lse = q_ok ? a.lse[qrow] : INFINITY;
     const float lse2 = lse == -INFINITY ? INFINITY : lse * kLog2e;  // a row without keys has no pair
     RowCtx rc;
     row_ctx(a.pat, q + a.pat.q_offset, rc);
@@ -166,52 +275,76 @@ bwd_dq_kernel(BwdParams a)
 #pragma unroll
         for (int i = 0; i < 16; ++i) dq[db][i] = 0.f;
 
-    const int64_t lrow = (a.per_head_lists ? (int64_t)bh * a.nqb : 0) + qb;
-    const int cnt = min(a.kv_count[lrow], a.nkb);
-    for (int e = 0; e < cnt; ++e) {
-        const int j = a.kv_index[lrow * a.nkb + e];
-        if ((unsigned)j >= (unsigned)a.nkb) continue;
-        const bool part = a.kv_partial[lrow * a.nkb + e] != 0;
-        for (int t = 0; t < BK / 32; ++t) {
-            const int k0 = j * BK + 32 * t;
-            if (k0 >= a.n_kv) break;
-            const bool need_mask = part || k0 + 32 > a.n_kv;
-            __syncthreads();
-            stage32<D, true>(kg, k0, a.n_kv, kt, ktt, tid, NT);
-            stage32<D, false>(vg, k0, a.n_kv, vt, nullptr, tid, NT);
-            __syncthreads();
+    const int cnt = max(0, min(a.kv_count[lrow], a.nkb));
+    const int nsteps = cnt * SUB;
+    const int32_t* idx = a.kv_index + lrow * a.nkb;
+    const uint8_t* prt = a.kv_partial + lrow * a.nkb;
+    const uint16_t* kg = a.k + (int64_t)bh * a.n_kv * D;
+    const uint16_t* vg = a.v + (int64_t)bh * a.n_kv * D;
+    // first key of step s, or -1 when the step holds no key
+    auto step_k0 = [&](int s) -> int {
+        const int j = idx[s / SUB];
+        if ((unsigned)j >= (unsigned)a.nkb) return -1;
+        const int k0 = j * BK + 32 * (s % SUB);
+        return k0 < a.n_kv ? k0 : -1;
+    };
+    KStage kst;
+    VStage vst;
+    int k0 = -1;
+    if (nsteps > 0) {
+        k0 = step_k0(0);
+        if (k0 >= 0) {
+            kst.load(kg, k0, a.n_kv, tid);
+            vst.load(vg, k0, a.n_kv, tid);
+            kst.store(k_rm[0], k_tr[0], tid);
+            vst.store(v_rm[0], nullptr, tid);
+        }
+    }
+    __syncthreads();
+    for (int s = 0; s < nsteps; ++s) {
+        const int b = s & 1;
+        const int k0n = s + 1 < nsteps ? step_k0(s + 1) : -1;
+        if (k0n >= 0) {
+            kst.load(kg, k0n, a.n_kv, tid);
+            vst.load(vg, k0n, a.n_kv, tid);
+        }
+        if (k0 >= 0) {
             // S^T = K Q^T and dP^T = V dO^T: lane = query, element i = key 8(i/4) + 4hh + i%4
-            f32x16 s, dp;
+            f32x16 st, dpt;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+            for (int i = 0; i < 16; ++i) st[i] = dpt[i] = 0.f;
+            const uint16_t* kr = k_rm[b] + l32 * RS + 8 * hh;
+            const uint16_t* vr = v_rm[b] + l32 * RS + 8 * hh;
 #pragma unroll
             for (int c = 0; c < NDC; ++c) {
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds8(kt + l32 * D + 16 * c + 8 * hh), qop[c], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds8(vt + l32 * D + 16 * c + 8 * hh), gop[c], dp, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds8(kr + 16 * c), qop[c], st, 0, 0, 0);
+                dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds8(vr + 16 * c), gop[c], dpt, 0, 0, 0);
             }
             uint32_t mbits = 0xFFFFFFFFu;
-            if (need_mask) mbits = allowed_bits32(a.pat, rc, k0) >> (4 * hh);
-            uint16_t* myds = dst[w];
+            if (prt[s / SUB] != 0 || k0 + 32 > a.n_kv) mbits = allowed_bits32(a.pat, rc, k0) >> (4 * hh);
+            f32x16 ds;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const bool ok = (mbits >> (8 * (i >> 2) + (i & 3))) & 1u;
-                const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], a.scale_log2, -lse2)) : 0.f;
-                const float ds = p * (dp[i] - dsum);
-                myds[l32 * 32 + 8 * (i >> 2) + 4 * hh + (i & 3)] = bf16_bits(ds);
+                const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[i], a.scale_log2, -lse2)) : 0.f;
+                ds[i] = p * (dpt[i] - dsum);
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             // dQ (queries x d) += dS (queries x keys) K (keys x d)
+            const bf16x8 a0 = pack8(ds, 0), a1 = pack8(ds, 8);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 aop = lds8(myds + l32 * 32 + 16 * ks + 8 * hh);
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        aop, lds8(ktt + (32 * db + l32) * 32 + 16 * ks + 8 * hh), dq[db], 0, 0, 0);
+            for (int db = 0; db < NDB; ++db) {
+                dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, tr_op(k_tr[b], 32 * db + l32, 4 * hh), dq[db],
+                                                                 0, 0, 0);
+                dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, tr_op(k_tr[b], 32 * db + l32, 16 + 4 * hh),
+                                                                 dq[db], 0, 0, 0);
             }
         }
+        if (k0n >= 0) {
+            kst.store(k_rm[b ^ 1], k_tr[b ^ 1], tid);
+            vst.store(v_rm[b ^ 1], nullptr, tid);
+        }
+        __syncthreads();
+        k0 = k0n;
     }
     // dq element (db, i): query row 8(i/4) + 4hh + i%4 of the wave, dim 32 db + l32
     float* dqg = a.dq + (int64_t)bh * a.n_q * D;
@@ -225,33 +358,44 @@ bwd_dq_kernel(BwdParams a)
 }
 
 template <int D, int BQ, int BK>
-__global__ void __launch_bounds__(BK * 2)
+__global__ void __launch_bounds__(BK * 2, 1)
 bwd_dkdv_kernel(BwdParams a)
 {
-    constexpr int NW = BK / 32, NT = BK * 2, NDC = D / 16, NDB = D / 32;
-    __shared__ __attribute__((aligned(16))) uint16_t qt[32 * D];
-    __shared__ __attribute__((aligned(16))) uint16_t qtt[D * 32];
-    __shared__ __attribute__((aligned(16))) uint16_t gt[32 * D];
-    __shared__ __attribute__((aligned(16))) uint16_t gtt[D * 32];
-    __shared__ __attribute__((aligned(16))) uint16_t ptt[NW][32 * 32];
-    __shared__ __attribute__((aligned(16))) uint16_t dstt[NW][32 * 32];
-    __shared__ float lse_s[32], dsum_s[32];
+    constexpr int NT = BK * 2, NW = BK / 32, NDC = D / 16, NDB = D / 32, RS = D + 8, SUB = BQ / 32;
+    using QStage = Stage32<D, NT, true>;
+    __shared__ __attribute__((aligned(16))) uint16_t q_rm[2][32 * RS];
+    __shared__ __attribute__((aligned(16))) uint16_t q_tr[2][D * kTS];
+    __shared__ __attribute__((aligned(16))) uint16_t g_rm[2][32 * RS];
+    __shared__ __attribute__((aligned(16))) uint16_t g_tr[2][D * kTS];
+    __shared__ __attribute__((aligned(16))) float lse_s[2][32];
+    __shared__ __attribute__((aligned(16))) float dsum_s[2][32];
+    __shared__ __attribute__((aligned(16))) uint32_t mw_s[2][NW][32];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
-    const int kb = blockIdx.x % a.nkb, bh = blockIdx.x / a.nkb;
-    const int kv = kb * BK + 32 * w + l32;  // this lane's key row
+    const int BH = a.batch * a.heads;
+    int bh, kb;
+    int64_t lrow;
+    if (a.per_head_lists) {
+        const int t = a.order_k[blockIdx.x];
+        bh = t / a.nkb;
+        kb = t % a.nkb;
+        lrow = t;
+    } else {
+        bh = (int)(blockIdx.x % (unsigned)BH);
+        kb = a.order_k[blockIdx.x / (unsigned)BH];
+        lrow = kb;
+    }
+    const int kbase = kb * BK + 32 * w;  // this wave's keys
+    const int kv = kbase + l32;          // this lane's key row
     const bool k_ok = kv < a.n_kv;
-    const uint16_t* qg = a.q + (int64_t)bh * a.n_q * D;
-    const uint16_t* gg = a.dout + (int64_t)bh * a.n_q * D;
-    const uint16_t* kg = a.k + (int64_t)bh * a.n_kv * D;
-    const uint16_t* vg = a.v + (int64_t)bh * a.n_kv * D;
+    const int64_t krow = (int64_t)bh * a.n_kv + kv;
     // B operands K^T and V^T: lane holds key row kv, dims 16s + 8hh .. + 7
     bf16x8 kop[NDC], vop[NDC];
 #pragma unroll
     for (int s = 0; s < NDC; ++s) {
         u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
         if (k_ok) {
-            x = *reinterpret_cast<const u32x4*>(kg + (int64_t)kv * D + 16 * s + 8 * hh);
-            y = *reinterpret_cast<const u32x4*>(vg + (int64_t)kv * D + 16 * s + 8 * hh);
+            x = *reinterpret_cast<const u32x4*>(a.k + krow * D + 16 * s + 8 * hh);
+            y = *reinterpret_cast<const u32x4*>(a.v + krow * D + 16 * s + 8 * hh);
         }
         kop[s] = __builtin_bit_cast(bf16x8, x);
         vop[s] = __builtin_bit_cast(bf16x8, y);
@@ -262,64 +406,106 @@ bwd_dkdv_kernel(BwdParams a)
 #pragma unroll
         for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
 
-    const int64_t lrow = (a.per_head_lists ? (int64_t)bh * a.nkb : 0) + kb;
-    const int cnt = min(a.q_count[lrow], a.nqb);
-    for (int e = 0; e < cnt; ++e) {
-        const int i_blk = a.q_index[lrow * a.nqb + e];
-        const bool part = a.q_partial[lrow * a.nqb + e] != 0;
-        for (int t = 0; t < BQ / 32; ++t) {
-            const int q0 = i_blk * BQ + 32 * t;
-            if (q0 >= a.n_q) break;
-            const bool need_mask = part || q0 + 32 > a.n_q || kb * BK + BK > a.n_kv;
-            __syncthreads();
-            stage32<D, true>(qg, q0, a.n_q, qt, qtt, tid, NT);
-            stage32<D, true>(gg, q0, a.n_q, gt, gtt, tid, NT);
-            if (tid < 32) {
-                const int qr = q0 + tid;
-                const float l = qr < a.n_q ? a.lse[(int64_t)bh * a.n_q + qr] : INFINITY;
-                lse_s[tid] = l == -INFINITY ? INFINITY : l * kLog2e;
-                dsum_s[tid] = qr < a.n_q ? a.dsum[(int64_t)bh * a.n_q + qr] : 0.f;
-            }
-            __syncthreads();
+    const int cnt = max(0, min(a.q_count[lrow], a.nqb));
+    const int nsteps = cnt * SUB;
+    const int32_t* idx = a.q_index + lrow * a.nqb;
+    const uint8_t* prt = a.q_partial + lrow * a.nqb;
+    const uint16_t* qg = a.q + (int64_t)bh * a.n_q * D;
+    const uint16_t* gg = a.dout + (int64_t)bh * a.n_q * D;
+    const float* lseg = a.lse + (int64_t)bh * a.n_q;
+    const float* dsg = a.dsum + (int64_t)bh * a.n_q;
+    // first query of step s (-1: none); whether its pairs need the pattern
+    auto step_q0 = [&](int s) -> int {
+        const int q0 = idx[s / SUB] * BQ + 32 * (s % SUB);
+        return q0 < a.n_q ? q0 : -1;
+    };
+    QStage qst, gst;
+    float lse_r = INFINITY, dsum_r = 0.f;
+    uint32_t mword = 0;
+    // issue the reads of step s's staged data (rows, LSE, D, mask words)
+    auto fetch = [&](int s, int q0) {
+        qst.load(qg, q0, a.n_q, tid);
+        gst.load(gg, q0, a.n_q, tid);
+        if (tid < 32) {
+            const int qr = q0 + tid;
+            const float l = qr < a.n_q ? lseg[qr] : INFINITY;
+            lse_r = l == -INFINITY ? INFINITY : l * kLog2e;
+            dsum_r = qr < a.n_q ? dsg[qr] : 0.f;
+        }
+        if (prt[s / SUB] != 0) {
+            // bit l of word r: key kbase + l is allowed for query q0 + r
+            const int qr = q0 + l32;
+            RowCtx rc;
+            row_ctx(a.pat, qr + a.pat.q_offset, rc);
+            mword = qr < a.n_q ? allowed_bits32(a.pat, rc, kbase) : 0u;
+        }
+    };
+    auto put = [&](int s, int buf) {
+        qst.store(q_rm[buf], q_tr[buf], tid);
+        gst.store(g_rm[buf], g_tr[buf], tid);
+        if (tid < 32) {
+            lse_s[buf][tid] = lse_r;
+            dsum_s[buf][tid] = dsum_r;
+        }
+        if (prt[s / SUB] != 0 && hh == 0) mw_s[buf][w][l32] = mword;
+    };
+    int q0 = -1;
+    if (nsteps > 0) {
+        q0 = step_q0(0);
+        if (q0 >= 0) {
+            fetch(0, q0);
+            put(0, 0);
+        }
+    }
+    __syncthreads();
+    for (int s = 0; s < nsteps; ++s) {
+        const int b = s & 1;
+        const int q0n = s + 1 < nsteps ? step_q0(s + 1) : -1;
+        if (q0n >= 0) fetch(s + 1, q0n);
+        if (q0 >= 0) {
             // S = Q K^T and dP = dO V^T: lane = key, element i = query 8(i/4) + 4hh + i%4
-            f32x16 s, dp;
+            f32x16 sv, dp;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+            for (int i = 0; i < 16; ++i) sv[i] = dp[i] = 0.f;
+            const uint16_t* qr = q_rm[b] + l32 * RS + 8 * hh;
+            const uint16_t* gr = g_rm[b] + l32 * RS + 8 * hh;
 #pragma unroll
             for (int c = 0; c < NDC; ++c) {
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds8(qt + l32 * D + 16 * c + 8 * hh), kop[c], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds8(gt + l32 * D + 16 * c + 8 * hh), vop[c], dp, 0, 0, 0);
+                sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds8(qr + 16 * c), kop[c], sv, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds8(gr + 16 * c), vop[c], dp, 0, 0, 0);
             }
-            uint16_t* myp = ptt[w];
-            uint16_t* myds = dstt[w];
+            const bool masked = prt[s / SUB] != 0;
+            f32x16 pv, ds;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int qi = 8 * (i >> 2) + 4 * hh + (i & 3);
-                const int qr = q0 + qi;
-                bool ok = true;
-                if (need_mask) ok = qr < a.n_q && allowed_pair(a.pat, qr + a.pat.q_offset, kv);
-                const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], a.scale_log2, -lse_s[qi])) : 0.f;
-                const float ds = p * (dp[i] - dsum_s[qi]);
-                myp[l32 * 32 + qi] = bf16_bits(p);
-                myds[l32 * 32 + qi] = bf16_bits(ds);
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // dV (keys x d) += P^T (keys x queries) dO; dK += dS^T Q
+            for (int m = 0; m < 4; ++m) {
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[b][8 * m + 4 * hh]);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dsum_s[b][8 * m + 4 * hh]);
+                u32x4 w4 = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+                if (masked) w4 = *reinterpret_cast<const u32x4*>(&mw_s[b][w][8 * m + 4 * hh]);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 pop = lds8(myp + l32 * 32 + 16 * ks + 8 * hh);
-                const bf16x8 sop = lds8(myds + l32 * 32 + 16 * ks + 8 * hh);
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        pop, lds8(gtt + (32 * db + l32) * 32 + 16 * ks + 8 * hh), dv[db], 0, 0, 0);
-                    dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        sop, lds8(qtt + (32 * db + l32) * 32 + 16 * ks + 8 * hh), dk[db], 0, 0, 0);
+                for (int c = 0; c < 4; ++c) {
+                    const int i = 4 * m + c;
+                    const bool ok = (w4[c] >> l32) & 1u;
+                    const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], a.scale_log2, -l4[c])) : 0.f;
+                    pv[i] = p;
+                    ds[i] = p * (dp[i] - d4[c]);
                 }
             }
+            // dV (keys x d) += P^T (keys x queries) dO; dK += dS^T Q
+            const bf16x8 p0 = pack8(pv, 0), p1 = pack8(pv, 8);
+            const bf16x8 s0 = pack8(ds, 0), s1 = pack8(ds, 8);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const int dim = 32 * db + l32;
+                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p0, tr_op(g_tr[b], dim, 4 * hh), dv[db], 0, 0, 0);
+                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(s0, tr_op(q_tr[b], dim, 4 * hh), dk[db], 0, 0, 0);
+                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p1, tr_op(g_tr[b], dim, 16 + 4 * hh), dv[db], 0, 0, 0);
+                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(s1, tr_op(q_tr[b], dim, 16 + 4 * hh), dk[db], 0, 0, 0);
+            }
         }
+        if (q0n >= 0) put(s + 1, b ^ 1);
+        __syncthreads();
+        q0 = q0n;
     }
     // element (db, i): key row 8(i/4) + 4hh + i%4 of the wave, dim 32 db + l32
     float* dkg = a.dk + (int64_t)bh * a.n_kv * D;
@@ -328,7 +514,7 @@ bwd_dkdv_kernel(BwdParams a)
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int kr = kb * BK + 32 * w + 8 * (i >> 2) + 4 * hh + (i & 3);
+            const int kr = kbase + 8 * (i >> 2) + 4 * hh + (i & 3);
             if (kr < a.n_kv) {
                 dkg[(int64_t)kr * D + 32 * db + l32] = dk[db][i] * a.scale;
                 dvg[(int64_t)kr * D + 32 * db + l32] = dv[db][i];
@@ -340,8 +526,10 @@ template <int D, int BQ, int BK>
 hipError_t launch_bwd_t(const BwdParams& a, hipStream_t stream)
 {
     const int64_t bh = (int64_t)a.batch * a.heads;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, BQ, BK>), dim3((unsigned)(bh * a.nqb)), dim3(BQ * 2), 0, stream, a);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BQ, BK>), dim3((unsigned)(bh * a.nkb)), dim3(BK * 2), 0, stream, a);
+    if (bh * a.nqb > 0)
+        hipLaunchKernelGGL((bwd_dq_kernel<D, BQ, BK>), dim3((unsigned)(bh * a.nqb)), dim3(BQ * 2), 0, stream, a);
+    if (bh * a.nkb > 0)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, BQ, BK>), dim3((unsigned)(bh * a.nkb)), dim3(BK * 2), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -359,17 +547,17 @@ hipError_t launch_bwd_d(const BwdParams& a, int bq, int bk, hipStream_t stream)
 
 hipError_t launch_attn_bwd(const BwdParams& a, int head_dim, int block_q, int block_kv, hipStream_t stream)
 {
-    const int64_t rows = (int64_t)a.batch * a.heads * a.n_q;
-    hipLaunchKernelGGL(bwd_dsum_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, a.dout, a.o, rows,
-                       head_dim, a.dsum);
+    if (head_dim != 128 && head_dim != 64) return hipErrorInvalidValue;
     const int64_t nt = (int64_t)a.n_lists * a.nkb;
-    hipLaunchKernelGGL(bwd_transpose_kernel, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, stream, a.kv_count,
-                       a.kv_index, a.kv_partial, a.n_lists, a.nqb, a.nkb, a.q_count, a.q_index, a.q_partial);
+    if (nt > 0)
+        hipLaunchKernelGGL(bwd_transpose_kernel, dim3((unsigned)((nt + 3) / 4)), dim3(256), 0, stream, a.kv_count,
+                           a.kv_index, a.kv_partial, a.n_lists, a.nqb, a.nkb, a.q_count, a.q_index, a.q_partial);
+    hipLaunchKernelGGL(bwd_order_kernel, dim3(2), dim3(1024), 0, stream, a.kv_count, a.n_lists * a.nqb, a.nkb,
+                       a.order_q, a.q_count, a.n_lists * a.nkb, a.nqb, a.order_k);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (head_dim == 128) return launch_bwd_d<128>(a, block_q, block_kv, stream);
-    if (head_dim == 64) return launch_bwd_d<64>(a, block_q, block_kv, stream);
-    return hipErrorInvalidValue;
+    return launch_bwd_d<64>(a, block_q, block_kv, stream);
 }
 
 }  // namespace sa

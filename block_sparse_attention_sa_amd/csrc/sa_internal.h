@@ -333,9 +333,11 @@ struct BwdParams {
     int32_t* q_count;   // [n_lists][nkb]
     int32_t* q_index;   // [n_lists][nkb][nqb]
     uint8_t* q_partial; // [n_lists][nkb][nqb]
+    int32_t* order_q;   // [n_lists*nqb] list rows, longest first
+    int32_t* order_k;   // [n_lists*nkb] transposed rows, longest first
 };
 struct BwdLayout {
-    int64_t dsum, q_count, q_index, q_partial, total;
+    int64_t dsum, q_count, q_index, q_partial, order_q, order_k, total;
 };
 inline BwdLayout bwd_layout(int64_t rows, int64_t n_lists, int64_t nqb, int64_t nkb)
 {
@@ -345,7 +347,9 @@ inline BwdLayout bwd_layout(int64_t rows, int64_t n_lists, int64_t nqb, int64_t 
     L.q_count = up(rows * 4);
     L.q_index = up(L.q_count + n_lists * nkb * 4);
     L.q_partial = up(L.q_index + n_lists * nkb * nqb * 4);
-    L.total = up(L.q_partial + n_lists * nkb * nqb);
+    L.order_q = up(L.q_partial + n_lists * nkb * nqb);
+    L.order_k = up(L.order_q + n_lists * nqb * 4);
+    L.total = up(L.order_k + n_lists * nkb * 4);
     return L;
 }
 hipError_t launch_attn_bwd(const BwdParams& a, int head_dim, int block_q, int block_kv, hipStream_t stream);

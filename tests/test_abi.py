@@ -362,8 +362,10 @@ def test_attn_bwd_workspace_and_errors():
 
     up = lambda x: (x + 255) // 256 * 256
     nqb = nkb = 5
-    exp = up(up(up(2 * 300 * 4) + nkb * 4) + nkb * nqb * 4) + nkb * nqb
-    assert L.sa_attn_bwd_workspace(ctypes.byref(bwd())) == up(exp)
+    q_partial = up(up(up(2 * 300 * 4) + nkb * 4) + nkb * nqb * 4)
+    order_q = up(q_partial + nkb * nqb)
+    order_k = up(order_q + nqb * 4)
+    assert L.sa_attn_bwd_workspace(ctypes.byref(bwd())) == up(order_k + nkb * 4)
     for kw, status, word in ((dict(head_dim=96), _lib.SA_ERR_UNSUPPORTED, "head_dim"),
                              (dict(block_kv=32), _lib.SA_ERR_UNSUPPORTED, "block"),
                              (dict(per_head_lists=3), _lib.SA_ERR_INVALID_ARG, "per_head_lists"),
