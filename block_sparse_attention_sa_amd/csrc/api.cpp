@@ -438,6 +438,7 @@ sa_status sa_attn_fwd(const sa_attn_args* a, void* stream)
         p.lse_sh = a->n_q;
         p.lse_sn = 1;
         p.merge = 0;
+        p.last_first = 1;
         p.batch = (int32_t)a->batch;
         p.heads = (int32_t)a->heads;
         p.n_q = (int32_t)a->n_q;
@@ -465,6 +466,7 @@ sa_status sa_attn_fwd(const sa_attn_args* a, void* stream)
             if (a->per_head_lists != 0 && a->per_head_lists != 1)
                 return fail(SA_ERR_INVALID_ARG, "per_head_lists must be 0 or 1");
             p.per_head_lists = (int32_t)a->per_head_lists;
+            p.last_first = a->pattern.causal != 0;
             // key tiles are fetched with 32-bit byte offsets from the (batch, head) base
             const int64_t row_b = 2 * std::max(a->k_strides[2], a->v_strides[2]);
             if ((a->n_kv + 256) * row_b > kI32Max)

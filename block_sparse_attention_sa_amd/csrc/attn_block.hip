@@ -117,8 +117,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 // TAIL: n_kv is not a multiple of the 64-key sub-tile, so one sub-tile per
 // query block may reach past the last key (launched only then: the extra
 // copy path costs registers).
+// two waves per SIMD: with 64-row blocks at head_dim 64 four workgroups fit
+// in LDS, otherwise two
+template <int D, int BQ, int NB>
+constexpr int attn_min_blocks()
+{
+    return NB != 1 ? 1 : ((BQ == 64 && D == 64) ? 4 : 2);
+}
+
 template <int D, int BQ, int BK, bool OF32, int NB, bool TAIL>
-__global__ void __launch_bounds__(BQ * 2 / NB, NB == 1 ? 2 : 1)
+__global__ void __launch_bounds__(BQ * 2 / NB, (attn_min_blocks<D, BQ, NB>()))
 attn_block_kernel(AttnParams a)
 {
     constexpr int NW = BQ / (32 * NB);            // waves, 32*NB query rows each
@@ -149,11 +157,12 @@ attn_block_kernel(AttnParams a)
     const int hh = lane >> 5;  // half-wave
     const int l32 = lane & 31;
 
-    // query blocks of a head run from the last to the first: causal rows
-    // near the start see the fewest key tiles, so the short workgroups come
-    // last and fill the gaps at the end of the launch
+    // Longer lists first, so the short workgroups fill the gaps at the end of
+    // the launch: under causality rows near the start see the fewest key
+    // tiles (query blocks run from the last to the first); without it the
+    // long rows are the global-token rows at the start (first to last).
     const int item = xcd_remap(blockIdx.x, gridDim.x);
-    const int qb = a.nqb - 1 - item % a.nqb;
+    const int qb = a.last_first ? a.nqb - 1 - item % a.nqb : item % a.nqb;
     const int bh = item / a.nqb;
     const int b = bh / a.heads, h = bh % a.heads;
 

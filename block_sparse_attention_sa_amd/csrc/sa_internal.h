@@ -182,6 +182,7 @@ struct AttnParams {
     const int32_t* kv_index;
     const uint8_t* kv_partial;
     int32_t per_head_lists;  // lists of (b, h) at (b*heads + h) * nqb [* nkb]
+    int32_t last_first;      // dispatch a head's query blocks from the last one
     DevPattern pat;
     // gather mode
     const int32_t* gidx;
