@@ -81,6 +81,8 @@ def main() -> int:
     ap.add_argument("--no-select", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-other", action="store_true", help="skip the tiny and BigBird-style block workloads")
+    ap.add_argument("--only", choices=["dsa", "strided", "select", "bwd", "window128", "bigbird"],
+                    help="time one secondary workload alone (for per-kernel profiles; prints only its object)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="the CPU oracle repeats whole passes over the workload until this much time has passed")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -130,6 +132,18 @@ def main() -> int:
     live_pairs = live_pairs_per_head * cfg.B * cfg.H
     flops = 4.0 * cfg.d * live_pairs
     tile_flops = 4.0 * cfg.d * cfg.block * cfg.block * live_blocks * cfg.B * cfg.H
+
+    if args.only:
+        sections = {
+            "dsa": lambda: _bench_dsa(sa, W, np, torch, dev, dev_bf16),
+            "strided": lambda: _bench_strided(sa, W, np, torch, dev, dev_bf16),
+            "select": lambda: _bench_select(sa, W, np, torch, dev, dev_bf16),
+            "bwd": lambda: _bench_bwd(sa, np, torch, dev, cfg, q, k, v, bl, out, lse, live_pairs, live_blocks),
+            "window128": lambda: _bench_blocks(sa, W, np, torch, dev, dev_bf16, 1),
+            "bigbird": lambda: _bench_blocks(sa, W, np, torch, dev, dev_bf16, 4),
+        }
+        print(json.dumps({args.only: sections[args.only]()}), flush=True)
+        return 0
 
     if args.copy_calib_mib > 0:
         n = args.copy_calib_mib * (1 << 20) // 4
@@ -306,7 +320,8 @@ def _bench_strided(sa, W, np, torch, dev, dev_bf16, reps=10):
 def _bench_bwd(sa, np, torch, dev, cfg, q, k, v, bl, out, lse, live_pairs, live_blocks, reps=20):
     """The backward at the headline workload: dQ, dK, dV from the forward's O and LSE.
     Algorithmic work: 5 products per live pair (S, dP, dV, dQ, dK), 10 * d flop."""
-    g = torch.randn(q.shape, device=dev).to(torch.bfloat16)
+    gen = torch.Generator(device=dev).manual_seed(20261203)
+    g = torch.randn(q.shape, device=dev, generator=gen).to(torch.bfloat16)
     sa.attn_fwd(q, k, v, bl, out=out, lse=lse)
     dq, dk, dv = sa.attn_bwd(q, k, v, out, lse, g, bl)
     torch.cuda.synchronize()

@@ -400,11 +400,20 @@ bwd_dkdv_kernel(BwdParams a)
         kop[s] = __builtin_bit_cast(bf16x8, x);
         vop[s] = __builtin_bit_cast(bf16x8, y);
     }
+    // zero accumulators made by a matrix instruction (0 * 0 + 0), so that they
+    // are born in the registers the loop's matrix instructions accumulate in
     f32x16 dk[NDB], dv[NDB];
+    {
+        const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        f32x16 zacc;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+        for (int i = 0; i < 16; ++i) zacc[i] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
+        for (int db = 0; db < NDB; ++db) {
+            dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, zacc, 0, 0, 0);
+            dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, zacc, 0, 0, 0);
+        }
+    }
 
     const int cnt = max(0, min(a.q_count[lrow], a.nqb));
     const int nsteps = cnt * SUB;
@@ -414,98 +423,132 @@ bwd_dkdv_kernel(BwdParams a)
     const uint16_t* gg = a.dout + (int64_t)bh * a.n_q * D;
     const float* lseg = a.lse + (int64_t)bh * a.n_q;
     const float* dsg = a.dsum + (int64_t)bh * a.n_q;
-    // first query of step s (-1: none); whether its pairs need the pattern
-    auto step_q0 = [&](int s) -> int {
-        const int q0 = idx[s / SUB] * BQ + 32 * (s % SUB);
-        return q0 < a.n_q ? q0 : -1;
+    // first query of step s; a step past the last query (the ragged end of the
+    // last block) stages zero rows with LSE = +inf, so it adds nothing
+    auto step_q0 = [&](int s) -> int { return idx[s / SUB] * BQ + 32 * (s % SUB); };
+    // Staged data of one step (rows, LSE, D, mask words), loaded into
+    // registers two steps ahead of its use and written to LDS one step ahead.
+    struct Fetched {
+        QStage q, g;
+        float lse, dsum;
+        uint32_t mword;
     };
-    QStage qst, gst;
-    float lse_r = INFINITY, dsum_r = 0.f;
-    uint32_t mword = 0;
-    // issue the reads of step s's staged data (rows, LSE, D, mask words)
-    auto fetch = [&](int s, int q0) {
-        qst.load(qg, q0, a.n_q, tid);
-        gst.load(gg, q0, a.n_q, tid);
+    auto fetch = [&](Fetched& f, int s) {
+        const int q0 = step_q0(s);
+        f.q.load(qg, q0, a.n_q, tid);
+        f.g.load(gg, q0, a.n_q, tid);
+        f.lse = INFINITY;
+        f.dsum = 0.f;
         if (tid < 32) {
             const int qr = q0 + tid;
             const float l = qr < a.n_q ? lseg[qr] : INFINITY;
-            lse_r = l == -INFINITY ? INFINITY : l * kLog2e;
-            dsum_r = qr < a.n_q ? dsg[qr] : 0.f;
+            f.lse = l == -INFINITY ? INFINITY : l * kLog2e;
+            f.dsum = qr < a.n_q ? dsg[qr] : 0.f;
         }
+        f.mword = 0u;
         if (prt[s / SUB] != 0) {
             // bit l of word r: key kbase + l is allowed for query q0 + r
             const int qr = q0 + l32;
             RowCtx rc;
             row_ctx(a.pat, qr + a.pat.q_offset, rc);
-            mword = qr < a.n_q ? allowed_bits32(a.pat, rc, kbase) : 0u;
+            f.mword = qr < a.n_q ? allowed_bits32(a.pat, rc, kbase) : 0u;
         }
     };
-    auto put = [&](int s, int buf) {
-        qst.store(q_rm[buf], q_tr[buf], tid);
-        gst.store(g_rm[buf], g_tr[buf], tid);
+    auto put = [&](const Fetched& f, int s, int buf) {
+        f.q.store(q_rm[buf], q_tr[buf], tid);
+        f.g.store(g_rm[buf], g_tr[buf], tid);
         if (tid < 32) {
-            lse_s[buf][tid] = lse_r;
-            dsum_s[buf][tid] = dsum_r;
+            lse_s[buf][tid] = f.lse;
+            dsum_s[buf][tid] = f.dsum;
         }
-        if (prt[s / SUB] != 0 && hh == 0) mw_s[buf][w][l32] = mword;
+        if (prt[s / SUB] != 0 && hh == 0) mw_s[buf][w][l32] = f.mword;
     };
-    int q0 = -1;
+    // one step on the data in LDS buffer b.  Every step runs the same
+    // straight-line body (no step is skipped), so the dK and dV accumulators
+    // stay in the matrix unit's registers across the loop.
+    auto compute = [&](int s, int b) {
+        // S = Q K^T and dP = dO V^T: lane = key, element i = query 8(i/4) + 4hh + i%4
+        f32x16 sv, dp;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sv[i] = dp[i] = 0.f;
+        const uint16_t* qr = q_rm[b] + l32 * RS + 8 * hh;
+        const uint16_t* gr = g_rm[b] + l32 * RS + 8 * hh;
+        // LDS operands are requested two k-steps ahead (a ring of three)
+        bf16x8 qa[3], ga[3];
+        auto ld_a = [&](int slot, int c) {
+            qa[slot] = lds8(qr + 16 * c);
+            ga[slot] = lds8(gr + 16 * c);
+        };
+        ld_a(0, 0);
+        ld_a(1, 1);
+#pragma unroll
+        for (int c = 0; c < NDC; ++c) {
+            if (c + 2 < NDC) ld_a((c + 2) % 3, c + 2);
+            sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[c % 3], kop[c], sv, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[c % 3], vop[c], dp, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // the first B operands of dV / dK land while the softmax runs;
+        // step it = ks * NDB + db reads rows 16ks + 4hh.. of dim 32db + l32
+        bf16x8 gb[3], qb2[3];
+        auto ld_b = [&](int slot, int it) {
+            const int ks = it / NDB, dim = 32 * (it % NDB) + l32;
+            gb[slot] = tr_op(g_tr[b], dim, 16 * ks + 4 * hh);
+            qb2[slot] = tr_op(q_tr[b], dim, 16 * ks + 4 * hh);
+        };
+        ld_b(0, 0);
+        ld_b(1, 1);
+        const bool masked = prt[s / SUB] != 0;
+        f32x16 pv, ds;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[b][8 * m + 4 * hh]);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dsum_s[b][8 * m + 4 * hh]);
+            u32x4 w4 = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+            if (masked) w4 = *reinterpret_cast<const u32x4*>(&mw_s[b][w][8 * m + 4 * hh]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int i = 4 * m + c;
+                const bool ok = (w4[c] >> l32) & 1u;
+                const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], a.scale_log2, -l4[c])) : 0.f;
+                pv[i] = p;
+                ds[i] = p * (dp[i] - d4[c]);
+            }
+        }
+        // dV (keys x d) += P^T (keys x queries) dO; dK += dS^T Q
+        const bf16x8 pa[2] = {pack8(pv, 0), pack8(pv, 8)};
+        const bf16x8 sa[2] = {pack8(ds, 0), pack8(ds, 8)};
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int it = 0; it < 2 * NDB; ++it) {
+            if (it + 2 < 2 * NDB) ld_b((it + 2) % 3, it + 2);
+            const int ks = it / NDB, db = it % NDB;
+            dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], gb[it % 3], dv[db], 0, 0, 0);
+            dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[ks], qb2[it % 3], dk[db], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // Two register sets alternate, so the loop is unrolled by two and names
+    // them statically: at step s, set s%2 (whose data went to LDS last step)
+    // takes the loads of step s+2 and set (s+1)%2 goes to LDS buffer (s+1)%2.
+    Fetched f0, f1;
     if (nsteps > 0) {
-        q0 = step_q0(0);
-        if (q0 >= 0) {
-            fetch(0, q0);
-            put(0, 0);
-        }
+        fetch(f0, 0);
+        put(f0, 0, 0);
     }
+    if (nsteps > 1) fetch(f1, 1);
     __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
-        const int b = s & 1;
-        const int q0n = s + 1 < nsteps ? step_q0(s + 1) : -1;
-        if (q0n >= 0) fetch(s + 1, q0n);
-        if (q0 >= 0) {
-            // S = Q K^T and dP = dO V^T: lane = key, element i = query 8(i/4) + 4hh + i%4
-            f32x16 sv, dp;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sv[i] = dp[i] = 0.f;
-            const uint16_t* qr = q_rm[b] + l32 * RS + 8 * hh;
-            const uint16_t* gr = g_rm[b] + l32 * RS + 8 * hh;
-#pragma unroll
-            for (int c = 0; c < NDC; ++c) {
-                sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds8(qr + 16 * c), kop[c], sv, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds8(gr + 16 * c), vop[c], dp, 0, 0, 0);
-            }
-            const bool masked = prt[s / SUB] != 0;
-            f32x16 pv, ds;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[b][8 * m + 4 * hh]);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dsum_s[b][8 * m + 4 * hh]);
-                u32x4 w4 = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
-                if (masked) w4 = *reinterpret_cast<const u32x4*>(&mw_s[b][w][8 * m + 4 * hh]);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int i = 4 * m + c;
-                    const bool ok = (w4[c] >> l32) & 1u;
-                    const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], a.scale_log2, -l4[c])) : 0.f;
-                    pv[i] = p;
-                    ds[i] = p * (dp[i] - d4[c]);
-                }
-            }
-            // dV (keys x d) += P^T (keys x queries) dO; dK += dS^T Q
-            const bf16x8 p0 = pack8(pv, 0), p1 = pack8(pv, 8);
-            const bf16x8 s0 = pack8(ds, 0), s1 = pack8(ds, 8);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const int dim = 32 * db + l32;
-                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p0, tr_op(g_tr[b], dim, 4 * hh), dv[db], 0, 0, 0);
-                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(s0, tr_op(q_tr[b], dim, 4 * hh), dk[db], 0, 0, 0);
-                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p1, tr_op(g_tr[b], dim, 16 + 4 * hh), dv[db], 0, 0, 0);
-                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(s1, tr_op(q_tr[b], dim, 16 + 4 * hh), dk[db], 0, 0, 0);
-            }
-        }
-        if (q0n >= 0) put(s + 1, b ^ 1);
+    for (int s0 = 0; s0 < nsteps; s0 += 2) {
+        if (s0 + 2 < nsteps) fetch(f0, s0 + 2);
+        compute(s0, 0);
+        if (s0 + 1 < nsteps) put(f1, s0 + 1, 1);
         __syncthreads();
-        q0 = q0n;
+        if (s0 + 1 < nsteps) {
+            if (s0 + 3 < nsteps) fetch(f1, s0 + 3);
+            compute(s0 + 1, 1);
+            if (s0 + 2 < nsteps) put(f0, s0 + 2, 0);
+            __syncthreads();
+        }
     }
     // element (db, i): key row 8(i/4) + 4hh + i%4 of the wave, dim 32 db + l32
     float* dkg = a.dk + (int64_t)bh * a.n_kv * D;
