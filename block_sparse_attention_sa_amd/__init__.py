@@ -172,9 +172,10 @@ def attn_fwd(q, k, v, blocks: Optional[BlockLists] = None, gather_idx=None, *,
 
     q [B, H, n_q, d], k/v [B, H, n_kv, d] bfloat16 on the GPU.  ``gather_idx``
     is int32 [n_q, topk] shared by every (b, h), or [B, H, n_q, topk].
-    In gather mode over a long key range the library can take a split form
-    that needs scratch (``attn_workspace_bytes``): pass a uint8 CUDA tensor
-    as ``workspace``, or leave it None and one is allocated for the call;
+    In gather mode over a long key range, and in block mode for the rows of
+    global tokens that see every key, the library can take a split form that
+    needs scratch (``attn_workspace_bytes``): pass a uint8 CUDA tensor as
+    ``workspace``, or leave it None and one is allocated for the call;
     ``split=False`` forces the single-pass form.
     Returns (O [B, H, n_q, d] in ``o_dtype`` (default float32), LSE float32
     [B, H, n_q] or None).
@@ -240,14 +241,14 @@ def attn_fwd(q, k, v, blocks: Optional[BlockLists] = None, gather_idx=None, *,
         else:
             raise ValueError("gather_idx must be [n_q, topk] or [B, H, n_q, topk]")
         keep.append(g)
-        need = int(_lib.lib().sa_attn_workspace_bytes(ctypes.byref(a))) if split else 0
-        if need > 0:
-            if workspace is None:
-                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-            if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
-                raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
-            a.workspace = workspace.data_ptr()
-            a.workspace_bytes = workspace.numel()
+    need = int(_lib.lib().sa_attn_workspace_bytes(ctypes.byref(a))) if split else 0
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel()
     _lib.check(_lib.lib().sa_attn_fwd(ctypes.byref(a), _stream_ptr(q.device)))
     return out, lse
 
@@ -403,6 +404,20 @@ def attn_workspace_bytes_strided(pattern, batch: int, heads: int, n: int, head_d
     a.batch, a.heads, a.n_q, a.n_kv, a.head_dim = batch, heads, n, n, head_dim
     a.mode = _lib.SA_MODE_STRIDED
     a.pattern = _template_struct(pattern)
+    return int(_lib.lib().sa_attn_workspace_bytes(ctypes.byref(a)))
+
+
+def attn_workspace_bytes_blocks(blocks: BlockLists, batch: int, heads: int, head_dim: int) -> int:
+    """Scratch bytes of block mode's long-row split for these lists (0 if it has none):
+    without causality the query blocks of global tokens list every key block, and with
+    more than 16 key blocks they are walked in chunks by separate workgroups.  Touches
+    no device."""
+    a = _lib.SaAttnArgs()
+    a.batch, a.heads, a.n_q, a.n_kv, a.head_dim = batch, heads, blocks.n_q, blocks.n_kv, head_dim
+    a.mode = _lib.SA_MODE_BLOCKS
+    a.block_q, a.block_kv = blocks.block_q, blocks.block_kv
+    a.pattern = blocks.pattern.struct
+    a.per_head_lists = 1 if blocks.per_head else 0
     return int(_lib.lib().sa_attn_workspace_bytes(ctypes.byref(a)))
 
 

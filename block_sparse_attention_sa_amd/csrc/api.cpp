@@ -376,8 +376,35 @@ sa_status sa_build_block_mask(const sa_pattern* pattern, int64_t n_q, int64_t n_
     }
 }
 
+// Block mode's long-row split of the pattern's global-token query blocks
+// (shared lists only) and the bytes of its partial results: normalised O
+// rows, then one LSE per row.
+static int32_t long_row_split_of(const sa_attn_args* a, int64_t nqb, int64_t nkb, int32_t& chunks, int32_t& per_chunk)
+{
+    chunks = per_chunk = 0;
+    if (a->per_head_lists != 0) return 0;
+    return sa::long_row_split(a->pattern.causal, a->pattern.global_tokens, a->pattern.q_offset, a->n_q, nqb, nkb,
+                              a->block_q, chunks, per_chunk);
+}
+
+static int64_t split_bytes(const sa_attn_args* a, int32_t gq, int32_t chunks)
+{
+    const int64_t slots = a->batch * a->heads * gq * chunks * a->block_q;
+    return ((slots * a->head_dim * 4 + 255) & ~int64_t(255)) + ((slots * 4 + 255) & ~int64_t(255));
+}
+
 size_t sa_attn_workspace_bytes(const sa_attn_args* a)
 {
+    if (a && a->mode == SA_MODE_BLOCKS) {
+        if (a->batch <= 0 || a->heads <= 0 || a->n_q <= 0 || a->n_kv <= 0 || a->per_head_lists != 0 ||
+            (a->head_dim != 64 && a->head_dim != 128) || (a->block_q != 64 && a->block_q != 128) ||
+            (a->block_kv != 64 && a->block_kv != 128) || a->n_q > kI32Max || a->n_kv > kI32Max)
+            return 0;
+        const int64_t nqb = (a->n_q + a->block_q - 1) / a->block_q, nkb = (a->n_kv + a->block_kv - 1) / a->block_kv;
+        int32_t chunks = 0, per_chunk = 0;
+        const int32_t gq = long_row_split_of(a, nqb, nkb, chunks, per_chunk);
+        return gq > 0 ? (size_t)split_bytes(a, gq, chunks) : 0;
+    }
     if (a && a->mode == SA_MODE_STRIDED) {
         const int64_t S = strided_template(a);
         return S > 0 && a->n_q <= kI32Max ? (size_t)strided_layout(a->n_q, S).total : 0;
@@ -471,9 +498,29 @@ sa_status sa_attn_fwd(const sa_attn_args* a, void* stream)
             const int64_t row_b = 2 * std::max(a->k_strides[2], a->v_strides[2]);
             if ((a->n_kv + 256) * row_b > kI32Max)
                 return fail(SA_ERR_UNSUPPORTED, "n_kv times the K/V row stride must stay below 2^31 bytes");
-            return launched(sa::launch_attn_blocks(p, (int)a->head_dim, (int)a->block_q,
-                                                   (int)a->block_kv, o_f32, s),
-                            "sa_attn_fwd");
+            // long-row split (optional: with workspace == NULL the rows run whole)
+            int32_t chunks = 0, per_chunk = 0;
+            const int32_t gq = long_row_split_of(a, p.nqb, p.nkb, chunks, per_chunk);
+            if (gq > 0 && a->workspace) {
+                const int64_t need = split_bytes(a, gq, chunks);
+                if (a->workspace_bytes < need)
+                    return fail(SA_ERR_INVALID_ARG, "workspace smaller than sa_attn_workspace_bytes (%lld bytes)",
+                                (long long)need);
+                if (((uintptr_t)a->workspace & 255u) != 0)
+                    return fail(SA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+                if (a->batch * a->heads * (p.nqb - gq + (int64_t)gq * chunks) > kI32Max)
+                    return fail(SA_ERR_UNSUPPORTED, "too many work items");
+                const int64_t slots = a->batch * a->heads * gq * chunks * a->block_q;
+                p.split_q = gq;
+                p.split_c = chunks;
+                p.split_e = per_chunk;
+                p.part_o = (float*)a->workspace;
+                p.part_lse = (float*)((uint8_t*)a->workspace + ((slots * a->head_dim * 4 + 255) & ~int64_t(255)));
+            }
+            st = launched(sa::launch_attn_blocks(p, (int)a->head_dim, (int)a->block_q, (int)a->block_kv, o_f32, s),
+                          "sa_attn_fwd");
+            if (st != SA_OK || p.split_q == 0) return st;
+            return launched(sa::launch_split_merge(p, (int)a->head_dim, (int)a->block_q, o_f32, s), "sa_attn_fwd");
         }
         if (!a->gather_idx) return fail(SA_ERR_INVALID_ARG, "gather_idx is NULL");
         {

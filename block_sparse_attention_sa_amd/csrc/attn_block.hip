@@ -161,9 +161,21 @@ attn_block_kernel(AttnParams a)
     // the launch: under causality rows near the start see the fewest key
     // tiles (query blocks run from the last to the first); without it the
     // long rows are the global-token rows at the start (first to last).
+    // With the long-row split, the first split_q query blocks of every head
+    // are split_c work items each (list chunks), dispatched before the rest.
     const int item = xcd_remap(blockIdx.x, gridDim.x);
-    const int qb = a.last_first ? a.nqb - 1 - item % a.nqb : item % a.nqb;
-    const int bh = item / a.nqb;
+    const int n_split = (a.batch * a.heads) * a.split_q * a.split_c;
+    int qb, bh, chunk = -1;
+    if (item < n_split) {
+        chunk = item % a.split_c;
+        const int t = item / a.split_c;
+        qb = t % a.split_q;
+        bh = t / a.split_q;
+    } else {
+        const int j = item - n_split, nrest = a.nqb - a.split_q;
+        qb = a.split_q + (a.last_first ? nrest - 1 - j % nrest : j % nrest);
+        bh = j / nrest;
+    }
     const int b = bh / a.heads, h = bh % a.heads;
 
     const uint16_t* qg = a.q + b * a.q_sb + h * a.q_sh;
@@ -173,9 +185,12 @@ attn_block_kernel(AttnParams a)
     const uint32_t vrow_b = (uint32_t)(a.v_sn * 2);
 
     const int64_t lrow = (a.per_head_lists ? (int64_t)bh * a.nqb : 0) + qb;  // list row of this work item
-    const int32_t* idx_row = a.kv_index + lrow * a.nkb;
-    const uint8_t* part_row = a.kv_partial + lrow * a.nkb;
-    const int cnt = min(a.kv_count[lrow], a.nkb);
+    // a split item walks list entries [chunk*split_e, chunk*split_e + split_e)
+    const int e_first = chunk >= 0 ? chunk * a.split_e : 0;
+    const int32_t* idx_row = a.kv_index + lrow * a.nkb + e_first;
+    const uint8_t* part_row = a.kv_partial + lrow * a.nkb + e_first;
+    int cnt = min(a.kv_count[lrow], a.nkb);
+    if (chunk >= 0) cnt = max(0, min(cnt - e_first, a.split_e));
     const int n_sub = cnt * SUB;
     // The live list is held in registers, 64 entries at a time (lane j holds
     // entry base + j) and read with readlane, so the loop issues no memory
@@ -523,6 +538,28 @@ attn_block_kernel(AttnParams a)
     }
 
     // ---- epilogue
+    if (chunk >= 0) {
+        // a list chunk of a split row: normalised partial O and its LSE
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const float l_tot = l_run[nb] + other_half(l_run[nb]);
+            const int r = qrow[nb] - qb * BQ;  // row within the block
+            const int64_t slot = (((int64_t)bh * a.split_q + qb) * a.split_c + chunk) * BQ + r;
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            float* op = a.part_o + slot * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int dv = 32 * db + 8 * r4 + 4 * hh;
+                    *reinterpret_cast<float4*>(op + dv) =
+                        make_float4(o[nb][db][4 * r4 + 0] * inv, o[nb][db][4 * r4 + 1] * inv,
+                                    o[nb][db][4 * r4 + 2] * inv, o[nb][db][4 * r4 + 3] * inv);
+                }
+            if (hh == 0) a.part_lse[slot] = l_tot > 0.f ? m_run[nb] * a.scale + logf(l_tot) : -INFINITY;
+        }
+        return;
+    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const float l_tot = l_run[nb] + other_half(l_run[nb]);
@@ -587,7 +624,7 @@ hipError_t launch_one(const AttnParams& a, hipStream_t stream)
     // one 32-query column block per wave at both head dims (two per wave ran
     // 15-36 % slower at head_dim 64)
     constexpr int NB = 1;
-    const int64_t items = (int64_t)a.batch * a.heads * a.nqb;
+    const int64_t items = (int64_t)a.batch * a.heads * (a.nqb - a.split_q + (int64_t)a.split_q * a.split_c);
     if (a.n_kv % 64)
         hipLaunchKernelGGL((attn_block_kernel<D, BQ, BK, OF32, NB, true>), dim3((unsigned)items), dim3(BQ * 2 / NB), 0,
                            stream, a);
@@ -613,7 +650,80 @@ hipError_t launch_d(const AttnParams& a, int bq, int bk, int o_f32, hipStream_t 
     return hipErrorInvalidValue;
 }
 
+// Long-row split, second pass: one wave per split row folds its chunks'
+// partial (O, LSE) into the row's O and LSE with log-sum-exp weights,
+// O = sum_c e^(l_c - L) O_c, L = log sum_c e^(l_c); chunks without keys
+// (l_c = -inf) weigh nothing, a row without any key gets O = 0, L = -inf.
+template <int D, bool OF32>
+__global__ void __launch_bounds__(256) split_merge_kernel(AttnParams a, int32_t bq)
+{
+    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int64_t rows = (int64_t)a.batch * a.heads * a.split_q * bq;
+    if (w >= rows) return;
+    const int r = (int)(w % bq);
+    const int64_t t = w / bq;
+    const int qb = (int)(t % a.split_q), bh = (int)(t / a.split_q);
+    const int q = qb * bq + r;
+    if (q >= a.n_q) return;
+    const int b = bh / a.heads, h = bh % a.heads;
+    const int64_t slot0 = ((int64_t)bh * a.split_q + qb) * a.split_c * bq + r;  // chunk c at slot0 + c*bq
+    // chunk weights, 64 chunks at a time: lane c holds chunk c0 + c
+    constexpr int PER = D / 64;
+    float acc[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+    float m = -INFINITY;
+    for (int c0 = 0; c0 < a.split_c; c0 += 64)
+        if (c0 + lane < a.split_c) m = fmaxf(m, a.part_lse[slot0 + (int64_t)(c0 + lane) * bq]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    float s = 0.f;
+    if (m != -INFINITY) {
+        for (int c0 = 0; c0 < a.split_c; c0 += 64) {
+            const int nc = min(64, a.split_c - c0);
+            const float wl = lane < nc ? __expf(a.part_lse[slot0 + (int64_t)(c0 + lane) * bq] - m) : 0.f;
+            float ws = wl;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) ws += __shfl_xor(ws, off);
+            s += ws;
+            const float* po = a.part_o + (slot0 + (int64_t)c0 * bq) * D + lane;
+#pragma unroll 8
+            for (int c = 0; c < nc; ++c) {
+                const float wc = __shfl(wl, c);  // 0 for a chunk without keys
+#pragma unroll
+                for (int i = 0; i < PER; ++i) acc[i] += wc * po[(int64_t)c * bq * D + 64 * i];
+            }
+        }
+    }
+    const float inv = s > 0.f ? 1.f / s : 0.f;
+    const int64_t obase = b * a.o_sb + h * a.o_sh + (int64_t)q * a.o_sn;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const float x = acc[i] * inv;
+        if (OF32) reinterpret_cast<float*>(a.o)[obase + lane + 64 * i] = x;
+        else reinterpret_cast<uint16_t*>(a.o)[obase + lane + 64 * i] = __builtin_bit_cast(uint16_t, (__bf16)x);
+    }
+    if (a.lse && lane == 0)
+        a.lse[b * a.lse_sb + h * a.lse_sh + (int64_t)q * a.lse_sn] = s > 0.f ? m + logf(s) : -INFINITY;
+}
+
 }  // namespace
+
+hipError_t launch_split_merge(const AttnParams& a, int head_dim, int block_q, int o_f32, hipStream_t stream)
+{
+    const int64_t rows = (int64_t)a.batch * a.heads * a.split_q * block_q;
+    if (rows <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    if (head_dim == 128) {
+        if (o_f32) hipLaunchKernelGGL((split_merge_kernel<128, true>), grid, dim3(256), 0, stream, a, block_q);
+        else hipLaunchKernelGGL((split_merge_kernel<128, false>), grid, dim3(256), 0, stream, a, block_q);
+    } else {
+        if (o_f32) hipLaunchKernelGGL((split_merge_kernel<64, true>), grid, dim3(256), 0, stream, a, block_q);
+        else hipLaunchKernelGGL((split_merge_kernel<64, false>), grid, dim3(256), 0, stream, a, block_q);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_attn_blocks(const AttnParams& a, int head_dim, int block_q, int block_kv,
                               int o_f32, hipStream_t stream)

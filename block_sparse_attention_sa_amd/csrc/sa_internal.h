@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace sa {
 
 // Exact unsigned division by an invariant divisor s >= 1 for 0 <= n < 2^31:
@@ -183,6 +185,14 @@ struct AttnParams {
     const uint8_t* kv_partial;
     int32_t per_head_lists;  // lists of (b, h) at (b*heads + h) * nqb [* nkb]
     int32_t last_first;      // dispatch a head's query blocks from the last one
+    // long-row split (block mode, shared lists): query blocks [0, split_q) are
+    // walked as split_c chunks of split_e list entries each by separate
+    // workgroups, which write normalised partial O and LSE to part_o /
+    // part_lse ([batch*heads][split_q][split_c][block_q] rows); a merge
+    // launch folds them into O and LSE.  split_q = 0: no split.
+    int32_t split_q, split_c, split_e;
+    float* part_o;
+    float* part_lse;
     DevPattern pat;
     // gather mode
     const int32_t* gidx;
@@ -197,6 +207,26 @@ struct AttnParams {
     float* g_po;        // [batch*heads*n_q][g_nchunk][head_dim]
     float* g_pml;       // [batch*heads*n_q][g_nchunk][2]: max (log2 units), sum
 };
+
+// Long-row split of block mode: the query blocks every key is visible from.
+// Without causality a query row below global_tokens attends to every key, so
+// the blocks holding such rows list every key block; with more than
+// kSplitEntries key blocks they are split.  Returns split_q (0: none) and
+// the chunk count and size.
+constexpr int32_t kSplitEntries = 16;
+inline int32_t long_row_split(int64_t causal, int64_t global_tokens, int64_t q_offset, int64_t n_q, int64_t nqb,
+                              int64_t nkb, int64_t block_q, int32_t& chunks, int32_t& per_chunk)
+{
+    chunks = per_chunk = 0;
+    if (causal || global_tokens <= 0 || nkb <= kSplitEntries || nqb <= 0) return 0;
+    const int64_t rows = std::min(global_tokens - q_offset, n_q);
+    if (rows <= 0) return 0;
+    const int64_t gq = std::min((rows + block_q - 1) / block_q, nqb);
+    per_chunk = kSplitEntries;
+    chunks = (int32_t)((nkb + kSplitEntries - 1) / kSplitEntries);
+    return (int32_t)gq;
+}
+hipError_t launch_split_merge(const AttnParams& a, int head_dim, int block_q, int o_f32, hipStream_t stream);
 
 hipError_t launch_attn_blocks(const AttnParams& a, int head_dim, int block_q, int block_kv,
                               int o_f32, hipStream_t stream);

@@ -255,8 +255,19 @@ sa_status sa_select_blocks(const sa_select_args *args, void *stream);
 /*
  * sa_attn_workspace_bytes -- bytes of device scratch that sa_attn_fwd needs
  * (SA_MODE_STRIDED: the block lists of its parts; 0 if the pattern is not
- * the strided template) or that let it take its split form (gather mode),
- * 0 when it has none.
+ * the strided template) or that let it take its split form (gather mode;
+ * block mode with a long-row split), 0 when it has none.
+ *
+ * Block mode, lists shared by every (b, h), pattern not causal with
+ * global_tokens > 0 and more than 16 key blocks: a query row below
+ * global_tokens attends to every key (glossary, section on common sparsity
+ * patterns: global tokens attend to all), so the query blocks holding such
+ * rows list every key block.  Each of those blocks is walked in chunks of 16
+ * list entries by separate workgroups, which write the chunk's normalised O
+ * and LSE to the workspace ([batch*heads][blocks][chunks][block_q] rows of
+ * head_dim floats, then one float per row); a second launch merges the
+ * chunks of a row with log-sum-exp weights into O and LSE.  The result is
+ * the same softmax; only the order of the float32 sums differs.
  *
  * Gather mode over a long key range (n_kv above 2^21 / (4 * head_dim)
  * keys, at most 256 ranges, batch * heads * ranges * n_q below 2^31) has a

@@ -71,6 +71,33 @@ def test_score_ranges_across_tiles(profile, d, bq, bk):
                 ctx=f"{profile} d={d} bq={bq} bk={bk}")
 
 
+SPLIT_CASES = [(2048, 2048, 64, 64, 64, "f32", 0, 130), (1500, 1777, 128, 64, 128, "bf16", 0, 200),
+               (1333, 2200, 64, 128, 64, "f32", 40, 100), (2100, 2100, 128, 128, 128, "f32", 0, 300)]
+
+
+@pytest.mark.parametrize("n_q,n_kv,bq,bk,d,of,q_off,g", SPLIT_CASES)
+def test_long_row_split_global_tokens(n_q, n_kv, bq, bk, d, of, q_off, g):
+    """Without causality the query blocks of global tokens list every key block; past 16
+    key blocks they run as chunks of 16 list entries whose partial (O, LSE) are merged by
+    log-sum-exp.  Every row against the oracle, with the split and without it."""
+    rng = np.random.default_rng(n_q + n_kv + bq + bk + d + q_off + g)
+    q, k, v = _rand(rng, 2, 2, n_q, n_kv, d)
+    u = 64
+    table = rng.integers(-1, -(-n_kv // u), size=(-(-(n_q + q_off) // u), 3)).astype(np.int32)
+    pat = dict(causal=0, global_tokens=g, unit=u, unit_window=1, rand_table=table, q_offset=q_off)
+    bl = sa.build_block_mask(pat, n_q, n_kv, bq, bk)
+    assert sa.attn_workspace_bytes_blocks(bl, 2, 2, d) > 0
+    qd, kd, vd = (to_dev_bf16(x) for x in (q, k, v))
+    od = torch.float32 if of == "f32" else torch.bfloat16
+    print(f"attn long-row split n_q={n_q} n_kv={n_kv} bq={bq} bk={bk} d={d} {of} q_off={q_off} g={g}", flush=True)
+    o_ref, lse_ref = oracle.attn_rows(pat, q, k, v)
+    for split in (True, False):
+        o, lse = sa.attn_fwd(qd, kd, vd, bl, o_dtype=od, split=split)
+        torch.cuda.synchronize()
+        check_o_lse(o.float().cpu().numpy().reshape(-1, d), lse.cpu().numpy().reshape(-1), o_ref, lse_ref,
+                    bf16_out=(of == "bf16"), ctx=f"split={split} n_q={n_q} bq={bq} bk={bk} {of}")
+
+
 @pytest.mark.parametrize("seed", range(16))
 def test_random_patterns(seed):
     rng = np.random.default_rng(900 + seed)
