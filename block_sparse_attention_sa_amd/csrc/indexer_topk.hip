@@ -591,29 +591,34 @@ topk_kernel(const float* __restrict__ scores, int32_t n_q, int32_t n_kv, int32_t
 // Streaming indexer + top-k: the selection without the score matrix.
 //
 // 1. stream_sample_kernel scores one 64-key tile in every SPERIOD keys (a
-//    1/32 sample spread over the row) on the same matrix-core chain and
-//    stores their order keys (0 where a key is not a candidate).
+//    1/32 sample spread over the row) on the float32 chain and stores their
+//    order keys (0 where a key is not a candidate).
 // 2. stream_bracket_kernel picks, per query row, the order key LO of the
 //    sample rank rho + 6 sqrt(rho) + 8, rho = k * sample size / candidates:
 //    LO sits well below the k-th largest candidate, so about 1.9 k
 //    candidates have keys >= LO.  LO = 0 marks a row that goes the direct
-//    way in step 4 (too few candidates for a sample).
-// 3. stream_filter_kernel walks every candidate like indexer_kernel and, in
-//    place of the score store, keeps the (key, position) of every candidate
-//    with key >= LO in a region of SCAP slots per (row, 512-key chunk) that
-//    the two half-waves holding the row fill from either end, counting on
-//    without storing once their counts add up to more than SCAP.
-// 4. stream_select_kernel, one workgroup per row: if no region overflowed
-//    and at least k candidates were kept, every candidate with key < LO
-//    ranks below the k-th kept one, so the exact selection among the kept
-//    keys is the row's top-k: one 11-bit histogram pass finds the bin of the
-//    k-th key and the few keys of that bin are ranked directly (more radix
-//    passes only when the bin is crowded); each thread then emits its
-//    region's selected positions, ties taken in position order.
+//    way in step 5 (too few candidates for a sample).
+//    stream_norm_kernel stores the largest key norm of every 64-key tile.
+// 3. stream_filter_kernel scores every candidate approximately on bf16
+//    matrix instructions (the products of two bf16 values are exact; only
+//    the order and rounding of the float32 sums differ from the chain) and
+//    keeps the position of every candidate whose approximate score is not
+//    below LO minus a bound on that difference, in a region of SCAP slots
+//    per (row, 512-key chunk) that the two half-waves holding the row fill
+//    from either end, counting on once their counts add up to more than
+//    SCAP.  Every candidate whose chain score reaches LO is kept.
+// 4. stream_select_kernel, one workgroup per row: if no region overflowed,
+//    the kept candidates are scored again on the exact chain; if at least k
+//    of them reach LO, every other candidate ranks below the k-th of those,
+//    so the exact selection among them is the row's top-k: one 11-bit
+//    histogram pass finds the bin of the k-th key and the few keys of that
+//    bin are ranked directly (more radix passes only when the bin is
+//    crowded); the selected positions leave ascending, ties taken in
+//    position order.
 // 5. stream_direct_kernel takes the other rows -- an adversarial order that
 //    fooled the sample: their scores are recomputed with the same float32
-//    chain (vector FMA in dimension order) at each pass of an exact
-//    selection over the whole row.  Every other row's workgroup exits at once.
+//    chain at each pass of an exact selection over the whole row.  Every
+//    other row's workgroup exits at once.
 constexpr int SPERIOD = kStreamPeriod;  // keys per sample tile
 constexpr int SCAP = kStreamCap;        // kept slots per (row, chunk)
 static_assert(kStreamChunk == XKC, "filter regions are the indexer's key chunks");
@@ -705,22 +710,76 @@ __device__ __forceinline__ float key_float(uint32_t key)
     return __uint_as_float(key >= 0x80000000u ? key & 0x7FFFFFFFu : ~key);
 }
 
+// Largest norm of the key rows of every 64-key tile (one wave per tile, the
+// float32 sum of squares in dimension order, rows past n_kv skipped).
+__global__ void __launch_bounds__(256) stream_norm_kernel(const uint16_t* __restrict__ ki, int32_t n_kv, int32_t d,
+                                                          int32_t ntile, float* __restrict__ tnorm)
+{
+    const int tile = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (tile >= ntile) return;
+    const int s = tile * 64 + lane;
+    float ss = 0.f;
+    if (s < n_kv) {
+        const uint16_t* kr = ki + (int64_t)s * d;
+        for (int i = 0; i < d; i += 8) {
+            const u32x4 kw = *reinterpret_cast<const u32x4*>(kr + i);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const float lo = __uint_as_float(kw[x] << 16), hi = __uint_as_float(kw[x] & 0xFFFF0000u);
+                ss = __builtin_fmaf(lo, lo, ss);
+                ss = __builtin_fmaf(hi, hi, ss);
+            }
+        }
+    }
+    float m = sqrtf(ss);
+    // a non-finite norm stays the maximum (NaN compares false: keep it)
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float o = __shfl_xor(m, off);
+        m = (o > m || o != o) ? o : m;
+    }
+    if (lane == 0) tnorm[tile] = m;
+}
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+// The approximate scores: S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = the
+// lane's key row, B = the lane's query), two 32-key blocks per 64-key tile;
+// element i of block b of a lane is key s0 + 32b + 8(i/4) + 4hh + i%4 of query
+// col.  The sum of d exact products differs from the dimension-order chain
+// only in the order and rounding of its float32 additions: each of the two is
+// within (d - 1) u sum|q_i k_i| of the exact dot product (u = 2^-24; twice u
+// for an adder that truncates), and sum|q_i k_i| <= |q| |k|, so the two scores
+// differ by less than 4 d u |q| |k| (+1 % for the rounding of the norms, plus
+// d * 2^-125 for flushed denormal partial sums).  A candidate is kept when its
+// approximate score is not below LO's float minus that bound, with |k| the
+// tile's largest key norm: every candidate whose chain score reaches LO passes.
+template <int NC>
 __global__ void __launch_bounds__(64 * XW, 2)
 stream_filter_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict__ ki, int32_t n_q, int32_t n_kv,
-                     int32_t d, int32_t q_offset, const uint32_t* __restrict__ lo, int32_t nchunk,
-                     uint32_t* __restrict__ ccnt, uint32_t* __restrict__ ckey, uint16_t* __restrict__ cpos)
+                     int32_t d, int32_t q_offset, const uint32_t* __restrict__ lo, const float* __restrict__ tnorm,
+                     int32_t nchunk, uint32_t* __restrict__ ccnt, uint32_t* __restrict__ ckept)
 {
-    // a lane's 32 scores of the current tile, so that the few kept ones can be
-    // fetched by a per-lane index: [wave][score group of 4][lane][4]
-    __shared__ float4 stage[XW][8][64];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    // the workgroup's four waves share each 64-key tile, staged in LDS through
+    // registers (double-buffered, the next tile's loads in flight during this
+    // tile's products); rows padded to KRS elements so that the A-operand
+    // reads of 16 lanes hit distinct banks
+    constexpr int KRS = NC * 16 + 8;
+    constexpr int CPR = NC * 2;                                // 16-byte chunks per row
+    constexpr int SPT = (XT * CPR + 64 * XW - 1) / (64 * XW);  // chunks per thread
+    __shared__ __attribute__((aligned(16))) uint16_t kt[2][XT * KRS];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int hh = lane >> 5, col = lane & 31;
-    const int r0 = (blockIdx.y * XW + w) * XQ;
-    if (r0 >= n_q) return;
+    const int rg0 = blockIdx.y * XW * XQ;  // the workgroup's first query row
+    if (rg0 >= n_q) return;
     const int s_begin = blockIdx.x * XKC;
-    const int t_max = q_offset + min(r0 + XQ, n_q) - 1;
-    const int s_end = min(min(s_begin + XKC, n_kv), t_max + 1);
-    if (s_begin >= s_end) return;  // no row of the wave reads this chunk's counts
+    const int s_end_g = min(min(s_begin + XKC, n_kv), q_offset + min(rg0 + XW * XQ, n_q));
+    if (s_begin >= s_end_g) return;  // no row of the workgroup reads this chunk's counts
+    const int r0 = rg0 + w * XQ;
+    const bool wave_on = r0 < n_q;
+    // this wave's candidates end before s_end (none: the wave only stages)
+    const int s_end = wave_on ? min(min(s_begin + XKC, n_kv), q_offset + min(r0 + XQ, n_q)) : s_begin;
     const int t_min = q_offset + r0;  // first query position of the wave
 
     const int r = r0 + col;
@@ -728,65 +787,211 @@ stream_filter_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict
     const int t = q_offset + r;
     const uint32_t lo_r = r_ok ? lo[r] : 0u;
     const float lo_f = key_float(lo_r);
-    // the region of (row, chunk): half-wave 0 fills it from the front, half-wave
-    // 1 from the back; it overflows when the two counts add up to more than SCAP
+    // B operand: the lane's query, dims 16c + 8hh .. + 7 (zero past d), and |q|
+    bf16x8 qop[NC];
+    float qq = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (r_ok && 16 * c + 8 * hh < d) x = *reinterpret_cast<const u32x4*>(qi + (int64_t)r * d + 16 * c + 8 * hh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float a = __uint_as_float(x[e] << 16), b = __uint_as_float(x[e] & 0xFFFF0000u);
+            qq = __builtin_fmaf(a, a, qq);
+            qq = __builtin_fmaf(b, b, qq);
+        }
+        qop[c] = __builtin_bit_cast(bf16x8, x);
+    }
+    qq += __shfl_xor(qq, 32);
+    const float cq = 4.04f * (float)d * 0x1p-24f * sqrtf(qq);
+    const float cabs = (float)d * 0x1p-125f;
+
     const int64_t region = (int64_t)(r_ok ? r : 0) * nchunk + blockIdx.x;
-    uint32_t* kdst = ckey + region * SCAP;
-    uint16_t* pdst = cpos + region * SCAP;
-    const float* my = reinterpret_cast<const float*>(&stage[w][0][lane]);  // score e at my[(e >> 2) * 256 + (e & 3)]
+    uint32_t* kdst = ckept + region * SCAP;
     uint32_t cnt = 0;
-    indexer_walk(qi, ki, n_q, n_kv, d, r0, s_begin, s_end, [&](int s0, const f32x32& acc) {
-        // bit e = 16*b + 4*m + i: score e (key s0 + 32b + 8m + 4hh + i) is kept
-        uint32_t keep = 0;
+    // staging: thread chunk it = tid + 256 i is row it / CPR, 16-byte chunk it % CPR
+    u32x4 stg[SPT];
+    auto fetch = [&](int s0) {
 #pragma unroll
-        for (int e = 0; e < 32; ++e) keep |= (!(acc[e] < lo_f) ? 1u : 0u) << e;
-        if (s0 + XT - 1 > min(t_min, n_kv - 1)) {  // a tile past some row's last candidate
-            uint32_t ok = 0;
-#pragma unroll
-            for (int e = 0; e < 32; ++e) {
-                const int sk = s0 + 32 * (e >> 4) + 8 * ((e >> 2) & 3) + 4 * hh + (e & 3);
-                ok |= (sk <= t && sk < n_kv ? 1u : 0u) << e;
+        for (int i = 0; i < SPT; ++i) {
+            const int it = tid + 64 * XW * i;
+            const int row = it / CPR, ch = it % CPR;
+            stg[i] = u32x4{0u, 0u, 0u, 0u};
+            if (it < XT * CPR && 8 * ch < d) {
+                const int64_t key = min(s0 + row, n_kv - 1);
+                stg[i] = *reinterpret_cast<const u32x4*>(ki + key * d + 8 * ch);
             }
-            keep &= ok;
         }
-        if (lo_r == 0u) keep = 0;  // row selected directly (or not a row)
-        if (!keep) return;
+    };
+    auto put = [&](int buf) {
 #pragma unroll
-        for (int g = 0; g < 8; ++g) stage[w][g][lane] = make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
-        while (keep) {
-            const int e = __builtin_ctz(keep);
-            keep &= keep - 1u;
-            if (cnt < (uint32_t)SCAP) {
-                const int slot = hh ? SCAP - 1 - (int)cnt : (int)cnt;
-                kdst[slot] = order_key(my[(e >> 2) * 256 + (e & 3)]);
-                pdst[slot] = (uint16_t)(s0 - s_begin + 32 * (e >> 4) + 8 * ((e >> 2) & 3) + 4 * hh + (e & 3));
-            }
-            ++cnt;
+        for (int i = 0; i < SPT; ++i) {
+            const int it = tid + 64 * XW * i;
+            if (it < XT * CPR) *reinterpret_cast<u32x4*>(&kt[buf][(it / CPR) * KRS + 8 * (it % CPR)]) = stg[i];
         }
-    });
-    if (r_ok) ccnt[region * 2 + hh] = cnt;
+    };
+    fetch(s_begin);
+    put(0);
+    __syncthreads();
+    int buf = 0;
+    for (int s0 = s_begin; s0 < s_end_g; s0 += XT, buf ^= 1) {
+        const bool more = s0 + XT < s_end_g;
+        if (more) fetch(s0 + XT);
+        if (s0 < s_end) {
+            f32x16 acc[2];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
+                const uint16_t* kr = &kt[buf][(32 * b + col) * KRS + 8 * hh];
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kr + 16 * c)), qop[c], acc[b], 0,
+                        0, 0);
+            }
+            // lo_f minus the bound, widened by |lo_f| 2^-22 so that the rounding
+            // of the subtraction cannot raise the threshold; NaN (non-finite
+            // norms) keeps everything
+            const float thr = lo_f - (cq * tnorm[s0 / XT] + cabs + fabsf(lo_f) * 0x1p-22f);
+            // bit e = 16b + i: the key s0 + 32b + 8(i/4) + 4hh + i%4 is kept
+            uint32_t keep = 0;
+#pragma unroll
+            for (int e = 0; e < 32; ++e) keep |= (!(acc[e >> 4][e & 15] < thr) ? 1u : 0u) << e;
+            if (s0 + XT - 1 > min(t_min, n_kv - 1)) {  // a tile past some row's last candidate
+                uint32_t ok = 0;
+#pragma unroll
+                for (int e = 0; e < 32; ++e) {
+                    const int sk = s0 + 32 * (e >> 4) + 8 * ((e >> 2) & 3) + 4 * hh + (e & 3);
+                    ok |= (sk <= t && sk < n_kv ? 1u : 0u) << e;
+                }
+                keep &= ok;
+            }
+            if (lo_r == 0u) keep = 0;  // row selected directly (or not a row)
+            // kept scores by group of four (static register indices; one select
+            // among four per kept score), in position order
+#pragma unroll
+            for (int g = 0; g < 8; ++g) {
+                uint32_t m = (keep >> (4 * g)) & 0xFu;
+                const float x0 = acc[g >> 2][4 * (g & 3)], x1 = acc[g >> 2][4 * (g & 3) + 1];
+                const float x2 = acc[g >> 2][4 * (g & 3) + 2], x3 = acc[g >> 2][4 * (g & 3) + 3];
+                while (m) {
+                    const int i = __builtin_ctz(m);
+                    m &= m - 1u;
+                    if (cnt < (uint32_t)SCAP) {
+                        const int slot = hh ? SCAP - 1 - (int)cnt : (int)cnt;
+                        const float x = i == 0 ? x0 : (i == 1 ? x1 : (i == 2 ? x2 : x3));
+                        const uint32_t p = (uint32_t)(s0 - s_begin + 32 * (g >> 2) + 8 * (g & 3) + 4 * hh + i);
+                        kdst[slot] = (__float_as_uint(x) & 0xFFFFFE00u) | p;  // p < 512
+                    }
+                    ++cnt;
+                }
+            }
+        }
+        if (more) put(buf ^ 1);
+        __syncthreads();
+    }
+    if (r_ok && s_begin < s_end) ccnt[region * 2 + hh] = cnt;
+}
+
+// The indexer's float32 chain for one (query, key): fused multiply-adds in
+// dimension order from zero (the same bits as the matrix-core chain).
+__device__ __forceinline__ float chain_score(const float* __restrict__ qf, const uint16_t* __restrict__ kr, int d)
+{
+    float acc = 0.f;
+    for (int i = 0; i < d; i += 8) {
+        const u32x4 kw = *reinterpret_cast<const u32x4*>(kr + i);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            acc = __builtin_fmaf(qf[i + 2 * x], __uint_as_float(kw[x] << 16), acc);
+            acc = __builtin_fmaf(qf[i + 2 * x + 1], __uint_as_float(kw[x] & 0xFFFF0000u), acc);
+        }
+    }
+    return acc;
 }
 
 constexpr int SKC = 6144;   // kept candidates a row may carry into the select
+constexpr int SAMB = 1024;  // candidates a row may leave ambiguous
 constexpr int SMALL = 256;  // keys in the rank's histogram bin that are ranked directly
 
 struct __attribute__((aligned(16))) SelectLds {
-    uint32_t sel[KWORDS];   // bit p: candidate p is selected
-    uint32_t hist[KBINS];   // digit histogram; the keys of the rank's bin; tie bitmap
-    uint32_t key[SKC];      // kept keys - LO; output staging
+    uint32_t sel[KWORDS];     // bit p: candidate p is selected
+    uint32_t hist[KBINS];     // digit histogram; the keys of the rank's bin; tie bitmap
+    float ap[SKC];            // approximate scores of the kept candidates; output staging
+    uint16_t pos[SKC];        // their positions in the row
+    uint32_t amb[SAMB];       // chain keys of the ambiguous candidates
+    uint16_t apos[SAMB];      // their positions
+    float tn[KMAXN / XT];     // largest key norm of every 64-key tile of the row
     uint32_t wsum[KWAVES];
     uint32_t wmax[KWAVES];
     uint32_t state[4];
 };
 
-// Exact top-k of row r from its kept candidates.  A row that cannot be
-// selected this way (threshold 0, a region overflowed, fewer than k or more
-// than SKC candidates kept) gets lo[r] = 0 and is left to
+// The T-th largest of the keys that each(f) hands to f and how many keys
+// equal to it rank within the first T (`width` significant bits): one
+// histogram pass, then the rank's bin ranked directly when it is small, else
+// the radix passes.
+template <class Each>
+__device__ void select_rank(SelectLds& L, Each&& each, uint32_t width, uint32_t rank, uint32_t& T, uint32_t& rem_out)
+{
+    const int tid = threadIdx.x;
+    const uint32_t nb = min(11u, width), shift = width - nb;
+    zero_words(L.hist, KBINS);
+    __syncthreads();
+    each([&](uint32_t v) { atomicAdd(&L.hist[v >> shift], 1u); });
+    __syncthreads();
+    find_digits(L, rank, 0u);
+    const uint32_t bin = L.state[0], rem = L.state[1];
+    const uint32_t m = L.hist[bin];
+    __syncthreads();
+    if (m <= (uint32_t)SMALL && shift > 0u) {
+        uint32_t* bk = L.hist;
+        if (tid == 0) L.state[2] = 0u;
+        __syncthreads();
+        each([&](uint32_t v) {
+            if ((v >> shift) == bin) bk[atomicAdd(&L.state[2], 1u)] = v;
+        });
+        __syncthreads();
+        if ((uint32_t)tid < m) {
+            const uint32_t x = bk[tid];
+            uint32_t gt = 0, ge = 0;
+            for (uint32_t j = 0; j < m; ++j) {
+                const uint32_t y = bk[j];
+                gt += y > x ? 1u : 0u;
+                ge += y >= x ? 1u : 0u;
+            }
+            if (gt < rem && rem <= ge) {  // x is the key (every thread holding it writes the same)
+                L.state[0] = x;
+                L.state[1] = rem - gt;
+            }
+        }
+        __syncthreads();
+        T = L.state[0];
+        rem_out = L.state[1];
+        __syncthreads();
+    } else {
+        radix_select(L, each, width, rank, T, rem_out);
+    }
+}
+
+// Exact top-k of row r from its kept candidates.  Each chain score c lies
+// within a bound b of its approximate score a (the filter's bound, widened
+// for the rounding of a +- b), and every b of the row is at most bmax, so the
+// k-th largest chain score lies within bmax of A_k, the k-th largest
+// approximate score.  A candidate with a - b above that interval is in the
+// top-k, one with a + b below it is not, and only the rest -- the few near
+// the k-th score -- are scored on the chain and ranked exactly (ties by
+// position).  If the interval lies at or above LO, at least k candidates
+// reach LO, so every candidate the filter dropped ranks below the top-k.  A
+// row that cannot be settled this way (threshold 0, a region overflowed,
+// more than SKC kept or SAMB ambiguous, fewer than k kept, the interval
+// below LO, a non-finite score or bound) gets lo[r] = 0 and is left to
 // stream_direct_kernel.
 __global__ void __launch_bounds__(KTH)
-stream_select_kernel(int32_t n_kv, int32_t q_offset, int32_t k, uint32_t* __restrict__ lo, int32_t nchunk,
-                     const uint32_t* __restrict__ ccnt, const uint32_t* __restrict__ ckey,
-                     const uint16_t* __restrict__ cpos, int32_t* __restrict__ idx_out)
+stream_select_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict__ ki, int32_t n_kv, int32_t d,
+                     int32_t q_offset, int32_t k, uint32_t* __restrict__ lo, int32_t nchunk,
+                     const uint32_t* __restrict__ ccnt, const float* __restrict__ tnorm,
+                     const uint32_t* __restrict__ ckept, int32_t* __restrict__ idx_out)
 {
     __shared__ SelectLds L;
     const int r = blockIdx.x, tid = threadIdx.x;
@@ -810,110 +1015,164 @@ stream_select_kernel(int32_t n_kv, int32_t q_offset, int32_t k, uint32_t* __rest
     const bool ovf = __syncthreads_or(c0 + c1 > (uint32_t)SCAP) != 0;
     uint32_t total;
     const uint32_t before = block_excl_scan(ovf ? 0u : c0 + c1, L.wsum, &total);
-    if (lo_r == 0u || ovf || total < (uint32_t)k || total > (uint32_t)SKC) {
+    auto direct = [&]() {
         if (tid == 0) lo[r] = 0u;
-        return;
-    }
-    // ---- the owner loads all slots of its region (independent 16-byte loads)
-    // and keeps them in registers; the filled ones -- the first c0 and the
-    // last c1 -- go to LDS as keys relative to LO ----
-    u32x4 kw[SCAP / 4], pw[SCAP / 8];
-    uint32_t fm[3];  // filled slots, 32 per word
-#pragma unroll
-    for (int x = 0; x < 3; ++x) {
-        auto below = [](int64_t n) { return n <= 0 ? 0u : (n >= 32 ? 0xFFFFFFFFu : (1u << n) - 1u); };
-        const int64_t base = 32 * x;
-        fm[x] = mine ? (below((int64_t)c0 - base) |
-                        (~below((int64_t)SCAP - (int64_t)c1 - base) & below((int64_t)SCAP - base)))
-                     : 0u;
-    }
-    auto filled = [&](int j) { return ((fm[j >> 5] >> (j & 31)) & 1u) != 0u; };
-    uint32_t kmax = 0;
+    };
+    if (lo_r == 0u || ovf || total < (uint32_t)k || total > (uint32_t)SKC) return direct();
+    // ---- kept (score, position) to LDS: the first c0 and the last c1 slots of
+    // each region; the region's tile norms; and, folded into one block
+    // reduction, the largest tile norm, the largest |score|, the smallest and
+    // largest score keys, |q|^2 and whether any score is not finite ----
+    uint32_t tmax = 0, amax = 0, kmin_n = 0, kmax = 0;  // kmin_n = ~(smallest key)
+    uint32_t bad = 0;
+    float qq = 0.f;
     if (mine) {
-        const u32x4* ks = reinterpret_cast<const u32x4*>(ckey + reg * SCAP);
-        const u32x4* ps = reinterpret_cast<const u32x4*>(cpos + reg * SCAP);
+        // the whole region in independent 16-byte loads
+        const u32x4* ks = reinterpret_cast<const u32x4*>(ckept + reg * SCAP);
+        u32x4 kw[SCAP / 4];
 #pragma unroll
         for (int i = 0; i < SCAP / 4; ++i) kw[i] = ks[i];
+        // the region's eight tile norms (tiles past n_kv read as tile 0's)
+        constexpr int TPR = XKC / XT;
+        float tnr[TPR];
 #pragma unroll
-        for (int i = 0; i < SCAP / 8; ++i) pw[i] = ps[i];
+        for (int i = 0; i < TPR; ++i) {
+            const int tl = tid * TPR + i;
+            tnr[i] = tnorm[tl * XT < n_kv ? tl : 0];
+            L.tn[tl] = tnr[i];
+            tmax = max(tmax, __float_as_uint(tnr[i]));  // >= 0 (NaN: the largest bits)
+        }
+        const uint32_t pbase = (uint32_t)tid * XKC;
         uint32_t n = before;
 #pragma unroll
         for (int j = 0; j < SCAP; ++j) {
-            if (filled(j)) {
-                const uint32_t u = kw[j >> 2][j & 3] - lo_r;
-                L.key[n++] = u;
-                kmax = max(kmax, u);
+            if ((uint32_t)j < c0 || (uint32_t)j >= (uint32_t)SCAP - c1) {
+                const uint32_t v = kw[j >> 2][j & 3];
+                const float a = __uint_as_float(v & 0xFFFFFE00u);
+                L.ap[n] = a;
+                L.pos[n] = (uint16_t)(pbase + (v & 0x1FFu));
+                ++n;
+                bad |= !(fabsf(a) <= 1.0e38f) ? 1u : 0u;
+                amax = max(amax, __float_as_uint(fabsf(a)));
+                const uint32_t key = order_key(a);
+                kmin_n = max(kmin_n, ~key);
+                kmax = max(kmax, key);
             }
         }
     }
-    // The kept keys lie in [LO, max]: selecting on key - LO with only the bits
-    // that span needs spreads the digits over the histogram bins.
-    kmax = block_max(kmax, L.wmax);  // (its barriers publish the keys)
-    const uint32_t width = kmax == 0u ? 0u : 32u - (uint32_t)__clz(kmax);
-    auto kept = [&](auto&& f) {
-        for (uint32_t j = tid; j < total; j += KTH) f(L.key[j]);
+    for (int i = tid; i < d; i += KTH) {
+        const float x = __uint_as_float((uint32_t)qi[(int64_t)r * d + i] << 16);
+        qq = __builtin_fmaf(x, x, qq);
+    }
+    {
+        const int lane = tid & 63, w = tid >> 6;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            tmax = max(tmax, (uint32_t)__shfl_xor(tmax, off));
+            amax = max(amax, (uint32_t)__shfl_xor(amax, off));
+            kmin_n = max(kmin_n, (uint32_t)__shfl_xor(kmin_n, off));
+            kmax = max(kmax, (uint32_t)__shfl_xor(kmax, off));
+            bad |= (uint32_t)__shfl_xor(bad, off);
+            qq += __shfl_xor(qq, off);
+        }
+        uint32_t* red = L.hist;  // [6][KWAVES]
+        if (lane == 0) {
+            red[0 * KWAVES + w] = tmax;
+            red[1 * KWAVES + w] = amax;
+            red[2 * KWAVES + w] = kmin_n;
+            red[3 * KWAVES + w] = kmax;
+            red[4 * KWAVES + w] = bad;
+            red[5 * KWAVES + w] = __float_as_uint(qq);
+        }
+        __syncthreads();  // also publishes L.ap, L.pos, L.tn
+        tmax = amax = kmin_n = kmax = bad = 0;
+        qq = 0.f;
+#pragma unroll
+        for (int i = 0; i < KWAVES; ++i) {
+            tmax = max(tmax, red[i]);
+            amax = max(amax, red[KWAVES + i]);
+            kmin_n = max(kmin_n, red[2 * KWAVES + i]);
+            kmax = max(kmax, red[3 * KWAVES + i]);
+            bad |= red[4 * KWAVES + i];
+            qq += __uint_as_float(red[5 * KWAVES + i]);
+        }
+        __syncthreads();
+    }
+    if (bad) return direct();
+    const float cq = 4.04f * (float)d * 0x1p-24f * sqrtf(qq);
+    const float cabs = (float)d * 0x1p-125f;
+    // chain score c_j within b_j of the stored a_j: the filter's bound, plus
+    // the 9 mantissa bits the filter dropped (less than 2^-14 |a_j| for a
+    // normal value, 2^-140 below; 2^-12 |a_j| + 2^-126 covers it), widened for
+    // the rounding of a_j +- b_j; bmax bounds every b_j of the row
+    auto bound = [&](uint32_t j) {
+        const float a = fabsf(L.ap[j]);
+        const float b = cq * L.tn[L.pos[j] / XT] + cabs + a * 0x1p-12f + 0x1p-126f;
+        return b + (a + b) * 0x1p-21f;
     };
-    // ---- T (relative) and how many keys equal to it are taken ----
-    uint32_t T, need_eq;
-    const uint32_t nb = min(11u, width), shift = width - nb;
-    zero_words(L.hist, KBINS);
+    float bmax = cq * __uint_as_float(tmax) + cabs + __uint_as_float(amax) * 0x1p-12f + 0x1p-126f;
+    bmax += (__uint_as_float(amax) + bmax) * 0x1p-21f;
+    if (!(bmax <= 1.0e30f)) return direct();  // non-finite norms: the direct way
+    // ---- A_k, the k-th largest approximate score (keys relative to the row's
+    // smallest kept key, only the bits their range needs) ----
+    const uint32_t kmin = ~kmin_n;
+    const uint32_t span = kmax - kmin;
+    const uint32_t width = span == 0u ? 0u : 32u - (uint32_t)__clz(span);
+    auto each_a = [&](auto&& f) {
+        for (uint32_t j = tid; j < total; j += KTH) f(order_key(L.ap[j]) - kmin);
+    };
+    uint32_t akr, rem;
+    select_rank(L, each_a, width, (uint32_t)k, akr, rem);
+    const float ak = key_float(akr + kmin);
+    // the k-th largest chain score lies within bmax of A_k: [lo_e, hi_e]
+    const float marg = bmax + (fabsf(ak) + bmax) * 0x1p-21f;
+    const float hi_e = ak + marg, lo_e = ak - marg;
+    if (!(lo_e >= key_float(lo_r))) return direct();  // fewer than k provably reach LO
+    // ---- sure-in to the bitmap; the ambiguous ones scored on the chain ----
+    __syncthreads();  // every thread has read the rank out of L.state / L.hist
+    zero_words(L.sel, KWORDS);
+    if (tid == 0) L.state[2] = 0u;
+    for (int i = tid; i < d; i += KTH) reinterpret_cast<float*>(L.hist)[i] = __uint_as_float((uint32_t)qi[(int64_t)r * d + i] << 16);
     __syncthreads();
-    kept([&](uint32_t v) { atomicAdd(&L.hist[v >> shift], 1u); });
-    __syncthreads();
-    find_digits(L, (uint32_t)k, 0u);
-    const uint32_t bin = L.state[0], rem = L.state[1];
-    const uint32_t m = L.hist[bin];
-    __syncthreads();
-    if (m <= (uint32_t)SMALL && shift > 0u) {
-        // rank the bin's keys directly: the rem-th largest of them is T
-        uint32_t* bk = L.hist;
-        if (tid == 0) L.state[2] = 0u;
-        __syncthreads();
-        kept([&](uint32_t v) {
-            if ((v >> shift) == bin) bk[atomicAdd(&L.state[2], 1u)] = v;
-        });
-        __syncthreads();
-        if ((uint32_t)tid < m) {
-            const uint32_t x = bk[tid];
-            uint32_t gt = 0, ge = 0;
-            for (uint32_t j = 0; j < m; ++j) {
-                const uint32_t y = bk[j];
-                gt += y > x ? 1u : 0u;
-                ge += y >= x ? 1u : 0u;
-            }
-            if (gt < rem && rem <= ge) {  // x is T (every thread holding T writes the same)
-                L.state[0] = x;
-                L.state[1] = rem - gt;
+    uint32_t n_in = 0;
+    bool full = false;
+    for (uint32_t j = tid; j < total; j += KTH) {
+        const float a = L.ap[j], b = bound(j);
+        const uint32_t p = L.pos[j];
+        if (a - b > hi_e) {
+            atomicOr(&L.sel[p >> 5], 1u << (p & 31));
+            ++n_in;
+        } else if (!(a + b < lo_e)) {
+            const uint32_t slot = atomicAdd(&L.state[2], 1u);
+            if (slot < (uint32_t)SAMB) {
+                L.amb[slot] = order_key(chain_score(reinterpret_cast<const float*>(L.hist), ki + (int64_t)p * d, d));
+                L.apos[slot] = (uint16_t)p;
+            } else {
+                full = true;
             }
         }
-        __syncthreads();
-        T = L.state[0];
-        need_eq = L.state[1];
-    } else {
-        radix_select(L, kept, width, (uint32_t)k, T, need_eq);
     }
-    // ---- selected (> T) and tied (== T) positions as bitmaps, then emitted
-    // in ascending order ----
+    uint32_t n_in_all;
+    block_excl_scan(n_in, L.wsum, &n_in_all);
+    if (__syncthreads_or(full)) return direct();
+    const uint32_t n_amb = L.state[2];
+    const uint32_t k2 = (uint32_t)k - n_in_all;  // >= 1: sure-in scores exceed the k-th
+    // ---- the k2-th largest chain key among the ambiguous ones ----
+    auto each_amb = [&](auto&& f) {
+        for (uint32_t j = tid; j < n_amb; j += KTH) f(L.amb[j]);
+    };
+    uint32_t T, need_eq;
+    select_rank(L, each_amb, 32u, k2, T, need_eq);
     uint32_t* tie = L.hist;
-    __syncthreads();
-    zero_words(L.sel, KWORDS);
     zero_words(tie, KWORDS);
     __syncthreads();
-    if (mine) {
-        const uint32_t pbase = (uint32_t)tid * XKC;
-#pragma unroll
-        for (int j = 0; j < SCAP; ++j) {
-            if (filled(j)) {
-                const uint32_t u = kw[j >> 2][j & 3] - lo_r;
-                const uint32_t w2 = pw[j >> 3][(j >> 1) & 3];
-                const uint32_t p = pbase + ((j & 1) ? w2 >> 16 : w2 & 0xFFFFu);
-                if (u > T) atomicOr(&L.sel[p >> 5], 1u << (p & 31));
-                else if (u == T) atomicOr(&tie[p >> 5], 1u << (p & 31));
-            }
-        }
+    for (uint32_t j = tid; j < n_amb; j += KTH) {
+        const uint32_t u = L.amb[j], p = L.apos[j];
+        if (u > T) atomicOr(&L.sel[p >> 5], 1u << (p & 31));
+        else if (u == T) atomicOr(&tie[p >> 5], 1u << (p & 31));
     }
     __syncthreads();
-    emit_ascending(L, L.sel, tie, need_eq, k, L.key, out);
+    emit_ascending(L, L.sel, tie, need_eq, k, reinterpret_cast<uint32_t*>(L.ap), out);
 }
 
 // The rows stream_select_kernel left (lo[r] == 0 with more than k
@@ -933,19 +1192,7 @@ stream_direct_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict
     if (n_cand <= k || lo[r] != 0u) return;
     for (int i = tid; i < d; i += KTH) qf[i] = __uint_as_float((uint32_t)qi[(int64_t)r * d + i] << 16);
     __syncthreads();
-    auto score_key = [&](int p) {
-        const uint16_t* kr = ki + (int64_t)p * d;
-        float acc = 0.f;
-        for (int i = 0; i < d; i += 8) {
-            const u32x4 kw = *reinterpret_cast<const u32x4*>(kr + i);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                acc = __builtin_fmaf(qf[i + 2 * x], __uint_as_float(kw[x] << 16), acc);
-                acc = __builtin_fmaf(qf[i + 2 * x + 1], __uint_as_float(kw[x] & 0xFFFF0000u), acc);
-            }
-        }
-        return order_key(acc);
-    };
+    auto score_key = [&](int p) { return order_key(chain_score(qf, ki + (int64_t)p * d, d)); };
     auto all = [&](auto&& f) {
         for (int p = tid; p < n_cand; p += KTH) f(score_key(p));
     };
@@ -1006,17 +1253,27 @@ hipError_t launch_indexer_topk_stream(const uint16_t* q_idx, const uint16_t* k_i
     uint32_t* samp = reinterpret_cast<uint32_t*>(ws + L.samp);
     uint32_t* lo = reinterpret_cast<uint32_t*>(ws + L.lo);
     uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + L.cnt);
-    uint32_t* key = reinterpret_cast<uint32_t*>(ws + L.key);
-    uint16_t* pos = reinterpret_cast<uint16_t*>(ws + L.pos);
+    float* tnorm = reinterpret_cast<float*>(ws + L.tnorm);
+    uint32_t* kept = reinterpret_cast<uint32_t*>(ws + L.kept);
     const unsigned qgroups = (unsigned)((n_q + XQ * XW - 1) / (XQ * XW));
     hipLaunchKernelGGL(stream_sample_kernel, dim3((unsigned)(L.s_max / XT), qgroups), dim3(64 * XW), 0, stream, q_idx,
                        k_idx, n_q, n_kv, d_idx, q_offset, samp, L.s_max);
     hipLaunchKernelGGL(stream_bracket_kernel, dim3((unsigned)n_q), dim3(KTH), 0, stream, samp, L.s_max, n_kv, q_offset,
                        topk, lo);
-    hipLaunchKernelGGL(stream_filter_kernel, dim3((unsigned)L.nchunk, qgroups), dim3(64 * XW), 0, stream, q_idx, k_idx,
-                       n_q, n_kv, d_idx, q_offset, lo, L.nchunk, cnt, key, pos);
-    hipLaunchKernelGGL(stream_select_kernel, dim3((unsigned)n_q), dim3(KTH), 0, stream, n_kv, q_offset, topk, lo,
-                       L.nchunk, cnt, key, pos, idx_out);
+    hipLaunchKernelGGL(stream_norm_kernel, dim3((unsigned)((L.ntile + 3) / 4)), dim3(256), 0, stream, k_idx, n_kv,
+                       d_idx, L.ntile, tnorm);
+    const dim3 fgrid((unsigned)L.nchunk, qgroups);
+    if (d_idx <= 64)
+        hipLaunchKernelGGL(stream_filter_kernel<4>, fgrid, dim3(64 * XW), 0, stream, q_idx, k_idx, n_q, n_kv, d_idx,
+                           q_offset, lo, tnorm, L.nchunk, cnt, kept);
+    else if (d_idx <= 128)
+        hipLaunchKernelGGL(stream_filter_kernel<8>, fgrid, dim3(64 * XW), 0, stream, q_idx, k_idx, n_q, n_kv, d_idx,
+                           q_offset, lo, tnorm, L.nchunk, cnt, kept);
+    else
+        hipLaunchKernelGGL(stream_filter_kernel<16>, fgrid, dim3(64 * XW), 0, stream, q_idx, k_idx, n_q, n_kv, d_idx,
+                           q_offset, lo, tnorm, L.nchunk, cnt, kept);
+    hipLaunchKernelGGL(stream_select_kernel, dim3((unsigned)n_q), dim3(KTH), 0, stream, q_idx, k_idx, n_kv, d_idx,
+                       q_offset, topk, lo, L.nchunk, cnt, tnorm, kept, idx_out);
     hipLaunchKernelGGL(stream_direct_kernel, dim3((unsigned)n_q), dim3(KTH), 0, stream, q_idx, k_idx, n_kv, d_idx,
                        q_offset, topk, lo, idx_out);
     return hipGetLastError();

@@ -283,16 +283,18 @@ hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t stream);
 //   samp  uint32 [n_q][s_max]            order keys of the sampled tiles
 //   lo    uint32 [n_q]                   per-row keep threshold (0: direct)
 //   cnt   uint32 [n_q][nchunk][2]        kept candidates per (row, chunk) and half-wave
-//   key   uint32 [n_q][nchunk][cap]      their order keys (half-wave 0 from the
-//                                        front, half-wave 1 from the back)
-//   pos   uint16 [n_q][nchunk][cap]      their positions within the chunk
+//   tnorm float  [n_tiles]               largest key norm of every 64-key tile
+//   kept  uint32 [n_q][nchunk][cap]      kept candidates: approximate score with
+//                                        its low 9 bits dropped, position within
+//                                        the chunk in those 9 bits; half-wave 0
+//                                        fills from the front, 1 from the back
 constexpr int kStreamPeriod = 2048;  // one 64-key sample tile per this many keys
 constexpr int kStreamChunk = 512;    // keys per filter chunk
 constexpr int kStreamCap = 72;       // kept slots per (row, chunk)
 constexpr int64_t kStreamMaxKv = 65536;
 struct StreamTopkLayout {
-    int32_t s_max, nchunk;
-    int64_t samp, lo, cnt, key, pos, total;
+    int32_t s_max, nchunk, ntile;
+    int64_t samp, lo, cnt, tnorm, kept, total;
 };
 inline bool stream_topk_layout(int64_t n_q, int64_t n_kv, StreamTopkLayout& L)
 {
@@ -303,10 +305,11 @@ inline bool stream_topk_layout(int64_t n_q, int64_t n_kv, StreamTopkLayout& L)
     const int64_t regions = n_q * L.nchunk;
     L.samp = 0;
     L.lo = up(L.samp + n_q * L.s_max * 4);
+    L.ntile = (int32_t)((n_kv + 63) / 64);
     L.cnt = up(L.lo + n_q * 4);
-    L.key = up(L.cnt + regions * 2 * 4);
-    L.pos = up(L.key + regions * kStreamCap * 4);
-    L.total = up(L.pos + regions * kStreamCap * 2);
+    L.tnorm = up(L.cnt + regions * 2 * 4);
+    L.kept = up(L.tnorm + (int64_t)L.ntile * 4);
+    L.total = up(L.kept + regions * kStreamCap * 4);
     return true;
 }
 hipError_t launch_indexer_topk_stream(const uint16_t* q_idx, const uint16_t* k_idx, int32_t n_q, int32_t n_kv,

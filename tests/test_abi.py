@@ -180,15 +180,16 @@ def test_indexer_topk_argument_errors():
 
 def test_indexer_topk_workspace_sizes():
     """The streaming scratch: per row a 1/32 sample (64 keys of every 2,048), a
-    threshold, and per 512-key chunk two counts and 72 kept slots of a 4-byte key
-    and a 2-byte position, each array 256-byte aligned."""
+    threshold, one largest key norm per 64-key tile, and per 512-key chunk two
+    counts and 72 kept 4-byte slots (approximate score, 9-bit position);
+    each array 256-byte aligned."""
     L = _lib.lib()
     up = lambda x: (x + 255) // 256 * 256
 
     def expect(n_q, n_kv):
         s_max = 64 * -(-n_kv // 2048)
         reg = n_q * -(-n_kv // 512)
-        return up(up(up(up(up(n_q * s_max * 4) + n_q * 4) + reg * 2 * 4) + reg * 72 * 4) + reg * 72 * 2)
+        return up(up(up(up(up(n_q * s_max * 4) + n_q * 4) + reg * 2 * 4) + -(-n_kv // 64) * 4) + reg * 72 * 4)
 
     for n_q, n_kv in ((1024, 65536), (1, 1), (77, 5000), (3, 65535)):
         assert L.sa_indexer_topk_workspace(n_q, n_kv, 2048) == expect(n_q, n_kv)

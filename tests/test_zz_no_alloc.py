@@ -30,8 +30,9 @@ def test_noalloc_matches_workspace_form_twice_then_rejects_oversize():
         torch.cuda.synchronize()
         assert torch.equal(got, want)
     # above the fixed scratch: a clear error before any launch
-    qi = torch.zeros((2048, 64), dtype=torch.bfloat16, device="cuda")
+    qi = torch.zeros((4096, 64), dtype=torch.bfloat16, device="cuda")
     ki = torch.zeros((65536, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(_lib.SaError) as e:
+        assert sa.indexer_topk_workspace_bytes(4096, 65536, 2048) > 64 << 20
         sa.indexer_topk_noalloc(qi, ki, 0, 2048)
     assert e.value.status == _lib.SA_ERR_UNSUPPORTED and "scratch" in str(e.value)
