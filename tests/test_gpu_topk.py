@@ -97,6 +97,38 @@ def test_streaming_topk_adversarial_orders(kind, n_kv, k):
     np.testing.assert_array_equal(idx.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("kind", ["nan_keys", "inf_keys", "huge", "tiny", "mixed_scale"])
+def test_streaming_topk_special_values(kind):
+    """The streaming form on indexer inputs whose scores are NaN or infinite, whose
+    norms overflow float32 (the filter's bound is infinite), whose scores lie in the
+    denormal range, or whose key norms differ by many octaves within a tile (the bound
+    taken from the tile's largest norm is loose for the others): every row equals the
+    oracle's selection (NaN above every number, ties to the lower index)."""
+    rng = np.random.default_rng(len(kind) * 7 + 5)
+    n_q, n_kv, k = 5, 20000, 1000
+    qf = rng.standard_normal((n_q, 64)).astype(np.float32)
+    kf = rng.standard_normal((n_kv, 64)).astype(np.float32)
+    if kind == "nan_keys":
+        kf[rng.integers(0, n_kv, 300), rng.integers(0, 64, 300)] = np.nan
+    elif kind == "inf_keys":
+        kf[rng.integers(0, n_kv, 300), rng.integers(0, 64, 300)] = np.inf
+        kf[rng.integers(0, n_kv, 300), rng.integers(0, 64, 300)] = -np.inf
+    elif kind == "huge":
+        kf *= np.float32(2.0 ** 100)
+        qf *= np.float32(2.0 ** 20)
+    elif kind == "tiny":
+        kf *= np.float32(2.0 ** -70)
+        qf *= np.float32(2.0 ** -60)
+    else:
+        kf *= (np.float32(2.0) ** rng.integers(-30, 30, (n_kv, 1))).astype(np.float32)
+    qi, ki = W.f32_to_bf16_bits(qf), W.f32_to_bf16_bits(kf)
+    off = n_kv - n_q
+    print(f"streaming top-k special values {kind}", flush=True)
+    idx, _ = sa.indexer_topk(to_dev_bf16(qi), to_dev_bf16(ki), off, k)
+    want = oracle.topk_rows(oracle.indexer_scores(qi, ki, off), np.arange(n_q) + off + 1, k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), want)
+
+
 def test_streaming_topk_reused_workspace_and_short_rows():
     """Rows from fewer candidates than k (padding) up to the whole key range in
     one call, and a workspace reused by a second, smaller call."""
