@@ -673,6 +673,56 @@ __global__ void __launch_bounds__(256) split_merge_kernel(AttnParams a, int32_t 
     float acc[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+    const int64_t obase = b * a.o_sb + h * a.o_sh + (int64_t)q * a.o_sn;
+    if (a.split_c <= 64) {
+        // Up to 64 chunks: one LSE per lane, and the partial O of the first
+        // PF chunks requested together with it, so the row costs one memory
+        // round trip before its arithmetic instead of three.
+        constexpr int PF = 16;
+        const int nc = a.split_c;
+        const float* po = a.part_o + slot0 * D + lane;
+        const float lv = lane < nc ? a.part_lse[slot0 + (int64_t)lane * bq] : -INFINITY;
+        float ob[PF][PER];
+#pragma unroll
+        for (int c = 0; c < PF; ++c)
+#pragma unroll
+            for (int i = 0; i < PER; ++i) ob[c][i] = c < nc ? po[(int64_t)c * bq * D + 64 * i] : 0.f;
+        float m = lv;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+        const float wl = m != -INFINITY ? __expf(lv - m) : 0.f;  // 0 for a chunk without keys
+        float s = wl;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+#pragma unroll
+        for (int c = 0; c < PF; ++c) {
+            const float wc = __shfl(wl, c);
+#pragma unroll
+            for (int i = 0; i < PER; ++i) acc[i] += wc * ob[c][i];
+        }
+        for (int c0 = PF; c0 < nc; c0 += PF) {
+#pragma unroll
+            for (int c = 0; c < PF; ++c)
+#pragma unroll
+                for (int i = 0; i < PER; ++i) ob[c][i] = c0 + c < nc ? po[(int64_t)(c0 + c) * bq * D + 64 * i] : 0.f;
+#pragma unroll
+            for (int c = 0; c < PF; ++c) {
+                const float wc = __shfl(wl, c0 + c);
+#pragma unroll
+                for (int i = 0; i < PER; ++i) acc[i] += wc * ob[c][i];
+            }
+        }
+        const float inv = s > 0.f ? 1.f / s : 0.f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const float x = acc[i] * inv;
+            if (OF32) reinterpret_cast<float*>(a.o)[obase + lane + 64 * i] = x;
+            else reinterpret_cast<uint16_t*>(a.o)[obase + lane + 64 * i] = __builtin_bit_cast(uint16_t, (__bf16)x);
+        }
+        if (a.lse && lane == 0)
+            a.lse[b * a.lse_sb + h * a.lse_sh + (int64_t)q * a.lse_sn] = s > 0.f ? m + logf(s) : -INFINITY;
+        return;
+    }
     float m = -INFINITY;
     for (int c0 = 0; c0 < a.split_c; c0 += 64)
         if (c0 + lane < a.split_c) m = fmaxf(m, a.part_lse[slot0 + (int64_t)(c0 + lane) * bq]);
@@ -697,7 +747,6 @@ __global__ void __launch_bounds__(256) split_merge_kernel(AttnParams a, int32_t 
         }
     }
     const float inv = s > 0.f ? 1.f / s : 0.f;
-    const int64_t obase = b * a.o_sb + h * a.o_sh + (int64_t)q * a.o_sn;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const float x = acc[i] * inv;
