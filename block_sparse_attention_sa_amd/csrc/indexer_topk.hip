@@ -910,18 +910,23 @@ __device__ __forceinline__ float chain_score(const float* __restrict__ qf, const
     return acc;
 }
 
-constexpr int SKC = 6144;   // kept candidates a row may carry into the select
-constexpr int SAMB = 1024;  // candidates a row may leave ambiguous
+// The caps keep the select's LDS within a quarter of a CU's 160 KB, so that
+// four rows run per CU.  A row past either cap takes the direct path.
+constexpr int SKC = 5120;   // kept candidates a row may carry into the select
+constexpr int SAMB = 256;   // candidates a row may leave ambiguous
+constexpr int SREG = KMAXN / XKC;  // regions of a row at most
+static_assert(SKC >= 4096, "the kept words stage the output of up to 4096 indices");
+static_assert(2 * SREG == KTH, "two threads per region in the classification");
 constexpr int SMALL = 256;  // keys in the rank's histogram bin that are ranked directly
 
 struct __attribute__((aligned(16))) SelectLds {
     uint32_t sel[KWORDS];     // bit p: candidate p is selected
     uint32_t hist[KBINS];     // digit histogram; the keys of the rank's bin; tie bitmap
-    float ap[SKC];            // approximate scores of the kept candidates; output staging
-    uint16_t pos[SKC];        // their positions in the row
+    uint32_t kw[SKC];         // kept words, region after region; output staging
     uint32_t amb[SAMB];       // chain keys of the ambiguous candidates
     uint16_t apos[SAMB];      // their positions
-    float tn[KMAXN / XT];     // largest key norm of every 64-key tile of the row
+    uint32_t rfirst[SREG];    // where each region's kept words start in kw
+    uint32_t rcount[SREG];    // and how many there are
     uint32_t wsum[KWAVES];
     uint32_t wmax[KWAVES];
     uint32_t state[4];
@@ -1034,23 +1039,20 @@ stream_select_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict
         for (int i = 0; i < SCAP / 4; ++i) kw[i] = ks[i];
         // the region's eight tile norms (tiles past n_kv read as tile 0's)
         constexpr int TPR = XKC / XT;
-        float tnr[TPR];
 #pragma unroll
         for (int i = 0; i < TPR; ++i) {
             const int tl = tid * TPR + i;
-            tnr[i] = tnorm[tl * XT < n_kv ? tl : 0];
-            L.tn[tl] = tnr[i];
-            tmax = max(tmax, __float_as_uint(tnr[i]));  // >= 0 (NaN: the largest bits)
+            tmax = max(tmax, __float_as_uint(tnorm[tl * XT < n_kv ? tl : 0]));  // >= 0 (NaN: the largest bits)
         }
-        const uint32_t pbase = (uint32_t)tid * XKC;
+        L.rfirst[tid] = before;
+        L.rcount[tid] = c0 + c1;
         uint32_t n = before;
 #pragma unroll
         for (int j = 0; j < SCAP; ++j) {
             if ((uint32_t)j < c0 || (uint32_t)j >= (uint32_t)SCAP - c1) {
                 const uint32_t v = kw[j >> 2][j & 3];
                 const float a = __uint_as_float(v & 0xFFFFFE00u);
-                L.ap[n] = a;
-                L.pos[n] = (uint16_t)(pbase + (v & 0x1FFu));
+                L.kw[n] = v;
                 ++n;
                 bad |= !(fabsf(a) <= 1.0e38f) ? 1u : 0u;
                 amax = max(amax, __float_as_uint(fabsf(a)));
@@ -1084,7 +1086,7 @@ stream_select_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict
             red[4 * KWAVES + w] = bad;
             red[5 * KWAVES + w] = __float_as_uint(qq);
         }
-        __syncthreads();  // also publishes L.ap, L.pos, L.tn
+        __syncthreads();  // also publishes L.kw, L.rfirst, L.rcount
         tmax = amax = kmin_n = kmax = bad = 0;
         qq = 0.f;
 #pragma unroll
@@ -1105,9 +1107,9 @@ stream_select_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict
     // the 9 mantissa bits the filter dropped (less than 2^-14 |a_j| for a
     // normal value, 2^-140 below; 2^-12 |a_j| + 2^-126 covers it), widened for
     // the rounding of a_j +- b_j; bmax bounds every b_j of the row
-    auto bound = [&](uint32_t j) {
-        const float a = fabsf(L.ap[j]);
-        const float b = cq * L.tn[L.pos[j] / XT] + cabs + a * 0x1p-12f + 0x1p-126f;
+    auto bound = [&](float a_signed, float tn) {
+        const float a = fabsf(a_signed);
+        const float b = cq * tn + cabs + a * 0x1p-12f + 0x1p-126f;
         return b + (a + b) * 0x1p-21f;
     };
     float bmax = cq * __uint_as_float(tmax) + cabs + __uint_as_float(amax) * 0x1p-12f + 0x1p-126f;
@@ -1119,7 +1121,7 @@ stream_select_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict
     const uint32_t span = kmax - kmin;
     const uint32_t width = span == 0u ? 0u : 32u - (uint32_t)__clz(span);
     auto each_a = [&](auto&& f) {
-        for (uint32_t j = tid; j < total; j += KTH) f(order_key(L.ap[j]) - kmin);
+        for (uint32_t j = tid; j < total; j += KTH) f(order_key(__uint_as_float(L.kw[j] & 0xFFFFFE00u)) - kmin);
     };
     uint32_t akr, rem;
     select_rank(L, each_a, width, (uint32_t)k, akr, rem);
@@ -1134,11 +1136,30 @@ stream_select_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict
     if (tid == 0) L.state[2] = 0u;
     for (int i = tid; i < d; i += KTH) reinterpret_cast<float*>(L.hist)[i] = __uint_as_float((uint32_t)qi[(int64_t)r * d + i] << 16);
     __syncthreads();
+    // two threads per region, alternate words; the region's tile norms in
+    // registers
     uint32_t n_in = 0;
     bool full = false;
-    for (uint32_t j = tid; j < total; j += KTH) {
-        const float a = L.ap[j], b = bound(j);
-        const uint32_t p = L.pos[j];
+    const int g = tid % SREG, half = tid / SREG;
+    if (g < n_reg) {
+        constexpr int TPR = XKC / XT;
+        float tnr[TPR];
+#pragma unroll
+        for (int i = 0; i < TPR; ++i) {
+            const int tl = g * TPR + i;
+            tnr[i] = tnorm[tl * XT < n_kv ? tl : 0];
+        }
+        const uint32_t first = L.rfirst[g], cnt = L.rcount[g];
+        const uint32_t pbase = (uint32_t)g * XKC;
+    for (uint32_t i = half; i < cnt; i += 2) {
+        const uint32_t v = L.kw[first + i];
+        const float a = __uint_as_float(v & 0xFFFFFE00u);
+        const uint32_t pl = v & 0x1FFu;
+        float tn = tnr[0];
+#pragma unroll
+        for (int x = 1; x < TPR; ++x) tn = (pl >> 6) == (uint32_t)x ? tnr[x] : tn;
+        const float b = bound(a, tn);
+        const uint32_t p = pbase + pl;
         if (a - b > hi_e) {
             atomicOr(&L.sel[p >> 5], 1u << (p & 31));
             ++n_in;
@@ -1151,6 +1172,7 @@ stream_select_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict
                 full = true;
             }
         }
+    }
     }
     uint32_t n_in_all;
     block_excl_scan(n_in, L.wsum, &n_in_all);
@@ -1172,7 +1194,7 @@ stream_select_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict
         else if (u == T) atomicOr(&tie[p >> 5], 1u << (p & 31));
     }
     __syncthreads();
-    emit_ascending(L, L.sel, tie, need_eq, k, reinterpret_cast<uint32_t*>(L.ap), out);
+    emit_ascending(L, L.sel, tie, need_eq, k, L.kw, out);
 }
 
 // The rows stream_select_kernel left (lo[r] == 0 with more than k
