@@ -597,8 +597,8 @@ topk_kernel(const float* __restrict__ scores, int32_t n_q, int32_t n_kv, int32_t
 //    sample rank rho + 6 sqrt(rho) + 8, rho = k * sample size / candidates:
 //    LO sits well below the k-th largest candidate, so about 1.9 k
 //    candidates have keys >= LO.  LO = 0 marks a row that goes the direct
-//    way in step 5 (too few candidates for a sample).
-//    stream_norm_kernel stores the largest key norm of every 64-key tile.
+//    way (too few candidates for a sample).  The same launch stores the
+//    largest key norm of every 64-key tile (stream_norm_tiles).
 // 3. stream_filter_kernel scores every candidate approximately on bf16
 //    matrix instructions (the products of two bf16 values are exact; only
 //    the order and rounding of the float32 sums differ from the chain) and
@@ -607,18 +607,17 @@ topk_kernel(const float* __restrict__ scores, int32_t n_q, int32_t n_kv, int32_t
 //    per (row, 512-key chunk) that the two half-waves holding the row fill
 //    from either end, counting on once their counts add up to more than
 //    SCAP.  Every candidate whose chain score reaches LO is kept.
-// 4. stream_select_kernel, one workgroup per row: if no region overflowed,
-//    the kept candidates are scored again on the exact chain; if at least k
-//    of them reach LO, every other candidate ranks below the k-th of those,
-//    so the exact selection among them is the row's top-k: one 11-bit
-//    histogram pass finds the bin of the k-th key and the few keys of that
-//    bin are ranked directly (more radix passes only when the bin is
-//    crowded); the selected positions leave ascending, ties taken in
-//    position order.
-// 5. stream_direct_kernel takes the other rows -- an adversarial order that
-//    fooled the sample: their scores are recomputed with the same float32
-//    chain at each pass of an exact selection over the whole row.  Every
-//    other row's workgroup exits at once.
+// 4. stream_select_kernel, one workgroup per row: every kept candidate's
+//    chain score lies within a known bound of its stored approximate score,
+//    so the k-th largest approximate score brackets the k-th chain score;
+//    candidates clear of that bracket are in or out for certain, and only
+//    the few inside it are scored on the exact chain and ranked (ties in
+//    position order).  The selected positions leave ascending.
+// 5. A row step 4 cannot settle (an adversarial order that fooled the
+//    sample, a region that overflowed, a non-finite score) is selected by
+//    the same workgroup directly (select_direct): its scores are recomputed
+//    with the same float32 chain at each pass of an exact selection over the
+//    whole row.
 constexpr int SPERIOD = kStreamPeriod;  // keys per sample tile
 constexpr int SCAP = kStreamCap;        // kept slots per (row, chunk)
 static_assert(kStreamChunk == XKC, "filter regions are the indexer's key chunks");
@@ -662,18 +661,28 @@ stream_sample_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict
                  [&](int s0, const f32x32& acc) { store(s0, &acc); });
 }
 
+__device__ void stream_norm_tiles(const uint16_t* __restrict__ ki, int32_t n_kv, int32_t d, int32_t ntile,
+                                  float* __restrict__ tnorm, int blk);
+
 struct __attribute__((aligned(16))) BracketLds {
     uint32_t hist[KBINS];
     uint32_t wsum[KWAVES];
     uint32_t state[4];
 };
 
+// The first nnorm blocks store the key tiles' norms (stream_norm_tiles), the
+// rest pick LO, one block per query row.
 __global__ void __launch_bounds__(KTH)
 stream_bracket_kernel(const uint32_t* __restrict__ samp, int32_t s_max, int32_t n_kv, int32_t q_offset, int32_t k,
-                      uint32_t* __restrict__ lo)
+                      uint32_t* __restrict__ lo, const uint16_t* __restrict__ ki, int32_t d, int32_t ntile,
+                      int32_t nnorm, float* __restrict__ tnorm)
 {
+    if ((int)blockIdx.x < nnorm) {
+        stream_norm_tiles(ki, n_kv, d, ntile, tnorm, (int)blockIdx.x);
+        return;
+    }
     __shared__ BracketLds L;
-    const int r = blockIdx.x, tid = threadIdx.x;
+    const int r = (int)blockIdx.x - nnorm, tid = threadIdx.x;
     const int64_t t = (int64_t)q_offset + r;
     const int n_cand = (int)min((int64_t)n_kv, t + 1);
     // sample positions among the candidates: the first XT of every SPERIOD
@@ -711,11 +720,13 @@ __device__ __forceinline__ float key_float(uint32_t key)
 }
 
 // Largest norm of the key rows of every 64-key tile (one wave per tile, the
-// float32 sum of squares in dimension order, rows past n_kv skipped).
-__global__ void __launch_bounds__(256) stream_norm_kernel(const uint16_t* __restrict__ ki, int32_t n_kv, int32_t d,
-                                                          int32_t ntile, float* __restrict__ tnorm)
+// float32 sum of squares in dimension order, rows past n_kv skipped); block
+// `blk` of KTH threads covers tiles 4*blk .. 4*blk + 3.
+__device__ void stream_norm_tiles(const uint16_t* __restrict__ ki, int32_t n_kv, int32_t d, int32_t ntile,
+                                  float* __restrict__ tnorm, int blk)
 {
-    const int tile = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    static_assert(KTH == 256, "four tiles per block");
+    const int tile = blk * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (tile >= ntile) return;
     const int s = tile * 64 + lane;
     float ss = 0.f;
@@ -927,6 +938,7 @@ struct __attribute__((aligned(16))) SelectLds {
     uint16_t apos[SAMB];      // their positions
     uint32_t rfirst[SREG];    // where each region's kept words start in kw
     uint32_t rcount[SREG];    // and how many there are
+    uint32_t rc0[SREG];       // how many of them fill the region from its start
     uint32_t wsum[KWAVES];
     uint32_t wmax[KWAVES];
     uint32_t state[4];
@@ -979,6 +991,46 @@ __device__ void select_rank(SelectLds& L, Each&& each, uint32_t width, uint32_t 
     }
 }
 
+// Exact top-k of row r straight from the scores, for the rows the bracket
+// cannot settle: the scores are recomputed with the indexer's float32 chain
+// (vector FMA in dimension order, the same bits) at each pass of an exact
+// selection over the whole row.  Called by every thread of the workgroup;
+// qf holds d floats and stage k words of LDS, both apart from L's fields.
+template <class Lds>
+__device__ void select_direct(Lds& L, float* qf, uint32_t* stage, const uint16_t* __restrict__ qi,
+                              const uint16_t* __restrict__ ki, int r, int n_cand, int d, int k,
+                              int32_t* __restrict__ out)
+{
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    __syncthreads();  // the caller's last reads of L are done
+    for (int i = tid; i < d; i += KTH) qf[i] = __uint_as_float((uint32_t)qi[(int64_t)r * d + i] << 16);
+    __syncthreads();
+    auto score_key = [&](int p) { return order_key(chain_score(qf, ki + (int64_t)p * d, d)); };
+    auto all = [&](auto&& f) {
+        for (int p = tid; p < n_cand; p += KTH) f(score_key(p));
+    };
+    uint32_t T, need_eq;
+    radix_select(L, all, 32u, (uint32_t)k, T, need_eq);
+    uint32_t* tie = L.hist;
+    // every bitmap word is written once: 64 positions per wave step
+    for (int p0 = 0; p0 < KMAXN; p0 += KTH) {
+        const int p = p0 + tid;
+        const bool valid = p < n_cand;
+        const uint32_t u = valid ? score_key(p) : 0u;
+        const uint64_t g = __ballot(valid && u > T);
+        const uint64_t e = __ballot(valid && u == T);
+        if (lane == 0) {
+            const int wd = (p0 + 64 * w) >> 5;
+            L.sel[wd] = (uint32_t)g;
+            L.sel[wd + 1] = (uint32_t)(g >> 32);
+            tie[wd] = (uint32_t)e;
+            tie[wd + 1] = (uint32_t)(e >> 32);
+        }
+    }
+    __syncthreads();
+    emit_ascending(L, L.sel, tie, need_eq, k, stage, out);
+}
+
 // Exact top-k of row r from its kept candidates.  Each chain score c lies
 // within a bound b of its approximate score a (the filter's bound, widened
 // for the rounding of a +- b), and every b of the row is at most bmax, so the
@@ -990,8 +1042,7 @@ __device__ void select_rank(SelectLds& L, Each&& each, uint32_t width, uint32_t 
 // reach LO, so every candidate the filter dropped ranks below the top-k.  A
 // row that cannot be settled this way (threshold 0, a region overflowed,
 // more than SKC kept or SAMB ambiguous, fewer than k kept, the interval
-// below LO, a non-finite score or bound) gets lo[r] = 0 and is left to
-// stream_direct_kernel.
+// below LO, a non-finite score or bound) is selected by select_direct.
 __global__ void __launch_bounds__(KTH)
 stream_select_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict__ ki, int32_t n_kv, int32_t d,
                      int32_t q_offset, int32_t k, uint32_t* __restrict__ lo, int32_t nchunk,
@@ -1020,9 +1071,11 @@ stream_select_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict
     const bool ovf = __syncthreads_or(c0 + c1 > (uint32_t)SCAP) != 0;
     uint32_t total;
     const uint32_t before = block_excl_scan(ovf ? 0u : c0 + c1, L.wsum, &total);
+    // the direct way: q staged past the k output words the staging needs
     auto direct = [&]() {
-        if (tid == 0) lo[r] = 0u;
+        select_direct(L, reinterpret_cast<float*>(L.kw + 4096), L.kw, qi, ki, r, n_cand, d, k, out);
     };
+    static_assert(SKC >= 4096 + 256, "q (d <= 256) staged past the output staging");
     if (lo_r == 0u || ovf || total < (uint32_t)k || total > (uint32_t)SKC) return direct();
     // ---- kept (score, position) to LDS: the first c0 and the last c1 slots of
     // each region; the region's tile norms; and, folded into one block
@@ -1031,12 +1084,21 @@ stream_select_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict
     uint32_t tmax = 0, amax = 0, kmin_n = 0, kmax = 0;  // kmin_n = ~(smallest key)
     uint32_t bad = 0;
     float qq = 0.f;
-    if (mine) {
-        // the whole region in independent 16-byte loads
-        const u32x4* ks = reinterpret_cast<const u32x4*>(ckept + reg * SCAP);
-        u32x4 kw[SCAP / 4];
+    // The row's regions lie one after another in memory; every thread takes
+    // 16-byte pieces of them (coalesced), loaded before the region table is
+    // known.  Slot j of a region goes to first + j when j < c0, and to
+    // first + c0 + (j - (SCAP - c1)) when it is one of the last c1.
+    constexpr int PPR = SCAP / 4;                        // pieces per region
+    constexpr int PPT = (SREG * PPR + KTH - 1) / KTH;    // pieces per thread at most
+    const int npieces = n_reg * PPR;
+    const u32x4* rowk = reinterpret_cast<const u32x4*>(ckept + (int64_t)r * nchunk * SCAP);
+    u32x4 kw[PPT];
 #pragma unroll
-        for (int i = 0; i < SCAP / 4; ++i) kw[i] = ks[i];
+    for (int i = 0; i < PPT; ++i) {
+        const int pc = tid + KTH * i;
+        kw[i] = pc < npieces ? rowk[pc] : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (mine) {
         // the region's eight tile norms (tiles past n_kv read as tile 0's)
         constexpr int TPR = XKC / XT;
 #pragma unroll
@@ -1045,20 +1107,30 @@ stream_select_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict
             tmax = max(tmax, __float_as_uint(tnorm[tl * XT < n_kv ? tl : 0]));  // >= 0 (NaN: the largest bits)
         }
         L.rfirst[tid] = before;
+        L.rc0[tid] = c0;
         L.rcount[tid] = c0 + c1;
-        uint32_t n = before;
+    }
+    __syncthreads();
 #pragma unroll
-        for (int j = 0; j < SCAP; ++j) {
-            if ((uint32_t)j < c0 || (uint32_t)j >= (uint32_t)SCAP - c1) {
-                const uint32_t v = kw[j >> 2][j & 3];
-                const float a = __uint_as_float(v & 0xFFFFFE00u);
-                L.kw[n] = v;
-                ++n;
-                bad |= !(fabsf(a) <= 1.0e38f) ? 1u : 0u;
-                amax = max(amax, __float_as_uint(fabsf(a)));
-                const uint32_t key = order_key(a);
-                kmin_n = max(kmin_n, ~key);
-                kmax = max(kmax, key);
+    for (int i = 0; i < PPT; ++i) {
+        const int pc = tid + KTH * i;
+        if (pc < npieces) {
+            const int g = pc / PPR, j0 = 4 * (pc % PPR);
+            const uint32_t first = L.rfirst[g], c0g = L.rc0[g];
+            const uint32_t tail0 = (uint32_t)SCAP - (L.rcount[g] - c0g);  // first of the last c1 slots
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const uint32_t j = (uint32_t)(j0 + x);
+                if (j < c0g || j >= tail0) {
+                    const uint32_t v = kw[i][x];
+                    const float a = __uint_as_float(v & 0xFFFFFE00u);
+                    L.kw[j < c0g ? first + j : first + c0g + (j - tail0)] = v;
+                    bad |= !(fabsf(a) <= 1.0e38f) ? 1u : 0u;
+                    amax = max(amax, __float_as_uint(fabsf(a)));
+                    const uint32_t key = order_key(a);
+                    kmin_n = max(kmin_n, ~key);
+                    kmax = max(kmax, key);
+                }
             }
         }
     }
@@ -1165,12 +1237,8 @@ stream_select_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict
             ++n_in;
         } else if (!(a + b < lo_e)) {
             const uint32_t slot = atomicAdd(&L.state[2], 1u);
-            if (slot < (uint32_t)SAMB) {
-                L.amb[slot] = order_key(chain_score(reinterpret_cast<const float*>(L.hist), ki + (int64_t)p * d, d));
-                L.apos[slot] = (uint16_t)p;
-            } else {
-                full = true;
-            }
+            if (slot < (uint32_t)SAMB) L.apos[slot] = (uint16_t)p;
+            else full = true;
         }
     }
     }
@@ -1178,6 +1246,13 @@ stream_select_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict
     block_excl_scan(n_in, L.wsum, &n_in_all);
     if (__syncthreads_or(full)) return direct();
     const uint32_t n_amb = L.state[2];
+    // the ambiguous ones on the chain, all at once (one key row per thread):
+    // scored inside the loop above, a wave would wait for a row's load at
+    // every trip that meets one
+    static_assert(SAMB <= KTH, "one ambiguous candidate per thread");
+    if ((uint32_t)tid < n_amb)
+        L.amb[tid] = order_key(chain_score(reinterpret_cast<const float*>(L.hist), ki + (int64_t)L.apos[tid] * d, d));
+    __syncthreads();
     const uint32_t k2 = (uint32_t)k - n_in_all;  // >= 1: sure-in scores exceed the k-th
     // ---- the k2-th largest chain key among the ambiguous ones ----
     auto each_amb = [&](auto&& f) {
@@ -1195,49 +1270,6 @@ stream_select_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict
     }
     __syncthreads();
     emit_ascending(L, L.sel, tie, need_eq, k, L.kw, out);
-}
-
-// The rows stream_select_kernel left (lo[r] == 0 with more than k
-// candidates): the scores are recomputed with the indexer's float32 chain
-// (vector FMA in dimension order, the same bits) at each pass of an exact
-// selection over the whole row.
-__global__ void __launch_bounds__(KTH)
-stream_direct_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict__ ki, int32_t n_kv, int32_t d,
-                     int32_t q_offset, int32_t k, const uint32_t* __restrict__ lo, int32_t* __restrict__ idx_out)
-{
-    __shared__ TopkLds L;
-    __shared__ float qf[256];
-    const int r = blockIdx.x, tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
-    const int64_t t = (int64_t)q_offset + r;
-    const int n_cand = (int)min((int64_t)n_kv, t + 1);
-    if (n_cand <= k || lo[r] != 0u) return;
-    for (int i = tid; i < d; i += KTH) qf[i] = __uint_as_float((uint32_t)qi[(int64_t)r * d + i] << 16);
-    __syncthreads();
-    auto score_key = [&](int p) { return order_key(chain_score(qf, ki + (int64_t)p * d, d)); };
-    auto all = [&](auto&& f) {
-        for (int p = tid; p < n_cand; p += KTH) f(score_key(p));
-    };
-    uint32_t T, need_eq;
-    radix_select(L, all, 32u, (uint32_t)k, T, need_eq);
-    uint32_t* tie = L.hist;
-    // every bitmap word is written once: 64 positions per wave step
-    for (int p0 = 0; p0 < KMAXN; p0 += KTH) {
-        const int p = p0 + tid;
-        const bool valid = p < n_cand;
-        const uint32_t u = valid ? score_key(p) : 0u;
-        const uint64_t g = __ballot(valid && u > T);
-        const uint64_t e = __ballot(valid && u == T);
-        if (lane == 0) {
-            const int wd = (p0 + 64 * w) >> 5;
-            L.sel[wd] = (uint32_t)g;
-            L.sel[wd + 1] = (uint32_t)(g >> 32);
-            tie[wd] = (uint32_t)e;
-            tie[wd + 1] = (uint32_t)(e >> 32);
-        }
-    }
-    __syncthreads();
-    emit_ascending(L, L.sel, tie, need_eq, k, L.mid, idx_out + (int64_t)r * k);
 }
 
 }  // namespace
@@ -1280,10 +1312,9 @@ hipError_t launch_indexer_topk_stream(const uint16_t* q_idx, const uint16_t* k_i
     const unsigned qgroups = (unsigned)((n_q + XQ * XW - 1) / (XQ * XW));
     hipLaunchKernelGGL(stream_sample_kernel, dim3((unsigned)(L.s_max / XT), qgroups), dim3(64 * XW), 0, stream, q_idx,
                        k_idx, n_q, n_kv, d_idx, q_offset, samp, L.s_max);
-    hipLaunchKernelGGL(stream_bracket_kernel, dim3((unsigned)n_q), dim3(KTH), 0, stream, samp, L.s_max, n_kv, q_offset,
-                       topk, lo);
-    hipLaunchKernelGGL(stream_norm_kernel, dim3((unsigned)((L.ntile + 3) / 4)), dim3(256), 0, stream, k_idx, n_kv,
-                       d_idx, L.ntile, tnorm);
+    const int nnorm = (L.ntile + 3) / 4;
+    hipLaunchKernelGGL(stream_bracket_kernel, dim3((unsigned)(nnorm + n_q)), dim3(KTH), 0, stream, samp, L.s_max, n_kv,
+                       q_offset, topk, lo, k_idx, d_idx, L.ntile, nnorm, tnorm);
     const dim3 fgrid((unsigned)L.nchunk, qgroups);
     if (d_idx <= 64)
         hipLaunchKernelGGL(stream_filter_kernel<4>, fgrid, dim3(64 * XW), 0, stream, q_idx, k_idx, n_q, n_kv, d_idx,
@@ -1296,8 +1327,6 @@ hipError_t launch_indexer_topk_stream(const uint16_t* q_idx, const uint16_t* k_i
                            q_offset, lo, tnorm, L.nchunk, cnt, kept);
     hipLaunchKernelGGL(stream_select_kernel, dim3((unsigned)n_q), dim3(KTH), 0, stream, q_idx, k_idx, n_kv, d_idx,
                        q_offset, topk, lo, L.nchunk, cnt, tnorm, kept, idx_out);
-    hipLaunchKernelGGL(stream_direct_kernel, dim3((unsigned)n_q), dim3(KTH), 0, stream, q_idx, k_idx, n_kv, d_idx,
-                       q_offset, topk, lo, idx_out);
     return hipGetLastError();
 }
 
