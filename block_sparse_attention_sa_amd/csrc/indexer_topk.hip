@@ -1076,7 +1076,7 @@ stream_select_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict
         select_direct(L, reinterpret_cast<float*>(L.kw + 4096), L.kw, qi, ki, r, n_cand, d, k, out);
     };
     static_assert(SKC >= 4096 + 256, "q (d <= 256) staged past the output staging");
-    if (lo_r == 0u || ovf || total < (uint32_t)k || total > (uint32_t)SKC) return direct();
+    if (lo_r == 0u || ovf || total < (uint32_t)k) return direct();
     // ---- kept (score, position) to LDS: the first c0 and the last c1 slots of
     // each region; the region's tile norms; and, folded into one block
     // reduction, the largest tile norm, the largest |score|, the smallest and
@@ -1084,19 +1084,29 @@ stream_select_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict
     uint32_t tmax = 0, amax = 0, kmin_n = 0, kmax = 0;  // kmin_n = ~(smallest key)
     uint32_t bad = 0;
     float qq = 0.f;
-    // The row's regions lie one after another in memory; every thread takes
-    // 16-byte pieces of them (coalesced), loaded before the region table is
-    // known.  Slot j of a region goes to first + j when j < c0, and to
-    // first + c0 + (j - (SCAP - c1)) when it is one of the last c1.
+    // The row's regions lie one after another in memory, in 16-byte pieces.
     constexpr int PPR = SCAP / 4;                        // pieces per region
     constexpr int PPT = (SREG * PPR + KTH - 1) / KTH;    // pieces per thread at most
     const int npieces = n_reg * PPR;
     const u32x4* rowk = reinterpret_cast<const u32x4*>(ckept + (int64_t)r * nchunk * SCAP);
+    auto take = [&](uint32_t v) {  // a word into the reductions
+        const float a = __uint_as_float(v & 0xFFFFFE00u);
+        bad |= !(fabsf(a) <= 1.0e38f) ? 1u : 0u;
+        amax = max(amax, __float_as_uint(fabsf(a)));
+        const uint32_t key = order_key(a);
+        kmin_n = max(kmin_n, ~key);
+        kmax = max(kmax, key);
+    };
+    const bool trim = total > (uint32_t)SKC;
     u32x4 kw[PPT];
+    if (!trim) {
+        // every thread takes pieces (coalesced), loaded before the region
+        // table is known
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-        const int pc = tid + KTH * i;
-        kw[i] = pc < npieces ? rowk[pc] : u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < PPT; ++i) {
+            const int pc = tid + KTH * i;
+            kw[i] = pc < npieces ? rowk[pc] : u32x4{0u, 0u, 0u, 0u};
+        }
     }
     if (mine) {
         // the region's eight tile norms (tiles past n_kv read as tile 0's)
@@ -1111,28 +1121,96 @@ stream_select_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict
         L.rcount[tid] = c0 + c1;
     }
     __syncthreads();
+    // kept words of a region: slots [0, c0) and [SCAP - c1, SCAP)
+    auto kept_slot = [&](int g, uint32_t j, uint32_t& rank) {
+        const uint32_t c0g = L.rc0[g];
+        const uint32_t tail0 = (uint32_t)SCAP - (L.rcount[g] - c0g);  // first of the last c1 slots
+        rank = j < c0g ? j : c0g + (j - tail0);
+        return j < c0g || j >= tail0;
+    };
+    uint32_t xkey = 0u;  // a trimmed row keeps the words whose key is at least xkey
+    if (!trim) {
+        // slot j goes to first + its rank among the region's kept words
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-        const int pc = tid + KTH * i;
-        if (pc < npieces) {
-            const int g = pc / PPR, j0 = 4 * (pc % PPR);
-            const uint32_t first = L.rfirst[g], c0g = L.rc0[g];
-            const uint32_t tail0 = (uint32_t)SCAP - (L.rcount[g] - c0g);  // first of the last c1 slots
+        for (int i = 0; i < PPT; ++i) {
+            const int pc = tid + KTH * i;
+            if (pc < npieces) {
+                const int g = pc / PPR, j0 = 4 * (pc % PPR);
+                const uint32_t first = L.rfirst[g];
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const uint32_t j = (uint32_t)(j0 + x);
-                if (j < c0g || j >= tail0) {
-                    const uint32_t v = kw[i][x];
-                    const float a = __uint_as_float(v & 0xFFFFFE00u);
-                    L.kw[j < c0g ? first + j : first + c0g + (j - tail0)] = v;
-                    bad |= !(fabsf(a) <= 1.0e38f) ? 1u : 0u;
-                    amax = max(amax, __float_as_uint(fabsf(a)));
-                    const uint32_t key = order_key(a);
-                    kmin_n = max(kmin_n, ~key);
-                    kmax = max(kmax, key);
+                for (int x = 0; x < 4; ++x) {
+                    uint32_t rank;
+                    if (kept_slot(g, (uint32_t)(j0 + x), rank)) {
+                        L.kw[first + rank] = kw[i][x];
+                        take(kw[i][x]);
+                    }
                 }
             }
         }
+    } else {
+        // More kept words than LDS holds (rare: about one row in several
+        // thousand at the DSA prefill shape): keep those whose key is at least
+        // the (SKC - 256)-th largest, read from memory at every pass.  The
+        // words left out are shown to rank below the top-k once the bracket
+        // of the k-th score is known, else the row takes the direct way.
+        auto each_kept = [&](auto&& f) {
+            for (int pc = tid; pc < npieces; pc += KTH) {
+                const int g = pc / PPR, j0 = 4 * (pc % PPR);
+                const u32x4 v4 = rowk[pc];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    uint32_t rank;
+                    if (kept_slot(g, (uint32_t)(j0 + x), rank)) f(order_key(__uint_as_float(v4[x] & 0xFFFFFE00u)));
+                }
+            }
+        };
+        uint32_t gmin_n = 0, gmax = 0;
+        each_kept([&](uint32_t key) {
+            gmin_n = max(gmin_n, ~key);
+            gmax = max(gmax, key);
+        });
+        gmin_n = block_max(gmin_n, L.wmax);
+        gmax = block_max(gmax, L.wmax);
+        const uint32_t gmin = ~gmin_n, gspan = gmax - gmin;
+        const uint32_t gwidth = gspan == 0u ? 0u : 32u - (uint32_t)__clz(gspan);
+        uint32_t xrel, xrem;
+        select_rank(L, [&](auto&& f) { each_kept([&](uint32_t key) { f(key - gmin); }); }, gwidth,
+                    (uint32_t)(SKC - 256), xrel, xrem);
+        xkey = xrel + gmin;
+        // the region owners count and place their words at or above xkey,
+        // reading the region twice in 16-byte pieces
+        auto region_pass = [&](auto&& f) {
+#pragma unroll 1
+            for (int i = 0; i < PPR; ++i) {
+                const u32x4 v4 = rowk[tid * PPR + i];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    uint32_t rank;
+                    const uint32_t v = v4[x];
+                    if (kept_slot(tid, (uint32_t)(4 * i + x), rank) &&
+                        order_key(__uint_as_float(v & 0xFFFFFE00u)) >= xkey)
+                        f(v);
+                }
+            }
+        };
+        uint32_t nk = 0;
+        if (mine) region_pass([&](uint32_t) { ++nk; });
+        uint32_t total2;
+        const uint32_t first = block_excl_scan(nk, L.wsum, &total2);
+        if (total2 > (uint32_t)SKC) return direct();  // ties at xkey
+        if (mine) {
+            uint32_t n = first;
+            region_pass([&](uint32_t v) {
+                L.kw[n++] = v;
+                take(v);
+            });
+        }
+        __syncthreads();  // every thread has read rc0 / rcount of the untrimmed regions
+        if (mine) {
+            L.rfirst[tid] = first;
+            L.rcount[tid] = nk;
+        }
+        total = total2;
     }
     for (int i = tid; i < d; i += KTH) {
         const float x = __uint_as_float((uint32_t)qi[(int64_t)r * d + i] << 16);
@@ -1202,6 +1280,13 @@ stream_select_kernel(const uint16_t* __restrict__ qi, const uint16_t* __restrict
     const float marg = bmax + (fabsf(ak) + bmax) * 0x1p-21f;
     const float hi_e = ak + marg, lo_e = ak - marg;
     if (!(lo_e >= key_float(lo_r))) return direct();  // fewer than k provably reach LO
+    if (xkey != 0u) {
+        // a word left out has a stored score below xf, so a chain score below
+        // xf + bmax: that must lie at or below the bracket of the k-th
+        const float xf = key_float(xkey);
+        const float xe = xf + bmax + (fabsf(xf) + bmax) * 0x1p-21f;
+        if (!(xe <= lo_e)) return direct();
+    }
     // ---- sure-in to the bitmap; the ambiguous ones scored on the chain ----
     __syncthreads();  // every thread has read the rank out of L.state / L.hist
     zero_words(L.sel, KWORDS);

@@ -129,6 +129,76 @@ def test_streaming_topk_special_values(kind):
     np.testing.assert_array_equal(idx.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("n_kv,k", [(65536, 2048), (20000, 1000)])
+def test_streaming_topk_ties_at_kth(n_kv, k):
+    """Exact ties straddling the k-th score on the streaming path itself: the key
+    at rank k of each query row is copied to a few positions before and after it,
+    so several candidates share the k-th score and only the lowest positions among
+    them may be taken. Random keys otherwise, so the row is settled by the bracket
+    and the tie rule of the select decides (not the direct fallback)."""
+    rng = np.random.default_rng(n_kv + 3 * k)
+    n_q = 4
+    qf = rng.standard_normal((n_q, 64)).astype(np.float32)
+    kf = rng.standard_normal((n_kv, 64)).astype(np.float32)
+    qi, ki = W.f32_to_bf16_bits(qf), W.f32_to_bf16_bits(kf)
+    off = n_kv - n_q
+    base = oracle.indexer_scores(qi, ki, off)
+    used = np.zeros(n_kv, bool)  # k-th keys and their copies stay as placed
+    for row in range(n_q):
+        order = np.argsort(-base[row, : off + row + 1], kind="stable")
+        kth = int(order[k - 1])
+        used[kth] = True
+        free = np.setdiff1d(np.nonzero(~used[: off + 1])[0], order[:k + 64])
+        dst = rng.choice(free, 5, replace=False)
+        ki[dst] = ki[kth]
+        used[dst] = True
+    print(f"streaming top-k ties at k n_kv={n_kv} k={k}", flush=True)
+    idx, _ = sa.indexer_topk(to_dev_bf16(qi), to_dev_bf16(ki), off, k)
+    scores = oracle.indexer_scores(qi, ki, off)
+    want = oracle.topk_rows(scores, np.arange(n_q) + off + 1, k)
+    # the copies tie with the k-th score of their row (a later row's copies can
+    # shift an earlier row's rank, so not necessarily in every row)
+    tied = 0
+    for row in range(n_q):
+        kth_score = np.sort(scores[row, : off + row + 1])[::-1][k - 1]
+        tied += int((scores[row, : off + row + 1] == kth_score).sum() >= 2)
+    assert tied >= n_q - 1
+    np.testing.assert_array_equal(idx.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("scale", [0.88, 0.9])
+def test_streaming_topk_rows_past_the_kept_cap(scale):
+    """Rows that keep more candidates than the select holds at once: the sampled
+    key rows (the first 64 of every 2,048) are scaled down, so the sample's upper
+    quantile, and with it the threshold, sits lower and about 4,900 to 5,600
+    candidates pass the filter, past the 5,120 the select loads. Such a row is
+    trimmed to its largest kept scores before the selection; the result must
+    still equal the oracle's top-k."""
+    n_kv, k, n_q = 65536, 2048, 4
+    rng = np.random.default_rng(7)
+    qf = rng.standard_normal((n_q, 64)).astype(np.float32)
+    kf = rng.standard_normal((n_kv, 64)).astype(np.float32)
+    sampled = (np.arange(n_kv) % 2048) < 64
+    kf[sampled] *= np.float32(scale)
+    qi, ki = W.f32_to_bf16_bits(qf), W.f32_to_bf16_bits(kf)
+    off = n_kv - n_q
+    scores = oracle.indexer_scores(qi, ki, off)
+    # the setup does what it says: rows past 5,120 kept at the sample threshold
+    over = 0
+    for row in range(n_q):
+        nc = off + row + 1
+        srow = scores[row, :nc]
+        samp = srow[sampled[:nc]]
+        rho = k * samp.size / nc
+        lo = np.sort(samp)[::-1][int(np.ceil(rho + 6 * np.sqrt(rho) + 8)) - 1]
+        over += int((srow >= lo).sum() > 5120)
+    assert over >= 2
+    print(f"streaming top-k past the kept cap, scale {scale}", flush=True)
+    idx, _ = sa.indexer_topk(to_dev_bf16(qi), to_dev_bf16(ki), off, k)
+    want = oracle.topk_rows(scores, np.arange(n_q) + off + 1, k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), want)
+
+
 def test_streaming_topk_reused_workspace_and_short_rows():
     """Rows from fewer candidates than k (padding) up to the whole key range in
     one call, and a workspace reused by a second, smaller call."""
