@@ -26,8 +26,9 @@
 //     and transposed) and V in LDS, double-buffered, the next tile's loads in
 //     flight while the current one is computed, one barrier per step.  It
 //     also forms D = rowsum(dO * O) for its queries.
-//   * bwd_dkdv_kernel: a wave owns 32 keys (K and V in registers) and walks
-//     the query tiles whose lists hold its key block (the lists transposed by
+//   * bwd_dkdv_kernel: two waves own each 32 keys (K, and V for dP, in
+//     registers), one accumulating dV and one dK, and walk the query tiles
+//     whose lists hold their key block (the lists transposed by
 //     bwd_transpose_kernel), staging Q and dO the same way.
 //   * Work items start longest list first (bwd_order_kernel), so that key
 //     blocks every query sees (attention sinks, global tokens) do not finish
@@ -358,10 +359,14 @@ bwd_dq_kernel(BwdParams a)
 }
 
 template <int D, int BQ, int BK>
-__global__ void __launch_bounds__(BK * 2, 1)
+__global__ void __launch_bounds__(BK * 4, 1)
 bwd_dkdv_kernel(BwdParams a)
 {
-    constexpr int NT = BK * 2, NW = BK / 32, NDC = D / 16, NDB = D / 32, RS = D + 8, SUB = BQ / 32;
+    // Two waves per 32-key group: the first BK/32 waves accumulate dV, the
+    // others dK.  Both form S; only the dK waves form dP.  Each wave then holds
+    // one 32 x D accumulator (64 registers a lane), so two waves fit per SIMD
+    // and one wave's vector work runs beside the other's matrix instructions.
+    constexpr int NT = BK * 4, NW = BK / 32, NDC = D / 16, NDB = D / 32, RS = D + 8, SUB = BQ / 32;
     using QStage = Stage32<D, NT, true>;
     __shared__ __attribute__((aligned(16))) uint16_t q_rm[2][32 * RS];
     __shared__ __attribute__((aligned(16))) uint16_t q_tr[2][D * kTS];
@@ -371,6 +376,8 @@ bwd_dkdv_kernel(BwdParams a)
     __shared__ __attribute__((aligned(16))) float dsum_s[2][32];
     __shared__ __attribute__((aligned(16))) uint32_t mw_s[2][NW][32];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
+    const int grp = w % NW;          // the wave's 32 keys
+    const bool dk_wave = w >= NW;    // wave-uniform role
     const int BH = a.batch * a.heads;
     int bh, kb;
     int64_t lrow;
@@ -384,36 +391,29 @@ bwd_dkdv_kernel(BwdParams a)
         kb = a.order_k[blockIdx.x / (unsigned)BH];
         lrow = kb;
     }
-    const int kbase = kb * BK + 32 * w;  // this wave's keys
-    const int kv = kbase + l32;          // this lane's key row
+    const int kbase = kb * BK + 32 * grp;  // this wave's keys
+    const int kv = kbase + l32;            // this lane's key row
     const bool k_ok = kv < a.n_kv;
     const int64_t krow = (int64_t)bh * a.n_kv + kv;
-    // B operands K^T and V^T: lane holds key row kv, dims 16s + 8hh .. + 7
-    bf16x8 kop[NDC], vop[NDC];
+    // B operands K^T (and V^T in the dK waves): lane holds key row kv, dims 16s + 8hh .. + 7
+    auto load_op = [&](const uint16_t* src, bf16x8* op) {
 #pragma unroll
-    for (int s = 0; s < NDC; ++s) {
-        u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-        if (k_ok) {
-            x = *reinterpret_cast<const u32x4*>(a.k + krow * D + 16 * s + 8 * hh);
-            y = *reinterpret_cast<const u32x4*>(a.v + krow * D + 16 * s + 8 * hh);
+        for (int s = 0; s < NDC; ++s) {
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (k_ok) x = *reinterpret_cast<const u32x4*>(src + krow * D + 16 * s + 8 * hh);
+            op[s] = __builtin_bit_cast(bf16x8, x);
         }
-        kop[s] = __builtin_bit_cast(bf16x8, x);
-        vop[s] = __builtin_bit_cast(bf16x8, y);
-    }
+    };
     // zero accumulators made by a matrix instruction (0 * 0 + 0), so that they
     // are born in the registers the loop's matrix instructions accumulate in
-    f32x16 dk[NDB], dv[NDB];
-    {
+    auto zero_acc = [&](f32x16* acc) {
         const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
         f32x16 zacc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) zacc[i] = 0.f;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, zacc, 0, 0, 0);
-            dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, zacc, 0, 0, 0);
-        }
-    }
+        for (int db = 0; db < NDB; ++db) acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, zacc, 0, 0, 0);
+    };
 
     const int cnt = max(0, min(a.q_count[lrow], a.nqb));
     const int nsteps = cnt * SUB;
@@ -446,7 +446,7 @@ bwd_dkdv_kernel(BwdParams a)
             f.dsum = qr < a.n_q ? dsg[qr] : 0.f;
         }
         f.mword = 0u;
-        if (prt[s / SUB] != 0) {
+        if (!dk_wave && prt[s / SUB] != 0) {
             // bit l of word r: key kbase + l is allowed for query q0 + r
             const int qr = q0 + l32;
             RowCtx rc;
@@ -461,14 +461,10 @@ bwd_dkdv_kernel(BwdParams a)
             lse_s[buf][tid] = f.lse;
             dsum_s[buf][tid] = f.dsum;
         }
-        if (prt[s / SUB] != 0 && hh == 0) mw_s[buf][w][l32] = f.mword;
+        if (!dk_wave && prt[s / SUB] != 0 && hh == 0) mw_s[buf][grp][l32] = f.mword;
     };
-    // one step on the data in LDS buffer b.  Every step runs the same
-    // straight-line body (no step is skipped), so the dK and dV accumulators
-    // stay in the matrix unit's registers across the loop.
-    auto compute = [&](int s, int b) {
-        // S = Q K^T and dP = dO V^T: lane = key, element i = query 8(i/4) + 4hh + i%4
-        f32x16 sv, dp;
+    // S = Q K^T (and dP = dO V^T): lane = key, element i = query 8(i/4) + 4hh + i%4
+    auto scores = [&](int b, const bf16x8* kop, const bf16x8* vop, f32x16& sv, f32x16& dp, bool with_dp) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) sv[i] = dp[i] = 0.f;
         const uint16_t* qr = q_rm[b] + l32 * RS + 8 * hh;
@@ -477,7 +473,7 @@ bwd_dkdv_kernel(BwdParams a)
         bf16x8 qa[3], ga[3];
         auto ld_a = [&](int slot, int c) {
             qa[slot] = lds8(qr + 16 * c);
-            ga[slot] = lds8(gr + 16 * c);
+            if (with_dp) ga[slot] = lds8(gr + 16 * c);
         };
         ld_a(0, 0);
         ld_a(1, 1);
@@ -485,84 +481,115 @@ bwd_dkdv_kernel(BwdParams a)
         for (int c = 0; c < NDC; ++c) {
             if (c + 2 < NDC) ld_a((c + 2) % 3, c + 2);
             sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[c % 3], kop[c], sv, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[c % 3], vop[c], dp, 0, 0, 0);
+            if (with_dp) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[c % 3], vop[c], dp, 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // the first B operands of dV / dK land while the softmax runs;
-        // step it = ks * NDB + db reads rows 16ks + 4hh.. of dim 32db + l32
-        bf16x8 gb[3], qb2[3];
+    };
+    // acc (keys x d) += X^T (keys x queries) Y with X from the softmax and Y
+    // read transposed from LDS; step it = ks * NDB + db reads rows 16ks + 4hh..
+    // of dim 32db + l32
+    auto accumulate = [&](const uint16_t* ytr, const f32x16& x, f32x16* acc) {
+        bf16x8 yb[3];
         auto ld_b = [&](int slot, int it) {
             const int ks = it / NDB, dim = 32 * (it % NDB) + l32;
-            gb[slot] = tr_op(g_tr[b], dim, 16 * ks + 4 * hh);
-            qb2[slot] = tr_op(q_tr[b], dim, 16 * ks + 4 * hh);
+            yb[slot] = tr_op(ytr, dim, 16 * ks + 4 * hh);
         };
         ld_b(0, 0);
         ld_b(1, 1);
+        const bf16x8 xa[2] = {pack8(x, 0), pack8(x, 8)};
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int it = 0; it < 2 * NDB; ++it) {
+            if (it + 2 < 2 * NDB) ld_b((it + 2) % 3, it + 2);
+            const int ks = it / NDB, db = it % NDB;
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[ks], yb[it % 3], acc[db], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // P (and dS = P (dP - D)) of one step
+    auto softmax = [&](int s, int b, const f32x16& sv, const f32x16& dp, f32x16& pv, f32x16& ds, bool with_ds) {
         const bool masked = prt[s / SUB] != 0;
-        f32x16 pv, ds;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[b][8 * m + 4 * hh]);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dsum_s[b][8 * m + 4 * hh]);
+            f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
+            if (with_ds) d4 = *reinterpret_cast<const f32x4*>(&dsum_s[b][8 * m + 4 * hh]);
             u32x4 w4 = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
-            if (masked) w4 = *reinterpret_cast<const u32x4*>(&mw_s[b][w][8 * m + 4 * hh]);
+            if (masked) w4 = *reinterpret_cast<const u32x4*>(&mw_s[b][grp][8 * m + 4 * hh]);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int i = 4 * m + c;
                 const bool ok = (w4[c] >> l32) & 1u;
                 const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], a.scale_log2, -l4[c])) : 0.f;
                 pv[i] = p;
-                ds[i] = p * (dp[i] - d4[c]);
+                if (with_ds) ds[i] = p * (dp[i] - d4[c]);
             }
-        }
-        // dV (keys x d) += P^T (keys x queries) dO; dK += dS^T Q
-        const bf16x8 pa[2] = {pack8(pv, 0), pack8(pv, 8)};
-        const bf16x8 sa[2] = {pack8(ds, 0), pack8(ds, 8)};
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int it = 0; it < 2 * NDB; ++it) {
-            if (it + 2 < 2 * NDB) ld_b((it + 2) % 3, it + 2);
-            const int ks = it / NDB, db = it % NDB;
-            dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], gb[it % 3], dv[db], 0, 0, 0);
-            dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[ks], qb2[it % 3], dk[db], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // Two register sets alternate, so the loop is unrolled by two and names
-    // them statically: at step s, set s%2 (whose data went to LDS last step)
-    // takes the loads of step s+2 and set (s+1)%2 goes to LDS buffer (s+1)%2.
-    Fetched f0, f1;
-    if (nsteps > 0) {
-        fetch(f0, 0);
-        put(f0, 0, 0);
-    }
-    if (nsteps > 1) fetch(f1, 1);
-    __syncthreads();
-    for (int s0 = 0; s0 < nsteps; s0 += 2) {
-        if (s0 + 2 < nsteps) fetch(f0, s0 + 2);
-        compute(s0, 0);
-        if (s0 + 1 < nsteps) put(f1, s0 + 1, 1);
-        __syncthreads();
-        if (s0 + 1 < nsteps) {
-            if (s0 + 3 < nsteps) fetch(f1, s0 + 3);
-            compute(s0 + 1, 1);
-            if (s0 + 2 < nsteps) put(f0, s0 + 2, 0);
-            __syncthreads();
+    // The step loop, the same straight-line body at every step (no step is
+    // skipped), so the accumulators stay in the matrix unit's registers.  Two
+    // register sets alternate, so the loop is unrolled by two and names them
+    // statically: at step s, set s%2 (whose data went to LDS last step) takes
+    // the loads of step s+2 and set (s+1)%2 goes to LDS buffer (s+1)%2.
+    auto run = [&](auto&& compute) {
+        Fetched f0, f1;
+        if (nsteps > 0) {
+            fetch(f0, 0);
+            put(f0, 0, 0);
         }
-    }
-    // element (db, i): key row 8(i/4) + 4hh + i%4 of the wave, dim 32 db + l32
-    float* dkg = a.dk + (int64_t)bh * a.n_kv * D;
-    float* dvg = a.dv + (int64_t)bh * a.n_kv * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int kr = kbase + 8 * (i >> 2) + 4 * hh + (i & 3);
-            if (kr < a.n_kv) {
-                dkg[(int64_t)kr * D + 32 * db + l32] = dk[db][i] * a.scale;
-                dvg[(int64_t)kr * D + 32 * db + l32] = dv[db][i];
+        if (nsteps > 1) fetch(f1, 1);
+        __syncthreads();
+        for (int s0 = 0; s0 < nsteps; s0 += 2) {
+            if (s0 + 2 < nsteps) fetch(f0, s0 + 2);
+            compute(s0, 0);
+            if (s0 + 1 < nsteps) put(f1, s0 + 1, 1);
+            __syncthreads();
+            if (s0 + 1 < nsteps) {
+                if (s0 + 3 < nsteps) fetch(f1, s0 + 3);
+                compute(s0 + 1, 1);
+                if (s0 + 2 < nsteps) put(f0, s0 + 2, 0);
+                __syncthreads();
             }
         }
+    };
+    // element (db, i): key row 8(i/4) + 4hh + i%4 of the wave, dim 32 db + l32
+    auto write = [&](float* dst, const f32x16* acc, float mul) {
+        float* g = dst + (int64_t)bh * a.n_kv * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int kr = kbase + 8 * (i >> 2) + 4 * hh + (i & 3);
+                if (kr < a.n_kv) g[(int64_t)kr * D + 32 * db + l32] = acc[db][i] * mul;
+            }
+    };
+    bf16x8 kop[NDC];
+    load_op(a.k, kop);
+    if (!dk_wave) {
+        // dV += P^T dO
+        f32x16 dv[NDB];
+        zero_acc(dv);
+        run([&](int s, int b) {
+            f32x16 sv, dp, pv, ds;
+            scores(b, kop, kop, sv, dp, false);
+            softmax(s, b, sv, dp, pv, ds, false);
+            accumulate(g_tr[b], pv, dv);
+        });
+        write(a.dv, dv, 1.f);
+    } else {
+        // dK += dS^T Q
+        bf16x8 vop[NDC];
+        load_op(a.v, vop);
+        f32x16 dk[NDB];
+        zero_acc(dk);
+        run([&](int s, int b) {
+            f32x16 sv, dp, pv, ds;
+            scores(b, kop, vop, sv, dp, true);
+            softmax(s, b, sv, dp, pv, ds, true);
+            accumulate(q_tr[b], ds, dk);
+        });
+        write(a.dk, dk, a.scale);
+    }
 }
 
 template <int D, int BQ, int BK>
@@ -572,7 +599,7 @@ hipError_t launch_bwd_t(const BwdParams& a, hipStream_t stream)
     if (bh * a.nqb > 0)
         hipLaunchKernelGGL((bwd_dq_kernel<D, BQ, BK>), dim3((unsigned)(bh * a.nqb)), dim3(BQ * 2), 0, stream, a);
     if (bh * a.nkb > 0)
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, BQ, BK>), dim3((unsigned)(bh * a.nkb)), dim3(BK * 2), 0, stream, a);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, BQ, BK>), dim3((unsigned)(bh * a.nkb)), dim3(BK * 4), 0, stream, a);
     return hipGetLastError();
 }
 
