@@ -282,33 +282,44 @@ bwd_dq_kernel(BwdParams a)
     const uint8_t* prt = a.kv_partial + lrow * a.nkb;
     const uint16_t* kg = a.k + (int64_t)bh * a.n_kv * D;
     const uint16_t* vg = a.v + (int64_t)bh * a.n_kv * D;
+    // A list of up to 64 entries sits in lane registers (lane e: entry e) and
+    // is read with readlane, so a step issues no load before its own.
+    const bool list_regs = cnt <= 64;
+    int l_idx = 0, l_prt = 0;
+    if (list_regs && lane < cnt) {
+        l_idx = idx[lane];
+        l_prt = prt[lane];
+    }
+    auto entry = [&](int e) { return list_regs ? __builtin_amdgcn_readlane(l_idx, e) : idx[e]; };
+    auto partial = [&](int e) { return (list_regs ? __builtin_amdgcn_readlane(l_prt, e) : (int)prt[e]) != 0; };
     // first key of step s, or -1 when the step holds no key
     auto step_k0 = [&](int s) -> int {
-        const int j = idx[s / SUB];
+        const int j = entry(s / SUB);
         if ((unsigned)j >= (unsigned)a.nkb) return -1;
         const int k0 = j * BK + 32 * (s % SUB);
         return k0 < a.n_kv ? k0 : -1;
     };
-    KStage kst;
-    VStage vst;
-    int k0 = -1;
-    if (nsteps > 0) {
-        k0 = step_k0(0);
+    // K and V rows of a step, loaded into registers two steps ahead of their
+    // use and written to LDS one step ahead
+    struct Fetched {
+        KStage k;
+        VStage v;
+    };
+    auto fetch = [&](Fetched& f, int s) {
+        const int k0 = step_k0(s);
         if (k0 >= 0) {
-            kst.load(kg, k0, a.n_kv, tid);
-            vst.load(vg, k0, a.n_kv, tid);
-            kst.store(k_rm[0], k_tr[0], tid);
-            vst.store(v_rm[0], nullptr, tid);
+            f.k.load(kg, k0, a.n_kv, tid);
+            f.v.load(vg, k0, a.n_kv, tid);
         }
-    }
-    __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
-        const int b = s & 1;
-        const int k0n = s + 1 < nsteps ? step_k0(s + 1) : -1;
-        if (k0n >= 0) {
-            kst.load(kg, k0n, a.n_kv, tid);
-            vst.load(vg, k0n, a.n_kv, tid);
+    };
+    auto put = [&](const Fetched& f, int s, int b) {
+        if (step_k0(s) >= 0) {
+            f.k.store(k_rm[b], k_tr[b], tid);
+            f.v.store(v_rm[b], nullptr, tid);
         }
+    };
+    auto compute = [&](int s, int b) {
+        const int k0 = step_k0(s);
         if (k0 >= 0) {
             // S^T = K Q^T and dP^T = V dO^T: lane = query, element i = key 8(i/4) + 4hh + i%4
             f32x16 st, dpt;
@@ -322,7 +333,7 @@ bwd_dq_kernel(BwdParams a)
                 dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds8(vr + 16 * c), gop[c], dpt, 0, 0, 0);
             }
             uint32_t mbits = 0xFFFFFFFFu;
-            if (prt[s / SUB] != 0 || k0 + 32 > a.n_kv) mbits = allowed_bits32(a.pat, rc, k0) >> (4 * hh);
+            if (partial(s / SUB) || k0 + 32 > a.n_kv) mbits = allowed_bits32(a.pat, rc, k0) >> (4 * hh);
             f32x16 ds;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -340,12 +351,41 @@ bwd_dq_kernel(BwdParams a)
                                                                  dq[db], 0, 0, 0);
             }
         }
-        if (k0n >= 0) {
-            kst.store(k_rm[b ^ 1], k_tr[b ^ 1], tid);
-            vst.store(v_rm[b ^ 1], nullptr, tid);
-        }
+    };
+    Fetched f0, f1;
+    if (nsteps > 0) {
+        fetch(f0, 0);
+        put(f0, 0, 0);
+    }
+    if constexpr (KStage::PER == 1 && D == 128) {
+        // Two register sets alternate, so the loop is unrolled by two and
+        // names them statically: at step s, set s%2 (whose data went to LDS
+        // last step) takes the loads of step s+2 and set (s+1)%2 goes to LDS
+        // buffer (s+1)%2.
+        if (nsteps > 1) fetch(f1, 1);
         __syncthreads();
-        k0 = k0n;
+        for (int s0 = 0; s0 < nsteps; s0 += 2) {
+            if (s0 + 2 < nsteps) fetch(f0, s0 + 2);
+            compute(s0, 0);
+            if (s0 + 1 < nsteps) put(f1, s0 + 1, 1);
+            __syncthreads();
+            if (s0 + 1 < nsteps) {
+                if (s0 + 3 < nsteps) fetch(f1, s0 + 3);
+                compute(s0 + 1, 1);
+                if (s0 + 2 < nsteps) put(f0, s0 + 2, 0);
+                __syncthreads();
+            }
+        }
+    } else {
+        // with more rows a thread (64-query blocks), or at head_dim 64 where a
+        // second set would cost a wave of occupancy: one set, one step ahead
+        __syncthreads();
+        for (int s = 0; s < nsteps; ++s) {
+            if (s + 1 < nsteps) fetch(f0, s + 1);
+            compute(s, s & 1);
+            if (s + 1 < nsteps) put(f0, s + 1, (s + 1) & 1);
+            __syncthreads();
+        }
     }
     // dq element (db, i): query row 8(i/4) + 4hh + i%4 of the wave, dim 32 db + l32
     float* dqg = a.dq + (int64_t)bh * a.n_q * D;
@@ -363,18 +403,24 @@ __global__ void __launch_bounds__(BK * 4, 1)
 bwd_dkdv_kernel(BwdParams a)
 {
     // Two waves per 32-key group: the first BK/32 waves accumulate dV, the
-    // others dK.  Both form S; only the dK waves form dP.  Each wave then holds
-    // one 32 x D accumulator (64 registers a lane), so two waves fit per SIMD
-    // and one wave's vector work runs beside the other's matrix instructions.
+    // others dK.  A dV wave forms S and P of step s, leaves P in LDS and adds
+    // P^T dO; the dK wave of its group runs one step behind, forming dP of
+    // step s - 1, dS from the P left there, and adding dS^T Q.  Each wave
+    // holds one 32 x D accumulator (64 registers a lane), so two waves fit
+    // per SIMD and one wave's vector work runs beside the other's matrix
+    // instructions.  The staged tiles of three steps are live at once (the
+    // dK waves' step, the dV waves' step, the next step being written).
     constexpr int NT = BK * 4, NW = BK / 32, NDC = D / 16, NDB = D / 32, RS = D + 8, SUB = BQ / 32;
-    using QStage = Stage32<D, NT, true>;
-    __shared__ __attribute__((aligned(16))) uint16_t q_rm[2][32 * RS];
-    __shared__ __attribute__((aligned(16))) uint16_t q_tr[2][D * kTS];
-    __shared__ __attribute__((aligned(16))) uint16_t g_rm[2][32 * RS];
-    __shared__ __attribute__((aligned(16))) uint16_t g_tr[2][D * kTS];
-    __shared__ __attribute__((aligned(16))) float lse_s[2][32];
-    __shared__ __attribute__((aligned(16))) float dsum_s[2][32];
-    __shared__ __attribute__((aligned(16))) uint32_t mw_s[2][NW][32];
+    // the dV waves stage the Q tile, the dK waves the dO tile
+    using QStage = Stage32<D, NT / 2, true>;
+    __shared__ __attribute__((aligned(16))) uint16_t q_rm[3][32 * RS];
+    __shared__ __attribute__((aligned(16))) uint16_t q_tr[3][D * kTS];
+    __shared__ __attribute__((aligned(16))) uint16_t g_rm[3][32 * RS];
+    __shared__ __attribute__((aligned(16))) uint16_t g_tr[3][D * kTS];
+    __shared__ __attribute__((aligned(16))) float lse_s[3][32];
+    __shared__ __attribute__((aligned(16))) float dsum_s[3][32];
+    __shared__ __attribute__((aligned(16))) uint32_t mw_s[3][NW][32];
+    __shared__ __attribute__((aligned(16))) f32x4 p_s[2][NW][4][64];  // P of a step: [group][i/4][lane]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
     const int grp = w % NW;          // the wave's 32 keys
     const bool dk_wave = w >= NW;    // wave-uniform role
@@ -419,34 +465,49 @@ bwd_dkdv_kernel(BwdParams a)
     const int nsteps = cnt * SUB;
     const int32_t* idx = a.q_index + lrow * a.nqb;
     const uint8_t* prt = a.q_partial + lrow * a.nqb;
+    // A list of up to 64 entries sits in lane registers (lane e: entry e) and
+    // is read with readlane, so a step issues no load before its own.
+    const bool list_regs = cnt <= 64;
+    int l_idx = 0, l_prt = 0;
+    if (list_regs && lane < cnt) {
+        l_idx = idx[lane];
+        l_prt = prt[lane];
+    }
+    auto entry = [&](int e) { return list_regs ? __builtin_amdgcn_readlane(l_idx, e) : idx[e]; };
+    auto partial = [&](int e) { return (list_regs ? __builtin_amdgcn_readlane(l_prt, e) : (int)prt[e]) != 0; };
     const uint16_t* qg = a.q + (int64_t)bh * a.n_q * D;
     const uint16_t* gg = a.dout + (int64_t)bh * a.n_q * D;
     const float* lseg = a.lse + (int64_t)bh * a.n_q;
     const float* dsg = a.dsum + (int64_t)bh * a.n_q;
     // first query of step s; a step past the last query (the ragged end of the
     // last block) stages zero rows with LSE = +inf, so it adds nothing
-    auto step_q0 = [&](int s) -> int { return idx[s / SUB] * BQ + 32 * (s % SUB); };
+    auto step_q0 = [&](int s) -> int { return entry(s / SUB) * BQ + 32 * (s % SUB); };
     // Staged data of one step (rows, LSE, D, mask words), loaded into
     // registers two steps ahead of its use and written to LDS one step ahead.
+    // Nothing loaded is used before the step is written to LDS (a use would
+    // wait for every load in flight).
     struct Fetched {
-        QStage q, g;
+        QStage x;  // Q rows (dV waves) or dO rows (dK waves)
         float lse, dsum;
         uint32_t mword;
     };
+    const int stid = tid % (NT / 2);
     auto fetch = [&](Fetched& f, int s) {
         const int q0 = step_q0(s);
-        f.q.load(qg, q0, a.n_q, tid);
-        f.g.load(gg, q0, a.n_q, tid);
+        f.x.load(dk_wave ? gg : qg, q0, a.n_q, stid);
         f.lse = INFINITY;
         f.dsum = 0.f;
-        if (tid < 32) {
-            const int qr = q0 + tid;
-            const float l = qr < a.n_q ? lseg[qr] : INFINITY;
-            f.lse = l == -INFINITY ? INFINITY : l * kLog2e;
-            f.dsum = qr < a.n_q ? dsg[qr] : 0.f;
+        if ((unsigned)(tid - NT / 2) < 32u) {
+            // rows past n_q read the last row's values; put() gives them
+            // LSE = +inf (P = 0), so their D never counts
+            const int qr = min(q0 + (tid - NT / 2), a.n_q - 1);
+            f.lse = lseg[qr];
+            f.dsum = dsg[qr];
         }
         f.mword = 0u;
-        if (!dk_wave && prt[s / SUB] != 0) {
+        // the mask words and the row values come from the dK waves, whose
+        // step is the shorter one
+        if (dk_wave && partial(s / SUB)) {
             // bit l of word r: key kbase + l is allowed for query q0 + r
             const int qr = q0 + l32;
             RowCtx rc;
@@ -455,33 +516,31 @@ bwd_dkdv_kernel(BwdParams a)
         }
     };
     auto put = [&](const Fetched& f, int s, int buf) {
-        f.q.store(q_rm[buf], q_tr[buf], tid);
-        f.g.store(g_rm[buf], g_tr[buf], tid);
-        if (tid < 32) {
-            lse_s[buf][tid] = f.lse;
-            dsum_s[buf][tid] = f.dsum;
+        if (dk_wave) f.x.store(g_rm[buf], g_tr[buf], stid);
+        else f.x.store(q_rm[buf], q_tr[buf], stid);
+        if ((unsigned)(tid - NT / 2) < 32u) {
+            // a row without keys (LSE = -inf) or past n_q has no pair
+            const int r = tid - NT / 2;
+            const bool row_ok = step_q0(s) + r < a.n_q;
+            lse_s[buf][r] = (!row_ok || f.lse == -INFINITY) ? INFINITY : f.lse * kLog2e;
+            dsum_s[buf][r] = f.dsum;
         }
-        if (!dk_wave && prt[s / SUB] != 0 && hh == 0) mw_s[buf][grp][l32] = f.mword;
+        if (dk_wave && partial(s / SUB) && hh == 0) mw_s[buf][grp][l32] = f.mword;
     };
-    // S = Q K^T (and dP = dO V^T): lane = key, element i = query 8(i/4) + 4hh + i%4
-    auto scores = [&](int b, const bf16x8* kop, const bf16x8* vop, f32x16& sv, f32x16& dp, bool with_dp) {
+    // X Y^T for row-major X (32 rows in LDS) and Y in registers: S = Q K^T,
+    // dP = dO V^T; lane = key, element i = query 8(i/4) + 4hh + i%4
+    auto product = [&](const uint16_t* xrm, const bf16x8* yop, f32x16& acc) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sv[i] = dp[i] = 0.f;
-        const uint16_t* qr = q_rm[b] + l32 * RS + 8 * hh;
-        const uint16_t* gr = g_rm[b] + l32 * RS + 8 * hh;
+        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+        const uint16_t* xr = xrm + l32 * RS + 8 * hh;
         // LDS operands are requested two k-steps ahead (a ring of three)
-        bf16x8 qa[3], ga[3];
-        auto ld_a = [&](int slot, int c) {
-            qa[slot] = lds8(qr + 16 * c);
-            if (with_dp) ga[slot] = lds8(gr + 16 * c);
-        };
-        ld_a(0, 0);
-        ld_a(1, 1);
+        bf16x8 xa[3];
+        xa[0] = lds8(xr);
+        xa[1] = lds8(xr + 16);
 #pragma unroll
         for (int c = 0; c < NDC; ++c) {
-            if (c + 2 < NDC) ld_a((c + 2) % 3, c + 2);
-            sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[c % 3], kop[c], sv, 0, 0, 0);
-            if (with_dp) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[c % 3], vop[c], dp, 0, 0, 0);
+            if (c + 2 < NDC) xa[(c + 2) % 3] = lds8(xr + 16 * (c + 2));
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[c % 3], yop[c], acc, 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -506,31 +565,27 @@ bwd_dkdv_kernel(BwdParams a)
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // P (and dS = P (dP - D)) of one step
-    auto softmax = [&](int s, int b, const f32x16& sv, const f32x16& dp, f32x16& pv, f32x16& ds, bool with_ds) {
-        const bool masked = prt[s / SUB] != 0;
+    // P of one step (masked keys 0)
+    auto softmax = [&](int s, int b, const f32x16& sv, f32x16& pv) {
+        const bool masked = partial(s / SUB);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[b][8 * m + 4 * hh]);
-            f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
-            if (with_ds) d4 = *reinterpret_cast<const f32x4*>(&dsum_s[b][8 * m + 4 * hh]);
             u32x4 w4 = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
             if (masked) w4 = *reinterpret_cast<const u32x4*>(&mw_s[b][grp][8 * m + 4 * hh]);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int i = 4 * m + c;
                 const bool ok = (w4[c] >> l32) & 1u;
-                const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], a.scale_log2, -l4[c])) : 0.f;
-                pv[i] = p;
-                if (with_ds) ds[i] = p * (dp[i] - d4[c]);
+                pv[i] = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], a.scale_log2, -l4[c])) : 0.f;
             }
         }
     };
-    // The step loop, the same straight-line body at every step (no step is
-    // skipped), so the accumulators stay in the matrix unit's registers.  Two
+    // Iteration j (0 .. nsteps) computes step j in the dV waves and step
+    // j - 1 in the dK waves; step s is staged in LDS buffer s % 3.  Two
     // register sets alternate, so the loop is unrolled by two and names them
-    // statically: at step s, set s%2 (whose data went to LDS last step) takes
-    // the loads of step s+2 and set (s+1)%2 goes to LDS buffer (s+1)%2.
+    // statically: at iteration j, set j%2 (whose data went to LDS last
+    // iteration) takes the loads of step j+2 and set (j+1)%2 goes to LDS.
     auto run = [&](auto&& compute) {
         Fetched f0, f1;
         if (nsteps > 0) {
@@ -539,15 +594,15 @@ bwd_dkdv_kernel(BwdParams a)
         }
         if (nsteps > 1) fetch(f1, 1);
         __syncthreads();
-        for (int s0 = 0; s0 < nsteps; s0 += 2) {
-            if (s0 + 2 < nsteps) fetch(f0, s0 + 2);
-            compute(s0, 0);
-            if (s0 + 1 < nsteps) put(f1, s0 + 1, 1);
+        for (int j0 = 0; j0 <= nsteps; j0 += 2) {
+            if (j0 + 2 < nsteps) fetch(f0, j0 + 2);
+            compute(j0);
+            if (j0 + 1 < nsteps) put(f1, j0 + 1, (j0 + 1) % 3);
             __syncthreads();
-            if (s0 + 1 < nsteps) {
-                if (s0 + 3 < nsteps) fetch(f1, s0 + 3);
-                compute(s0 + 1, 1);
-                if (s0 + 2 < nsteps) put(f0, s0 + 2, 0);
+            if (j0 + 1 <= nsteps) {
+                if (j0 + 3 < nsteps) fetch(f1, j0 + 3);
+                compute(j0 + 1);
+                if (j0 + 2 < nsteps) put(f0, j0 + 2, (j0 + 2) % 3);
                 __syncthreads();
             }
         }
@@ -563,29 +618,44 @@ bwd_dkdv_kernel(BwdParams a)
                 if (kr < a.n_kv) g[(int64_t)kr * D + 32 * db + l32] = acc[db][i] * mul;
             }
     };
-    bf16x8 kop[NDC];
-    load_op(a.k, kop);
+    f32x4* pmine = &p_s[0][grp][0][lane];  // this lane's P of the group, buffer 0
+    constexpr int PB = NW * 4 * 64;          // f32x4 per P buffer
     if (!dk_wave) {
-        // dV += P^T dO
+        // S, P of step j; P to LDS; dV += P^T dO
+        bf16x8 kop[NDC];
+        load_op(a.k, kop);
         f32x16 dv[NDB];
         zero_acc(dv);
-        run([&](int s, int b) {
-            f32x16 sv, dp, pv, ds;
-            scores(b, kop, kop, sv, dp, false);
-            softmax(s, b, sv, dp, pv, ds, false);
+        run([&](int j) {
+            if (j >= nsteps) return;
+            const int b = j % 3;
+            f32x16 sv, pv;
+            product(q_rm[b], kop, sv);
+            softmax(j, b, sv, pv);
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                pmine[(j & 1) * PB + 64 * m] = f32x4{pv[4 * m], pv[4 * m + 1], pv[4 * m + 2], pv[4 * m + 3]};
             accumulate(g_tr[b], pv, dv);
         });
         write(a.dv, dv, 1.f);
     } else {
-        // dK += dS^T Q
+        // dP of step j - 1, dS = P (dP - D) with that step's P; dK += dS^T Q
         bf16x8 vop[NDC];
         load_op(a.v, vop);
         f32x16 dk[NDB];
         zero_acc(dk);
-        run([&](int s, int b) {
-            f32x16 sv, dp, pv, ds;
-            scores(b, kop, vop, sv, dp, true);
-            softmax(s, b, sv, dp, pv, ds, true);
+        run([&](int j) {
+            if (j < 1) return;
+            const int s = j - 1, b = s % 3;
+            f32x16 dp, ds;
+            product(g_rm[b], vop, dp);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const f32x4 p4 = pmine[(s & 1) * PB + 64 * m];
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dsum_s[b][8 * m + 4 * hh]);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) ds[4 * m + c] = p4[c] * (dp[4 * m + c] - d4[c]);
+            }
             accumulate(q_tr[b], ds, dk);
         });
         write(a.dk, dk, a.scale);

@@ -48,7 +48,7 @@ def _run(pat, q, k, v, g, bq, bk, heads=None):
     return f(dq), f(dk), f(dv)
 
 
-@pytest.mark.parametrize("d,bq,bk", [(64, 64, 64), (128, 128, 128), (64, 128, 64), (128, 64, 128)])
+@pytest.mark.parametrize("d,bq,bk", [(d, bq, bk) for d in (64, 128) for bq in (64, 128) for bk in (64, 128)])
 def test_bwd_window_sinks_ragged(d, bq, bk):
     rng = np.random.default_rng(d + bq + 2 * bk)
     n_q, n_kv = 333, 301
@@ -74,6 +74,24 @@ def test_bwd_random_patterns(seed):
     rq, rk, rv = oracle.attn_bwd(pat, q, k, v, g)
     for name, a, b in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         _check(name, a, b, f"seed {seed}")
+
+
+def test_bwd_lists_longer_than_64():
+    """Lists of more than 64 entries: 65 blocks of 64, the first 8 rows global (their
+    query block sees every key block) and every row seeing those 8 keys (their key
+    block is seen by every query block), so both kernels read such a list from
+    memory instead of lane registers."""
+    rng = np.random.default_rng(44)
+    n, d, bs = 65 * 64, 64, 64
+    pat = dict(causal=0, window_left=64, window_right=64, global_tokens=8)
+    q, k, v, g = (_rand(rng, 1, 1, n, d) for _ in range(4))
+    bl = sa.build_block_mask(pat, n, n, bs, bs)
+    assert int(bl.kv_count.max()) == 65
+    print("bwd lists longer than 64", flush=True)
+    dq, dk, dv = _run(pat, q, k, v, g, bs, bs)
+    rq, rk, rv = oracle.attn_bwd(pat, q, k, v, g)
+    for name, a, b in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        _check(name, a, b, "long lists")
 
 
 def test_bwd_config1_whole():
