@@ -313,8 +313,8 @@ def _bench_strided(sa, W, np, torch, dev, dev_bf16, reps=10):
         "split_us": round(t["split"] * 1e6, 1),
         "split_tflops_over_live_pairs": round(flop / t["split"] / 1e12, 2),
         "split_note": "one sa_attn_fwd call (SA_MODE_STRIDED) on a plan built once by sa_attn_strided_plan: "
-                      "64x64 band tiles, causal 64-row tiles per (head, key residue) view and the last row, the "
-                      "later parts merged by log-sum-exp in the kernel epilogue",
+                      "64x64 band tiles, then causal 64-row tiles per (head, key residue) view (residue 0's "
+                      "view also holds the last row), merged by log-sum-exp in the kernel epilogue",
     }
 
 def _bench_bwd(sa, np, torch, dev, cfg, q, k, v, bl, out, lse, live_pairs, live_blocks, reps=20):

@@ -359,8 +359,8 @@ def attn_fwd_strided(q, k, v, pattern, *, softmax_scale: Optional[float] = None,
                      workspace=None):
     """The strided template as disjoint key sets per row (``sa_attn_fwd``, ``SA_MODE_STRIDED``):
     the local band through block lists, the strided keys as causal attention between
-    strided views (one per head and key residue) and the last row, merged by log-sum-exp in
-    the kernels.  q, k, v bfloat16 [B, H, n, d]; ``pattern`` must be the template (causal,
+    strided views (one per head and key residue; residue 0's view also holds the last row),
+    merged by log-sum-exp in the kernel epilogue.  q, k, v bfloat16 [B, H, n, d]; ``pattern`` must be the template (causal,
     window_left = stride - 1, stride_phase = stride - 1, no other term; n a multiple of the
     stride, at least three groups), else the library rejects it.  ``workspace`` is a plan
     from ``strided_plan`` (made for the call when None).  Returns (O float32 [B, H, n, d],

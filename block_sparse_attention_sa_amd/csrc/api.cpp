@@ -119,16 +119,15 @@ int64_t strided_template(const sa_attn_args* a)
     return S;
 }
 
-// Scratch of the strided form: the block lists of its three parts (band on
-// the natural layout; the (n/S - 2)-row residue views against all n/S key
-// groups -- the causal mask drops the groups past each row, and a key range
-// that is a multiple of the sub-tile keeps the copies on the fast path; the
-// last query row, as position n/S - 2 of a causal row over the same n/S
-// groups).
+// Scratch of the strided form: the block lists of its two parts (band on
+// the natural layout; the residue views, n/S - 1 rows (the last of them
+// exists for residue 0 only) against all n/S key groups -- the causal mask
+// drops the groups past each row, and a key range that is a multiple of the
+// sub-tile keeps the copies on the fast path).
 struct StridedLayout {
     struct Lists {
         int64_t n_q, n_kv, nqb, nkb, count, index, partial, live;
-    } band, res, last;
+    } band, res;
     int64_t total;
 };
 constexpr int kStridedBlock = 64;
@@ -151,31 +150,30 @@ StridedLayout strided_layout(int64_t n, int64_t S)
         at = up(l.live + 8);
     };
     lists(L.band, n, n);
-    lists(L.res, G - 2, G);
-    lists(L.last, 1, G);
+    lists(L.res, G - 1, G);
     L.total = at;
     return L;
 }
 
-// SA_MODE_STRIDED: the strided template as three disjoint key sets per
-// query row (the blog "Sparse transformers: how to cut the O(n^2) of
-// attention", section on the main sparsity templates; the masked softmax's
-// log-sum-exp splits over disjoint key sets):
+// SA_MODE_STRIDED: the strided template as two disjoint key sets per query
+// row (the blog "Sparse transformers: how to cut the O(n^2) of attention",
+// section on the main sparsity templates; the masked softmax's log-sum-exp
+// splits over disjoint key sets):
 //   band     kv in [q - (S - 1), q], block lists on the natural layout;
 //   residue  kv = q - (S - 1) - S*m (m >= 1): for each key residue rho the
 //            rows q = (i + 2)*S + rho - 1 against keys j*S + rho, j <= i --
 //            plain causal attention between strided views of the same
-//            tensors (no copy), one view per (head, residue);
-//   last     query row n - 1 (residue 0, one group past the views) against
-//            keys j*S, j <= n/S - 2.
-// The second and third parts are folded into the band's O and LSE in the
-// attention kernel's epilogue.  The block lists of all three (the plan) are
-// built into the workspace by sa_attn_strided_plan.
+//            tensors (no copy), one view per (head, residue).  The views
+//            hold n/S - 2 rows, except residue 0's, whose row n/S - 2 is
+//            query row n - 1.
+// The residue part is folded into the band's O and LSE in the attention
+// kernel's epilogue.  The block lists of both (the plan) are built into the
+// workspace by sa_attn_strided_plan.
 struct StridedParts {
     int64_t S, G;
     StridedLayout W;
-    sa_pattern pat[3];
-    sa::DevPattern dev[3];
+    sa_pattern pat[2];
+    sa::DevPattern dev[2];
 };
 
 sa_status strided_check(const sa_attn_args* a, StridedParts& P)
@@ -196,12 +194,11 @@ sa_status strided_check(const sa_attn_args* a, StridedParts& P)
     const int64_t row_b = 2 * std::max(a->k_strides[2], a->v_strides[2]);
     if ((n + 256 * P.S) * row_b > kI32Max)
         return fail(SA_ERR_UNSUPPORTED, "n_kv times the K/V row stride must stay below 2^31 bytes");
-    const StridedLayout::Lists* ls[3] = {&P.W.band, &P.W.res, &P.W.last};
-    for (int i = 0; i < 3; ++i) P.pat[i] = sa_pattern{};
+    const StridedLayout::Lists* ls[2] = {&P.W.band, &P.W.res};
+    for (int i = 0; i < 2; ++i) P.pat[i] = sa_pattern{};
     P.pat[0].causal = 1; P.pat[0].window_left = P.S - 1; P.pat[0].unit_window = -1;
     P.pat[1].causal = 1; P.pat[1].window_left = P.G; P.pat[1].unit_window = -1;
-    P.pat[2].causal = 1; P.pat[2].window_left = P.G; P.pat[2].unit_window = -1; P.pat[2].q_offset = P.G - 2;
-    for (int i = 0; i < 3; ++i) {
+    for (int i = 0; i < 2; ++i) {
         const sa_status st = make_pattern(&P.pat[i], ls[i]->n_q, ls[i]->n_kv, P.dev[i]);
         if (st != SA_OK) return st;
     }
@@ -214,8 +211,8 @@ sa_status strided_plan(const sa_attn_args* a, hipStream_t s)
     const sa_status st0 = strided_check(a, P);
     if (st0 != SA_OK) return st0;
     uint8_t* ws = (uint8_t*)a->workspace;
-    const StridedLayout::Lists* ls[3] = {&P.W.band, &P.W.res, &P.W.last};
-    for (int i = 0; i < 3; ++i) {
+    const StridedLayout::Lists* ls[2] = {&P.W.band, &P.W.res};
+    for (int i = 0; i < 2; ++i) {
         const sa_status st = launched(sa::launch_block_mask(P.dev[i], (int32_t)ls[i]->n_q, (int32_t)ls[i]->n_kv,
                                                             kStridedBlock, kStridedBlock, (int32_t*)(ws + ls[i]->count),
                                                             (int32_t*)(ws + ls[i]->index), ws + ls[i]->partial,
@@ -267,22 +264,12 @@ sa_status strided_fwd(const sa_attn_args* a, const sa::AttnParams& base, hipStre
         p.lse_sb = n; p.lse_sh = 1; p.lse_sn = S;
         p.batch = (int32_t)H;
         p.heads = (int32_t)S;
-        p.n_q = (int32_t)(G - 2);
+        p.n_q = (int32_t)(G - 1);       // residue 0: its last row is query row n - 1
+        p.n_q_rest = (int32_t)(G - 2);  // residues 1 .. S-1: that row would lie past n - 1
         p.n_kv = (int32_t)G;
         p.merge = 1;
-        sa_status st =
+        const sa_status st =
             launched(sa::launch_attn_blocks(p, (int)a->head_dim, kStridedBlock, kStridedBlock, 1, s), "sa_attn_fwd");
-        if (st != SA_OK) return st;
-        // the last row: position G - 2 of a causal row over the key groups j*S
-        sa::AttnParams l = p;
-        with_lists(l, 2, P.W.last);
-        l.q = base.q + b * a->q_strides[0] + (n - 1) * a->q_strides[2];
-        l.o = (float*)base.o + b * a->o_strides[0] + (n - 1) * a->o_strides[2];
-        l.heads = 1;
-        l.n_q = 1;
-        l.lse = a->lse + b * H * n + (n - 1);
-        l.lse_sb = n; l.lse_sh = 0; l.lse_sn = 0;
-        st = launched(sa::launch_attn_blocks(l, (int)a->head_dim, kStridedBlock, kStridedBlock, 1, s), "sa_attn_fwd");
         if (st != SA_OK) return st;
     }
     return ok();

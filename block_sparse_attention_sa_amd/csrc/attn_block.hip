@@ -177,6 +177,7 @@ attn_block_kernel(AttnParams a)
         bh = j / nrest;
     }
     const int b = bh / a.heads, h = bh % a.heads;
+    const int nq_h = (a.n_q_rest > 0 && h > 0) ? a.n_q_rest : a.n_q;  // rows of this head
 
     const uint16_t* qg = a.q + b * a.q_sb + h * a.q_sh;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + b * a.k_sb + h * a.k_sh, (int64_t)a.n_kv * a.k_sn * 2);
@@ -288,7 +289,7 @@ attn_block_kernel(AttnParams a)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         qrow[nb] = qb * BQ + wave * 32 * NB + nb * 32 + l32;
-        const bool ok = qrow[nb] < a.n_q;
+        const bool ok = qrow[nb] < nq_h;
 #pragma unroll
         for (int dc = 0; dc < NDC; ++dc) {
             u32x4 raw = {0u, 0u, 0u, 0u};
@@ -563,7 +564,7 @@ attn_block_kernel(AttnParams a)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const float l_tot = l_run[nb] + other_half(l_run[nb]);
-        if (qrow[nb] < a.n_q) {
+        if (qrow[nb] < nq_h) {
             float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
             const float lse = l_tot > 0.f ? m_run[nb] * a.scale + logf(l_tot) : -INFINITY;
             const int64_t obase = b * a.o_sb + h * a.o_sh + (int64_t)qrow[nb] * a.o_sn;

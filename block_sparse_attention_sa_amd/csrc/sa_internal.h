@@ -176,6 +176,7 @@ struct AttnParams {
     int64_t lse_sb, lse_sh, lse_sn;  // element strides of LSE (b, h, row)
     int32_t batch, heads, n_q, n_kv;
     int32_t merge;      // block mode, float32 O: fold into the O and LSE already there
+    int32_t n_q_rest;   // block mode: rows of heads 1.. when it differs from head 0's n_q (0: n_q)
     float scale;        // softmax scale (natural units)
     float scale_log2;   // scale * log2(e)
     // block mode

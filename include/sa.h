@@ -149,11 +149,12 @@ sa_status sa_build_block_mask(const sa_pattern *pattern, int64_t n_q, int64_t n_
  *   sparsity templates: near neighbours plus keys at a fixed step) --
  *   pattern causal, window_left = stride - 1, window_right = 0,
  *   stride_phase = stride - 1 and no other term, q_offset 0, n_q == n_kv a
- *   multiple of stride with n_q >= 3 * stride -- computed as three disjoint
- *   key sets per row: the local band through block lists, the strided keys
- *   as plain causal attention between strided views of the same tensors
- *   (one per head and key residue), and the last row; the later parts are
- *   merged into the first with log-sum-exp weights.  O must be float32 and
+ *   multiple of stride with n_q >= 3 * stride -- computed as two disjoint
+ *   key sets per row: the local band through block lists, and the strided
+ *   keys as plain causal attention between strided views of the same
+ *   tensors (one per head and key residue; residue 0's view also holds the
+ *   last row); the second part is merged into the first with log-sum-exp
+ *   weights.  O must be float32 and
  *   lse non-NULL; block_q, block_kv and the list pointers are ignored: the
  *   block lists of the parts are read from `workspace` (at least
  *   sa_attn_workspace_bytes bytes, 256-byte aligned), where
@@ -285,8 +286,8 @@ sa_status sa_select_blocks(const sa_select_args *args, void *stream);
 size_t sa_attn_workspace_bytes(const sa_attn_args *args);
 
 /*
- * sa_attn_strided_plan -- the block lists of SA_MODE_STRIDED's three parts
- * (band, residue views, last row) into args->workspace, built once for a
+ * sa_attn_strided_plan -- the block lists of SA_MODE_STRIDED's two parts
+ * (band, residue views) into args->workspace, built once for a
  * pattern and length and read by every later sa_attn_fwd in that mode.  Uses
  * mode (must be SA_MODE_STRIDED), pattern, n_q, n_kv, the K/V row strides
  * (for the offset limit), workspace and workspace_bytes of `args`; rejects
