@@ -307,6 +307,20 @@ def main() -> int:
     return 0
 
 
+def _sustained_us(fn, np, torch, settle=300, reps=50):
+    """Median of reps launches of fn (HIP events on the current stream) after settle
+    untimed ones: the rate once the GPU's clock has settled under sustained load."""
+    for _ in range(settle):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+
+
 def _bench_strided(sa, W, np, torch, dev, dev_bf16, reps=10):
     """The strided workload both ways: block lists of the whole pattern (every causal tile is
     live, since the strided term touches each one), and the local band plus residue views."""
@@ -338,6 +352,7 @@ def _bench_strided(sa, W, np, torch, dev, dev_bf16, reps=10):
         t[name] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e-3
     pairs = int(bl.live_pairs.item()) * cfg.B * cfg.H
     flop = 4.0 * cfg.d * pairs
+    split_sus = _sustained_us(ways["split"], np, torch)
     return {
         "workload": "causal strided, stride 128 + local band of 128, B=1 H=16 N=16384 d=64",
         "live_pairs": pairs,
@@ -345,6 +360,7 @@ def _bench_strided(sa, W, np, torch, dev, dev_bf16, reps=10):
         "blocks_tflops_over_live_pairs": round(flop / t["blocks"] / 1e12, 2),
         "split_us": round(t["split"] * 1e6, 1),
         "split_tflops_over_live_pairs": round(flop / t["split"] / 1e12, 2),
+        "split_us_median_sustained": round(split_sus, 1),
         "split_note": "one sa_attn_fwd call (SA_MODE_STRIDED) on a plan built once by sa_attn_strided_plan: "
                       "64x64 band tiles, then causal 64-row tiles per (head, key residue) view (residue 0's "
                       "view also holds the last row), merged by log-sum-exp in the kernel epilogue",
@@ -404,6 +420,7 @@ def _bench_blocks(sa, W, np, torch, dev, dev_bf16, cid, reps=50):
     torch.cuda.synchronize()
     tb = float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
     ta = float(np.median([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    ta_sus = _sustained_us(lambda: sa.attn_fwd(q, k, v, bl, out=o, lse=lse), np, torch)
     pairs = int(bl.live_pairs.item()) * cfg.B * cfg.H
     tiles = int(bl.kv_count.sum().item()) * cfg.B * cfg.H
     return {
@@ -413,6 +430,8 @@ def _bench_blocks(sa, W, np, torch, dev, dev_bf16, cid, reps=50):
         "attention_us_median": round(ta * 1e6, 2),
         "attention_tflops_over_live_pairs": round(4.0 * cfg.d * pairs / ta / 1e12, 2),
         "attention_tflops_over_live_tiles": round(4.0 * cfg.d * cfg.block * cfg.block * tiles / ta / 1e12, 2),
+        "attention_us_median_sustained": round(ta_sus, 2),
+        "sustained_note": "median of 50 launches after 300 untimed ones (settled clock)",
     }
 
 
