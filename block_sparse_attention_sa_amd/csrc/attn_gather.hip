@@ -45,7 +45,6 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg)
 }
 
 constexpr int kBlk = 128;  // keys per block of the online softmax
-constexpr int kQF = 4;     // score steps whose row loads are issued together
 constexpr int kVF = 4;     // value steps whose row loads are issued together
 constexpr int kPartItems = 1;  // (head, range, query) items per wave in the split form
 
@@ -87,16 +86,39 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
-// The query's bfloat16 pairs of the 32 columns [32*(lane % (D/32)), +32).
-template <int D>
-__device__ __forceinline__ void load_q2(const uint16_t* qrow, int lane, uint32_t (&q2)[16])
+// How the lanes of a wave read K rows for the scores: LQ lanes per row, each
+// taking PC pieces of 16 bytes, and QF steps of row loads issued together.
+//   packed: a lane's pieces are contiguous (lane s of a row reads bytes
+//           [s*PB, (s+1)*PB) with PB = 2*D/LQ), so one load instruction
+//           touches each row in LQ places;
+//   spread: piece x of lane s is bytes [16*(s + LQ*x), +16), so the LQ lanes
+//           of a row read 16*LQ contiguous bytes per instruction (a whole
+//           128-byte line at D = 128, LQ = 8).
+// The split form's waves share one key range in L2, and there the number of
+// lines an instruction touches sets the rate (spread, 8 lanes per row at
+// D = 128: 1,049 -> 816 us for 1024 queries x 16 heads x top-2048 over a
+// 64K context); the single pass, whose rows mostly miss L2, is faster packed.
+template <int D, int LQ_, bool SPREAD, int QF_>
+struct ScoreShape {
+    static constexpr int LQ = LQ_, QF = QF_;
+    static constexpr int PB = 2 * D / LQ, PC = PB / 16;
+    static_assert(PB % 16 == 0 && LQ >= 2 && 64 % LQ == 0, "score lane split");
+    __device__ static constexpr uint32_t off(int s, int x) { return SPREAD ? 16u * (s + LQ * x) : PB * s + 16u * x; }
+};
+template <int D> using ScorePacked = ScoreShape<D, D / 32, false, 4>;
+template <int D> using ScoreSpread = ScoreShape<D, D / 16, true, 8>;
+
+// The query's bfloat16 pairs that match this lane's K pieces: q2[4x + j] pairs
+// with word j of piece x.
+template <int D, class SS>
+__device__ __forceinline__ void load_q2(const uint16_t* qrow, int lane, uint32_t (&q2)[4 * SS::PC])
 {
-    const int qs = lane % (D / 32);
+    const int qs = lane % SS::LQ;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 32 * qs + 8 * i);
+    for (int x = 0; x < SS::PC; ++x) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(qrow) + SS::off(qs, x));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) q2[4 * i + j] = w[j];
+        for (int j = 0; j < 4; ++j) q2[4 * x + j] = w[j];
     }
 }
 
@@ -104,18 +126,19 @@ __device__ __forceinline__ void load_q2(const uint16_t* qrow, int lane, uint32_t
 // units, scale folded in), l (sum of exp2(s - m)) and acc (sum of
 // exp2(s - m) v over this lane's 8 columns [8*(lane % (D/8)), +8)).  With
 // `check`, entries outside [0, n_kv) are skipped.
-//   scores: D/32 lanes per key row, each a 64-byte slice, bf16 pair dot
-//           products, then a sum over the row's lanes;
+//   scores: SS::LQ lanes per key row, each PC pieces of 16 bytes (see
+//           ScoreShape), bf16 pair dot products, then a sum over the row's
+//           lanes;
 //   values: D/8 lanes per row, each 16 bytes; a lane group takes two keys
 //           per step, their values are interleaved into (key0, key1) pairs
 //           and one pair dot product with (p0, p1) adds both keys' terms.
-template <int D>
+template <int D, class SS>
 __device__ __forceinline__ void gather_online(const int32_t* keys, int n, bool check, int n_kv,
                                               const uint16_t* kg, uint32_t krow_b, const uint16_t* vg, uint32_t vrow_b,
-                                              const uint32_t (&q2)[16], float c, float* sc, uint32_t* ro, int lane,
+                                              const uint32_t (&q2)[4 * SS::PC], float c, float* sc, uint32_t* ro, int lane,
                                               float& m, float& l, float (&acc)[8])
 {
-    constexpr int LQ = D / 32, KQ = 64 / LQ;  // scores: lanes per row, rows per step
+    constexpr int LQ = SS::LQ, KQ = 64 / LQ, PC = SS::PC, kQF = SS::QF;  // scores: lanes per row, rows per step
     constexpr int QSTEPS = kBlk / KQ;
     constexpr int LPK = D / 8, GP = 64 / LPK;  // values: lanes per row, row groups
     constexpr int KPV = 2 * GP;                // keys per value step
@@ -146,40 +169,45 @@ __device__ __forceinline__ void gather_online(const int32_t* keys, int n, bool c
         float bmax = -INFINITY;
 #pragma unroll 1
         for (int g = 0; g < qlim; g += kQF) {
-            u32x4 w[kQF][4];
+            u32x4 w[kQF][PC];
             bool okk[kQF];
 #pragma unroll
             for (int i = 0; i < kQF; ++i) {
                 const uint32_t off = ro[(g + i) * KQ + qg];
                 okk[i] = (int32_t)off >= 0;
-                const char* row = reinterpret_cast<const char*>(kg) + (uint64_t)((off & 0x7FFFFFFFu) + 64u * qs);
+                const char* row = reinterpret_cast<const char*>(kg) + (uint64_t)(off & 0x7FFFFFFFu);
 #pragma unroll
-                for (int x = 0; x < 4; ++x) w[i][x] = *reinterpret_cast<const u32x4*>(row + 16 * x);
+                for (int x = 0; x < PC; ++x) w[i][x] = *reinterpret_cast<const u32x4*>(row + SS::off(qs, x));
             }
 #pragma unroll
             for (int i = 0; i < kQF; ++i) {
                 float d0 = 0.f, d1 = 0.f;
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
+                for (int x = 0; x < PC; ++x) {
                     d0 = dot2(w[i][x][0], q2[4 * x + 0], d0);
                     d1 = dot2(w[i][x][1], q2[4 * x + 1], d1);
                     d0 = dot2(w[i][x][2], q2[4 * x + 2], d0);
                     d1 = dot2(w[i][x][3], q2[4 * x + 3], d1);
                 }
                 float d = d0 + d1;
-                if (LQ == 4) {
+                if (LQ == 4 || LQ == 8) {
                     d = quad_sum(d);
+                    // 8 lanes per row: lanes 4..7 of the row's group add the
+                    // quad below theirs (row_ror 4); lanes 0..3 then hold no
+                    // row's score and stay out of the maximum
+                    if (LQ == 8) d += dpp<0x124>(d);
                 } else {
 #pragma unroll
                     for (int off = 1; off < LQ; off <<= 1) d += __shfl_xor(d, off, 64);
                 }
                 const float sv = okk[i] ? d * c : -INFINITY;
-                bmax = fmaxf(bmax, sv);
-                if (qs == 0) sc[(g + i) * KQ + qg] = sv;
+                bmax = fmaxf(bmax, LQ == 8 && qs < 4 ? -INFINITY : sv);
+                if (qs == (LQ == 8 ? 4 : 0)) sc[(g + i) * KQ + qg] = sv;
             }
         }
-        if (LQ == 4) {
-            // equal within quads already: fold the row's quads, then the rows
+        if (LQ == 4 || LQ == 8) {
+            // equal within quads already (or -inf in a whole quad): fold the
+            // row's quads, then the rows
             bmax = fmaxf(bmax, dpp<0x124>(bmax));
             bmax = fmaxf(bmax, dpp<0x128>(bmax));
             for (int off = 16; off < 64; off <<= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, off, 64));
@@ -262,10 +290,11 @@ __global__ void __launch_bounds__(kWaves * 64) attn_gather_kernel(AttnParams a)
     const int bh = (int)(item / a.n_q);
     const int b = bh / a.heads, h = bh % a.heads;
     const int sub = lane % LPK, kgrp = lane / LPK;
-    uint32_t q2[16];
-    load_q2<D>(a.q + b * a.q_sb + h * a.q_sh + (int64_t)t * a.q_sn, lane, q2);
+    typedef ScorePacked<D> SS;
+    uint32_t q2[4 * SS::PC];
+    load_q2<D, SS>(a.q + b * a.q_sb + h * a.q_sh + (int64_t)t * a.q_sn, lane, q2);
     float m, l, acc[8];
-    gather_online<D>(a.gidx + bh * a.g_bh_stride + (int64_t)t * a.topk, a.topk, true, a.n_kv,
+    gather_online<D, SS>(a.gidx + bh * a.g_bh_stride + (int64_t)t * a.topk, a.topk, true, a.n_kv,
                      a.k + b * a.k_sb + h * a.k_sh, (uint32_t)(2 * a.k_sn), a.v + b * a.v_sb + h * a.v_sh,
                      (uint32_t)(2 * a.v_sn), q2, a.scale_log2, sc_all[wave], ro_all[wave], lane, m, l, acc);
     if (kgrp == 0) {
@@ -436,10 +465,11 @@ __global__ void __launch_bounds__(kWaves * 64) gather_part_kernel(AttnParams a)
         const int64_t row = a.g_bh_stride == 0 ? (int64_t)t : (int64_t)bh * nq + t;
         const int32_t* offs = a.g_offs + row * (nch + 1);
         const int o0 = offs[rg], o1 = offs[rg + 1];
-        uint32_t q2[16];
-        load_q2<D>(a.q + b * a.q_sb + h * a.q_sh + (int64_t)t * a.q_sn, lane, q2);
+        typedef ScoreSpread<D> SS;
+        uint32_t q2[4 * SS::PC];
+        load_q2<D, SS>(a.q + b * a.q_sb + h * a.q_sh + (int64_t)t * a.q_sn, lane, q2);
         float m, l, acc[8];
-        gather_online<D>(a.g_lists + row * a.topk + o0, o1 - o0, false, a.n_kv, kg, (uint32_t)(2 * a.k_sn), vg,
+        gather_online<D, SS>(a.g_lists + row * a.topk + o0, o1 - o0, false, a.n_kv, kg, (uint32_t)(2 * a.k_sn), vg,
                          (uint32_t)(2 * a.v_sn), q2, a.scale_log2, sc_all[wave], ro_all[wave], lane, m, l, acc);
         const int64_t pidx = ((int64_t)bh * nq + t) * nch + rg;
         if (kgrp == 0) {
