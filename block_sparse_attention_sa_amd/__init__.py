@@ -410,7 +410,7 @@ def attn_workspace_bytes_strided(pattern, batch: int, heads: int, n: int, head_d
 def attn_workspace_bytes_blocks(blocks: BlockLists, batch: int, heads: int, head_dim: int) -> int:
     """Scratch bytes of block mode's long-row split for these lists (0 if it has none):
     without causality the query blocks of global tokens list every key block, and with
-    more than 16 key blocks they are walked in chunks by separate workgroups.  Touches
+    more than 8 key blocks they are walked in chunks by separate workgroups.  Touches
     no device."""
     a = _lib.SaAttnArgs()
     a.batch, a.heads, a.n_q, a.n_kv, a.head_dim = batch, heads, blocks.n_q, blocks.n_kv, head_dim

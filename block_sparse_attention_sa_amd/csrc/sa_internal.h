@@ -213,8 +213,12 @@ struct AttnParams {
 // Without causality a query row below global_tokens attends to every key, so
 // the blocks holding such rows list every key block; with more than
 // kSplitEntries key blocks they are split.  Returns split_q (0: none) and
-// the chunk count and size.
-constexpr int32_t kSplitEntries = 16;
+// the chunk count and size.  Chunks of 8 entries are about as long as the
+// other rows' lists of a BigBird-style pattern (window, global and random
+// blocks: 7-8 entries), so the dispatcher balances them with the rest; on
+// the BigBird-style workload chunks of 4, 6, 8, 16 and 32 entries measured
+// 150, 132, 124, 156 and 182 us.
+constexpr int32_t kSplitEntries = 8;
 inline int32_t long_row_split(int64_t causal, int64_t global_tokens, int64_t q_offset, int64_t n_q, int64_t nqb,
                               int64_t nkb, int64_t block_q, int32_t& chunks, int32_t& per_chunk)
 {

@@ -260,10 +260,10 @@ sa_status sa_select_blocks(const sa_select_args *args, void *stream);
  * block mode with a long-row split), 0 when it has none.
  *
  * Block mode, lists shared by every (b, h), pattern not causal with
- * global_tokens > 0 and more than 16 key blocks: a query row below
+ * global_tokens > 0 and more than 8 key blocks: a query row below
  * global_tokens attends to every key (glossary, section on common sparsity
  * patterns: global tokens attend to all), so the query blocks holding such
- * rows list every key block.  Each of those blocks is walked in chunks of 16
+ * rows list every key block.  Each of those blocks is walked in chunks of 8
  * list entries by separate workgroups, which write the chunk's normalised O
  * and LSE to the workspace ([batch*heads][blocks][chunks][block_q] rows of
  * head_dim floats, then one float per row); a second launch merges the

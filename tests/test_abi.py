@@ -237,7 +237,7 @@ def test_gather_workspace_size_and_errors():
 
 def test_block_long_row_split_workspace_size_and_errors():
     """Block mode without causality and with global tokens: the query blocks of global
-    rows list every key block and, past 16 key blocks, take the chunked form, whose
+    rows list every key block and, past 8 key blocks, take the chunked form, whose
     partial O rows and LSEs need scratch."""
     L = _lib.lib()
     up = lambda x: (x + 255) // 256 * 256
@@ -245,12 +245,12 @@ def test_block_long_row_split_workspace_size_and_errors():
     a = _args(batch=2, heads=3, n_q=1000, n_kv=2000, pattern=pat())
     for s in (a.q_strides, a.k_strides, a.v_strides, a.o_strides):
         s[:] = [1 << 24, 1 << 20, 64]
-    gq, chunks = 3, 2                                  # ceil(130 / 64) blocks; 32 key blocks in chunks of 16
+    gq, chunks = 3, 4                                  # ceil(130 / 64) blocks; 32 key blocks in chunks of 8
     slots = 2 * 3 * gq * chunks * 64
     need = L.sa_attn_workspace_bytes(ctypes.byref(a))
     assert need == up(slots * 64 * 4) + up(slots * 4)
     for kw in (dict(pattern=pat(causal=1)), dict(pattern=pat(global_tokens=0)), dict(per_head_lists=1),
-               dict(n_kv=1024), dict(pattern=pat(q_offset=130))):
+               dict(n_kv=512), dict(pattern=pat(q_offset=130))):
         assert L.sa_attn_workspace_bytes(ctypes.byref(_args(batch=2, heads=3, n_q=1000,
                                                             **{"n_kv": 2000, **kw}))) == 0, kw
     a.workspace, a.workspace_bytes = 1 << 20, need - 1

@@ -77,8 +77,8 @@ SPLIT_CASES = [(2048, 2048, 64, 64, 64, "f32", 0, 130), (1500, 1777, 128, 64, 12
 
 @pytest.mark.parametrize("n_q,n_kv,bq,bk,d,of,q_off,g", SPLIT_CASES)
 def test_long_row_split_global_tokens(n_q, n_kv, bq, bk, d, of, q_off, g):
-    """Without causality the query blocks of global tokens list every key block; past 16
-    key blocks they run as chunks of 16 list entries whose partial (O, LSE) are merged by
+    """Without causality the query blocks of global tokens list every key block; past 8
+    key blocks they run as chunks of 8 list entries whose partial (O, LSE) are merged by
     log-sum-exp.  Every row against the oracle, with the split and without it."""
     rng = np.random.default_rng(n_q + n_kv + bq + bk + d + q_off + g)
     q, k, v = _rand(rng, 2, 2, n_q, n_kv, d)

@@ -105,17 +105,16 @@ def test_bwd_config1_whole():
         _check(name, a, b, "config 1")
 
 
-def test_bwd_config2_full_size_two_heads():
+def test_bwd_config2_full_size_all_heads():
     """The glossary's worked pattern at full size (B=1, H=32, N=8192, d=128); every
-    row of two heads against the oracle."""
+    row of every head against the oracle."""
     cfg = W.attn_config(2)
     inp = W.attn_inputs(cfg)
     g = _rand(np.random.default_rng(42), cfg.B, cfg.H, cfg.N, cfg.d)
     pat = cfg.pattern.as_dict()
-    heads = [0, 31]
-    print("bwd config 2 full size", flush=True)
-    dq, dk, dv = _run(pat, inp["q"], inp["k"], inp["v"], g, cfg.block, cfg.block, heads=heads)
-    rq, rk, rv = oracle.attn_bwd(pat, inp["q"], inp["k"], inp["v"], g, heads=heads)
+    print("bwd config 2 full size, all heads", flush=True)
+    dq, dk, dv = _run(pat, inp["q"], inp["k"], inp["v"], g, cfg.block, cfg.block)
+    rq, rk, rv = oracle.attn_bwd(pat, inp["q"], inp["k"], inp["v"], g)
     for name, a, b in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         _check(name, a, b, "config 2")
 
