@@ -321,7 +321,7 @@ __global__ void __launch_bounds__(kWaves * 64) attn_gather_kernel(AttnParams a)
 // ---------------------------------------------------------------------------
 // Split form.  With the lists of all queries in hand, the work is regrouped
 // by key range so that the K and V rows a workgroup gathers come from one
-// 2 MB range per head, which the workgroups of one XCD share in its L2:
+// 4 MB range per head, which the workgroups of one XCD share in its L2:
 //   partition: every list is reordered by key range (list order kept inside
 //              a range) and the range starts are recorded;
 //   part:      one wave per (batch*head, range, query) attends to the keys

@@ -270,10 +270,10 @@ sa_status sa_select_blocks(const sa_select_args *args, void *stream);
  * chunks of a row with log-sum-exp weights into O and LSE.  The result is
  * the same softmax; only the order of the float32 sums differs.
  *
- * Gather mode over a long key range (n_kv above 2^21 / (4 * head_dim)
+ * Gather mode over a long key range (n_kv above 2^22 / (4 * head_dim)
  * keys, at most 256 ranges, batch * heads * ranges * n_q below 2^31) has a
  * split form: each key list is first partitioned by key range
- * (ranges of 2 MB of K and V per head), every range is then attended to
+ * (ranges of 4 MB of K and V per head), every range is then attended to
  * separately by workgroups that share it in one L2 cache, and the partial
  * results (running max, sum and unnormalised output per range) are merged.
  * The result is the same softmax; only the order of the float32 sums

@@ -221,7 +221,7 @@ def test_gather_workspace_size_and_errors():
     for s in (a.q_strides, a.k_strides, a.v_strides, a.o_strides):
         s[:] = [1 << 24, 1 << 24, 128]
     assert L.sa_attn_workspace_bytes(ctypes.byref(a)) == 0      # one key range: no split form
-    a.n_kv = 20000                                              # 5 ranges of 4096 keys
+    a.n_kv = 40000                                              # 5 ranges of 8192 keys
     need = L.sa_attn_workspace_bytes(ctypes.byref(a))
     rows, items, nch = 64, 64, 5
     up = lambda x: (x + 255) // 256 * 256

@@ -401,13 +401,13 @@ def test_config5_gather_all_rows():
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("per_head", [False, True])
 def test_gather_split_form(d, per_head):
-    """Key ranges of 2 MB of K+V per head: n_kv spans several ranges, so the
+    """Key ranges of 4 MB of K+V per head: n_kv spans several ranges, so the
     split form (partition, partial softmax per range, merge) runs; unsorted
     lists, duplicates, out-of-range entries, a list inside one range and an
     empty list are covered."""
     rng = np.random.default_rng(100 + d + per_head)
     B, H, n_q, k = 2, 2, 37, 300
-    n_kv = (3 << 21) // (4 * d) + 123           # three full ranges and a ragged tail
+    n_kv = (3 << 22) // (4 * d) + 123           # three full ranges and a ragged tail
     q, kk, v = _rbf(rng, B, H, n_q, d), _rbf(rng, B, H, n_kv, d), _rbf(rng, B, H, n_kv, d)
     nl = B * H if per_head else 1
     lists = rng.integers(0, n_kv, size=(nl, n_q, k)).astype(np.int32)  # unsorted, duplicates
@@ -434,17 +434,17 @@ def test_gather_split_form(d, per_head):
 
 
 def test_gather_split_many_ranges():
-    """More key ranges than the merge takes in one batch (41 ranges of 4,096
+    """More key ranges than the merge takes in one batch (41 ranges of 8,192
     keys at d = 128): rows whose maxima rise from batch to batch, a row with
     no key in the first batch, a row whose keys all sit in the last range and
     an empty row."""
     rng = np.random.default_rng(4242)
     B, H, n_q, k, d = 1, 2, 24, 400, 128
-    n_kv = 40 * 4096 + 77
+    n_kv = 40 * 8192 + 77
     q, kk, v = _rbf(rng, B, H, n_q, d), _rbf(rng, B, H, n_kv, d), _rbf(rng, B, H, n_kv, d)
     lists = rng.integers(0, n_kv, size=(n_q, k)).astype(np.int32)
-    lists[1] = rng.integers(20 * 4096, n_kv, size=k)        # nothing in the first sixteen ranges
-    lists[2] = rng.integers(40 * 4096, n_kv, size=k)        # the ragged last range only
+    lists[1] = rng.integers(20 * 8192, n_kv, size=k)        # nothing in the first sixteen ranges
+    lists[2] = rng.integers(40 * 8192, n_kv, size=k)        # the ragged last range only
     lists[3] = -1                                            # no key
     lists[4, : k // 2] = -1                                  # half padding
     assert sa.attn_workspace_bytes(B, H, n_q, n_kv, d, k) > 0
@@ -463,7 +463,7 @@ def test_gather_list_lengths_at_batch_edges(split):
     split form all keys of a list sit in one key range."""
     rng = np.random.default_rng(77 + split)
     d, B, H, k = 128, 1, 2, 300
-    n_kv = (2 << 21) // (4 * d) + 5 if split else 4096   # two ranges (split) or one short row
+    n_kv = (1 << 22) // (4 * d) + 5 if split else 4096   # two ranges (split) or one short row
     lengths = [1, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 130, 191, 192, 193, 255,
                256, 257, 300]
     n_q = len(lengths)
