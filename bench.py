@@ -81,7 +81,7 @@ def main() -> int:
     ap.add_argument("--no-select", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-other", action="store_true", help="skip the tiny and BigBird-style block workloads")
-    ap.add_argument("--only", choices=["dsa", "strided", "select", "bwd", "window128", "bigbird"],
+    ap.add_argument("--only", choices=["dsa", "strided", "select", "bwd", "window128", "bigbird", "dma_calib"],
                     help="time one secondary workload alone (for per-kernel profiles; prints only its object)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="the CPU oracle repeats whole passes over the workload until this much time has passed")
@@ -92,6 +92,9 @@ def main() -> int:
                     help="no GPU: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) of a run with --copy-calib-mib into the committed traffic figure")
     ap.add_argument("--calib-mib", type=int, default=256, help="size used with --copy-calib-mib")
+    ap.add_argument("--dma-calib-from", metavar="FETCH_CSV",
+                    help="no GPU: FETCH_SIZE factor of the attention kernel's own loads, from a rocprofv3 "
+                         "--pmc FETCH_SIZE counter_collection.csv of a run with --only dma_calib")
     ap.add_argument("--sustain-steps", type=int, default=300,
                     help="after the timed steps, run this many more steps untimed and then time 50 again "
                          "(the 'sustained' object: the shader clock settles after a few hundred steps of "
@@ -99,6 +102,8 @@ def main() -> int:
     args = ap.parse_args()
     if args.traffic_from:
         return _write_traffic(args.traffic_from[0], args.traffic_from[1], args.calib_mib)
+    if args.dma_calib_from:
+        return _dma_factor(args.dma_calib_from)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -145,6 +150,7 @@ def main() -> int:
             "bwd": lambda: _bench_bwd(sa, np, torch, dev, cfg, q, k, v, bl, out, lse, live_pairs, live_blocks),
             "window128": lambda: _bench_blocks(sa, W, np, torch, dev, dev_bf16, 1),
             "bigbird": lambda: _bench_blocks(sa, W, np, torch, dev, dev_bf16, 4),
+            "dma_calib": lambda: _dma_calib(sa, torch, dev, cfg, q, k, v, out, lse),
         }
         print(json.dumps({args.only: sections[args.only]()}), flush=True)
         return 0
@@ -574,6 +580,46 @@ def _counter_means(path, counter):
             sums[k] = sums.get(k, 0.0) + float(r["Counter_Value"])
             counts[k] = counts.get(k, 0) + 1
     return {k: (sums[k] / counts[k], counts[k]) for k in sums}
+
+
+DMA_CALIB_LAUNCHES = 5
+
+
+def _dma_calib(sa, torch, dev, cfg, q, k, v, out, lse):
+    """The headline kernel on a block-diagonal pattern at the headline shape: each
+    query block lists only its own key block, so every K and V tile is copied into
+    LDS (LDS-DMA) by exactly one workgroup and Q is read once.  A FETCH_SIZE pass
+    over this run gives the counter's factor for the kernel's own loads."""
+    pat = dict(causal=1, window_left=0, window_right=0)
+    bl = sa.build_block_mask(pat, cfg.N, cfg.N, cfg.block, cfg.block, device=dev)
+    torch.cuda.synchronize()
+    assert int(bl.kv_count.max()) == 1 and int(bl.kv_count.min()) == 1
+    for _ in range(DMA_CALIB_LAUNCHES):
+        sa.attn_fwd(q, k, v, bl, out=out, lse=lse)
+    torch.cuda.synchronize()
+    tensor = cfg.B * cfg.H * cfg.N * cfg.d * 2
+    return {"workload": "block-diagonal lists at B=1 H=32 N=8192 d=128, 128x128 blocks", "launches":
+            DMA_CALIB_LAUNCHES, "q_bytes": tensor, "kv_bytes": 2 * tensor}
+
+
+def _dma_factor(fetch_csv):
+    """Bytes the block-diagonal launch must read (Q, K and V once each) per FETCH_SIZE
+    KiB, for each of its dispatches."""
+    import csv
+    per = {}
+    with open(fetch_csv) as f:
+        for r in csv.DictReader(f):
+            if "attn_block_kernel<128, 128, 128" in r["Kernel_Name"] and r["Counter_Name"] == "FETCH_SIZE":
+                per[int(r["Dispatch_Id"])] = per.get(int(r["Dispatch_Id"]), 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit("no attention dispatches in " + fetch_csv)
+    kib = [per[d] for d in sorted(per)]
+    tensor = 1 * 32 * 8192 * 128 * 2
+    need = 3 * tensor
+    out = {"dispatches": len(kib), "fetch_kib_per_dispatch": [round(x, 1) for x in kib],
+           "bytes_read_once": need, "factor_per_dispatch": [round(need / (x * 1024.0), 4) for x in kib]}
+    print(json.dumps(out))
+    return 0
 
 
 def _write_traffic(fetch_csv, write_csv, calib_mib):
