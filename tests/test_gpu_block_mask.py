@@ -71,8 +71,8 @@ def test_repeat_is_identical():
 
 @pytest.mark.parametrize("seed", range(4))
 def test_long_rows(seed):
-    """Rows of more than 512 key blocks (several count workgroups per query block
-    and a compaction over a long row)."""
+    """Rows of more than 512 key blocks: many count workgroups per query block, and
+    a compaction in which each of the 256 threads owns several cells."""
     rng = np.random.default_rng(900 + seed)
     n_q, n_kv, bq, bk = int(rng.integers(40, 130)), int(rng.integers(16500, 21000)), 64, 32
     assert (n_kv + bk - 1) // bk > 512
