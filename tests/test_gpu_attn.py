@@ -72,7 +72,15 @@ def test_score_ranges_across_tiles(profile, d, bq, bk):
 
 
 SPLIT_CASES = [(2048, 2048, 64, 64, 64, "f32", 0, 130), (1500, 1777, 128, 64, 128, "bf16", 0, 200),
-               (1333, 2200, 64, 128, 64, "f32", 40, 100), (2100, 2100, 128, 128, 128, "f32", 0, 300)]
+               (1333, 2200, 64, 128, 64, "f32", 40, 100), (2100, 2100, 128, 128, 128, "f32", 0, 300),
+               (600, 560, 64, 64, 128, "f32", 0, 70), (700, 1100, 128, 128, 64, "bf16", 5, 150)]
+
+
+def test_long_row_split_threshold():
+    """Nine key blocks split (chunks of 8 and 1 list entries), eight do not."""
+    pat = dict(causal=0, global_tokens=70, unit=64, unit_window=1)
+    assert sa.attn_workspace_bytes_blocks(sa.build_block_mask(pat, 600, 560, 64, 64), 2, 2, 128) > 0
+    assert sa.attn_workspace_bytes_blocks(sa.build_block_mask(pat, 600, 512, 64, 64), 2, 2, 128) == 0
 
 
 @pytest.mark.parametrize("n_q,n_kv,bq,bk,d,of,q_off,g", SPLIT_CASES)
