@@ -156,9 +156,18 @@ compact_kernel(int32_t n_q, int32_t n_kv, int32_t bq, int32_t bk, int32_t nkb, i
         kv_partial[rowbase + e] = 0;
     }
     if (t == 0) kv_count[i] = total_live;
-    // wave reduction, one atomic per wave (integers: exact in any order)
+    // wave sums, then one atomic per workgroup (integers: exact in any order);
+    // every wave's atomic on the one counter would be serialised
+    __shared__ long long wpairs[kThreads / 64];
     for (int off = 32; off > 0; off >>= 1) pairs += __shfl_down(pairs, off, 64);
-    if (lane == 0 && pairs) atomicAdd(live_pairs, (unsigned long long)pairs);
+    if (lane == 0) wpairs[w] = pairs;
+    __syncthreads();
+    if (t == 0) {
+        long long sum = 0;
+#pragma unroll
+        for (int k = 0; k < kThreads / 64; ++k) sum += wpairs[k];
+        if (sum) atomicAdd(live_pairs, (unsigned long long)sum);
+    }
 }
 
 }  // namespace
