@@ -20,10 +20,12 @@
 // of the first: lane half h of an output tile holds rows 8m + 4h + c
 // (m, c < 4), so the k-slots 8h .. 8h+7 of chunk ks carry rows
 // 16ks + 4h + {0..3} and 16ks + 8 + 4h + {0..3}, and the other operand is
-// read with the same order from a transposed LDS copy (two 8-byte reads).
+// read with the same order: at head_dim 128 by transposing 16-bit reads
+// (ds_read_b64_tr_b16) of the one, swizzled row-major LDS copy, at head_dim
+// 64 from a second, transposed copy (two 8-byte reads).
 //   * bwd_dq_kernel: a wave owns 32 queries (Q and dO in registers) and walks
-//     the live key tiles 32 keys at a time; the workgroup stages K (row-major
-//     and transposed) and V in LDS, double-buffered, the next tile's loads in
+//     the live key tiles 32 keys at a time; the workgroup stages K and V in
+//     LDS, double-buffered, the next tile's loads in
 //     flight while the current one is computed, one barrier per step.  It
 //     also forms D = rowsum(dO * O) for its queries.
 //   * bwd_dkdv_kernel: two waves own each 32 keys (K, and V for dP, in
@@ -53,6 +55,61 @@ constexpr int kTS = 36;
 __device__ __forceinline__ bf16x8 lds8(const uint16_t* p)
 {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// At head_dim 128 the staged tiles are kept once, row-major and unpadded,
+// and the transposed operands are read from them with transposing 16-bit
+// reads (ds_read_b64_tr_b16) instead of from a second, transposed copy:
+// 16-byte chunk c of row r is stored at
+// chunk c ^ tswz(r).  The swizzle is a bijection on a row's chunks and takes
+// distinct values on any 16 consecutive rows (row reads: 16 lanes, one chunk,
+// 16 rows); on four rows from a multiple of four it sends four consecutive
+// chunks to sixteen distinct ones (transposing reads: 32 lanes, 4 rows x 4
+// chunks), so both reads hit distinct banks.
+template <int D>
+__device__ __forceinline__ int tswz(int r)
+{
+    return D == 128 ? ((r & 15) ^ ((r & 3) << 2)) : (((r >> 1) & 7) ^ (((r >> 1) & 1) << 2));
+}
+// Byte offsets of a lane's reads.  Row reads (A operand, lane row l32,
+// chunks 2c + hh): chunk (2c + hh) ^ tswz(l32) = (hh ^ tswz(l32)) ^ 2c, so
+// the read of chunk pair c is at row_off ^ (c << 5).  Transposing reads (rows
+// 16ks + rof and 16ks + rof + 8, 8 bytes at column 32db + cof): the swizzle of
+// those rows does not depend on ks (rof < 8), and chunk 4db + cof/8 XOR the
+// swizzle is (cof/8 ^ swizzle) ^ 4db, so the read is at
+// 16ks rows + (tr_off[h] ^ (db << 6)).
+template <int D>
+struct LaneOffs {
+    int row_off, tr_off0, tr_off1;
+    __device__ __forceinline__ LaneOffs(int lane)
+    {
+        const int l32 = lane & 31, hh = lane >> 5;
+        const int rof = 4 * (lane >> 5) + ((lane & 15) >> 2), cof = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        row_off = l32 * 2 * D + ((hh ^ tswz<D>(l32)) << 4);
+        tr_off0 = rof * 2 * D + (((cof >> 3) ^ tswz<D>(rof)) << 4) + 2 * (cof & 7);
+        tr_off1 = (rof + 8) * 2 * D + (((cof >> 3) ^ tswz<D>(rof + 8)) << 4) + 2 * (cof & 7);
+    }
+    // keep the XORed addresses from being hoisted out of the step loop (they
+    // would take a register each)
+    __device__ __forceinline__ void opaque() { asm volatile("" : "+v"(row_off), "+v"(tr_off0), "+v"(tr_off1)); }
+};
+__device__ __forceinline__ bf16x8 row_op(const uint16_t* t, int off)
+{
+    return lds8(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(t) + off));
+}
+// B operand with the permuted contraction order (rows 16ks + 4hh .. + 3 and
+// 16ks + 8 + 4hh .. + 3 of column 32db + l32) by transposing 16-bit reads of
+// the row-major tile
+template <int D>
+__device__ __forceinline__ bf16x8 trr_op(const uint16_t* t, int ks, int db, const LaneOffs<D>& o)
+{
+    const char* b = reinterpret_cast<const char*>(t + 16 * ks * D);
+    const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(b + (o.tr_off0 ^ (db << 6))));
+    const bf16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(b + (o.tr_off1 ^ (db << 6))));
+    return bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
 }
 
 // B operand with the permuted contraction order: rows r0 .. r0+3 and
@@ -105,6 +162,18 @@ struct Stage32 {
                 if (r < n) r0[i] = *reinterpret_cast<const u32x4*>(src + r * D + 8 * ch);
                 if (r + 1 < n) r1[i] = *reinterpret_cast<const u32x4*>(src + (r + 1) * D + 8 * ch);
             }
+        }
+    }
+    // the unpadded, swizzled row-major copy only
+    __device__ __forceinline__ void store_swz(uint16_t* t, int tid) const
+    {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int it = tid + i * NT;
+            if (it >= ITEMS) continue;
+            const int p = it & 15, ch = it >> 4;
+            *reinterpret_cast<u32x4*>(t + (2 * p) * D + ((ch ^ tswz<D>(2 * p)) << 3)) = r0[i];
+            *reinterpret_cast<u32x4*>(t + (2 * p + 1) * D + ((ch ^ tswz<D>(2 * p + 1)) << 3)) = r1[i];
         }
     }
     __device__ __forceinline__ void store(uint16_t* rm, uint16_t* tr, int tid) const
@@ -224,10 +293,14 @@ __global__ void __launch_bounds__(BQ * 2, 2)
 bwd_dq_kernel(BwdParams a)
 {
     constexpr int NT = BQ * 2, NDC = D / 16, NDB = D / 32, RS = D + 8, SUB = BK / 32;
-    using KStage = Stage32<D, NT, true>;
+    // head_dim 128: K once, swizzled, Kᵀ operands by transposing reads; head_dim
+    // 64: padded row-major and transposed copies (the swizzled form measured
+    // slower there on the BigBird-style workload)
+    constexpr bool SW = D == 128;
+    using KStage = Stage32<D, NT, !SW>;
     using VStage = Stage32<D, NT, false>;
-    __shared__ __attribute__((aligned(16))) uint16_t k_rm[2][32 * RS];
-    __shared__ __attribute__((aligned(16))) uint16_t k_tr[2][D * kTS];
+    __shared__ __attribute__((aligned(16))) uint16_t k_rm[2][32 * (SW ? D : RS)];
+    __shared__ __attribute__((aligned(16))) uint16_t k_tr[2][SW ? 8 : D * kTS];
     __shared__ __attribute__((aligned(16))) uint16_t v_rm[2][32 * RS];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
     const int BH = a.batch * a.heads;
@@ -244,6 +317,7 @@ bwd_dq_kernel(BwdParams a)
         lrow = qb;
     }
     const int q = qb * BQ + 32 * w + l32;  // this lane's query row
+    LaneOffs<D> lo(lane);
     const bool q_ok = q < a.n_q;
     const int64_t qrow = (int64_t)bh * a.n_q + q;
     // B operands Q^T and dO^T: lane holds row q, dims 16s + 8hh .. + 7; and
@@ -314,13 +388,15 @@ bwd_dq_kernel(BwdParams a)
     };
     auto put = [&](const Fetched& f, int s, int b) {
         if (step_k0(s) >= 0) {
-            f.k.store(k_rm[b], k_tr[b], tid);
+            if constexpr (SW) f.k.store_swz(k_rm[b], tid);
+            else f.k.store(k_rm[b], k_tr[b], tid);
             f.v.store(v_rm[b], nullptr, tid);
         }
     };
     auto compute = [&](int s, int b) {
         const int k0 = step_k0(s);
         if (k0 >= 0) {
+            if constexpr (SW) lo.opaque();
             // S^T = K Q^T and dP^T = V dO^T: lane = query, element i = key 8(i/4) + 4hh + i%4
             f32x16 st, dpt;
 #pragma unroll
@@ -329,7 +405,7 @@ bwd_dq_kernel(BwdParams a)
             const uint16_t* vr = v_rm[b] + l32 * RS + 8 * hh;
 #pragma unroll
             for (int c = 0; c < NDC; ++c) {
-                st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds8(kr + 16 * c), qop[c], st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_32x32x16_bf16((SW ? row_op(k_rm[b], lo.row_off ^ (c << 5)) : lds8(kr + 16 * c)), qop[c], st, 0, 0, 0);
                 dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds8(vr + 16 * c), gop[c], dpt, 0, 0, 0);
             }
             uint32_t mbits = 0xFFFFFFFFu;
@@ -345,10 +421,10 @@ bwd_dq_kernel(BwdParams a)
             const bf16x8 a0 = pack8(ds, 0), a1 = pack8(ds, 8);
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, tr_op(k_tr[b], 32 * db + l32, 4 * hh), dq[db],
-                                                                 0, 0, 0);
-                dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, tr_op(k_tr[b], 32 * db + l32, 16 + 4 * hh),
-                                                                 dq[db], 0, 0, 0);
+                const bf16x8 b0 = SW ? trr_op<D>(k_rm[b], 0, db, lo) : tr_op(k_tr[b], 32 * db + l32, 4 * hh);
+                const bf16x8 b1 = SW ? trr_op<D>(k_rm[b], 1, db, lo) : tr_op(k_tr[b], 32 * db + l32, 16 + 4 * hh);
+                dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, dq[db], 0, 0, 0);
+                dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, dq[db], 0, 0, 0);
             }
         }
     };
@@ -412,11 +488,14 @@ bwd_dkdv_kernel(BwdParams a)
     // dK waves' step, the dV waves' step, the next step being written).
     constexpr int NT = BK * 4, NW = BK / 32, NDC = D / 16, NDB = D / 32, RS = D + 8, SUB = BQ / 32;
     // the dV waves stage the Q tile, the dK waves the dO tile
-    using QStage = Stage32<D, NT / 2, true>;
-    __shared__ __attribute__((aligned(16))) uint16_t q_rm[3][32 * RS];
-    __shared__ __attribute__((aligned(16))) uint16_t q_tr[3][D * kTS];
-    __shared__ __attribute__((aligned(16))) uint16_t g_rm[3][32 * RS];
-    __shared__ __attribute__((aligned(16))) uint16_t g_tr[3][D * kTS];
+    // head_dim 128: each tile once, swizzled, transposed operands by
+    // transposing reads (as in bwd_dq_kernel)
+    constexpr bool SW = D == 128;
+    using QStage = Stage32<D, NT / 2, !SW>;
+    __shared__ __attribute__((aligned(16))) uint16_t q_rm[3][32 * (SW ? D : RS)];
+    __shared__ __attribute__((aligned(16))) uint16_t q_tr[3][SW ? 8 : D * kTS];
+    __shared__ __attribute__((aligned(16))) uint16_t g_rm[3][32 * (SW ? D : RS)];
+    __shared__ __attribute__((aligned(16))) uint16_t g_tr[3][SW ? 8 : D * kTS];
     __shared__ __attribute__((aligned(16))) float lse_s[3][32];
     __shared__ __attribute__((aligned(16))) float dsum_s[3][32];
     __shared__ __attribute__((aligned(16))) uint32_t mw_s[3][NW][32];
@@ -438,6 +517,7 @@ bwd_dkdv_kernel(BwdParams a)
         lrow = kb;
     }
     const int kbase = kb * BK + 32 * grp;  // this wave's keys
+    LaneOffs<D> lo(lane);
     const int kv = kbase + l32;            // this lane's key row
     const bool k_ok = kv < a.n_kv;
     const int64_t krow = (int64_t)bh * a.n_kv + kv;
@@ -516,7 +596,8 @@ bwd_dkdv_kernel(BwdParams a)
         }
     };
     auto put = [&](const Fetched& f, int s, int buf) {
-        if (dk_wave) f.x.store(g_rm[buf], g_tr[buf], stid);
+        if constexpr (SW) f.x.store_swz(dk_wave ? g_rm[buf] : q_rm[buf], stid);
+        else if (dk_wave) f.x.store(g_rm[buf], g_tr[buf], stid);
         else f.x.store(q_rm[buf], q_tr[buf], stid);
         if ((unsigned)(tid - NT / 2) < 32u) {
             // a row without keys (LSE = -inf) or past n_q has no pair
@@ -533,25 +614,28 @@ bwd_dkdv_kernel(BwdParams a)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[i] = 0.f;
         const uint16_t* xr = xrm + l32 * RS + 8 * hh;
+        if constexpr (SW) lo.opaque();
+        auto x_op = [&](int c) { return SW ? row_op(xrm, lo.row_off ^ (c << 5)) : lds8(xr + 16 * c); };
         // LDS operands are requested two k-steps ahead (a ring of three)
         bf16x8 xa[3];
-        xa[0] = lds8(xr);
-        xa[1] = lds8(xr + 16);
+        xa[0] = x_op(0);
+        xa[1] = x_op(1);
 #pragma unroll
         for (int c = 0; c < NDC; ++c) {
-            if (c + 2 < NDC) xa[(c + 2) % 3] = lds8(xr + 16 * (c + 2));
+            if (c + 2 < NDC) xa[(c + 2) % 3] = x_op(c + 2);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[c % 3], yop[c], acc, 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
     // acc (keys x d) += X^T (keys x queries) Y with X from the softmax and Y
-    // read transposed from LDS; step it = ks * NDB + db reads rows 16ks + 4hh..
-    // of dim 32db + l32
+    // read transposed from LDS (ytr: the transposed copy, or at head_dim 128
+    // the swizzled row-major tile); step it = ks * NDB + db reads rows
+    // 16ks + 4hh.. of dim 32db + l32
     auto accumulate = [&](const uint16_t* ytr, const f32x16& x, f32x16* acc) {
         bf16x8 yb[3];
         auto ld_b = [&](int slot, int it) {
             const int ks = it / NDB, dim = 32 * (it % NDB) + l32;
-            yb[slot] = tr_op(ytr, dim, 16 * ks + 4 * hh);
+            yb[slot] = SW ? trr_op<D>(ytr, ks, it % NDB, lo) : tr_op(ytr, dim, 16 * ks + 4 * hh);
         };
         ld_b(0, 0);
         ld_b(1, 1);
@@ -635,7 +719,7 @@ bwd_dkdv_kernel(BwdParams a)
 #pragma unroll
             for (int m = 0; m < 4; ++m)
                 pmine[(j & 1) * PB + 64 * m] = f32x4{pv[4 * m], pv[4 * m + 1], pv[4 * m + 2], pv[4 * m + 3]};
-            accumulate(g_tr[b], pv, dv);
+            accumulate(SW ? g_rm[b] : g_tr[b], pv, dv);
         });
         write(a.dv, dv, 1.f);
     } else {
@@ -656,7 +740,7 @@ bwd_dkdv_kernel(BwdParams a)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) ds[4 * m + c] = p4[c] * (dp[4 * m + c] - d4[c]);
             }
-            accumulate(q_tr[b], ds, dk);
+            accumulate(SW ? q_rm[b] : q_tr[b], ds, dk);
         });
         write(a.dk, dk, a.scale);
     }
